@@ -1,0 +1,149 @@
+"""Seeded synthetic inputs for the gated-delta-rule workloads.
+
+This module only draws random tensors and shapes them; it holds none of the
+method's arithmetic, so both the CPU oracle and the GPU library can consume
+its output.  Every tensor is drawn in fp32 as N(0, 1) from a seeded
+``torch.Generator``, transformed, then cast once to its storage dtype.  Draw
+order is fixed: q, k, v, beta (or erase gate b), write gate w, log-decay g,
+initial state.
+
+Transforms (the workload descriptions):
+  q, k  : x / ||x||_2 over the key dimension (per head, per token)
+  v     : x
+  beta, b, w : sigmoid(x)            (values in (0, 1))
+  g     : -softplus(x) = log(alpha)  (alpha = exp(-softplus(x)) in (0, 1))
+  state : 0.02 * x                   (decode workload; zeros otherwise)
+
+The gate tensors are handed over in log space (g = log alpha), see the design doc.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class ChunkConfig:
+    name: str
+    B: int
+    T: int
+    Hk: int
+    Hv: int
+    dk: int
+    dv: int
+    channel: bool          # GDN-2 channel gates (b, w, g per channel) vs scalar beta/g
+    io_dtype: torch.dtype  # q, k, v, o
+    gate_dtype: torch.dtype
+    seed: int
+    state_std: float = 0.0  # 0 -> S0 = 0
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    N: int
+    Hk: int
+    Hv: int
+    dk: int
+    dv: int
+    channel: bool
+    io_dtype: torch.dtype
+    gate_dtype: torch.dtype
+    seed: int
+    state_std: float = 0.02
+
+
+# The five workloads.  Index = seed.
+CONFIGS = {
+    "gdn1_fp32_small": ChunkConfig("gdn1_fp32_small", B=1, T=256, Hk=2, Hv=2, dk=64, dv=64,
+                                   channel=False, io_dtype=torch.float32,
+                                   gate_dtype=torch.float32, seed=1),
+    "gdn1_bf16_train": ChunkConfig("gdn1_bf16_train", B=8, T=4096, Hk=16, Hv=16, dk=128, dv=128,
+                                   channel=False, io_dtype=torch.bfloat16,
+                                   gate_dtype=torch.bfloat16, seed=2),
+    "gdn2_bf16_train": ChunkConfig("gdn2_bf16_train", B=8, T=4096, Hk=16, Hv=16, dk=128, dv=128,
+                                   channel=True, io_dtype=torch.bfloat16,
+                                   gate_dtype=torch.bfloat16, seed=3),
+    "gdn1_grouped_long": ChunkConfig("gdn1_grouped_long", B=1, T=32768, Hk=16, Hv=128, dk=128,
+                                     dv=128, channel=False, io_dtype=torch.bfloat16,
+                                     gate_dtype=torch.bfloat16, seed=4),
+    "gdn2_decode": DecodeConfig("gdn2_decode", N=256, Hk=16, Hv=128, dk=128, dv=128,
+                                channel=True, io_dtype=torch.bfloat16,
+                                gate_dtype=torch.bfloat16, seed=5),
+}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn(shape, gen, device):
+    return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+
+def _unit(x):
+    return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+
+
+def chunk_inputs(cfg: ChunkConfig, *, device="cpu", seed=None, T=None, B=None,
+                 state_std=None):
+    """Inputs of a chunk-forward workload as a dict of tensors on ``device``.
+
+    Keys: q, k, v, beta_or_b, w (None in scalar mode), g, state_in (None when
+    the initial state is zero).  ``T``, ``B``, ``seed`` and ``state_std``
+    override the configuration (used for parity cases at reduced size).
+    """
+    B = cfg.B if B is None else B
+    T = cfg.T if T is None else T
+    seed = cfg.seed if seed is None else seed
+    state_std = cfg.state_std if state_std is None else state_std
+    gen = _gen(seed, device)
+    q = _unit(_randn((B, T, cfg.Hk, cfg.dk), gen, device)).to(cfg.io_dtype)
+    k = _unit(_randn((B, T, cfg.Hk, cfg.dk), gen, device)).to(cfg.io_dtype)
+    v = _randn((B, T, cfg.Hv, cfg.dv), gen, device).to(cfg.io_dtype)
+    if cfg.channel:
+        b = torch.sigmoid(_randn((B, T, cfg.Hv, cfg.dk), gen, device)).to(cfg.gate_dtype)
+        w = torch.sigmoid(_randn((B, T, cfg.Hv, cfg.dv), gen, device)).to(cfg.gate_dtype)
+        g = (-torch.nn.functional.softplus(_randn((B, T, cfg.Hv, cfg.dk), gen, device))
+             ).to(cfg.gate_dtype)
+    else:
+        b = torch.sigmoid(_randn((B, T, cfg.Hv), gen, device)).to(cfg.gate_dtype)
+        w = None
+        g = (-torch.nn.functional.softplus(_randn((B, T, cfg.Hv), gen, device))
+             ).to(cfg.gate_dtype)
+    s0 = None
+    if state_std:
+        s0 = (state_std * _randn((B, cfg.Hv, cfg.dk, cfg.dv), gen, device)).contiguous()
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), beta_or_b=b.contiguous(),
+                w=None if w is None else w.contiguous(), g=g.contiguous(), state_in=s0)
+
+
+def decode_inputs(cfg: DecodeConfig, *, device="cpu", seed=None, N=None, Hv=None, Hk=None):
+    """Inputs of a decode step as a dict: q, k, v, beta_or_b, w, g, state."""
+    N = cfg.N if N is None else N
+    Hv = cfg.Hv if Hv is None else Hv
+    Hk = cfg.Hk if Hk is None else Hk
+    seed = cfg.seed if seed is None else seed
+    gen = _gen(seed, device)
+    q = _unit(_randn((N, Hk, cfg.dk), gen, device)).to(cfg.io_dtype)
+    k = _unit(_randn((N, Hk, cfg.dk), gen, device)).to(cfg.io_dtype)
+    v = _randn((N, Hv, cfg.dv), gen, device).to(cfg.io_dtype)
+    if cfg.channel:
+        b = torch.sigmoid(_randn((N, Hv, cfg.dk), gen, device)).to(cfg.gate_dtype)
+        w = torch.sigmoid(_randn((N, Hv, cfg.dv), gen, device)).to(cfg.gate_dtype)
+        g = (-torch.nn.functional.softplus(_randn((N, Hv, cfg.dk), gen, device))
+             ).to(cfg.gate_dtype)
+    else:
+        b = torch.sigmoid(_randn((N, Hv), gen, device)).to(cfg.gate_dtype)
+        w = None
+        g = (-torch.nn.functional.softplus(_randn((N, Hv), gen, device))).to(cfg.gate_dtype)
+    state = (cfg.state_std * _randn((N, Hv, cfg.dk, cfg.dv), gen, device)).contiguous()
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), beta_or_b=b.contiguous(),
+                w=None if w is None else w.contiguous(), g=g.contiguous(), state=state)
