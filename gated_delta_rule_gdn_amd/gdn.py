@@ -1,0 +1,180 @@
+"""ctypes binding of libgdn.so (the C ABI in include/gdn.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, turned into raw device pointers and handed to the library with the
+current HIP stream.  Every step of the computation runs in the library's
+kernels; there is no fallback of any kind.  If libgdn.so is missing the import
+of this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+GDN_F32, GDN_BF16 = 0, 1
+GDN_GATES_SCALAR, GDN_GATES_CHANNEL = 0, 1
+ABI_VERSION = 1
+
+
+class GdnFwdDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
+                ("gate_mode", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class GdnDecodeDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64),
+                ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
+                ("gate_mode", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_gdn_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.gdn_chunk_fwd.argtypes = [ctypes.POINTER(GdnFwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_abi_version.restype = ctypes.c_int
+    if lib.gdn_abi_version() != ABI_VERSION:
+        raise ImportError("libgdn.so ABI version mismatch")
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.gdn_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return lib.gdn_abi_version()
+
+
+_DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(t, name, shape=None, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def gdn_chunk_fwd(q, k, v, beta_or_b, w=None, g=None, state_in=None, state_out=None, o=None,
+                  scale: float = 1.0, chunk: int = 64, stream=None):
+    """Chunkwise forward (see include/gdn.h).  Returns (o, state_out).
+
+    q, k [B,T,Hk,dk]; v [B,T,Hv,dv]; beta_or_b [B,T,Hv] (scalar gates) or
+    [B,T,Hv,dk] (channel gates, then w [B,T,Hv,dv] is required); g like
+    beta_or_b or None; state_in/state_out [B,Hv,dk,dv] fp32 or None.  o is
+    allocated when not given.
+    """
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    io = q.dtype
+    if io not in _DT:
+        raise ValueError("q must be float32 or bfloat16")
+    gdt = beta_or_b.dtype
+    channel = w is not None
+    gshape = (B, T, Hv, dk) if channel else (B, T, Hv)
+    _check(q, "q", (B, T, Hk, dk), io)
+    _check(k, "k", (B, T, Hk, dk), io)
+    _check(v, "v", (B, T, Hv, dv), io)
+    _check(beta_or_b, "beta_or_b", gshape, gdt)
+    _check(w, "w", (B, T, Hv, dv), gdt)
+    _check(g, "g", gshape, gdt)
+    _check(state_in, "state_in", (B, Hv, dk, dv), torch.float32)
+    _check(state_out, "state_out", (B, Hv, dk, dv), torch.float32)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=io, device=q.device)
+    _check(o, "o", (B, T, Hv, dv), io)
+    if gdt not in _DT:
+        raise ValueError("gates must be float32 or bfloat16")
+    desc = GdnFwdDesc(B, T, Hk, Hv, dk, dv, _DT[io], _DT[gdt],
+                      GDN_GATES_CHANNEL if channel else GDN_GATES_SCALAR, chunk, float(scale))
+    st = lib.gdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b),
+                           _ptr(w), _ptr(g), _ptr(state_in), _ptr(state_out), _ptr(o),
+                           _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_fwd")
+    return o, state_out
+
+
+def gdn_decode_step(q, k, v, beta_or_b, state, w=None, g=None, o=None, scale: float = 1.0,
+                    stream=None):
+    """One decode step, state updated in place (see include/gdn.h).  Returns o.
+
+    q, k [N,Hk,dk]; v [N,Hv,dv]; beta_or_b [N,Hv] or [N,Hv,dk]; w [N,Hv,dv]
+    or None; g like beta_or_b or None; state [N,Hv,dk,dv] fp32.
+    """
+    N, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    io = q.dtype
+    if io not in _DT:
+        raise ValueError("q must be float32 or bfloat16")
+    gdt = beta_or_b.dtype
+    channel = w is not None
+    gshape = (N, Hv, dk) if channel else (N, Hv)
+    _check(q, "q", (N, Hk, dk), io)
+    _check(k, "k", (N, Hk, dk), io)
+    _check(v, "v", (N, Hv, dv), io)
+    _check(beta_or_b, "beta_or_b", gshape, gdt)
+    _check(w, "w", (N, Hv, dv), gdt)
+    _check(g, "g", gshape, gdt)
+    _check(state, "state", (N, Hv, dk, dv), torch.float32)
+    if o is None:
+        o = torch.empty((N, Hv, dv), dtype=io, device=q.device)
+    _check(o, "o", (N, Hv, dv), io)
+    if gdt not in _DT:
+        raise ValueError("gates must be float32 or bfloat16")
+    desc = GdnDecodeDesc(N, Hk, Hv, dk, dv, _DT[io], _DT[gdt],
+                         GDN_GATES_CHANNEL if channel else GDN_GATES_SCALAR, float(scale))
+    st = lib.gdn_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b),
+                             _ptr(w), _ptr(g), _ptr(state), _ptr(o), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_step")
+    return o

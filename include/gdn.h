@@ -1,0 +1,152 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the gated delta rule (GDN-2, with Gated DeltaNet
+ * and DeltaNet as special cases) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per value head; S is the d_k x d_v state, fp32, row-major):
+ *
+ *   e_t = b_t (.) k_t                     erase/read direction
+ *   z_t = w_t (.) v_t                     gated write target
+ *   S_t = (I - k_t e_t^T) Diag(alpha_t) S_{t-1} + k_t z_t^T
+ *   o_t = scale * S_t^T q_t               read-out after the update
+ *
+ * defined by "Gated DeltaNet-2: Decoupling Erase and Write in Linear
+ * Attention" (gist.science summary), Methodologie §1 (update equation, erase
+ * gate b_t in [0,1]^{d_k}, write gate w_t in [0,1]^{d_v}, channel decay
+ * D_t = Diag(alpha_t)), and by the news page on the same paper (zubnet.ai),
+ * which restates the equation and the gate roles.  With b_t = w_t = beta_t
+ * (a scalar per token and head) and a scalar alpha_t it is the gated delta
+ * rule of "Gated DeltaNet" (docsaid.org notes, §Reunir les deux); with
+ * alpha = 1 it is DeltaNet (same notes, §DeltaNet).  The read-out is the
+ * notes' o_t = S_t q_t (§L'attention lineaire) in the transposed storage used
+ * here.
+ *
+ * Conventions shared by every entry point:
+ *  - Memory: every tensor pointer is a DEVICE pointer (hipMalloc'd or from the
+ *    caller's allocator), dense, row-major in the order given, contiguous, and
+ *    16-byte aligned.  Descriptors are HOST pointers, read during the call only.
+ *    The caller owns all memory; the library allocates nothing and keeps no
+ *    mutable global state, so calls are reentrant and thread-safe.
+ *  - Decay is passed in log space: g = log(alpha) (alpha = exp(g)); a NULL g
+ *    means alpha = 1 (DeltaNet).  Gates are not clamped: any finite b, w, g is
+ *    accepted (beta in (0, 2) is allowed); non-finite inputs give undefined
+ *    results.
+ *  - Key/value head grouping: value head h reads key head h / (H_v / H_k)
+ *    (architecture notes page "Gated DeltaNet", §La dissymetrie 16 / 128: eight
+ *    value heads share one key head).
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream).  GDN_OK means the launch succeeded, not that the work finished.
+ *  - Errors: arguments are validated synchronously before anything is
+ *    enqueued.  On GDN_ERR_INVALID_ARG or GDN_ERR_UNSUPPORTED nothing is
+ *    enqueued and no output is touched.  GDN_ERR_HIP reports a failed launch
+ *    (hipGetLastError).  Nothing is printed and no exception crosses the ABI.
+ *  - Aliasing: outputs must not overlap inputs, except state_out == state_in
+ *    exactly (in-place chaining), which is allowed.  Partial overlap is
+ *    rejected.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1, /* NULL/misaligned/overlapping pointer, bad shape  */
+  GDN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement      */
+  GDN_ERR_HIP = 3          /* the HIP runtime reported an error at launch      */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_gate_mode {
+  /* Gated DeltaNet / DeltaNet: beta [.., H_v], g [.., H_v]; w must be NULL.  */
+  GDN_GATES_SCALAR = 0,
+  /* GDN-2: b [.., H_v, d_k], w [.., H_v, d_v], g [.., H_v, d_k].             */
+  GDN_GATES_CHANNEL = 1
+} gdn_gate_mode;
+
+/* Chunked forward over a sequence batch. */
+typedef struct gdn_fwd_desc {
+  int64_t B;          /* batch, >= 0 (0: nothing to do)                          */
+  int64_t T;          /* tokens per sequence, >= 0 (0: state_out = state_in)     */
+  int32_t H_k, H_v;   /* >= 1, H_v % H_k == 0                                    */
+  int32_t d_k, d_v;   /* each 64 or 128                                          */
+  int32_t io_dtype;   /* gdn_dtype of q, k, v, o                                 */
+  int32_t gate_dtype; /* gdn_dtype of beta|b, w, g: equal to io_dtype, or F32    */
+  int32_t gate_mode;  /* gdn_gate_mode                                           */
+  int32_t chunk;      /* tokens per chunk; must be 64                            */
+  float scale;        /* finite; o = scale * S_t^T q_t                           */
+} gdn_fwd_desc;
+
+/*
+ * gdn_chunk_fwd -- o and the final state of the recurrence above for every
+ * token of a batch of sequences, computed chunkwise (64 tokens per chunk):
+ * inside a chunk the cumulative channel decay is absorbed into the erase and
+ * write factors and a unit lower-triangular system is solved; the fp32 state
+ * is passed from chunk to chunk ("Gated DeltaNet-2", §3 "Entrainement
+ * Parallele Efficace par Blocs"; "Gated DeltaNet", §Rendre l'entrainement
+ * parallele).  The result equals the token-by-token recurrence up to rounding.
+ *
+ *   q, k       [B, T, H_k, d_k]  io_dtype
+ *   v          [B, T, H_v, d_v]  io_dtype
+ *   beta_or_b  SCALAR: [B, T, H_v]        CHANNEL: [B, T, H_v, d_k]   gate_dtype
+ *   w          SCALAR: NULL               CHANNEL: [B, T, H_v, d_v]   gate_dtype
+ *   g          same shape as beta_or_b, gate_dtype; NULL => alpha = 1
+ *   state_in   [B, H_v, d_k, d_v] fp32, or NULL => zero initial state
+ *   state_out  [B, H_v, d_k, d_v] fp32, or NULL => final state not stored;
+ *              may equal state_in
+ *   o          [B, T, H_v, d_v]  io_dtype (output; rounded to nearest even)
+ *   stream     hipStream_t or NULL
+ */
+gdn_status gdn_chunk_fwd(const gdn_fwd_desc* desc, const void* q, const void* k,
+                         const void* v, const void* beta_or_b, const void* w,
+                         const void* g, const float* state_in, float* state_out,
+                         void* o, void* stream);
+
+/* Single-token decode step over N independent sequences. */
+typedef struct gdn_decode_desc {
+  int64_t N;          /* sequences, >= 0 (0: nothing to do)                      */
+  int32_t H_k, H_v;   /* >= 1, H_v % H_k == 0                                    */
+  int32_t d_k, d_v;   /* each 64 or 128                                          */
+  int32_t io_dtype;   /* gdn_dtype of q, k, v, o                                 */
+  int32_t gate_dtype; /* equal to io_dtype, or F32                               */
+  int32_t gate_mode;  /* gdn_gate_mode                                           */
+  float scale;        /* finite                                                  */
+} gdn_decode_desc;
+
+/*
+ * gdn_decode_step -- one step of the recurrence for one new token per
+ * sequence, updating the fp32 state IN PLACE.  The state is constant-size
+ * whatever the context length (architecture notes page "Gated DeltaNet",
+ * §L'etat, en memoire: 128 heads x 128 x 128 fp32 per layer), so the step
+ * streams the state once from and once to HBM.
+ *
+ *   q, k       [N, H_k, d_k]  io_dtype
+ *   v          [N, H_v, d_v]  io_dtype
+ *   beta_or_b  SCALAR: [N, H_v]   CHANNEL: [N, H_v, d_k]   gate_dtype
+ *   w          SCALAR: NULL       CHANNEL: [N, H_v, d_v]   gate_dtype
+ *   g          same shape as beta_or_b; NULL => alpha = 1
+ *   state      [N, H_v, d_k, d_v] fp32, read and overwritten
+ *   o          [N, H_v, d_v]  io_dtype (output)
+ *   stream     hipStream_t or NULL
+ */
+gdn_status gdn_decode_step(const gdn_decode_desc* desc, const void* q, const void* k,
+                           const void* v, const void* beta_or_b, const void* w,
+                           const void* g, float* state, void* o, void* stream);
+
+/* Static, never-NULL description of a status code. */
+const char* gdn_status_string(gdn_status s);
+
+/* Returns GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,166 @@
+"""The C-ABI library loads, exports what include/gdn.h declares, and rejects bad
+arguments on the host before any launch.  No GPU is needed: every call here
+fails validation, which returns before the HIP runtime is touched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+gdn = pytest.importorskip("gated_delta_rule_gdn_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(gdn_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared_functions() == sorted(
+        ["gdn_chunk_fwd", "gdn_decode_step", "gdn_status_string", "gdn_abi_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.gdn.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(gdn_\w+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(gdn.lib, name)
+
+
+def test_version_and_status_strings():
+    assert gdn.abi_version() == 1
+    for st in range(4):
+        s = gdn.status_string(st)
+        assert s.startswith("GDN_")
+    assert "UNKNOWN" in gdn.status_string(99)
+
+
+# ---------------------------------------------------------------------------
+# Validation: fake, never-dereferenced device addresses.
+# ---------------------------------------------------------------------------
+BASE = 0x7f0000000000   # 16-byte aligned fake addresses, far apart
+STEP = 1 << 36
+
+
+def _addr(i, off=0):
+    return ctypes.c_void_p(BASE + i * STEP + off)
+
+
+def _fwd_desc(**kw):
+    d = dict(B=2, T=100, H_k=2, H_v=4, d_k=128, d_v=128, io_dtype=gdn.GDN_BF16,
+             gate_dtype=gdn.GDN_BF16, gate_mode=gdn.GDN_GATES_CHANNEL, chunk=64, scale=1.0)
+    d.update(kw)
+    return gdn.GdnFwdDesc(**d)
+
+
+def _fwd(desc, **ptrs):
+    names = ["q", "k", "v", "b", "w", "g", "s_in", "s_out", "o"]
+    p = {n: _addr(i) for i, n in enumerate(names)}
+    if desc.gate_mode == gdn.GDN_GATES_SCALAR:
+        p["w"] = None
+    p.update(ptrs)
+    return gdn.lib.gdn_chunk_fwd(ctypes.byref(desc) if desc is not None else None,
+                                 *[p[n] for n in names], None)
+
+
+@pytest.mark.parametrize("field,value,expected", [
+    ("H_v", 3, 1),            # H_v % H_k != 0
+    ("H_k", 0, 1),
+    ("d_k", 96, 2),           # unsupported head size
+    ("d_v", 256, 2),
+    ("chunk", 32, 2),         # only C = 64 is built
+    ("io_dtype", 7, 1),
+    ("gate_mode", 5, 1),
+    ("B", -1, 1),
+    ("T", -5, 1),
+    ("scale", float("nan"), 1),
+    ("scale", float("inf"), 1),
+])
+def test_fwd_rejects_bad_descriptor(field, value, expected):
+    assert _fwd(_fwd_desc(**{field: value})) == expected
+
+
+def test_fwd_rejects_fp32_io_with_bf16_gates():
+    assert _fwd(_fwd_desc(io_dtype=gdn.GDN_F32, gate_dtype=gdn.GDN_BF16)) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_fwd_rejects_null_descriptor():
+    assert gdn.lib.gdn_chunk_fwd(None, *([None] * 10)) == gdn.GDN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "b", "o"])
+def test_fwd_rejects_null_required_pointer(name):
+    assert _fwd(_fwd_desc(), **{name: None}) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_fwd_gate_pointer_rules():
+    # channel mode needs w; scalar mode forbids it
+    assert _fwd(_fwd_desc(), w=None) == gdn.GDN_ERR_INVALID_ARG
+    assert _fwd(_fwd_desc(gate_mode=gdn.GDN_GATES_SCALAR), w=_addr(4)) == gdn.GDN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "b", "w", "g", "s_in", "s_out", "o"])
+def test_fwd_rejects_misaligned_pointer(name):
+    idx = ["q", "k", "v", "b", "w", "g", "s_in", "s_out", "o"].index(name)
+    assert _fwd(_fwd_desc(), **{name: _addr(idx, 2)}) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_fwd_rejects_output_overlapping_input():
+    assert _fwd(_fwd_desc(), o=_addr(0, 4096)) == gdn.GDN_ERR_INVALID_ARG      # o inside q
+    assert _fwd(_fwd_desc(), s_out=_addr(2, 4096)) == gdn.GDN_ERR_INVALID_ARG  # state_out inside v
+    assert _fwd(_fwd_desc(), s_out=_addr(6, 16)) == gdn.GDN_ERR_INVALID_ARG    # partial overlap w/ state_in
+
+
+def test_fwd_empty_batch_is_a_noop():
+    assert _fwd(_fwd_desc(B=0)) == gdn.GDN_OK
+
+
+def test_fwd_zero_tokens_in_place_state_is_a_noop():
+    # T = 0 with state_out == state_in (or no state_out) enqueues nothing.
+    assert _fwd(_fwd_desc(T=0), s_out=_addr(6)) == gdn.GDN_OK
+    assert _fwd(_fwd_desc(T=0), s_out=None) == gdn.GDN_OK
+
+
+def _dec_desc(**kw):
+    d = dict(N=4, H_k=2, H_v=4, d_k=128, d_v=128, io_dtype=gdn.GDN_BF16, gate_dtype=gdn.GDN_BF16,
+             gate_mode=gdn.GDN_GATES_CHANNEL, scale=1.0)
+    d.update(kw)
+    return gdn.GdnDecodeDesc(**d)
+
+
+def _dec(desc, **ptrs):
+    names = ["q", "k", "v", "b", "w", "g", "s", "o"]
+    p = {n: _addr(i) for i, n in enumerate(names)}
+    if desc.gate_mode == gdn.GDN_GATES_SCALAR:
+        p["w"] = None
+    p.update(ptrs)
+    return gdn.lib.gdn_decode_step(ctypes.byref(desc), *[p[n] for n in names], None)
+
+
+@pytest.mark.parametrize("field,value,expected", [
+    ("H_v", 5, 1), ("d_k", 32, 2), ("N", -1, 1), ("io_dtype", 3, 1), ("scale", float("nan"), 1),
+])
+def test_decode_rejects_bad_descriptor(field, value, expected):
+    assert _dec(_dec_desc(**{field: value})) == expected
+
+
+def test_decode_pointer_rules():
+    assert _dec(_dec_desc(), s=None) == gdn.GDN_ERR_INVALID_ARG
+    assert _dec(_dec_desc(), w=None) == gdn.GDN_ERR_INVALID_ARG
+    assert _dec(_dec_desc(), o=_addr(6, 64)) == gdn.GDN_ERR_INVALID_ARG   # o inside state
+    assert _dec(_dec_desc(), s=_addr(0, 32)) == gdn.GDN_ERR_INVALID_ARG   # state inside q
+    assert _dec(_dec_desc(), q=_addr(0, 8)) == gdn.GDN_ERR_INVALID_ARG    # misaligned
+    assert _dec(_dec_desc(N=0)) == gdn.GDN_OK
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 64, 1, 128)
+    with pytest.raises(ValueError):
+        gdn.gdn_chunk_fwd(q, q, q, torch.zeros(1, 64, 1))
