@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated-delta-rule hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input:
+  1. gdn_chunk_fwd on the GDN-2 prefill workload
+     (B=8, H_k=H_v=16, T=4096, d_k=d_v=128, channel gates, bf16 inputs,
+      fp32 state, chunk 64), and
+  2. gdn_decode_step on the GDN-2 decode workload
+     (256 sequences x 128 value heads / 16 key heads, d=128, channel gates,
+      bf16 inputs, 2.1 GB fp32 state updated in place).
+
+Prints ONE JSON line.  `value` is the chunk forward's tokens/s (B*T per
+launch / mean launch time); the decode step's state bandwidth is reported in
+`decode_state_GBps`.  Inputs are resident in HBM before timing starts.  Kernel
+durations come from HIP events recorded on the stream the kernels run on.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+CHUNK = 64
+
+
+def chunk_algorithmic(cfg, gate_bytes, io_bytes=2, state_in=False):
+    """Bytes each input is read once, o and the final state written once; and
+    the flops the chunkwise method must do, triangular work counted as half:
+    2*[C/2*(3 d_k + 2 d_v) + 3 d_k d_v] per (token, value head)."""
+    B, T, Hk, Hv, dk, dv = cfg.B, cfg.T, cfg.Hk, cfg.Hv, cfg.dk, cfg.dv
+    qk = 2 * B * T * Hk * dk * io_bytes
+    v = B * T * Hv * dv * io_bytes
+    o = B * T * Hv * dv * io_bytes
+    if cfg.channel:
+        gates = B * T * Hv * (2 * dk + dv) * gate_bytes
+    else:
+        gates = 2 * B * T * Hv * gate_bytes
+    state = B * Hv * dk * dv * 4 * (2 if state_in else 1)
+    flops = 2.0 * (CHUNK / 2 * (3 * dk + 2 * dv) + 3 * dk * dv) * B * T * Hv
+    return qk + v + o + gates + state, flops
+
+
+def decode_algorithmic(cfg, io_bytes=2, gate_bytes=2):
+    N, Hk, Hv, dk, dv = cfg.N, cfg.Hk, cfg.Hv, cfg.dk, cfg.dv
+    state = 2 * N * Hv * dk * dv * 4
+    qk = 2 * N * Hk * dk * io_bytes
+    vo = 2 * N * Hv * dv * io_bytes
+    gates = N * Hv * (2 * dk + dv) * gate_bytes if cfg.channel else 2 * N * Hv * gate_bytes
+    flops = 6.0 * N * Hv * dk * dv
+    return state + qk + vo + gates, flops
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_gdn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, per_launch_bytes_alg):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic.json), or None when it is absent or was taken on other
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_digest") != source_digest():
+        return None
+    ent = data.get("kernels", {}).get(kernel_key)
+    if not ent:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(args):
+    """The oracle, untuned, on the machine's host cores over a bounded sample of
+    the same prefill workload (4 of the 8 sequences, all 16 heads, T=4096)."""
+    import torch
+
+    import oracle
+    import synth
+    cfg = synth.CONFIGS["gdn2_bf16_train"]
+    B = 4
+    inp = synth.chunk_inputs(cfg, B=B)
+    args64 = {k: (None if v is None else v.to(torch.float64).numpy()) for k, v in inp.items()}
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = min(cores, args.cpu_threads) if args.cpu_threads else cores
+    t0 = time.perf_counter()
+    oracle.recurrent(args64["q"], args64["k"], args64["v"], args64["beta_or_b"], args64["w"],
+                     args64["g"], nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": B * cfg.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"GDN-2 prefill, {B} of {cfg.B} sequences x {cfg.Hv} heads x T={cfg.T} "
+                      f"(fp64 token recurrence, OpenMP over heads); {dt:.2f} s wall",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=16,
+                    help="cap on oracle threads (the box's CPU share)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU component).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_gdn_amd as gdn
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg_c = synth.CONFIGS["gdn2_bf16_train"]
+    cfg_d = synth.CONFIGS["gdn2_decode"]
+    inp_c = synth.chunk_inputs(cfg_c, device="cuda")
+    inp_d = synth.decode_inputs(cfg_d, device="cuda")
+    o_c = torch.empty((cfg_c.B, cfg_c.T, cfg_c.Hv, cfg_c.dv), dtype=cfg_c.io_dtype, device=dev)
+    s_c = torch.empty((cfg_c.B, cfg_c.Hv, cfg_c.dk, cfg_c.dv), dtype=torch.float32, device=dev)
+    o_d = torch.empty((cfg_d.N, cfg_d.Hv, cfg_d.dv), dtype=cfg_d.io_dtype, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        gdn.gdn_chunk_fwd(inp_c["q"], inp_c["k"], inp_c["v"], inp_c["beta_or_b"], w=inp_c["w"],
+                          g=inp_c["g"], state_in=inp_c["state_in"], state_out=s_c, o=o_c)
+        if ev is not None:
+            ev[1].record()
+        gdn.gdn_decode_step(inp_d["q"], inp_d["k"], inp_d["v"], inp_d["beta_or_b"],
+                            inp_d["state"], w=inp_d["w"], g=inp_d["g"], o=o_d)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    chunk_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    chunk_avg = sum(chunk_ms) / len(chunk_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    gate_bytes = 2 if cfg_c.gate_dtype == torch.bfloat16 else 4
+    c_bytes, c_flops = chunk_algorithmic(cfg_c, gate_bytes, state_in=inp_c["state_in"] is not None)
+    d_bytes, d_flops = decode_algorithmic(cfg_d)
+    tokens = cfg_c.B * cfg_c.T
+    chunk_tps = tokens / (chunk_avg * 1e-3)
+    c_gbps = c_bytes / (chunk_avg * 1e-3) / 1e9
+    d_gbps = d_bytes / (dec_avg * 1e-3) / 1e9
+    c_tflops = c_flops / (chunk_avg * 1e-3) / 1e12
+
+    def roof(bytes_alg, avg_ms, key, flops=None):
+        r = {"bound": "hbm", "achieved": round(bytes_alg / (avg_ms * 1e-3) / 1e9, 1),
+             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+             "frac": round(bytes_alg / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+             "traffic": measured_traffic(key, bytes_alg),
+             "algorithmic_bytes_per_launch": bytes_alg, "avg_launch_ms": round(avg_ms, 4)}
+        if flops is not None:
+            r["mfma_tflops"] = round(flops / (avg_ms * 1e-3) / 1e12, 1)
+            r["mfma_frac"] = round(flops / (avg_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        return r
+
+    roof_c = roof(c_bytes, chunk_avg, "chunk_fwd", c_flops)
+    roof_d = roof(d_bytes, dec_avg, "decode_step")
+    dominant = "chunk_fwd" if chunk_avg >= dec_avg else "decode_step"
+    out = {
+        "metric": "tokens/s gated-delta chunk fwd (GDN-2, T=4K) + decode state HBM GB/s",
+        "value": round(chunk_tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), gates sigmoid/-softplus of N(0,1))",
+        "config": {
+            "workload": "gdn2_bf16_train chunk fwd + gdn2_decode step",
+            "chunk_fwd": {"B": cfg_c.B, "T": cfg_c.T, "H_k": cfg_c.Hk, "H_v": cfg_c.Hv,
+                          "d_k": cfg_c.dk, "d_v": cfg_c.dv, "gates": "channel (b, w, g) bf16",
+                          "chunk": CHUNK, "state": "fp32, S0=0"},
+            "decode": {"N": cfg_d.N, "H_k": cfg_d.Hk, "H_v": cfg_d.Hv, "d_k": cfg_d.dk,
+                       "d_v": cfg_d.dv, "gates": "channel bf16", "state": "fp32 in place, 2.15 GB"},
+            "global_batch": tokens,
+            "seq_len": cfg_c.T,
+            "parallelism": "single GPU",
+            "operands": "bf16 MFMA operands, fp32 accumulation and state",
+        },
+        "chunk_fwd_ms": round(chunk_avg, 4),
+        "chunk_fwd_GBps": round(c_gbps, 1),
+        "chunk_fwd_TFLOPs": round(c_tflops, 1),
+        "decode_step_ms": round(dec_avg, 4),
+        "decode_state_GBps": round(d_gbps, 1),
+        "decode_tokens_per_s": round(cfg_d.N / (dec_avg * 1e-3), 1),
+        "roofline": roof_c if dominant == "chunk_fwd" else roof_d,
+        "roofline_kernel": dominant,
+        "rooflines": {"chunk_fwd": roof_c, "decode_step": roof_d},
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(args)
+        out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
