@@ -1,0 +1,149 @@
+// chunk_common.hpp -- helpers shared by the chunkwise forward kernels
+// (chunk_fwd.hip: sequential-phase kernel; chunk_fwd_pipe.hip: producer /
+// consumer kernel).  Device code only; internal linkage in each unit.
+#pragma once
+
+#include "gdn_device.hpp"
+#include "gdn_kernels.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kC = 64;          // tokens per chunk
+
+// Position of index x inside its 32-block when stored in accumulator-row
+// order: k = 4g+i (k < 16) -> 8g+i, k = 16+4g+i -> 8g+4+i.
+__device__ __forceinline__ int sig(int x) {
+  const int k = x & 31;
+  const int p = (k < 16) ? (((k >> 2) << 3) + (k & 3)) : ((((k - 16) >> 2) << 3) + 4 + (k & 3));
+  return (x & ~31) + p;
+}
+
+__device__ __forceinline__ float dpp_row_shr(float x, int n) {
+  int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (n) {
+    case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// Value of lane n of each 16-lane row, broadcast to the whole row.
+template <int N>
+__device__ __forceinline__ float dpp_row_bcast(float x) {
+  static_assert(N >= 0 && N < 16, "lane");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x150 + N, 0xf, 0xf, false));
+}
+
+// NB bytes loaded as packed 32-bit words (one or two vector loads).
+template <int NB>
+struct Raw {
+  uint32_t w[NB / 4];
+};
+template <int NB>
+__device__ __forceinline__ void ld_raw(const void* p, Raw<NB>& r) {
+  if constexpr (NB == 8) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = u.x; r.w[1] = u.y;
+  } else if constexpr (NB == 16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w;
+  } else {
+    static_assert(NB == 32, "raw size");
+    const uint4 u = reinterpret_cast<const uint4*>(p)[0];
+    const uint4 v = reinterpret_cast<const uint4*>(p)[1];
+    r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w;
+    r.w[4] = v.x; r.w[5] = v.y; r.w[6] = v.z; r.w[7] = v.w;
+  }
+}
+// Unpack N elements of type E to fp32, zeroed when !valid.
+template <typename E, int N, int NB>
+__device__ __forceinline__ void unpack(const Raw<NB>& r, bool valid, float* out) {
+  static_assert(N * (int)sizeof(E) == NB, "raw size");
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float x;
+    if constexpr (sizeof(E) == 2) {
+      const uint32_t w = r.w[i >> 1];
+      x = __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+      x = __uint_as_float(r.w[i]);
+    }
+    out[i] = valid ? x : 0.f;
+  }
+}
+
+// Store 4 consecutive fp32 values as T.
+template <typename T>
+__device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 h = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    *reinterpret_cast<bf16x4*>(p) = h;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ Frag8<T> ld_frag8(const T* p) {
+  Frag8<T> f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+  } else {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag4<T> ld_frag4(const T* p) {
+  Frag4<T> f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = *reinterpret_cast<const bf16x4*>(p);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  }
+  return f;
+}
+
+// K=32 fragment from two accumulator tiles (rows 0-15 and 16-31 of a block),
+// optionally scaled per element.
+template <typename T>
+__device__ __forceinline__ Frag8<T> frag8_from_acc(const f32x4& lo, const f32x4& hi) {
+  Frag8<T> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.v[i] = from_f32<T>(lo[i]);
+    f.v[4 + i] = from_f32<T>(hi[i]);
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag4<T> frag4_from_acc(const f32x4& a) {
+  Frag4<T> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.v[i] = from_f32<T>(a[i]);
+  return f;
+}
+
+struct Params {
+  int64_t B, T;
+  int Hk, Hv;
+  float scale;
+  const void *q, *k, *v, *b, *w, *g;
+  const float* state_in;
+  float* state_out;
+  void* o;
+};
+
+}  // namespace
+}  // namespace gdn

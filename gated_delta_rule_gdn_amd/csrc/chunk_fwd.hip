@@ -37,102 +37,12 @@
 //    blocks: the 16x16 diagonal inverses are formed in fp32 on the VALU, the
 //    off-diagonal updates and the diagonal applications run on MFMA with the
 //    intermediate blocks kept in registers.
-#include "gdn_device.hpp"
-#include "gdn_kernels.hpp"
+#include "chunk_common.hpp"
 
 namespace gdn {
 namespace {
 
-constexpr int kC = 64;          // tokens per chunk
 constexpr int kThreads = 256;   // 4 waves
-
-// Position of index x inside its 32-block when stored in accumulator-row
-// order: k = 4g+i (k < 16) -> 8g+i, k = 16+4g+i -> 8g+4+i.
-__device__ __forceinline__ int sig(int x) {
-  const int k = x & 31;
-  const int p = (k < 16) ? (((k >> 2) << 3) + (k & 3)) : ((((k - 16) >> 2) << 3) + 4 + (k & 3));
-  return (x & ~31) + p;
-}
-
-__device__ __forceinline__ float dpp_row_shr(float x, int n) {
-  int v = __builtin_bit_cast(int, x);
-  int r;
-  switch (n) {
-    case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false); break;
-    case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false); break;
-    case 4: r = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false); break;
-    default: r = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false); break;
-  }
-  return __builtin_bit_cast(float, r);
-}
-
-// Store 4 consecutive fp32 values as T.
-template <typename T>
-__device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {
-  if constexpr (sizeof(T) == 2) {
-    bf16x4 h = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-    *reinterpret_cast<bf16x4*>(p) = h;
-  } else {
-    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ Frag8<T> ld_frag8(const T* p) {
-  Frag8<T> f;
-  if constexpr (sizeof(T) == 2) {
-    f.v = *reinterpret_cast<const bf16x8*>(p);
-  } else {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-  }
-  return f;
-}
-
-template <typename T>
-__device__ __forceinline__ Frag4<T> ld_frag4(const T* p) {
-  Frag4<T> f;
-  if constexpr (sizeof(T) == 2) {
-    f.v = *reinterpret_cast<const bf16x4*>(p);
-  } else {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-  }
-  return f;
-}
-
-// K=32 fragment from two accumulator tiles (rows 0-15 and 16-31 of a block),
-// optionally scaled per element.
-template <typename T>
-__device__ __forceinline__ Frag8<T> frag8_from_acc(const f32x4& lo, const f32x4& hi) {
-  Frag8<T> f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f.v[i] = from_f32<T>(lo[i]);
-    f.v[4 + i] = from_f32<T>(hi[i]);
-  }
-  return f;
-}
-
-template <typename T>
-__device__ __forceinline__ Frag4<T> frag4_from_acc(const f32x4& a) {
-  Frag4<T> f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.v[i] = from_f32<T>(a[i]);
-  return f;
-}
-
-struct Params {
-  int64_t B, T;
-  int Hk, Hv;
-  float scale;
-  const void *q, *k, *v, *b, *w, *g;
-  const float* state_in;
-  float* state_out;
-  void* o;
-};
 
 // LDS plan (byte offsets) for one instantiation.
 template <typename T, int DK, int DVS>
@@ -158,7 +68,13 @@ struct Lds {
   static_assert(4 * kFb <= kOpEnd, "fallback buffers must fit in the operand area");
   static constexpr int kZ = kOpEnd;
   static constexpr int kVec = kZ + rnd(DVS * ZP * 4);
-  static constexpr int kTotal = kVec + 2 * DK * 4 + 16;
+  static constexpr int kBase = kVec + 2 * DK * 4 + 16;
+  // K_hat^T gets its own region when it fits (written with the other
+  // operands); otherwise it reuses R's region once the Gram tiles are done.
+  static constexpr int kKtSz = rnd(DK * CP * ES);
+  static constexpr bool kKtSeparate = kBase + kKtSz <= 160 * 1024;
+  static constexpr int kKt = kKtSeparate ? kBase : kRK;
+  static constexpr int kTotal = kKtSeparate ? kBase + kKtSz : kBase;
   static_assert(kTotal <= 160 * 1024, "LDS budget");
 };
 
@@ -177,7 +93,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
   T* sLn = reinterpret_cast<T*>(smem + L::kLn);
   T* sM = reinterpret_cast<T*>(smem + L::kM);
   T* sR = reinterpret_cast<T*>(smem + L::kRK);
-  T* sKt = reinterpret_cast<T*>(smem + L::kRK);
+  T* sKt = reinterpret_cast<T*>(smem + L::kKt);
   T* sP = reinterpret_cast<T*>(smem + L::kP);
   T* sAo = reinterpret_cast<T*>(smem + L::kAo);
   T* sTd = reinterpret_cast<T*>(smem + L::kTd);
@@ -240,44 +156,97 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
   const int zc = tid % ZCG;
   const int zt = (tid / ZCG) * TPZ;
 
-  const int64_t nchunks = (Tn + kC - 1) / kC;
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
-    const int64_t t0 = ci * kC;
-
-    // ================= elementwise phase: load, cumulative decay, operands
-    float qv[4][CPT], kv[4][CPT], bv[4][CPT], G[4][CPT], graw[4][CPT];
+  // Raw inputs of one chunk in packed registers.  Every load is issued
+  // unconditionally (the token index is clamped into the sequence; values of
+  // tokens past the end are zeroed when unpacked) so that the whole chunk is
+  // in flight at once, and the next chunk is requested while this one computes.
+  constexpr int QB = CPT * (int)sizeof(T);
+  constexpr int GB = CPT * (int)sizeof(GT);
+  constexpr int VB = 4 * (int)sizeof(T);
+  constexpr int WB = 4 * (int)sizeof(GT);
+  Raw<QB> rq[4], rk[4];
+  Raw<GB> rb[4], rg[4];
+  float sb[4], sg[4];
+  Raw<VB> rv[TPZ];
+  Raw<WB> rw[TPZ];
+  float zb[TPZ];
+  auto load_chunk = [&](int64_t tc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t tok = t0 + 4 * tg + i;
-      const bool valid = tok < Tn;
-      if (valid) {
-        const int64_t qk_off = ((bidx * Tn + tok) * p.Hk + hk) * (int64_t)DK + ch0;
-        load_f32<CPT, T>(gq + qk_off, qv[i]);
-        load_f32<CPT, T>(gk + qk_off, kv[i]);
+      int64_t tok = tc + 4 * tg + i;
+      tok = tok < Tn ? tok : Tn - 1;
+      const int64_t qk_off = ((bidx * Tn + tok) * p.Hk + hk) * (int64_t)DK + ch0;
+      ld_raw<QB>(gq + qk_off, rq[i]);
+      ld_raw<QB>(gk + qk_off, rk[i]);
+      if constexpr (CHANNEL) {
+        const int64_t g_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DK + ch0;
+        ld_raw<GB>(gb + g_off, rb[i]);
+        if constexpr (HAS_G) ld_raw<GB>(gg + g_off, rg[i]);
+      } else {
+        const int64_t s_off = (bidx * Tn + tok) * p.Hv + hv;
+        sb[i] = to_f32(gb[s_off]);
+        sg[i] = HAS_G ? to_f32(gg[s_off]) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TPZ; ++i) {
+      int64_t tok = tc + zt + i;
+      tok = tok < Tn ? tok : Tn - 1;
+      const int64_t v_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DV + c0 + 4 * zc;
+      ld_raw<VB>(gv + v_off, rv[i]);
+      if constexpr (CHANNEL) ld_raw<WB>(gw + v_off, rw[i]);
+      else zb[i] = to_f32(gb[(bidx * Tn + tok) * p.Hv + hv]);
+    }
+  };
+
+  const int64_t nchunks = (Tn + kC - 1) / kC;
+  load_chunk(0);
+  for (int64_t ci = 0; ci < nchunks; ++ci) {
+    const int64_t t0 = ci * kC;
+    const bool has_next = ci + 1 < nchunks;
+
+    // ================= elementwise phase: unpack, cumulative decay, operands
+    float qv[4][CPT], kv[4][CPT], bv[4][CPT], G[4][CPT], graw[4][CPT];
+    auto unpack_chunk = [&]() {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = t0 + 4 * tg + i < Tn;
+        unpack<T, CPT>(rq[i], valid, qv[i]);
+        unpack<T, CPT>(rk[i], valid, kv[i]);
         if constexpr (CHANNEL) {
-          const int64_t g_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DK + ch0;
-          load_f32<CPT, GT>(gb + g_off, bv[i]);
+          unpack<GT, CPT>(rb[i], valid, bv[i]);
           if constexpr (HAS_G) {
-            load_f32<CPT, GT>(gg + g_off, graw[i]);
+            unpack<GT, CPT>(rg[i], valid, graw[i]);
           } else {
 #pragma unroll
             for (int e = 0; e < CPT; ++e) graw[i][e] = 0.f;
           }
         } else {
-          const int64_t s_off = (bidx * Tn + tok) * p.Hv + hv;
-          const float beta = to_f32(gb[s_off]);
-          const float gl = HAS_G ? to_f32(gg[s_off]) : 0.f;
 #pragma unroll
-          for (int e = 0; e < CPT; ++e) { bv[i][e] = beta; graw[i][e] = gl; }
+          for (int e = 0; e < CPT; ++e) {
+            bv[i][e] = valid ? sb[i] : 0.f;
+            graw[i][e] = valid ? sg[i] : 0.f;
+          }
         }
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) graw[i][e] *= kLog2e;  // log2 units
+      }
+    };
+    unpack_chunk();
+    float zv[TPZ][4];
+#pragma unroll
+    for (int i = 0; i < TPZ; ++i) {
+      const bool valid = t0 + zt + i < Tn;
+      unpack<T, 4>(rv[i], valid, zv[i]);
+      if constexpr (CHANNEL) {
+        float wz[4];
+        unpack<GT, 4>(rw[i], valid, wz);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zv[i][e] *= wz[e];
       } else {
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-          qv[i][e] = 0.f; kv[i][e] = 0.f; bv[i][e] = 0.f; graw[i][e] = 0.f;
-        }
+        for (int e = 0; e < 4; ++e) zv[i][e] *= zb[i];
       }
-#pragma unroll
-      for (int e = 0; e < CPT; ++e) graw[i][e] *= kLog2e;  // log2 units
     }
     // inclusive prefix over the chunk: in-thread over 4 tokens, then across
     // the 16 token groups of the DPP row
@@ -298,8 +267,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
         const float excl = x - tot;
 #pragma unroll
         for (int i = 0; i < 4; ++i) G[i][e] += excl;
-        rr[e] = __shfl(G[3][e], (lane & 48) | 7);   // G at token 31
-        gc[e] = __shfl(G[3][e], (lane & 48) | 15);  // G at token 63 (chunk end)
+        rr[e] = dpp_row_bcast<7>(G[3][e]);   // G at token 31
+        gc[e] = dpp_row_bcast<15>(G[3][e]);  // G at token 63 (chunk end)
 #pragma unroll
         for (int i = 0; i < 4; ++i) bad |= !(fabsf(G[i][e] - rr[e]) <= kRange);
         bad |= !(rr[e] >= -100.f);
@@ -316,26 +285,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
 
     // Z^T = (w (.) v)^T for this workgroup's columns (both paths read it)
 #pragma unroll
-    for (int i = 0; i < TPZ; ++i) {
-      const int64_t tok = t0 + zt + i;
-      float vz[4] = {0.f, 0.f, 0.f, 0.f};
-      if (tok < Tn) {
-        const int64_t v_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DV + c0 + 4 * zc;
-        load_f32<4, T>(gv + v_off, vz);
-        if constexpr (CHANNEL) {
-          float wz[4];
-          load_f32<4, GT>(gw + v_off, wz);
+    for (int i = 0; i < TPZ; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vz[e] *= wz[e];
-        } else {
-          const float beta = to_f32(gb[(bidx * Tn + tok) * p.Hv + hv]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vz[e] *= beta;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sZ[(4 * zc + e) * L::ZP + zt + i] = vz[e];
-    }
+      for (int e = 0; e < 4; ++e) sZ[(4 * zc + e) * L::ZP + zt + i] = zv[i][e];
 
     if (!slow) {
       // ---------------- factored path ----------------
@@ -367,6 +319,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
           st4<T>(sR + t * L::DKP + pos, kv[i][4 * u], kv[i][4 * u + 1], kv[i][4 * u + 2], kv[i][4 * u + 3]);
         }
       }
+      if constexpr (L::kKtSeparate) {
+#pragma unroll
+        for (int e = 0; e < CPT; ++e)
+          st4<T>(sKt + (ch0 + e) * L::CP + sig(4 * tg), kh[0][e], kh[1][e], kh[2][e], kh[3][e]);
+      }
       if (tg == 0) {
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
@@ -375,9 +332,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
         }
       }
       __syncthreads();  // B1
+      if (has_next) load_chunk(t0 + kC);
 
       // ---- A and P tiles: D[s][t] = sum_c R[s][c] X[t][c], X = Ln (gives -A) or M (gives P)
-      for (int tile = wave; tile < 20; tile += 4) {
+#pragma unroll
+      for (int it = 0; it < 5; ++it) {
+        const int tile = wave + 4 * it;
         const bool isP = tile >= 10;
         const int tt = isP ? tile - 10 : tile;
         // (ms, nt) enumeration of the lower block triangle
@@ -416,27 +376,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
       __syncthreads();  // B2: R is dead, A/P written
 
       // K_hat^T over R's space: sKt[c][sig(s)]
+      if constexpr (!L::kKtSeparate) {
 #pragma unroll
-      for (int e = 0; e < CPT; ++e)
-        st4<T>(sKt + (ch0 + e) * L::CP + sig(4 * tg), kh[0][e], kh[1][e], kh[2][e], kh[3][e]);
-
-      // 16x16 diagonal inverses T_bb = (I + A_bb)^{-1} in fp32 on wave 0:
-      // lane (j, bl) forms row j of block bl from T[r][s] = -sum_{u>s} T[r][u] A[u][s].
-      if (wave == 0) {
-        const int bl = g, r = j;
-        float trow[16];
-#pragma unroll
-        for (int s = 15; s >= 0; --s) {
-          const float* acol = sAd + (bl * 16 + s) * 16;  // A[u][s] for u = 0..15
-          float acc = 0.f;
-#pragma unroll
-          for (int u = s + 1; u < 16; ++u) acc -= trow[u] * acol[u];
-          trow[s] = (s > r) ? 0.f : ((s == r) ? 1.f : acc);
-        }
-        T* dst = sTd + (bl * 16 + r) * L::TDP;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          st4<T>(dst + 4 * u, trow[4 * u], trow[4 * u + 1], trow[4 * u + 2], trow[4 * u + 3]);
+        for (int e = 0; e < CPT; ++e)
+          st4<T>(sKt + (ch0 + e) * L::CP + sig(4 * tg), kh[0][e], kh[1][e], kh[2][e], kh[3][e]);
       }
 
       // S~ = Diag(exp(r)) S as K=32 fragments; X' = Z + Ln S~ (= Z - E_bar S);
@@ -471,6 +414,48 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
             const Frag8<T> bm = ld_frag8<T>(sM + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
             mma32(O[mt], sf[kb], bm);
           }
+        }
+      }
+      // 16x16 diagonal inverses T_bb = (I + A_bb)^{-1} in fp32, wave w forming
+      // block w (issued after this wave's MFMAs above, which run meanwhile).
+      // Row form, each row independent: T[r][r] = 1 and, for s = r-1 .. 0,
+      // T[r][s] = -sum_{u>s} T[r][u] A[u][s].  Lane j forms row j (the four
+      // lane groups compute the same rows); column s of A is read as 4 x 16 B
+      // one step ahead of its use.
+      {
+        const int r = j;
+        const float* ad = sAd + wave * 256;  // ad[s * 16 + u] = A[u][s]
+        float trow[16];
+        float cur[16], nxt[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(ad + 15 * 16 + 4 * q4);
+          cur[4 * q4] = c4.x; cur[4 * q4 + 1] = c4.y; cur[4 * q4 + 2] = c4.z; cur[4 * q4 + 3] = c4.w;
+        }
+#pragma unroll
+        for (int s = 15; s >= 0; --s) {
+          if (s > 0) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const float4 c4 = *reinterpret_cast<const float4*>(ad + (s - 1) * 16 + 4 * q4);
+              nxt[4 * q4] = c4.x; nxt[4 * q4 + 1] = c4.y; nxt[4 * q4 + 2] = c4.z; nxt[4 * q4 + 3] = c4.w;
+            }
+          }
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int u = s + 1; u < 16; ++u) {
+            if (u & 1) a1 -= trow[u] * cur[u];
+            else a0 -= trow[u] * cur[u];
+          }
+          trow[s] = (s > r) ? 0.f : ((s == r) ? 1.f : a0 + a1);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) cur[u] = nxt[u];
+        }
+        if (g == 0) {
+          T* dst = sTd + (wave * 16 + r) * L::TDP;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            st4<T>(dst + 4 * u, trow[4 * u], trow[4 * u + 1], trow[4 * u + 2], trow[4 * u + 3]);
         }
       }
       __syncthreads();  // B3: K_hat^T and the diagonal inverses are visible
@@ -536,6 +521,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
       // ---------------- token-by-token path (exact in fp32) ----------------
       // Used when the factored operands would leave the fp32 range.  Two
       // halves of 32 tokens are staged in LDS; the state stays in registers.
+      // The chunk is read again (this path is rare) rather than holding its
+      // unpacked values live through the common path.
+      load_chunk(t0);
+      unpack_chunk();
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if ((tg >> 3) == half) {
@@ -585,6 +574,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
         }
         __syncthreads();
       }
+      if (has_next) load_chunk(t0 + kC);
     }
   }
 
@@ -637,9 +627,10 @@ __global__ void state_copy_kernel(const float* __restrict__ src, float* __restri
 
 }  // namespace
 
+// bf16 operands run the producer/consumer kernel (chunk_fwd_pipe.hip); fp32
+// operands run the sequential-phase kernel of this file.
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
-  if (a.io == DType::BF16 && a.gate == DType::BF16) return pick_dims<bf16, bf16>(a, stream);
-  if (a.io == DType::BF16 && a.gate == DType::F32) return pick_dims<bf16, float>(a, stream);
+  if (a.io == DType::BF16) return launch_chunk_fwd_pipe(a, stream);
   return pick_dims<float, float>(a, stream);
 }
 

@@ -1,0 +1,629 @@
+// chunk_fwd_pipe.hip -- producer/consumer chunkwise forward (bf16 operands).
+//
+// Same mathematics as chunk_fwd.hip ("Gated DeltaNet-2", §3 "Entrainement
+// Parallele Efficace par Blocs"): per chunk of 64 tokens, with S the state
+// entering the chunk and r_c a per-channel reference of the cumulative
+// log-decay,
+//   L = e exp(G - r), M = q exp(G - r), R = k exp(r - G)     (elementwise)
+//   A = strict_lower(L R^T), P = lower(M R^T)                (Gram tiles)
+//   X = Z - L S~,  S~ = Diag(exp(r)) S                       (S-dependent)
+//   U = (I + A)^{-1} X                                        (forward subst.)
+//   O = M S~ + P U,  S' = Diag(exp(G_C)) S + K_hat^T U.
+//
+// Work split inside one workgroup of 8 waves (two per SIMD):
+//   consumer waves 0-3 own the fp32 state slice (16 value columns each, in
+//     MFMA accumulators) and run only the S-dependent MFMA chain;
+//   producer waves 4-7 build everything that does not depend on S for the
+//     NEXT chunk: loads (prefetched a chunk ahead), cumulative decay, the
+//     exponentials and gated operands (VALU), the A/P Gram tiles (MFMA) and
+//     the 16x16 diagonal inverses (VALU, fp32).
+// VALU work of the producers overlaps MFMA work of the consumers on each
+// SIMD.  Two workgroup barriers per chunk:
+//
+//   interval 2(c):  consumers  X = Z - L S~, O = M S~      | producers  Gram(c), inverses(c)
+//   ---- barrier A
+//   interval 1(c):  consumers  U, O += P U, S', store o(c) | producers  operands(c+1)
+//   ---- barrier B
+//
+// Only K_hat^T and the per-channel vectors are read by the consumers in the
+// interval where the producers rewrite them, so only they are double
+// buffered.  A chunk whose decay range would leave the fp32 range of the
+// factored operands is run token by token by the consumers instead.
+#include "chunk_common.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kPipeThreads = 512;  // 4 consumer + 4 producer waves
+
+template <typename T, int DK, int DVS>
+struct PipeLds {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int PADT = 16 / ES;
+  static constexpr int DKP = DK + PADT;  // pitch of [64][DK] operand arrays
+  static constexpr int CP = kC + PADT;   // pitch of [*][64] operand arrays
+  static constexpr int TDP = 16 + PADT;  // pitch of the diagonal inverses
+  static constexpr int ZP = kC + 4;      // pitch of Z^T (fp32)
+  static constexpr int rnd(int x) { return (x + 15) & ~15; }
+  static constexpr int kLn = 0;
+  static constexpr int kM = kLn + rnd(kC * DKP * ES);
+  static constexpr int kR = kM + rnd(kC * DKP * ES);
+  static constexpr int kKt = kR + rnd(kC * DKP * ES);  // two buffers
+  static constexpr int kKtSz = rnd(DK * CP * ES);
+  static constexpr int kP = kKt + 2 * kKtSz;
+  static constexpr int kAo = kP + rnd(kC * CP * ES);
+  static constexpr int kTd = kAo + rnd(kC * CP * ES);
+  static constexpr int kAd = kTd + rnd(4 * 16 * TDP * ES);
+  static constexpr int kZ = kAd + 4 * 16 * 16 * 4;
+  static constexpr int kVec = kZ + rnd(DVS * ZP * 4);  // two buffers of [exp(r) | exp(G_C)]
+  static constexpr int kFlag = kVec + 2 * 2 * DK * 4;  // two buffers of 4 ints
+  static constexpr int kTotal = kFlag + 2 * 4 * 4;
+  static_assert(kTotal <= 160 * 1024, "LDS budget");
+};
+
+// Gram tiles per producer wave: slot 0 is the diagonal A block of that wave
+// (inverted by the same wave), the others balance the remaining 16 tiles.
+// Tile ids 0-9 are A tiles, 10-19 P tiles, in (ms, nt) lower-triangle order.
+__device__ __forceinline__ int gram_tile(int pw, int slot) {
+  constexpr int tab[4][5] = {{0, 1, 3, 10, 11}, {2, 4, 6, 12, 13}, {5, 7, 8, 14, 15}, {9, 16, 17, 18, 19}};
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (w == pw) t = tab[w][slot];
+  return t;
+}
+
+template <typename T, typename GT, int DK, int DV, int DVS, bool CHANNEL, bool HAS_G>
+__global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params p) {
+  using L = PipeLds<T, DK, DVS>;
+  constexpr int NSPLIT = DV / DVS;
+  constexpr int CPT = DK / 16;  // channels per producer thread
+  constexpr int KB = DK / 32;
+  constexpr int MT = DK / 16;
+  constexpr float kRange = 90.f;  // |G - r| bound (log2 units) of the factored form
+  static_assert(DVS == 64 && CPT % 4 == 0, "shape");
+
+  __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+  T* sLn = reinterpret_cast<T*>(smem + L::kLn);
+  T* sM = reinterpret_cast<T*>(smem + L::kM);
+  T* sR = reinterpret_cast<T*>(smem + L::kR);
+  T* sKt0 = reinterpret_cast<T*>(smem + L::kKt);
+  T* sP = reinterpret_cast<T*>(smem + L::kP);
+  T* sAo = reinterpret_cast<T*>(smem + L::kAo);
+  T* sTd = reinterpret_cast<T*>(smem + L::kTd);
+  float* sAd = reinterpret_cast<float*>(smem + L::kAd);
+  float* sZ = reinterpret_cast<float*>(smem + L::kZ);
+  float* sVec0 = reinterpret_cast<float*>(smem + L::kVec);
+  int* sFlag = reinterpret_cast<int*>(smem + L::kFlag);
+
+  const T* __restrict__ gq = static_cast<const T*>(p.q);
+  const T* __restrict__ gk = static_cast<const T*>(p.k);
+  const T* __restrict__ gv = static_cast<const T*>(p.v);
+  const GT* __restrict__ gb = static_cast<const GT*>(p.b);
+  const GT* __restrict__ gw = static_cast<const GT*>(p.w);
+  const GT* __restrict__ gg = static_cast<const GT*>(p.g);
+  T* __restrict__ go = static_cast<T*>(p.o);
+
+  // Workgroup -> (head, d_v slice), XCD-aware (workgroup i runs on XCD i % 8).
+  const int64_t nwg = (int64_t)gridDim.x;
+  int64_t lid = blockIdx.x;
+  if ((nwg & 7) == 0) lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
+  const int64_t head = lid / NSPLIT;
+  const int split = (int)(lid - head * NSPLIT);
+  const int64_t bidx = head / p.Hv;
+  const int hv = (int)(head - bidx * p.Hv);
+  const int hk = hv / (p.Hv / p.Hk);
+  const int c0 = split * DVS;
+  const int64_t Tn = p.T;
+  const int64_t nchunks = (Tn + kC - 1) / kC;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool consumer = wave < 4;
+  const int j = lane & 15;
+  const int g = lane >> 4;
+
+  // =====================================================================
+  // Producer side (waves 4-7): thread ptid handles 4 consecutive tokens x
+  // CPT consecutive channels of the chunk, and 4 value columns x TPZ tokens.
+  // =====================================================================
+  const int pw = wave - 4;
+  const int ptid = tid - 256;
+  const int tg = lane & 15;
+  const int ch0 = (pw * 4 + (lane >> 4)) * CPT;
+  constexpr int ZCG = DVS / 4;
+  constexpr int TPZ = kC / (256 / ZCG);
+  const int zc = ptid % ZCG;
+  const int zt = (ptid / ZCG) * TPZ;
+
+  constexpr int QB = CPT * (int)sizeof(T);
+  constexpr int GB = CPT * (int)sizeof(GT);
+  constexpr int VB = 4 * (int)sizeof(T);
+  constexpr int WB = 4 * (int)sizeof(GT);
+  Raw<QB> rq[4], rk[4];
+  Raw<GB> rb[4], rg[4];
+  float sb[4], sg[4];
+  Raw<VB> rv[TPZ];
+  Raw<WB> rw[TPZ];
+  float zb[TPZ];
+
+  auto load_chunk = [&](int64_t tc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t tok = tc + 4 * tg + i;
+      tok = tok < Tn ? tok : Tn - 1;
+      const int64_t qk_off = ((bidx * Tn + tok) * p.Hk + hk) * (int64_t)DK + ch0;
+      ld_raw<QB>(gq + qk_off, rq[i]);
+      ld_raw<QB>(gk + qk_off, rk[i]);
+      if constexpr (CHANNEL) {
+        const int64_t g_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DK + ch0;
+        ld_raw<GB>(gb + g_off, rb[i]);
+        if constexpr (HAS_G) ld_raw<GB>(gg + g_off, rg[i]);
+      } else {
+        const int64_t s_off = (bidx * Tn + tok) * p.Hv + hv;
+        sb[i] = to_f32(gb[s_off]);
+        sg[i] = HAS_G ? to_f32(gg[s_off]) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TPZ; ++i) {
+      int64_t tok = tc + zt + i;
+      tok = tok < Tn ? tok : Tn - 1;
+      const int64_t v_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DV + c0 + 4 * zc;
+      ld_raw<VB>(gv + v_off, rv[i]);
+      if constexpr (CHANNEL) ld_raw<WB>(gw + v_off, rw[i]);
+      else zb[i] = to_f32(gb[(bidx * Tn + tok) * p.Hv + hv]);
+    }
+  };
+
+  // Operands of chunk ci from the raw registers (producer interval 1).
+  auto produce = [&](int64_t ci) {
+    const int64_t t0 = ci * kC;
+    const int slot = (int)(ci & 1);
+    T* sKt = sKt0 + slot * (L::kKtSz / L::ES);
+    float* sR2 = sVec0 + slot * 2 * DK;
+    float* sGC = sR2 + DK;
+    // Only the decay is unpacked for all four tokens (the prefix needs it);
+    // q, k and the erase gate stay packed and are unpacked token by token.
+    float G[4][CPT];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = t0 + 4 * tg + i < Tn;
+      if constexpr (HAS_G) {
+        if constexpr (CHANNEL) {
+          unpack<GT, CPT>(rg[i], valid, G[i]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < CPT; ++e) G[i][e] = valid ? sg[i] : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) G[i][e] = 0.f;
+      }
+    }
+    // Z^T = (w (.) v)^T for this workgroup's columns
+#pragma unroll
+    for (int i = 0; i < TPZ; ++i) {
+      const bool valid = t0 + zt + i < Tn;
+      float zv[4];
+      unpack<T, 4>(rv[i], valid, zv);
+      if constexpr (CHANNEL) {
+        float wz[4];
+        unpack<GT, 4>(rw[i], valid, wz);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zv[e] *= wz[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zv[e] *= zb[i];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sZ[(4 * zc + e) * L::ZP + zt + i] = zv[e];
+    }
+    // cumulative log2-decay over the chunk (4 tokens in-thread, then the 16
+    // token groups of the DPP row), reference r = G at token 31
+    float rr[CPT], gc[CPT], cC[CPT];
+    bool bad = false;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      if constexpr (HAS_G) {
+        G[0][e] *= kLog2e;
+#pragma unroll
+        for (int i = 1; i < 4; ++i) G[i][e] = G[i - 1][e] + G[i][e] * kLog2e;
+        const float tot = G[3][e];
+        float x = tot;
+        x += dpp_row_shr(x, 1);
+        x += dpp_row_shr(x, 2);
+        x += dpp_row_shr(x, 4);
+        x += dpp_row_shr(x, 8);
+        const float excl = x - tot;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) G[i][e] += excl;
+        rr[e] = dpp_row_bcast<7>(G[3][e]);
+        gc[e] = dpp_row_bcast<15>(G[3][e]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad |= !(fabsf(G[i][e] - rr[e]) <= kRange);
+        bad |= !(rr[e] >= -100.f);
+        cC[e] = exp2_fast(gc[e] - rr[e]);
+      } else {
+        rr[e] = 0.f;
+        gc[e] = 0.f;
+        cC[e] = 1.f;
+      }
+    }
+    if constexpr (HAS_G) {
+      const bool any_bad = __any(bad);
+      if (lane == 0) sFlag[slot * 4 + pw] = any_bad ? 1 : 0;
+    } else {
+      if (lane == 0) sFlag[slot * 4 + pw] = 0;
+    }
+    // gated operands, token by token; K_hat is kept (in G) for the
+    // token-contiguous K_hat^T store
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = t0 + 4 * tg + i < Tn;
+      float qv[CPT], kv[CPT], bv[CPT];
+      unpack<T, CPT>(rq[i], valid, qv);
+      unpack<T, CPT>(rk[i], valid, kv);
+      if constexpr (CHANNEL) {
+        unpack<GT, CPT>(rb[i], valid, bv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) bv[e] = valid ? sb[i] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        const float x = G[i][e] - rr[e];
+        const float e1 = HAS_G ? exp2_fast(x) : 1.f;
+        const float e2 = HAS_G ? exp2_fast(-x) : 1.f;
+        bv[e] = -(bv[e] * kv[e]) * e1;  // Ln = -e exp(G - r)
+        qv[e] = qv[e] * e1;             // M  =  q exp(G - r)
+        kv[e] = kv[e] * e2;             // R  =  k exp(r - G)
+        G[i][e] = kv[e] * cC[e];        // K_hat = k exp(G_C - G)
+      }
+      const int t = 4 * tg + i;
+#pragma unroll
+      for (int u = 0; u < CPT / 4; ++u) {
+        const int pos = sig(ch0 + 4 * u);
+        st4<T>(sLn + t * L::DKP + pos, bv[4 * u], bv[4 * u + 1], bv[4 * u + 2], bv[4 * u + 3]);
+        st4<T>(sM + t * L::DKP + pos, qv[4 * u], qv[4 * u + 1], qv[4 * u + 2], qv[4 * u + 3]);
+        st4<T>(sR + t * L::DKP + pos, kv[4 * u], kv[4 * u + 1], kv[4 * u + 2], kv[4 * u + 3]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < CPT; ++e)
+      st4<T>(sKt + (ch0 + e) * L::CP + sig(4 * tg), G[0][e], G[1][e], G[2][e], G[3][e]);
+    if (tg == 0) {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        sR2[ch0 + e] = HAS_G ? exp2_fast(rr[e]) : 1.f;
+        sGC[ch0 + e] = HAS_G ? exp2_fast(gc[e]) : 1.f;
+      }
+    }
+  };
+
+  // Gram tiles and diagonal inverses of the chunk whose operands are in LDS
+  // (producer interval 2).
+  auto gram_and_inverse = [&]() {
+#pragma unroll
+    for (int slot = 0; slot < 5; ++slot) {
+      const int tile = gram_tile(pw, slot);
+      const bool isP = tile >= 10;
+      const int tt = isP ? tile - 10 : tile;
+      const int nt = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+      const int ms = tt - (nt * (nt + 1)) / 2;
+      const T* X = isP ? sM : sLn;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const Frag8<T> a = ld_frag8<T>(sR + (16 * ms + j) * L::DKP + 32 * kb + 8 * g);
+        const Frag8<T> bq = ld_frag8<T>(X + (16 * nt + j) * L::DKP + 32 * kb + 8 * g);
+        mma32(acc, a, bq);
+      }
+      // acc[i] = D[s = 16ms + 4g + i][t = 16nt + j]  (= -A[t][s] or P[t][s])
+      const int t = 16 * nt + j;
+      if (isP) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = (16 * ms + 4 * g + i <= t) ? acc[i] : 0.f;
+        st4<T>(sP + t * L::CP + sig(16 * ms + 4 * g), pv[0], pv[1], pv[2], pv[3]);
+        if (ms == nt && (nt & 1) == 0)  // the causal product reads whole 32-token blocks
+          st4<T>(sP + t * L::CP + sig(16 * (ms + 1) + 4 * g), 0.f, 0.f, 0.f, 0.f);
+      } else if (ms == nt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int sl = 4 * g + i;
+          sAd[(ms * 16 + sl) * 16 + j] = (sl < j) ? -acc[i] : 0.f;  // sAd[blk][s][t] = A[t][s]
+        }
+      } else {
+        st4<T>(sAo + t * L::CP + 16 * ms + 4 * g, acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+    // The diagonal block of this wave was written by this wave only: order
+    // the LDS accesses inside the wave, then invert it.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Row form: T[r][r] = 1, T[r][s] = -sum_{u>s} T[r][u] A[u][s] for s < r.
+    {
+      const int r = j;
+      const float* ad = sAd + pw * 256;  // ad[s * 16 + u] = A[u][s]
+      float trow[16], cur[16], nxt[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 c4 = *reinterpret_cast<const float4*>(ad + 15 * 16 + 4 * q4);
+        cur[4 * q4] = c4.x; cur[4 * q4 + 1] = c4.y; cur[4 * q4 + 2] = c4.z; cur[4 * q4 + 3] = c4.w;
+      }
+#pragma unroll
+      for (int s = 15; s >= 0; --s) {
+        if (s > 0) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 c4 = *reinterpret_cast<const float4*>(ad + (s - 1) * 16 + 4 * q4);
+            nxt[4 * q4] = c4.x; nxt[4 * q4 + 1] = c4.y; nxt[4 * q4 + 2] = c4.z; nxt[4 * q4 + 3] = c4.w;
+          }
+        }
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int u = s + 1; u < 16; ++u) {
+          if (u & 1) a1 -= trow[u] * cur[u];
+          else a0 -= trow[u] * cur[u];
+        }
+        trow[s] = (s > r) ? 0.f : ((s == r) ? 1.f : a0 + a1);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) cur[u] = nxt[u];
+      }
+      if (g == 0) {
+        T* dst = sTd + (pw * 16 + r) * L::TDP;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          st4<T>(dst + 4 * u, trow[4 * u], trow[4 * u + 1], trow[4 * u + 2], trow[4 * u + 3]);
+      }
+    }
+  };
+
+  // =====================================================================
+  // Consumer side (waves 0-3): the state slice S[16mt + 4g + i][col],
+  // col = c0 + 16 * wave + j, in accumulator layout.
+  // =====================================================================
+  const int col = c0 + 16 * wave + j;
+  f32x4 S[MT], X[4], O[4];
+  if (consumer) {
+    const float* sin = p.state_in ? p.state_in + head * (int64_t)DK * DV : nullptr;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[mt][i] = sin ? sin[(16 * mt + 4 * g + i) * DV + col] : 0.f;
+  }
+
+  // X = Z + Ln S~ (= Z - E_bar S) and O^T = S~^T M^T (= (Q_bar S)^T).
+  auto consume_first = [&](int slot) {
+    const float* sR2 = sVec0 + slot * 2 * DK;
+    Frag8<T> sf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x4 lo = S[2 * kb], hi = S[2 * kb + 1];
+      if constexpr (HAS_G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo[i] *= sR2[32 * kb + 4 * g + i];
+          hi[i] *= sR2[32 * kb + 16 + 4 * g + i];
+        }
+      }
+      sf[kb] = frag8_from_acc<T>(lo, hi);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float4 z = *reinterpret_cast<const float4*>(sZ + (16 * wave + j) * L::ZP + 16 * mt + 4 * g);
+      X[mt][0] = z.x; X[mt][1] = z.y; X[mt][2] = z.z; X[mt][3] = z.w;
+      O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const Frag8<T> a = ld_frag8<T>(sLn + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
+        mma32(X[mt], a, sf[kb]);
+        const Frag8<T> bm = ld_frag8<T>(sM + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
+        mma32(O[mt], sf[kb], bm);
+      }
+    }
+  };
+
+  // U = (I + A)^{-1} X, O^T += U^T P^T, S' = Diag(exp(G_C)) S + K_hat^T U, store o.
+  auto consume_second = [&](int64_t ci) {
+    const int slot = (int)(ci & 1);
+    const T* sKt = sKt0 + slot * (L::kKtSz / L::ES);
+    const float* sGC = sVec0 + slot * 2 * DK + DK;
+    f32x4 U[4];
+    Frag4<T> uf[4];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      f32x4 acc = X[bi];
+#pragma unroll
+      for (int bj = 0; bj < bi; ++bj) {
+        const Frag4<T> a = ld_frag4<T>(sAo + (16 * bi + j) * L::CP + 16 * bj + 4 * g);
+        mma16(acc, a, uf[bj]);
+      }
+      const Frag4<T> xf = frag4_from_acc<T>(acc);
+      const Frag4<T> td = ld_frag4<T>(sTd + (bi * 16 + j) * L::TDP + 4 * g);
+      U[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma16(U[bi], td, xf);
+      uf[bi] = frag4_from_acc<T>(U[bi]);
+    }
+    Frag8<T> u8[2];
+    u8[0] = frag8_from_acc<T>(U[0], U[1]);
+    u8[1] = frag8_from_acc<T>(U[2], U[3]);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (32 * kb <= 16 * nt + 15) {
+          const Frag8<T> bp = ld_frag8<T>(sP + (16 * nt + j) * L::CP + 32 * kb + 8 * g);
+          mma32(O[nt], u8[kb], bp);
+        }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if constexpr (HAS_G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[mt][i] *= sGC[16 * mt + 4 * g + i];
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const Frag8<T> a = ld_frag8<T>(sKt + (16 * mt + j) * L::CP + 32 * kb + 8 * g);
+        mma32(S[mt], a, u8[kb]);
+      }
+    }
+    const int64_t t0 = ci * kC;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int64_t tok = t0 + 16 * nt + j;
+      if (tok < Tn) {
+        T* dst = go + ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + 4 * g;
+        st4<T>(dst, p.scale * O[nt][0], p.scale * O[nt][1], p.scale * O[nt][2], p.scale * O[nt][3]);
+      }
+    }
+  };
+
+  // Exact token-by-token recurrence for one chunk, straight from global
+  // memory (chunks whose decay range the factored form cannot represent).
+  auto consume_tokens = [&](int64_t ci) {
+    const int64_t t0 = ci * kC;
+    for (int tl = 0; tl < kC; ++tl) {
+      const int64_t tok = t0 + tl;
+      if (tok >= Tn) break;
+      const int64_t qk_off = ((bidx * Tn + tok) * p.Hk + hk) * (int64_t)DK;
+      const int64_t gt = (bidx * Tn + tok) * p.Hv + hv;
+      float sbeta = 0.f, salpha = 1.f;
+      if constexpr (!CHANNEL) {
+        sbeta = to_f32(gb[gt]);
+        if constexpr (HAS_G) salpha = exp2_fast(to_f32(gg[gt]) * kLog2e);
+      }
+      float rp = 0.f;
+      float kr[MT][4], qr[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = 16 * mt + 4 * g;
+        float er[4], ar[4];
+        load_f32<4, T>(gk + qk_off + row, kr[mt]);
+        load_f32<4, T>(gq + qk_off + row, qr[mt]);
+        if constexpr (CHANNEL) {
+          load_f32<4, GT>(gb + gt * DK + row, er);
+          if constexpr (HAS_G) {
+            load_f32<4, GT>(gg + gt * DK + row, ar);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ar[i] = exp2_fast(ar[i] * kLog2e);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ar[i] = 1.f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { er[i] = sbeta; ar[i] = salpha; }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          S[mt][i] *= ar[i];
+          rp += er[i] * kr[mt][i] * S[mt][i];
+        }
+      }
+      rp += __shfl_xor(rp, 16);
+      rp += __shfl_xor(rp, 32);
+      float z = to_f32(gv[gt * DV + col]);
+      if constexpr (CHANNEL) z *= to_f32(gw[gt * DV + col]);
+      else z *= sbeta;
+      const float d = z - rp;
+      float op = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          S[mt][i] += kr[mt][i] * d;
+          op += qr[mt][i] * S[mt][i];
+        }
+      op += __shfl_xor(op, 16);
+      op += __shfl_xor(op, 32);
+      if (g == 0) go[gt * DV + col] = from_f32<T>(p.scale * op);
+    }
+  };
+
+  // The two roles run separate loops with the same barrier sequence (one
+  // before the first chunk, two per chunk), so that each role's registers are
+  // allocated for its own live values only.
+  if (consumer) {
+    __syncthreads();  // operands of chunk 0 are ready
+    for (int64_t ci = 0; ci < nchunks; ++ci) {
+      const int slot = (int)(ci & 1);
+      const bool slow = (sFlag[slot * 4] | sFlag[slot * 4 + 1] | sFlag[slot * 4 + 2] |
+                         sFlag[slot * 4 + 3]) != 0;
+      if (slow) consume_tokens(ci);
+      else consume_first(slot);
+      __syncthreads();  // barrier A
+      if (!slow) consume_second(ci);
+      __syncthreads();  // barrier B
+    }
+    if (p.state_out) {
+      float* sout = p.state_out + head * (int64_t)DK * DV;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sout[(16 * mt + 4 * g + i) * DV + col] = S[mt][i];
+    }
+  } else {
+    load_chunk(0);
+    produce(0);
+    if (nchunks > 1) load_chunk(kC);
+    __syncthreads();
+    for (int64_t ci = 0; ci < nchunks; ++ci) {
+      const int slot = (int)(ci & 1);
+      const bool slow = (sFlag[slot * 4] | sFlag[slot * 4 + 1] | sFlag[slot * 4 + 2] |
+                         sFlag[slot * 4 + 3]) != 0;
+      if (!slow) gram_and_inverse();
+      __syncthreads();  // barrier A
+      if (ci + 1 < nchunks) {
+        produce(ci + 1);
+        if (ci + 2 < nchunks) load_chunk((ci + 2) * kC);
+      }
+      __syncthreads();  // barrier B
+    }
+  }
+}
+
+template <typename T, typename GT, int DK, int DV, bool CH, bool HG>
+hipError_t launch_pipe_typed(const ChunkArgs& a, hipStream_t stream) {
+  Params p;
+  p.B = a.B; p.T = a.T; p.Hk = a.Hk; p.Hv = a.Hv; p.scale = a.scale;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.b = a.b; p.w = a.w; p.g = a.g;
+  p.state_in = a.state_in; p.state_out = a.state_out; p.o = a.o;
+  const int64_t nwg = a.B * a.Hv * (DV / 64);
+  chunk_fwd_pipe_kernel<T, GT, DK, DV, 64, CH, HG><<<dim3((unsigned)nwg), dim3(kPipeThreads), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <typename GT, int DK, int DV>
+hipError_t pipe_gates(const ChunkArgs& a, hipStream_t s) {
+  const bool hg = a.g != nullptr;
+  if (a.channel) return hg ? launch_pipe_typed<bf16, GT, DK, DV, true, true>(a, s)
+                           : launch_pipe_typed<bf16, GT, DK, DV, true, false>(a, s);
+  return hg ? launch_pipe_typed<bf16, GT, DK, DV, false, true>(a, s)
+            : launch_pipe_typed<bf16, GT, DK, DV, false, false>(a, s);
+}
+
+template <typename GT>
+hipError_t pipe_dims(const ChunkArgs& a, hipStream_t s) {
+  if (a.dk == 128 && a.dv == 128) return pipe_gates<GT, 128, 128>(a, s);
+  if (a.dk == 128 && a.dv == 64) return pipe_gates<GT, 128, 64>(a, s);
+  if (a.dk == 64 && a.dv == 128) return pipe_gates<GT, 64, 128>(a, s);
+  return pipe_gates<GT, 64, 64>(a, s);
+}
+
+}  // namespace
+
+// bf16 operands: producer/consumer kernel.
+hipError_t launch_chunk_fwd_pipe(const ChunkArgs& a, hipStream_t stream) {
+  if (a.gate == DType::F32) return pipe_dims<float>(a, stream);
+  return pipe_dims<bf16>(a, stream);
+}
+
+}  // namespace gdn
