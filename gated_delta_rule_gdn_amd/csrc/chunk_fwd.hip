@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int j = lane & 15;   // MFMA: row/column within a 16x16 tile
   const int g = lane >> 4;   // MFMA: lane group
   const bool colwave = wave < NWC;

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool consumer = wave < 4;
   const int j = lane & 15;
   const int g = lane >> 4;
@@ -148,32 +148,68 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   Raw<WB> rw[TPZ];
   float zb[TPZ];
 
+  // Load addressing: a wave-uniform 64-bit base per chunk (SGPRs) plus a
+  // per-thread 32-bit byte offset that is the same for every chunk, so a
+  // load costs no vector address arithmetic.  Only a partial last chunk
+  // takes the clamped path (tokens past the end re-read the last token and
+  // are zeroed when unpacked).
+  const uint32_t qk_tok = (uint32_t)(p.Hk * DK * (int)sizeof(T));    // bytes per token
+  const uint32_t gc_tok = (uint32_t)(p.Hv * DK * (int)sizeof(GT));   // channel gates
+  const uint32_t gs_tok = (uint32_t)(p.Hv * (int)sizeof(GT));        // scalar gates
+  const uint32_t v_tok = (uint32_t)(p.Hv * DV * (int)sizeof(T));
+  const uint32_t w_tok = (uint32_t)(p.Hv * DV * (int)sizeof(GT));
+  // uniform bases (start of this sequence and head) ...
+  const char* bq = reinterpret_cast<const char*>(gq) + ((uint64_t)bidx * Tn * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
+  const char* bk = reinterpret_cast<const char*>(gk) + ((uint64_t)bidx * Tn * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
+  const char* bbc = reinterpret_cast<const char*>(gb) + ((uint64_t)bidx * Tn * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
+  const char* bgc = reinterpret_cast<const char*>(gg) + ((uint64_t)bidx * Tn * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
+  const char* bbs = reinterpret_cast<const char*>(gb) + ((uint64_t)bidx * Tn * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
+  const char* bgs = reinterpret_cast<const char*>(gg) + ((uint64_t)bidx * Tn * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
+  const char* bv = reinterpret_cast<const char*>(gv) + ((uint64_t)bidx * Tn * v_tok + (uint32_t)((hv * DV + c0) * (int)sizeof(T)));
+  const char* bw = reinterpret_cast<const char*>(gw) + ((uint64_t)bidx * Tn * w_tok + (uint32_t)((hv * DV + c0) * (int)sizeof(GT)));
+  // ... and per-thread 32-bit offsets inside a chunk
+  const uint32_t oq = (uint32_t)(ch0 * (int)sizeof(T));
+  const uint32_t og = (uint32_t)(ch0 * (int)sizeof(GT));
+  const uint32_t ov = (uint32_t)(4 * zc * (int)sizeof(T));
+  const uint32_t ow = (uint32_t)(4 * zc * (int)sizeof(GT));
   auto load_chunk = [&](int64_t tc) {
+    const bool full = tc + kC <= Tn;  // wave-uniform
+    const uint64_t tcu = (uint64_t)tc;
+    const char* cq = bq + tcu * qk_tok;
+    const char* ck = bk + tcu * qk_tok;
+    const char* cbc = bbc + tcu * gc_tok;
+    const char* cgc = bgc + tcu * gc_tok;
+    const char* cbs = bbs + tcu * gs_tok;
+    const char* cgs = bgs + tcu * gs_tok;
+    const char* cv = bv + tcu * v_tok;
+    const char* cw = bw + tcu * w_tok;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int64_t tok = tc + 4 * tg + i;
-      tok = tok < Tn ? tok : Tn - 1;
-      const int64_t qk_off = ((bidx * Tn + tok) * p.Hk + hk) * (int64_t)DK + ch0;
-      ld_raw<QB>(gq + qk_off, rq[i]);
-      ld_raw<QB>(gk + qk_off, rk[i]);
+      uint32_t t = (uint32_t)(4 * tg + i);
+      if (!full) {
+        const int64_t last = Tn - 1 - tc;
+        t = (int64_t)t < last ? t : (uint32_t)last;
+      }
+      ld_raw<QB>(cq + (t * qk_tok + oq), rq[i]);
+      ld_raw<QB>(ck + (t * qk_tok + oq), rk[i]);
       if constexpr (CHANNEL) {
-        const int64_t g_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DK + ch0;
-        ld_raw<GB>(gb + g_off, rb[i]);
-        if constexpr (HAS_G) ld_raw<GB>(gg + g_off, rg[i]);
+        ld_raw<GB>(cbc + (t * gc_tok + og), rb[i]);
+        if constexpr (HAS_G) ld_raw<GB>(cgc + (t * gc_tok + og), rg[i]);
       } else {
-        const int64_t s_off = (bidx * Tn + tok) * p.Hv + hv;
-        sb[i] = to_f32(gb[s_off]);
-        sg[i] = HAS_G ? to_f32(gg[s_off]) : 0.f;
+        sb[i] = to_f32(*reinterpret_cast<const GT*>(cbs + t * gs_tok));
+        sg[i] = HAS_G ? to_f32(*reinterpret_cast<const GT*>(cgs + t * gs_tok)) : 0.f;
       }
     }
 #pragma unroll
     for (int i = 0; i < TPZ; ++i) {
-      int64_t tok = tc + zt + i;
-      tok = tok < Tn ? tok : Tn - 1;
-      const int64_t v_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DV + c0 + 4 * zc;
-      ld_raw<VB>(gv + v_off, rv[i]);
-      if constexpr (CHANNEL) ld_raw<WB>(gw + v_off, rw[i]);
-      else zb[i] = to_f32(gb[(bidx * Tn + tok) * p.Hv + hv]);
+      uint32_t t = (uint32_t)(zt + i);
+      if (!full) {
+        const int64_t last = Tn - 1 - tc;
+        t = (int64_t)t < last ? t : (uint32_t)last;
+      }
+      ld_raw<VB>(cv + (t * v_tok + ov), rv[i]);
+      if constexpr (CHANNEL) ld_raw<WB>(cw + (t * w_tok + ow), rw[i]);
+      else zb[i] = to_f32(*reinterpret_cast<const GT*>(cbs + t * gs_tok));
     }
   };
 
@@ -363,13 +399,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
             nxt[4 * q4] = c4.x; nxt[4 * q4 + 1] = c4.y; nxt[4 * q4 + 2] = c4.z; nxt[4 * q4 + 3] = c4.w;
           }
         }
-        float a0 = 0.f, a1 = 0.f;
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = s + 1; u < 16; ++u) {
-          if (u & 1) a1 -= trow[u] * cur[u];
-          else a0 -= trow[u] * cur[u];
-        }
-        trow[s] = (s > r) ? 0.f : ((s == r) ? 1.f : a0 + a1);
+        for (int u = s + 1; u < 16; ++u) a4[u & 3] -= trow[u] * cur[u];
+        trow[s] = (s > r) ? 0.f : ((s == r) ? 1.f : (a4[0] + a4[1]) + (a4[2] + a4[3]));
 #pragma unroll
         for (int u = 0; u < 16; ++u) cur[u] = nxt[u];
       }

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int cg = tid % CG;
   const int rg = tid / CG;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
 
   float* __restrict__ Sh = S + head * (int64_t)(DK * DV);
 
