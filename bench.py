@@ -89,14 +89,15 @@ def measured_traffic(kernel_key, per_launch_bytes_alg):
 
 
 def cpu_baseline(args):
-    """The oracle, untuned, on the machine's host cores over a bounded sample of
-    the same prefill workload (4 of the 8 sequences, all 16 heads, T=4096)."""
+    """The oracle, untuned, on the machine's host cores over the whole prefill
+    workload (8 sequences x 16 heads x T=4096: about 15 s of CPU work on 16
+    cores); the decode leg is not part of the sample."""
     import torch
 
     import oracle
     import synth
     cfg = synth.CONFIGS["gdn2_bf16_train"]
-    B = 4
+    B = cfg.B
     inp = synth.chunk_inputs(cfg, B=B)
     args64 = {k: (None if v is None else v.to(torch.float64).numpy()) for k, v in inp.items()}
     try:
@@ -109,9 +110,81 @@ def cpu_baseline(args):
                      args64["g"], nthreads=cores)
     dt = time.perf_counter() - t0
     return {"value": B * cfg.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"GDN-2 prefill, {B} of {cfg.B} sequences x {cfg.Hv} heads x T={cfg.T} "
-                      f"(fp64 token recurrence, OpenMP over heads); {dt:.2f} s wall",
+            "sample": f"GDN-2 prefill chunk forward only, all {B} sequences x {cfg.Hv} heads x "
+                      f"T={cfg.T} (fp64 token recurrence, OpenMP over heads); {dt:.2f} s wall",
             "seconds": dt}
+
+
+KERNEL_KEYS = {"chunk_fwd": ("chunk_fwd_pipe_kernel", "chunk_fwd_kernel"),
+               "decode_step": ("decode_kernel",)}
+
+
+def _kernel_key(name):
+    for key, pats in KERNEL_KEYS.items():
+        if any(p in name for p in pats):
+            return key
+    return None
+
+
+def summarize_profiles(kt_csv, fetch_csv, write_csv, commands):
+    """Turn rocprofv3 output into the committed summaries under profiles/:
+    kernel-trace stats (average launch duration per kernel) and HBM traffic
+    per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    what the same counter reads for the plain 1 GiB device copy that
+    `--copy-calibration` runs in the same process."""
+    import csv
+
+    def rows(path):
+        with open(path, newline="") as f:
+            return list(csv.DictReader(f))
+
+    stats = {}
+    for r in rows(kt_csv):
+        key = _kernel_key(r["Name"])
+        if key:
+            stats[key] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                          "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+
+    def counter(path, name):
+        per = {}
+        copy = []
+        for r in rows(path):
+            if r["Counter_Name"] != name:
+                continue
+            v = float(r["Counter_Value"])
+            key = _kernel_key(r["Kernel_Name"])
+            if key:
+                per.setdefault(key, []).append(v)
+            elif "copy" in r["Kernel_Name"].lower():
+                copy.append(v)
+        return per, copy
+
+    fetch, copy_f = counter(fetch_csv, "FETCH_SIZE")
+    write, copy_w = counter(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    # the calibration copy is the largest copy dispatch in the run
+    f_scale = gib_kib / max(copy_f) if copy_f else None
+    w_scale = gib_kib / max(copy_w) if copy_w else None
+    out = {"source_digest": source_digest(), "commands": commands,
+           "calibration": {"copy_bytes": 1 << 30, "fetch_kib": max(copy_f) if copy_f else None,
+                           "write_kib": max(copy_w) if copy_w else None,
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": {}}
+    for key in KERNEL_KEYS:
+        if key not in fetch or key not in write or not f_scale or not w_scale:
+            continue
+        fk = sum(fetch[key]) / len(fetch[key])
+        wk = sum(write[key]) / len(write[key])
+        out["kernels"][key] = {
+            "fetch_kib_raw": fk, "write_kib_raw": wk,
+            "hbm_bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024)),
+            "dispatches": len(fetch[key]),
+            "trace": stats.get(key)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out, stats
 
 
 def main():
@@ -124,7 +197,16 @@ def main():
                     help="cap on oracle threads (the box's CPU share)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("KERNEL_STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 output and exit (no GPU)")
+    ap.add_argument("--profile-commands", nargs="*", default=[],
+                    help="the rocprofv3 commands that made the CSVs (recorded in the summary)")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        out, _ = summarize_profiles(*args.summarize_profiles, commands=args.profile_commands)
+        print(json.dumps(out, indent=1))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
