@@ -77,6 +77,40 @@ __device__ __forceinline__ void unpack(const Raw<NB>& r, bool valid, float* out)
   }
 }
 
+// Unpack N elements of type E to fp32 (no masking: callers zero the raw words
+// of absent tokens).
+template <typename E, int N, int NB>
+__device__ __forceinline__ void unpack(const Raw<NB>& r, float* out) {
+  static_assert(N * (int)sizeof(E) == NB, "raw size");
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if constexpr (sizeof(E) == 2) {
+      const uint32_t w = r.w[i >> 1];
+      out[i] = __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+      out[i] = __uint_as_float(r.w[i]);
+    }
+  }
+}
+template <int NB>
+__device__ __forceinline__ void zero_raw(Raw<NB>& r) {
+#pragma unroll
+  for (int i = 0; i < NB / 4; ++i) r.w[i] = 0u;
+}
+
+// One gate element of type E kept as its raw bits in a 32-bit word (the
+// load is not waited for until the word is converted).
+template <typename E>
+__device__ __forceinline__ uint32_t ld_word(const void* p) {
+  if constexpr (sizeof(E) == 2) return (uint32_t)(*reinterpret_cast<const unsigned short*>(p));
+  else return *reinterpret_cast<const uint32_t*>(p);
+}
+template <typename E>
+__device__ __forceinline__ float word_f32(uint32_t w) {
+  if constexpr (sizeof(E) == 2) return __uint_as_float(w << 16);
+  else return __uint_as_float(w);
+}
+
 // Store 4 consecutive fp32 values as T.
 template <typename T>
 __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {

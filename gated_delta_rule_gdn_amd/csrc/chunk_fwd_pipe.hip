@@ -4,31 +4,35 @@
 // Parallele Efficace par Blocs"): per chunk of 64 tokens, with S the state
 // entering the chunk and r_c a per-channel reference of the cumulative
 // log-decay,
-//   L = e exp(G - r), M = q exp(G - r), R = k exp(r - G)     (elementwise)
+//   L = -e exp(G - r), M = q exp(G - r), R = k exp(r - G)    (elementwise)
 //   A = strict_lower(L R^T), P = lower(M R^T)                (Gram tiles)
-//   X = Z - L S~,  S~ = Diag(exp(r)) S                       (S-dependent)
+//   X = Z + L S~,  S~ = Diag(exp(r)) S                       (S-dependent)
 //   U = (I + A)^{-1} X                                        (forward subst.)
 //   O = M S~ + P U,  S' = Diag(exp(G_C)) S + K_hat^T U.
 //
 // Work split inside one workgroup of 8 waves (two per SIMD):
 //   consumer waves 0-3 own the fp32 state slice (16 value columns each, in
-//     MFMA accumulators) and run only the S-dependent MFMA chain;
-//   producer waves 4-7 build everything that does not depend on S for the
-//     NEXT chunk: loads (prefetched a chunk ahead), cumulative decay, the
-//     exponentials and gated operands (VALU), the A/P Gram tiles (MFMA) and
-//     the 16x16 diagonal inverses (VALU, fp32).
-// VALU work of the producers overlaps MFMA work of the consumers on each
-// SIMD.  Two workgroup barriers per chunk:
+//     MFMA accumulators); they run the S-dependent MFMA chain and, in the
+//     same pass over the operands, the 16 off-diagonal Gram tiles of A and P
+//     (their MFMA pipe would otherwise wait for the producers);
+//   producer waves 4-7 run the VALU side: loads (prefetched a chunk ahead),
+//     the cumulative decay, the exponentials and gated operands, and the four
+//     16x16 diagonal blocks of A with their fp32 inverses.
+// Two workgroup barriers per chunk c:
 //
-//   interval 2(c):  consumers  X = Z - L S~, O = M S~      | producers  Gram(c), inverses(c)
+//   interval 2(c): consumers  X, O (c); off-diagonal A, P tiles (c)
+//                  producers  diagonal A blocks + inverses (c);
+//                             decay prefix, flags, Z^T (c+1); load g, v, w (c+2)
 //   ---- barrier A
-//   interval 1(c):  consumers  U, O += P U, S', store o(c) | producers  operands(c+1)
+//   interval 1(c): consumers  U, O += P U, S', store o (c)
+//                  producers  gated operands L, M, R, K_hat^T (c+1); load q, k, b (c+2)
 //   ---- barrier B
 //
-// Only K_hat^T and the per-channel vectors are read by the consumers in the
-// interval where the producers rewrite them, so only they are double
-// buffered.  A chunk whose decay range would leave the fp32 range of the
-// factored operands is run token by token by the consumers instead.
+// L, M and R are written in interval 1 and read only in interval 2, so they
+// are single buffered; Z^T, K_hat^T, the per-channel vectors and the flags
+// are written one interval ahead of a reader of the previous chunk and are
+// double buffered.  A chunk whose decay range would leave the fp32 range of
+// the factored operands is run token by token by the consumers instead.
 #include "chunk_common.hpp"
 
 namespace gdn {
@@ -54,24 +58,13 @@ struct PipeLds {
   static constexpr int kAo = kP + rnd(kC * CP * ES);
   static constexpr int kTd = kAo + rnd(kC * CP * ES);
   static constexpr int kAd = kTd + rnd(4 * 16 * TDP * ES);
-  static constexpr int kZ = kAd + 4 * 16 * 16 * 4;
-  static constexpr int kVec = kZ + rnd(DVS * ZP * 4);  // two buffers of [exp(r) | exp(G_C)]
+  static constexpr int kZ = kAd + 4 * 16 * 16 * 4;     // two buffers
+  static constexpr int kZSz = rnd(DVS * ZP * 4);
+  static constexpr int kVec = kZ + 2 * kZSz;           // two buffers of [exp(r) | exp(G_C)]
   static constexpr int kFlag = kVec + 2 * 2 * DK * 4;  // two buffers of 4 ints
   static constexpr int kTotal = kFlag + 2 * 4 * 4;
   static_assert(kTotal <= 160 * 1024, "LDS budget");
 };
-
-// Gram tiles per producer wave: slot 0 is the diagonal A block of that wave
-// (inverted by the same wave), the others balance the remaining 16 tiles.
-// Tile ids 0-9 are A tiles, 10-19 P tiles, in (ms, nt) lower-triangle order.
-__device__ __forceinline__ int gram_tile(int pw, int slot) {
-  constexpr int tab[4][5] = {{0, 1, 3, 10, 11}, {2, 4, 6, 12, 13}, {5, 7, 8, 14, 15}, {9, 16, 17, 18, 19}};
-  int t = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-    if (w == pw) t = tab[w][slot];
-  return t;
-}
 
 template <typename T, typename GT, int DK, int DV, int DVS, bool CHANNEL, bool HAS_G>
 __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params p) {
@@ -92,7 +85,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   T* sAo = reinterpret_cast<T*>(smem + L::kAo);
   T* sTd = reinterpret_cast<T*>(smem + L::kTd);
   float* sAd = reinterpret_cast<float*>(smem + L::kAd);
-  float* sZ = reinterpret_cast<float*>(smem + L::kZ);
+  float* sZ0 = reinterpret_cast<float*>(smem + L::kZ);
   float* sVec0 = reinterpret_cast<float*>(smem + L::kVec);
   int* sFlag = reinterpret_cast<int*>(smem + L::kFlag);
 
@@ -104,7 +97,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   const GT* __restrict__ gg = static_cast<const GT*>(p.g);
   T* __restrict__ go = static_cast<T*>(p.o);
 
-  // Workgroup -> (head, d_v slice), XCD-aware (workgroup i runs on XCD i % 8).
+  // Workgroup -> (head, d_v slice), XCD-aware (workgroup i runs on XCD i % 8;
+  // the slices of one head land on the same XCD and share its L2).
   const int64_t nwg = (int64_t)gridDim.x;
   int64_t lid = blockIdx.x;
   if ((nwg & 7) == 0) lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
@@ -141,24 +135,24 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   constexpr int GB = CPT * (int)sizeof(GT);
   constexpr int VB = 4 * (int)sizeof(T);
   constexpr int WB = 4 * (int)sizeof(GT);
+  // raw words of the chunk being prefetched / consumed
   Raw<QB> rq[4], rk[4];
-  Raw<GB> rb[4], rg[4];
-  float sb[4], sg[4];
+  Raw<GB> rb[4], rg[4];     // channel gates
+  uint32_t ub[4], ug[4];    // scalar gates
   Raw<VB> rv[TPZ];
-  Raw<WB> rw[TPZ];
-  float zb[TPZ];
+  Raw<WB> rw[TPZ];          // channel write gate
+  uint32_t uz[TPZ];         // scalar beta for the write side
 
   // Load addressing: a wave-uniform 64-bit base per chunk (SGPRs) plus a
-  // per-thread 32-bit byte offset that is the same for every chunk, so a
-  // load costs no vector address arithmetic.  Only a partial last chunk
-  // takes the clamped path (tokens past the end re-read the last token and
-  // are zeroed when unpacked).
+  // per-thread 32-bit byte offset that is the same for every chunk.  Only a
+  // partial last chunk clamps the token index (tokens past the end re-read
+  // the last token) and then zeroes the raw words of the absent tokens, so
+  // full chunks need no masking anywhere.
   const uint32_t qk_tok = (uint32_t)(p.Hk * DK * (int)sizeof(T));    // bytes per token
   const uint32_t gc_tok = (uint32_t)(p.Hv * DK * (int)sizeof(GT));   // channel gates
   const uint32_t gs_tok = (uint32_t)(p.Hv * (int)sizeof(GT));        // scalar gates
   const uint32_t v_tok = (uint32_t)(p.Hv * DV * (int)sizeof(T));
   const uint32_t w_tok = (uint32_t)(p.Hv * DV * (int)sizeof(GT));
-  // uniform bases (start of this sequence and head) ...
   const char* bq = reinterpret_cast<const char*>(gq) + ((uint64_t)bidx * Tn * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
   const char* bk = reinterpret_cast<const char*>(gk) + ((uint64_t)bidx * Tn * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
   const char* bbc = reinterpret_cast<const char*>(gb) + ((uint64_t)bidx * Tn * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
@@ -167,155 +161,190 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   const char* bgs = reinterpret_cast<const char*>(gg) + ((uint64_t)bidx * Tn * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
   const char* bv = reinterpret_cast<const char*>(gv) + ((uint64_t)bidx * Tn * v_tok + (uint32_t)((hv * DV + c0) * (int)sizeof(T)));
   const char* bw = reinterpret_cast<const char*>(gw) + ((uint64_t)bidx * Tn * w_tok + (uint32_t)((hv * DV + c0) * (int)sizeof(GT)));
-  // ... and per-thread 32-bit offsets inside a chunk
   const uint32_t oq = (uint32_t)(ch0 * (int)sizeof(T));
   const uint32_t og = (uint32_t)(ch0 * (int)sizeof(GT));
   const uint32_t ov = (uint32_t)(4 * zc * (int)sizeof(T));
   const uint32_t ow = (uint32_t)(4 * zc * (int)sizeof(GT));
-  auto load_chunk = [&](int64_t tc) {
+
+  // Decay, value and write gate of the chunk starting at token tc.
+  auto load_gvw = [&](int64_t tc) {
     const bool full = tc + kC <= Tn;  // wave-uniform
+    const int64_t last = Tn - 1 - tc;
     const uint64_t tcu = (uint64_t)tc;
-    const char* cq = bq + tcu * qk_tok;
-    const char* ck = bk + tcu * qk_tok;
-    const char* cbc = bbc + tcu * gc_tok;
     const char* cgc = bgc + tcu * gc_tok;
-    const char* cbs = bbs + tcu * gs_tok;
     const char* cgs = bgs + tcu * gs_tok;
+    const char* cbs = bbs + tcu * gs_tok;
     const char* cv = bv + tcu * v_tok;
     const char* cw = bw + tcu * w_tok;
+    if constexpr (HAS_G) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t t = (uint32_t)(4 * tg + i);
-      if (!full) {
-        const int64_t last = Tn - 1 - tc;
-        t = (int64_t)t < last ? t : (uint32_t)last;
-      }
-      ld_raw<QB>(cq + (t * qk_tok + oq), rq[i]);
-      ld_raw<QB>(ck + (t * qk_tok + oq), rk[i]);
-      if constexpr (CHANNEL) {
-        ld_raw<GB>(cbc + (t * gc_tok + og), rb[i]);
-        if constexpr (HAS_G) ld_raw<GB>(cgc + (t * gc_tok + og), rg[i]);
-      } else {
-        sb[i] = to_f32(*reinterpret_cast<const GT*>(cbs + t * gs_tok));
-        sg[i] = HAS_G ? to_f32(*reinterpret_cast<const GT*>(cgs + t * gs_tok)) : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        uint32_t t = (uint32_t)(4 * tg + i);
+        if (!full) t = (int64_t)t < last ? t : (uint32_t)last;
+        if constexpr (CHANNEL) ld_raw<GB>(cgc + (t * gc_tok + og), rg[i]);
+        else ug[i] = ld_word<GT>(cgs + t * gs_tok);
       }
     }
 #pragma unroll
     for (int i = 0; i < TPZ; ++i) {
       uint32_t t = (uint32_t)(zt + i);
-      if (!full) {
-        const int64_t last = Tn - 1 - tc;
-        t = (int64_t)t < last ? t : (uint32_t)last;
-      }
+      if (!full) t = (int64_t)t < last ? t : (uint32_t)last;
       ld_raw<VB>(cv + (t * v_tok + ov), rv[i]);
       if constexpr (CHANNEL) ld_raw<WB>(cw + (t * w_tok + ow), rw[i]);
-      else zb[i] = to_f32(*reinterpret_cast<const GT*>(cbs + t * gs_tok));
+      else uz[i] = ld_word<GT>(cbs + t * gs_tok);
+    }
+    if (!full) {  // absent tokens: g = 0 (no decay), z = 0
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((int64_t)(4 * tg + i) > last) {
+          if constexpr (HAS_G) {
+            if constexpr (CHANNEL) zero_raw(rg[i]);
+            else ug[i] = 0u;
+          }
+        }
+#pragma unroll
+      for (int i = 0; i < TPZ; ++i)
+        if ((int64_t)(zt + i) > last) zero_raw(rv[i]);
+    }
+  };
+  // Query, key and erase gate of the chunk starting at token tc.
+  auto load_qkb = [&](int64_t tc) {
+    const bool full = tc + kC <= Tn;
+    const int64_t last = Tn - 1 - tc;
+    const uint64_t tcu = (uint64_t)tc;
+    const char* cq = bq + tcu * qk_tok;
+    const char* ck = bk + tcu * qk_tok;
+    const char* cbc = bbc + tcu * gc_tok;
+    const char* cbs = bbs + tcu * gs_tok;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t t = (uint32_t)(4 * tg + i);
+      if (!full) t = (int64_t)t < last ? t : (uint32_t)last;
+      ld_raw<QB>(cq + (t * qk_tok + oq), rq[i]);
+      ld_raw<QB>(ck + (t * qk_tok + oq), rk[i]);
+      if constexpr (CHANNEL) ld_raw<GB>(cbc + (t * gc_tok + og), rb[i]);
+      else ub[i] = ld_word<GT>(cbs + t * gs_tok);
+    }
+    if (!full) {  // absent tokens: q = k = 0, b = 0
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if ((int64_t)(4 * tg + i) > last) {
+          zero_raw(rq[i]);
+          zero_raw(rk[i]);
+          if constexpr (CHANNEL) zero_raw(rb[i]);
+          else ub[i] = 0u;
+        }
     }
   };
 
-  // Operands of chunk ci from the raw registers (producer interval 1).
-  auto produce = [&](int64_t ci) {
-    const int64_t t0 = ci * kC;
+  // Decay prefix of chunk ci, carried from part 1 to part 2 in registers:
+  // x = G - r (log2 units) per token and channel, and exp2(G_C - r).
+  float X2[4][CPT], cC[CPT];
+
+  // Part 1 of the operands of chunk ci: cumulative decay, range flag,
+  // per-channel vectors and Z^T (producer interval 2 of chunk ci - 1).
+  auto produce_decay = [&](int64_t ci) {
     const int slot = (int)(ci & 1);
-    T* sKt = sKt0 + slot * (L::kKtSz / L::ES);
+    float* sZ = sZ0 + slot * (L::kZSz / 4);
     float* sR2 = sVec0 + slot * 2 * DK;
     float* sGC = sR2 + DK;
-    // Only the decay is unpacked for all four tokens (the prefix needs it);
-    // q, k and the erase gate stay packed and are unpacked token by token.
-    float G[4][CPT];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool valid = t0 + 4 * tg + i < Tn;
-      if constexpr (HAS_G) {
-        if constexpr (CHANNEL) {
-          unpack<GT, CPT>(rg[i], valid, G[i]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < CPT; ++e) G[i][e] = valid ? sg[i] : 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) G[i][e] = 0.f;
-      }
-    }
     // Z^T = (w (.) v)^T for this workgroup's columns
 #pragma unroll
     for (int i = 0; i < TPZ; ++i) {
-      const bool valid = t0 + zt + i < Tn;
       float zv[4];
-      unpack<T, 4>(rv[i], valid, zv);
+      unpack<T, 4>(rv[i], zv);
       if constexpr (CHANNEL) {
         float wz[4];
-        unpack<GT, 4>(rw[i], valid, wz);
+        unpack<GT, 4>(rw[i], wz);
 #pragma unroll
         for (int e = 0; e < 4; ++e) zv[e] *= wz[e];
       } else {
+        const float beta = word_f32<GT>(uz[i]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) zv[e] *= zb[i];
+        for (int e = 0; e < 4; ++e) zv[e] *= beta;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) sZ[(4 * zc + e) * L::ZP + zt + i] = zv[e];
     }
-    // cumulative log2-decay over the chunk (4 tokens in-thread, then the 16
-    // token groups of the DPP row), reference r = G at token 31
-    float rr[CPT], gc[CPT], cC[CPT];
-    bool bad = false;
+    if constexpr (HAS_G) {
+      // cumulative log2-decay over the chunk (4 tokens in-thread, then the
+      // 16 token groups of the DPP row); reference r = G at token 31
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      if constexpr (HAS_G) {
-        G[0][e] *= kLog2e;
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (CHANNEL) {
+          unpack<GT, CPT>(rg[i], X2[i]);
+        } else {
+          const float gi = word_f32<GT>(ug[i]);
 #pragma unroll
-        for (int i = 1; i < 4; ++i) G[i][e] = G[i - 1][e] + G[i][e] * kLog2e;
-        const float tot = G[3][e];
+          for (int e = 0; e < CPT; ++e) X2[i][e] = gi;
+        }
+      }
+      float worst = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        X2[0][e] *= kLog2e;
+#pragma unroll
+        for (int i = 1; i < 4; ++i) X2[i][e] = X2[i - 1][e] + X2[i][e] * kLog2e;
+        const float tot = X2[3][e];
         float x = tot;
         x += dpp_row_shr(x, 1);
         x += dpp_row_shr(x, 2);
         x += dpp_row_shr(x, 4);
         x += dpp_row_shr(x, 8);
         const float excl = x - tot;
+        const float rr = dpp_row_bcast<7>(x);
+        const float gc = dpp_row_bcast<15>(x);
+        // x = G - r; the range test needs only the largest |x| of the thread
 #pragma unroll
-        for (int i = 0; i < 4; ++i) G[i][e] += excl;
-        rr[e] = dpp_row_bcast<7>(G[3][e]);
-        gc[e] = dpp_row_bcast<15>(G[3][e]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bad |= !(fabsf(G[i][e] - rr[e]) <= kRange);
-        bad |= !(rr[e] >= -100.f);
-        cC[e] = exp2_fast(gc[e] - rr[e]);
-      } else {
-        rr[e] = 0.f;
-        gc[e] = 0.f;
-        cC[e] = 1.f;
+        for (int i = 0; i < 4; ++i) X2[i][e] += excl - rr;
+        worst = fmaxf(worst, fmaxf(fmaxf(fabsf(X2[0][e]), fabsf(X2[1][e])),
+                                   fmaxf(fabsf(X2[2][e]), fabsf(X2[3][e]))));
+        worst = fmaxf(worst, -100.f - rr + kRange);  // > kRange iff r < -100
+        cC[e] = exp2_fast(gc - rr);
+        if (tg == 0) {
+          sR2[ch0 + e] = exp2_fast(rr);
+          sGC[ch0 + e] = exp2_fast(gc);
+        }
       }
-    }
-    if constexpr (HAS_G) {
-      const bool any_bad = __any(bad);
+      const bool any_bad = __any(!(worst <= kRange));
       if (lane == 0) sFlag[slot * 4 + pw] = any_bad ? 1 : 0;
     } else {
       if (lane == 0) sFlag[slot * 4 + pw] = 0;
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        if (tg == 0) {
+          sR2[ch0 + e] = 1.f;
+          sGC[ch0 + e] = 1.f;
+        }
+      }
     }
-    // gated operands, token by token; K_hat is kept (in G) for the
-    // token-contiguous K_hat^T store
+  };
+
+  // Part 2: gated operands of chunk ci (producer interval 1 of chunk ci - 1).
+  auto produce_operands = [&](int64_t ci) {
+    const int slot = (int)(ci & 1);
+    T* sKt = sKt0 + slot * (L::kKtSz / L::ES);
+    float kh[4][CPT];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool valid = t0 + 4 * tg + i < Tn;
       float qv[CPT], kv[CPT], bv[CPT];
-      unpack<T, CPT>(rq[i], valid, qv);
-      unpack<T, CPT>(rk[i], valid, kv);
+      unpack<T, CPT>(rq[i], qv);
+      unpack<T, CPT>(rk[i], kv);
       if constexpr (CHANNEL) {
-        unpack<GT, CPT>(rb[i], valid, bv);
+        unpack<GT, CPT>(rb[i], bv);
       } else {
+        const float beta = word_f32<GT>(ub[i]);
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) bv[e] = valid ? sb[i] : 0.f;
+        for (int e = 0; e < CPT; ++e) bv[e] = beta;
       }
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
-        const float x = G[i][e] - rr[e];
-        const float e1 = HAS_G ? exp2_fast(x) : 1.f;
-        const float e2 = HAS_G ? exp2_fast(-x) : 1.f;
-        bv[e] = -(bv[e] * kv[e]) * e1;  // Ln = -e exp(G - r)
-        qv[e] = qv[e] * e1;             // M  =  q exp(G - r)
-        kv[e] = kv[e] * e2;             // R  =  k exp(r - G)
-        G[i][e] = kv[e] * cC[e];        // K_hat = k exp(G_C - G)
+        const float e1 = HAS_G ? exp2_fast(X2[i][e]) : 1.f;
+        const float e2 = HAS_G ? exp2_fast(-X2[i][e]) : 1.f;
+        bv[e] = -(bv[e] * kv[e]) * e1;          // Ln = -e exp(G - r)
+        qv[e] = qv[e] * e1;                     // M  =  q exp(G - r)
+        kv[e] = kv[e] * e2;                     // R  =  k exp(r - G)
+        kh[i][e] = HAS_G ? kv[e] * cC[e] : kv[e];  // K_hat = k exp(G_C - G)
       }
       const int t = 4 * tg + i;
 #pragma unroll
@@ -328,90 +357,52 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
     }
 #pragma unroll
     for (int e = 0; e < CPT; ++e)
-      st4<T>(sKt + (ch0 + e) * L::CP + sig(4 * tg), G[0][e], G[1][e], G[2][e], G[3][e]);
-    if (tg == 0) {
-#pragma unroll
-      for (int e = 0; e < CPT; ++e) {
-        sR2[ch0 + e] = HAS_G ? exp2_fast(rr[e]) : 1.f;
-        sGC[ch0 + e] = HAS_G ? exp2_fast(gc[e]) : 1.f;
-      }
-    }
+      st4<T>(sKt + (ch0 + e) * L::CP + sig(4 * tg), kh[0][e], kh[1][e], kh[2][e], kh[3][e]);
   };
 
-  // Gram tiles and diagonal inverses of the chunk whose operands are in LDS
-  // (producer interval 2).
-  auto gram_and_inverse = [&]() {
+  // Diagonal block pw of A and its inverse (producer interval 2).
+  auto diag_inverse = [&]() {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int slot = 0; slot < 5; ++slot) {
-      const int tile = gram_tile(pw, slot);
-      const bool isP = tile >= 10;
-      const int tt = isP ? tile - 10 : tile;
-      const int nt = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
-      const int ms = tt - (nt * (nt + 1)) / 2;
-      const T* X = isP ? sM : sLn;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const Frag8<T> a = ld_frag8<T>(sR + (16 * ms + j) * L::DKP + 32 * kb + 8 * g);
-        const Frag8<T> bq = ld_frag8<T>(X + (16 * nt + j) * L::DKP + 32 * kb + 8 * g);
-        mma32(acc, a, bq);
-      }
-      // acc[i] = D[s = 16ms + 4g + i][t = 16nt + j]  (= -A[t][s] or P[t][s])
-      const int t = 16 * nt + j;
-      if (isP) {
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = (16 * ms + 4 * g + i <= t) ? acc[i] : 0.f;
-        st4<T>(sP + t * L::CP + sig(16 * ms + 4 * g), pv[0], pv[1], pv[2], pv[3]);
-        if (ms == nt && (nt & 1) == 0)  // the causal product reads whole 32-token blocks
-          st4<T>(sP + t * L::CP + sig(16 * (ms + 1) + 4 * g), 0.f, 0.f, 0.f, 0.f);
-      } else if (ms == nt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int sl = 4 * g + i;
-          sAd[(ms * 16 + sl) * 16 + j] = (sl < j) ? -acc[i] : 0.f;  // sAd[blk][s][t] = A[t][s]
-        }
-      } else {
-        st4<T>(sAo + t * L::CP + 16 * ms + 4 * g, acc[0], acc[1], acc[2], acc[3]);
-      }
+    for (int kb = 0; kb < KB; ++kb) {
+      const Frag8<T> a = ld_frag8<T>(sR + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
+      const Frag8<T> b = ld_frag8<T>(sLn + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
+      mma32(acc, a, b);
     }
-    // The diagonal block of this wave was written by this wave only: order
-    // the LDS accesses inside the wave, then invert it.
+    // acc[i] = -A[t = 16pw + j][s = 16pw + 4g + i]; keep the strict lower part
+    float* ad = sAd + pw * 256;  // ad[s * 16 + u] = A[u][s]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sl = 4 * g + i;
+      ad[sl * 16 + j] = (sl < j) ? -acc[i] : 0.f;
+    }
+    // The block was written by this wave only: order the LDS accesses inside
+    // the wave, then invert it.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // Row form: T[r][r] = 1, T[r][s] = -sum_{u>s} T[r][u] A[u][s] for s < r.
-    {
-      const int r = j;
-      const float* ad = sAd + pw * 256;  // ad[s * 16 + u] = A[u][s]
-      float trow[16], cur[16], nxt[16];
+    // Row form of (I + A)^{-1}: T[r][s] = [s == r] - sum_{u>s} T[r][u] A[u][s].
+    // For s > r every T[r][u] with u > s is zero, so no lane needs a branch.
+    const int r = j;
+    float trow[16];
+#pragma unroll
+    for (int s = 15; s >= 0; --s) {
+      float col[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 c4 = *reinterpret_cast<const float4*>(ad + 15 * 16 + 4 * q4);
-        cur[4 * q4] = c4.x; cur[4 * q4 + 1] = c4.y; cur[4 * q4 + 2] = c4.z; cur[4 * q4 + 3] = c4.w;
+        const float4 c4 = *reinterpret_cast<const float4*>(ad + s * 16 + 4 * q4);
+        col[4 * q4] = c4.x; col[4 * q4 + 1] = c4.y; col[4 * q4 + 2] = c4.z; col[4 * q4 + 3] = c4.w;
       }
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 15; s >= 0; --s) {
-        if (s > 0) {
+      for (int u = s + 1; u < 16; ++u) a4[u & 3] -= trow[u] * col[u];
+      trow[s] = ((a4[0] + a4[1]) + (a4[2] + a4[3])) + ((s == r) ? 1.f : 0.f);
+    }
+    if (g == 0) {
+      T* dst = sTd + (pw * 16 + r) * L::TDP;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 c4 = *reinterpret_cast<const float4*>(ad + (s - 1) * 16 + 4 * q4);
-            nxt[4 * q4] = c4.x; nxt[4 * q4 + 1] = c4.y; nxt[4 * q4 + 2] = c4.z; nxt[4 * q4 + 3] = c4.w;
-          }
-        }
-        float a4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = s + 1; u < 16; ++u) a4[u & 3] -= trow[u] * cur[u];
-        trow[s] = (s > r) ? 0.f : ((s == r) ? 1.f : (a4[0] + a4[1]) + (a4[2] + a4[3]));
-#pragma unroll
-        for (int u = 0; u < 16; ++u) cur[u] = nxt[u];
-      }
-      if (g == 0) {
-        T* dst = sTd + (pw * 16 + r) * L::TDP;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          st4<T>(dst + 4 * u, trow[4 * u], trow[4 * u + 1], trow[4 * u + 2], trow[4 * u + 3]);
-      }
+      for (int u = 0; u < 4; ++u)
+        st4<T>(dst + 4 * u, trow[4 * u], trow[4 * u + 1], trow[4 * u + 2], trow[4 * u + 3]);
     }
   };
 
@@ -430,9 +421,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
         S[mt][i] = sin ? sin[(16 * mt + 4 * g + i) * DV + col] : 0.f;
   }
 
-  // X = Z + Ln S~ (= Z - E_bar S) and O^T = S~^T M^T (= (Q_bar S)^T).
+  // X = Z + Ln S~ (= Z - E_bar S), O^T = S~^T M^T (= (Q_bar S)^T), and the
+  // Gram tiles of this wave w: P(ms = w, nt = n) for n >= w and
+  // A(ms = n, nt = w) for n < w (four tiles per wave, ten P and six
+  // off-diagonal A tiles in all), sharing the operand fragment loads.
   auto consume_first = [&](int slot) {
     const float* sR2 = sVec0 + slot * 2 * DK;
+    const float* sZ = sZ0 + slot * (L::kZSz / 4);
+    const int w = wave;
     Frag8<T> sf[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -446,20 +442,54 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
       }
       sf[kb] = frag8_from_acc<T>(lo, hi);
     }
+    f32x4 tacc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const float4 z = *reinterpret_cast<const float4*>(sZ + (16 * wave + j) * L::ZP + 16 * mt + 4 * g);
       X[mt][0] = z.x; X[mt][1] = z.y; X[mt][2] = z.z; X[mt][3] = z.w;
       O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      Frag8<T> ln[4], mm[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const Frag8<T> a = ld_frag8<T>(sLn + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
-        mma32(X[mt], a, sf[kb]);
-        const Frag8<T> bm = ld_frag8<T>(sM + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
-        mma32(O[mt], sf[kb], bm);
+        ln[mt] = ld_frag8<T>(sLn + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
+        mm[mt] = ld_frag8<T>(sM + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
+      }
+      const Frag8<T> rw = ld_frag8<T>(sR + (16 * w + j) * L::DKP + 32 * kb + 8 * g);
+      const Frag8<T> lw = ld_frag8<T>(sLn + (16 * w + j) * L::DKP + 32 * kb + 8 * g);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        mma32(X[mt], ln[mt], sf[kb]);
+        mma32(O[mt], sf[kb], mm[mt]);
+      }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        if (n >= w) {
+          mma32(tacc[n], rw, mm[n]);
+        } else {
+          const Frag8<T> rn = ld_frag8<T>(sR + (16 * n + j) * L::DKP + 32 * kb + 8 * g);
+          mma32(tacc[n], rn, lw);
+        }
+      }
+    }
+    // tacc[n][i] = D[s][t]: P tiles s = 16w + 4g + i, t = 16n + j;
+    //                       A tiles s = 16n + 4g + i, t = 16w + j (= -A[t][s])
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      if (n >= w) {
+        const int t = 16 * n + j;
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = (16 * w + 4 * g + i <= t) ? tacc[n][i] : 0.f;
+        st4<T>(sP + t * L::CP + sig(16 * w + 4 * g), pv[0], pv[1], pv[2], pv[3]);
+        if (n == w && (w & 1) == 0)  // the causal product reads whole 32-token blocks
+          st4<T>(sP + t * L::CP + sig(16 * (w + 1) + 4 * g), 0.f, 0.f, 0.f, 0.f);
+      } else {
+        const int t = 16 * w + j;
+        st4<T>(sAo + t * L::CP + 16 * n + 4 * g, tacc[n][0], tacc[n][1], tacc[n][2], tacc[n][3]);
       }
     }
   };
@@ -604,19 +634,28 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
         for (int i = 0; i < 4; ++i) sout[(16 * mt + 4 * g + i) * DV + col] = S[mt][i];
     }
   } else {
-    load_chunk(0);
-    produce(0);
-    if (nchunks > 1) load_chunk(kC);
+    load_gvw(0);
+    load_qkb(0);
+    produce_decay(0);
+    produce_operands(0);
+    if (nchunks > 1) {
+      load_gvw(kC);
+      load_qkb(kC);
+    }
     __syncthreads();
     for (int64_t ci = 0; ci < nchunks; ++ci) {
       const int slot = (int)(ci & 1);
       const bool slow = (sFlag[slot * 4] | sFlag[slot * 4 + 1] | sFlag[slot * 4 + 2] |
                          sFlag[slot * 4 + 3]) != 0;
-      if (!slow) gram_and_inverse();
+      if (!slow) diag_inverse();
+      if (ci + 1 < nchunks) {
+        produce_decay(ci + 1);
+        if (ci + 2 < nchunks) load_gvw((ci + 2) * kC);
+      }
       __syncthreads();  // barrier A
       if (ci + 1 < nchunks) {
-        produce(ci + 1);
-        if (ci + 2 < nchunks) load_chunk((ci + 2) * kC);
+        produce_operands(ci + 1);
+        if (ci + 2 < nchunks) load_qkb((ci + 2) * kC);
       }
       __syncthreads();  // barrier B
     }
