@@ -40,6 +40,11 @@ namespace {
 
 constexpr int kPipeThreads = 512;  // 4 consumer + 4 producer waves
 
+template <int N>
+struct IntTag {
+  static constexpr int value = N;
+};
+
 template <typename T, int DK, int DVS>
 struct PipeLds {
   static constexpr int ES = (int)sizeof(T);
@@ -57,8 +62,7 @@ struct PipeLds {
   static constexpr int kP = kKt + 2 * kKtSz;
   static constexpr int kAo = kP + rnd(kC * CP * ES);
   static constexpr int kTd = kAo + rnd(kC * CP * ES);
-  static constexpr int kAd = kTd + rnd(4 * 16 * TDP * ES);
-  static constexpr int kZ = kAd + 4 * 16 * 16 * 4;     // two buffers
+  static constexpr int kZ = kTd + rnd(4 * 16 * TDP * ES);  // two buffers
   static constexpr int kZSz = rnd(DVS * ZP * 4);
   static constexpr int kVec = kZ + 2 * kZSz;           // two buffers of [exp(r) | exp(G_C)]
   static constexpr int kFlag = kVec + 2 * 2 * DK * 4;  // two buffers of 4 ints
@@ -84,7 +88,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   T* sP = reinterpret_cast<T*>(smem + L::kP);
   T* sAo = reinterpret_cast<T*>(smem + L::kAo);
   T* sTd = reinterpret_cast<T*>(smem + L::kTd);
-  float* sAd = reinterpret_cast<float*>(smem + L::kAd);
   float* sZ0 = reinterpret_cast<float*>(smem + L::kZ);
   float* sVec0 = reinterpret_cast<float*>(smem + L::kVec);
   int* sFlag = reinterpret_cast<int*>(smem + L::kFlag);
@@ -360,50 +363,60 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
       st4<T>(sKt + (ch0 + e) * L::CP + sig(4 * tg), kh[0][e], kh[1][e], kh[2][e], kh[3][e]);
   };
 
-  // Diagonal block pw of A and its inverse (producer interval 2).
+  // Diagonal block pw of A and its inverse (producer interval 2).  With
+  // N = -A (strictly lower, so N^16 = 0),
+  //   (I + A)^{-1} = I + N + ... + N^15 = (I + N)(I + N^2)(I + N^4)(I + N^8),
+  // four levels of 16x16 products on the fp32 MFMA instead of a 16-step
+  // substitution.  Fragment layouts (lane = 16 g + j):
+  //   row form  rowL(X): X[j][4g + i]   (A operand of mma16)
+  //   acc form  accL(X): X[4g + i][j]   (B operand and result of mma16)
+  // mma16(acc, rowL(X), accL(Y)) adds accL(X Y); accL(X) = rowL(X^T).
   auto diag_inverse = [&]() {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 nrow = {0.f, 0.f, 0.f, 0.f}, ncol = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const Frag8<T> a = ld_frag8<T>(sR + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
       const Frag8<T> b = ld_frag8<T>(sLn + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
-      mma32(acc, a, b);
+      mma32(nrow, a, b);  // [4g+i][j] of R Ln^T = N[j][4g+i]
+      mma32(ncol, b, a);  // [4g+i][j] of Ln R^T = N[4g+i][j]
     }
-    // acc[i] = -A[t = 16pw + j][s = 16pw + 4g + i]; keep the strict lower part
-    float* ad = sAd + pw * 256;  // ad[s * 16 + u] = A[u][s]
+    Frag4<float> nr, nc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int sl = 4 * g + i;
-      ad[sl * 16 + j] = (sl < j) ? -acc[i] : 0.f;
+      nr.v[i] = (4 * g + i < j) ? nrow[i] : 0.f;  // rowL(N)
+      nc.v[i] = (j < 4 * g + i) ? ncol[i] : 0.f;  // accL(N)
     }
-    // The block was written by this wave only: order the LDS accesses inside
-    // the wave, then invert it.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // Row form of (I + A)^{-1}: T[r][s] = [s == r] - sum_{u>s} T[r][u] A[u][s].
-    // For s > r every T[r][u] with u > s is zero, so no lane needs a branch.
-    const int r = j;
-    float trow[16];
+    auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      mma16(acc, x, y);
+      Frag4<float> f;
 #pragma unroll
-    for (int s = 15; s >= 0; --s) {
-      float col[16];
+      for (int i = 0; i < 4; ++i) f.v[i] = acc[i];
+      return f;
+    };
+    const Frag4<float> n2c = prod(nr, nc);    // accL(N^2)
+    const Frag4<float> n2r = prod(nc, nr);    // rowL(N^2) = accL(N^T N^T)
+    const Frag4<float> n4c = prod(n2r, n2c);  // accL(N^4)
+    const Frag4<float> n4r = prod(n2c, n2r);  // rowL(N^4)
+    const Frag4<float> n8c = prod(n4r, n4c);  // accL(N^8)
+    // accL(T^T), T^T = (I + N^8)^T (I + N^4)^T (I + N^2)^T (I + N)^T, built
+    // by left products starting from accL((I + N)^T) = rowL(I + N).
+    Frag4<float> t;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 c4 = *reinterpret_cast<const float4*>(ad + s * 16 + 4 * q4);
-        col[4 * q4] = c4.x; col[4 * q4 + 1] = c4.y; col[4 * q4 + 2] = c4.z; col[4 * q4 + 3] = c4.w;
-      }
-      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) t.v[i] = nr.v[i] + ((4 * g + i == j) ? 1.f : 0.f);
+    auto step = [](const Frag4<float>& x, const Frag4<float>& c) {  // accL(C + X C), x = rowL(X)
+      f32x4 acc = {c.v[0], c.v[1], c.v[2], c.v[3]};
+      mma16(acc, x, c);
+      Frag4<float> f;
 #pragma unroll
-      for (int u = s + 1; u < 16; ++u) a4[u & 3] -= trow[u] * col[u];
-      trow[s] = ((a4[0] + a4[1]) + (a4[2] + a4[3])) + ((s == r) ? 1.f : 0.f);
-    }
-    if (g == 0) {
-      T* dst = sTd + (pw * 16 + r) * L::TDP;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        st4<T>(dst + 4 * u, trow[4 * u], trow[4 * u + 1], trow[4 * u + 2], trow[4 * u + 3]);
-    }
+      for (int i = 0; i < 4; ++i) f.v[i] = acc[i];
+      return f;
+    };
+    t = step(n2c, t);  // rowL((N^2)^T) = accL(N^2)
+    t = step(n4c, t);
+    t = step(n8c, t);
+    // t = accL(T^T) = rowL(T): lane (g, j) holds T[j][4g .. 4g+3]
+    st4<T>(sTd + (pw * 16 + j) * L::TDP + 4 * g, t.v[0], t.v[1], t.v[2], t.v[3]);
   };
 
   // =====================================================================
@@ -425,10 +438,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   // Gram tiles of this wave w: P(ms = w, nt = n) for n >= w and
   // A(ms = n, nt = w) for n < w (four tiles per wave, ten P and six
   // off-diagonal A tiles in all), sharing the operand fragment loads.
-  auto consume_first = [&](int slot) {
+  auto consume_first = [&](int slot, auto wave_tag) {
+    constexpr int w = decltype(wave_tag)::value;  // == wave
     const float* sR2 = sVec0 + slot * 2 * DK;
     const float* sZ = sZ0 + slot * (L::kZSz / 4);
-    const int w = wave;
     Frag8<T> sf[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -620,8 +633,18 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
       const int slot = (int)(ci & 1);
       const bool slow = (sFlag[slot * 4] | sFlag[slot * 4 + 1] | sFlag[slot * 4 + 2] |
                          sFlag[slot * 4 + 3]) != 0;
-      if (slow) consume_tokens(ci);
-      else consume_first(slot);
+      if (slow) {
+        consume_tokens(ci);
+      } else {
+        // one instantiation per wave, so the tile choice is resolved at
+        // compile time and the MFMA sequence has no branches
+        switch (wave) {
+          case 0: consume_first(slot, IntTag<0>{}); break;
+          case 1: consume_first(slot, IntTag<1>{}); break;
+          case 2: consume_first(slot, IntTag<2>{}); break;
+          default: consume_first(slot, IntTag<3>{}); break;
+        }
+      }
       __syncthreads();  // barrier A
       if (!slow) consume_second(ci);
       __syncthreads();  // barrier B
@@ -638,25 +661,24 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
     load_qkb(0);
     produce_decay(0);
     produce_operands(0);
-    if (nchunks > 1) {
-      load_gvw(kC);
-      load_qkb(kC);
-    }
+    load_gvw(nchunks > 1 ? kC : 0);
+    load_qkb(nchunks > 1 ? kC : 0);
     __syncthreads();
+    // The prefetch of chunk ci + 2 is issued on every iteration (the last
+    // two re-read the final chunk): with a fixed number of loads in flight
+    // the wait for the older half of the registers does not drain the
+    // younger loads, whose latency would otherwise be exposed.
     for (int64_t ci = 0; ci < nchunks; ++ci) {
       const int slot = (int)(ci & 1);
       const bool slow = (sFlag[slot * 4] | sFlag[slot * 4 + 1] | sFlag[slot * 4 + 2] |
                          sFlag[slot * 4 + 3]) != 0;
+      const int64_t pre = (ci + 2 < nchunks ? ci + 2 : nchunks - 1) * kC;
       if (!slow) diag_inverse();
-      if (ci + 1 < nchunks) {
-        produce_decay(ci + 1);
-        if (ci + 2 < nchunks) load_gvw((ci + 2) * kC);
-      }
+      if (ci + 1 < nchunks) produce_decay(ci + 1);
+      load_gvw(pre);
       __syncthreads();  // barrier A
-      if (ci + 1 < nchunks) {
-        produce_operands(ci + 1);
-        if (ci + 2 < nchunks) load_qkb((ci + 2) * kC);
-      }
+      if (ci + 1 < nchunks) produce_operands(ci + 1);
+      load_qkb(pre);
       __syncthreads();  // barrier B
     }
   }
