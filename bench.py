@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3        # MI355X dense fp32 MFMA, published
 CHUNK = 64
 
 
@@ -86,6 +87,49 @@ def measured_traffic(kernel_key, per_launch_bytes_alg):
     if not ent:
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
+    """Chunk-forward timings of the other prefill workloads (not part of the
+    step): launch time from HIP events on the launch stream, against the same
+    algorithmic bytes and flops as the headline workload."""
+    res = {}
+    for name in ("gdn1_fp32_small", "gdn1_bf16_train", "gdn1_grouped_long"):
+        cfg = synth.CONFIGS[name]
+        inp = synth.chunk_inputs(cfg, device="cuda")
+        o = torch.empty((cfg.B, cfg.T, cfg.Hv, cfg.dv), dtype=cfg.io_dtype, device=dev)
+        s = torch.empty((cfg.B, cfg.Hv, cfg.dk, cfg.dv), dtype=torch.float32, device=dev)
+
+        def run():
+            gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta_or_b"], w=inp["w"], g=inp["g"],
+                              state_in=inp["state_in"], state_out=s, o=o)
+        for _ in range(warmup):
+            run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            run()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        io_bytes = 4 if cfg.io_dtype == torch.float32 else 2
+        gate_bytes = 4 if cfg.gate_dtype == torch.float32 else 2
+        nbytes, flops = chunk_algorithmic(cfg, gate_bytes, io_bytes=io_bytes,
+                                          state_in=inp["state_in"] is not None)
+        if cfg.Hv != cfg.Hk:  # q k^T and k k^T are shared by the value heads of a key head
+            G = cfg.Hv // cfg.Hk
+            flops = 2.0 * (CHUNK / 2 * (cfg.dk + 2 * cfg.dv) + 3 * cfg.dk * cfg.dv
+                           + CHUNK * cfg.dk / G) * cfg.B * cfg.T * cfg.Hv
+        res[name] = {"ms": round(ms, 4), "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+                     "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
+                                        (PEAK_FP32_TFLOPS if io_bytes == 4 else PEAK_BF16_TFLOPS), 4)}
+        del inp, o, s
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(args):
@@ -193,6 +237,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the chunk-forward timings of the other prefill workloads")
     ap.add_argument("--cpu-threads", type=int, default=16,
                     help="cap on oracle threads (the box's CPU share)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -322,6 +368,8 @@ def main():
         "rooflines": {"chunk_fwd": roof_c, "decode_step": roof_d},
         "source_digest": source_digest(),
     }
+    if not args.no_secondary:
+        out["secondary"] = secondary_chunk_workloads(gdn, synth, torch, dev)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}

@@ -18,6 +18,12 @@
 //   producer waves 4-7 run the VALU side: loads (prefetched a chunk ahead),
 //     the cumulative decay, the exponentials and gated operands, and the four
 //     16x16 diagonal blocks of A with their fp32 inverses.
+// With scalar gates (Gated DeltaNet, DeltaNet) the decay factors out of the
+// Gram matrices ("Gated DeltaNet-2", §3; the GDN-1 form of the scope): the
+// producers store raw q and k, and the per-token factors exp(G_t - r),
+// exp(r - G_t), beta_t are applied as a 64x64 mask on the Gram tiles and as
+// row scales of the MFMA results, so the producers do no per-element math.
+//
 // Two workgroup barriers per chunk c:
 //
 //   interval 2(c): consumers  X, O (c); off-diagonal A, P tiles (c)
@@ -65,7 +71,8 @@ struct PipeLds {
   static constexpr int kZ = kTd + rnd(4 * 16 * TDP * ES);  // two buffers
   static constexpr int kZSz = rnd(DVS * ZP * 4);
   static constexpr int kVec = kZ + 2 * kZSz;           // two buffers of [exp(r) | exp(G_C)]
-  static constexpr int kFlag = kVec + 2 * 2 * DK * 4;  // two buffers of 4 ints
+  static constexpr int kTok = kVec + 2 * 2 * DK * 4;   // two buffers of [8][64] per-token factors
+  static constexpr int kFlag = kTok + 2 * 8 * kC * 4;  // two buffers of 4 ints
   static constexpr int kTotal = kFlag + 2 * 4 * 4;
   static_assert(kTotal <= 160 * 1024, "LDS budget");
 };
@@ -91,6 +98,16 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   float* sZ0 = reinterpret_cast<float*>(smem + L::kZ);
   float* sVec0 = reinterpret_cast<float*>(smem + L::kVec);
   int* sFlag = reinterpret_cast<int*>(smem + L::kFlag);
+  float* sTok0 = reinterpret_cast<float*>(smem + L::kTok);
+  // Scalar gates: per-token factors of chunk ci in sTok0 + (ci & 1) * 512,
+  // each a [64] vector (x_t = (G_t - r) log2 e, r = G at token 31):
+  constexpr int kFE1 = 0;  // exp2(x_t)
+  constexpr int kFE2 = 1;  // exp2(-x_t)
+  constexpr int kFNB = 2;  // -beta_t exp2(x_t)
+  constexpr int kFX = 3;   // -beta_t exp(G_t): X = Z + diag(FX) K S
+  constexpr int kFO = 4;   // exp(G_t):         O = diag(FO) Q S + P U
+  constexpr int kFK = 5;   // exp(G_C - G_t):   S' = exp(G_C) S + K^T diag(FK) U
+  constexpr int kFG = 6;   // [0] = exp(G_C)
 
   const T* __restrict__ gq = static_cast<const T*>(p.q);
   const T* __restrict__ gk = static_cast<const T*>(p.k);
@@ -269,7 +286,54 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
 #pragma unroll
       for (int e = 0; e < 4; ++e) sZ[(4 * zc + e) * L::ZP + zt + i] = zv[e];
     }
-    if constexpr (HAS_G) {
+    if constexpr (!CHANNEL) {
+      // one decay per token: prefix over the 4 tokens of the thread and the
+      // 16 token groups of the DPP row; every lane row computes the same.
+      float gt[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gt[i] = HAS_G ? word_f32<GT>(ug[i]) : 0.f;
+#pragma unroll
+      for (int i = 1; i < 4; ++i) gt[i] += gt[i - 1];
+      float x = gt[3];
+      x += dpp_row_shr(x, 1);
+      x += dpp_row_shr(x, 2);
+      x += dpp_row_shr(x, 4);
+      x += dpp_row_shr(x, 8);
+      const float rr = dpp_row_bcast<7>(x);
+      const float gc = dpp_row_bcast<15>(x);
+      const float sh = (x - gt[3] - rr) * kLog2e;
+      float xt[4];
+      float worst = -100.f - rr * kLog2e + kRange;  // > kRange iff r < -100 (log2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xt[i] = fmaf(gt[i], kLog2e, sh);
+        worst = fmaxf(worst, fabsf(xt[i]));
+      }
+      const bool any_bad = __any(!(worst <= kRange));
+      if (lane == 0) sFlag[slot * 4 + pw] = any_bad ? 1 : 0;
+      if (g == 0) {  // lanes 0-15 hold tokens 4 tg .. 4 tg + 3
+        float* tok = sTok0 + slot * 8 * kC;
+        const float r2 = exp2_fast(rr * kLog2e);
+        const float cC = exp2_fast((gc - rr) * kLog2e);
+        float f[6][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e1 = exp2_fast(xt[i]);
+          const float e2 = exp2_fast(-xt[i]);
+          const float nb = -word_f32<GT>(ub[i]) * e1;
+          f[kFE1][i] = e1;
+          f[kFE2][i] = e2;
+          f[kFNB][i] = nb;
+          f[kFX][i] = nb * r2;
+          f[kFO][i] = e1 * r2;
+          f[kFK][i] = cC * e2;
+        }
+#pragma unroll
+        for (int a = 0; a < 6; ++a)
+          *reinterpret_cast<float4*>(tok + a * kC + 4 * tg) = make_float4(f[a][0], f[a][1], f[a][2], f[a][3]);
+        if (tg == 0 && pw == 0) tok[kFG * kC] = exp2_fast(gc * kLog2e);
+      }
+    } else if constexpr (HAS_G) {
       // cumulative log2-decay over the chunk (4 tokens in-thread, then the
       // 16 token groups of the DPP row); reference r = G at token 31
 #pragma unroll
@@ -327,6 +391,30 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   auto produce_operands = [&](int64_t ci) {
     const int slot = (int)(ci & 1);
     T* sKt = sKt0 + slot * (L::kKtSz / L::ES);
+    if constexpr (!CHANNEL) {
+      // raw q and k rows (each run of 4 channels at its accumulator-order
+      // position) and raw k^T (4 tokens per channel, repacked with v_perm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * tg + i;
+#pragma unroll
+        for (int u = 0; u < CPT / 4; ++u) {
+          const int pos = sig(ch0 + 4 * u);
+          *reinterpret_cast<uint2*>(sM + t * L::DKP + pos) = make_uint2(rq[i].w[2 * u], rq[i].w[2 * u + 1]);
+          *reinterpret_cast<uint2*>(sR + t * L::DKP + pos) = make_uint2(rk[i].w[2 * u], rk[i].w[2 * u + 1]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < CPT / 2; ++m) {
+        const uint32_t lo01 = __builtin_amdgcn_perm(rk[1].w[m], rk[0].w[m], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(rk[3].w[m], rk[2].w[m], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(rk[1].w[m], rk[0].w[m], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(rk[3].w[m], rk[2].w[m], 0x07060302u);
+        *reinterpret_cast<uint2*>(sKt + (ch0 + 2 * m) * L::CP + sig(4 * tg)) = make_uint2(lo01, lo23);
+        *reinterpret_cast<uint2*>(sKt + (ch0 + 2 * m + 1) * L::CP + sig(4 * tg)) = make_uint2(hi01, hi23);
+      }
+      return;
+    }
     float kh[4][CPT];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -371,20 +459,43 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   //   row form  rowL(X): X[j][4g + i]   (A operand of mma16)
   //   acc form  accL(X): X[4g + i][j]   (B operand and result of mma16)
   // mma16(acc, rowL(X), accL(Y)) adds accL(X Y); accL(X) = rowL(X^T).
-  auto diag_inverse = [&]() {
-    f32x4 nrow = {0.f, 0.f, 0.f, 0.f}, ncol = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const Frag8<T> a = ld_frag8<T>(sR + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
-      const Frag8<T> b = ld_frag8<T>(sLn + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
-      mma32(nrow, a, b);  // [4g+i][j] of R Ln^T = N[j][4g+i]
-      mma32(ncol, b, a);  // [4g+i][j] of Ln R^T = N[4g+i][j]
-    }
+  auto diag_inverse = [&](int slot) {
     Frag4<float> nr, nc;
+    if constexpr (CHANNEL) {
+      f32x4 nrow = {0.f, 0.f, 0.f, 0.f}, ncol = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      nr.v[i] = (4 * g + i < j) ? nrow[i] : 0.f;  // rowL(N)
-      nc.v[i] = (j < 4 * g + i) ? ncol[i] : 0.f;  // accL(N)
+      for (int kb = 0; kb < KB; ++kb) {
+        const Frag8<T> a = ld_frag8<T>(sR + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
+        const Frag8<T> b = ld_frag8<T>(sLn + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
+        mma32(nrow, a, b);  // [4g+i][j] of R Ln^T = N[j][4g+i]
+        mma32(ncol, b, a);  // [4g+i][j] of Ln R^T = N[4g+i][j]
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        nr.v[i] = (4 * g + i < j) ? nrow[i] : 0.f;  // rowL(N)
+        nc.v[i] = (j < 4 * g + i) ? ncol[i] : 0.f;  // accL(N)
+      }
+    } else {
+      // K K^T is symmetric: one product gives both orientations; the mask
+      // -beta_t exp(G_t - G_s) = FNB[t] FE2[s] makes N[t][s] = -A[t][s].
+      const float* tok = sTok0 + slot * 8 * kC;
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const Frag8<T> a = ld_frag8<T>(sR + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
+        mma32(d, a, a);  // [4g+i][j] = k_(16pw+4g+i) . k_(16pw+j)
+      }
+      const float4 nb4 = *reinterpret_cast<const float4*>(tok + kFNB * kC + 16 * pw + 4 * g);
+      const float4 e24 = *reinterpret_cast<const float4*>(tok + kFE2 * kC + 16 * pw + 4 * g);
+      const float nbj = tok[kFNB * kC + 16 * pw + j];
+      const float e2j = tok[kFE2 * kC + 16 * pw + j];
+      const float nbv[4] = {nb4.x, nb4.y, nb4.z, nb4.w};
+      const float e2v[4] = {e24.x, e24.y, e24.z, e24.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        nr.v[i] = (4 * g + i < j) ? nbj * e2v[i] * d[i] : 0.f;
+        nc.v[i] = (j < 4 * g + i) ? nbv[i] * e2j * d[i] : 0.f;
+      }
     }
     auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -446,7 +557,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x4 lo = S[2 * kb], hi = S[2 * kb + 1];
-      if constexpr (HAS_G) {
+      if constexpr (HAS_G && CHANNEL) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           lo[i] *= sR2[32 * kb + 4 * g + i];
@@ -458,21 +569,27 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
     f32x4 tacc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const float4 z = *reinterpret_cast<const float4*>(sZ + (16 * wave + j) * L::ZP + 16 * mt + 4 * g);
-      X[mt][0] = z.x; X[mt][1] = z.y; X[mt][2] = z.z; X[mt][3] = z.w;
+      if constexpr (CHANNEL) {
+        const float4 z = *reinterpret_cast<const float4*>(sZ + (16 * wave + j) * L::ZP + 16 * mt + 4 * g);
+        X[mt][0] = z.x; X[mt][1] = z.y; X[mt][2] = z.z; X[mt][3] = z.w;
+      } else {
+        X[mt] = f32x4{0.f, 0.f, 0.f, 0.f};  // K S first, then Z + diag(FX) K S
+      }
       O[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       tacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // scalar gates: L is raw k (sR) and the decay is applied afterwards
+    const T* sL = CHANNEL ? sLn : sR;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       Frag8<T> ln[4], mm[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        ln[mt] = ld_frag8<T>(sLn + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
+        ln[mt] = ld_frag8<T>(sL + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
         mm[mt] = ld_frag8<T>(sM + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
       }
       const Frag8<T> rw = ld_frag8<T>(sR + (16 * w + j) * L::DKP + 32 * kb + 8 * g);
-      const Frag8<T> lw = ld_frag8<T>(sLn + (16 * w + j) * L::DKP + 32 * kb + 8 * g);
+      const Frag8<T> lw = CHANNEL ? ld_frag8<T>(sLn + (16 * w + j) * L::DKP + 32 * kb + 8 * g) : rw;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         mma32(X[mt], ln[mt], sf[kb]);
@@ -486,6 +603,29 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
           const Frag8<T> rn = ld_frag8<T>(sR + (16 * n + j) * L::DKP + 32 * kb + 8 * g);
           mma32(tacc[n], rn, lw);
         }
+      }
+    }
+    if constexpr (!CHANNEL) {
+      const float* tok = sTok0 + slot * 8 * kC;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float4 z = *reinterpret_cast<const float4*>(sZ + (16 * wave + j) * L::ZP + 16 * mt + 4 * g);
+        const float4 fx = *reinterpret_cast<const float4*>(tok + kFX * kC + 16 * mt + 4 * g);
+        const float fo = tok[kFO * kC + 16 * mt + j];  // O^T: token 16 mt + j of this lane
+        X[mt][0] = fmaf(fx.x, X[mt][0], z.x); X[mt][1] = fmaf(fx.y, X[mt][1], z.y);
+        X[mt][2] = fmaf(fx.z, X[mt][2], z.z); X[mt][3] = fmaf(fx.w, X[mt][3], z.w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[mt][i] *= fo;
+      }
+      // Gram masks: P[t][s] *= FE1[t] FE2[s], -A[t][s] = FNB[t] FE2[s] (k_t . k_s)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int t = (n >= w) ? 16 * n + j : 16 * w + j;
+        const int s0 = (n >= w) ? 16 * w + 4 * g : 16 * n + 4 * g;
+        const float ft = tok[((n >= w) ? kFE1 : kFNB) * kC + t];
+        const float4 fs = *reinterpret_cast<const float4*>(tok + kFE2 * kC + s0);
+        tacc[n][0] *= ft * fs.x; tacc[n][1] *= ft * fs.y;
+        tacc[n][2] *= ft * fs.z; tacc[n][3] *= ft * fs.w;
       }
     }
     // tacc[n][i] = D[s][t]: P tiles s = 16w + 4g + i, t = 16n + j;
@@ -531,6 +671,22 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
     Frag8<T> u8[2];
     u8[0] = frag8_from_acc<T>(U[0], U[1]);
     u8[1] = frag8_from_acc<T>(U[2], U[3]);
+    // state update operand: U itself (channel gates, K_hat^T holds the
+    // decay) or diag(FK) U with raw k^T (scalar gates)
+    Frag8<T> uk[2] = {u8[0], u8[1]};
+    float gC = 1.f;
+    if constexpr (!CHANNEL) {
+      const float* tok = sTok0 + slot * 8 * kC;
+      f32x4 us[4];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const float4 fk = *reinterpret_cast<const float4*>(tok + kFK * kC + 16 * bi + 4 * g);
+        us[bi] = f32x4{U[bi][0] * fk.x, U[bi][1] * fk.y, U[bi][2] * fk.z, U[bi][3] * fk.w};
+      }
+      uk[0] = frag8_from_acc<T>(us[0], us[1]);
+      uk[1] = frag8_from_acc<T>(us[2], us[3]);
+      gC = tok[kFG * kC];
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -541,14 +697,17 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
         }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      if constexpr (HAS_G) {
+      if constexpr (HAS_G && CHANNEL) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[mt][i] *= sGC[16 * mt + 4 * g + i];
+      } else if constexpr (HAS_G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[mt][i] *= gC;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const Frag8<T> a = ld_frag8<T>(sKt + (16 * mt + j) * L::CP + 32 * kb + 8 * g);
-        mma32(S[mt], a, u8[kb]);
+        mma32(S[mt], a, uk[kb]);
       }
     }
     const int64_t t0 = ci * kC;
@@ -673,7 +832,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
       const bool slow = (sFlag[slot * 4] | sFlag[slot * 4 + 1] | sFlag[slot * 4 + 2] |
                          sFlag[slot * 4 + 3]) != 0;
       const int64_t pre = (ci + 2 < nchunks ? ci + 2 : nchunks - 1) * kC;
-      if (!slow) diag_inverse();
+      if (!slow) diag_inverse(slot);
       if (ci + 1 < nchunks) produce_decay(ci + 1);
       load_gvw(pre);
       __syncthreads();  // barrier A
