@@ -588,8 +588,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
         ln[mt] = ld_frag8<T>(sL + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
         mm[mt] = ld_frag8<T>(sM + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
       }
-      const Frag8<T> rw = ld_frag8<T>(sR + (16 * w + j) * L::DKP + 32 * kb + 8 * g);
-      const Frag8<T> lw = CHANNEL ? ld_frag8<T>(sLn + (16 * w + j) * L::DKP + 32 * kb + 8 * g) : rw;
+      // Gram operands: with scalar gates L is raw k, so R(w) and R(n) are
+      // the L fragments already loaded; Ln(w) is always ln[w]
+      const Frag8<T> rw = CHANNEL ? ld_frag8<T>(sR + (16 * w + j) * L::DKP + 32 * kb + 8 * g) : ln[w];
+      const Frag8<T> lw = ln[w];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         mma32(X[mt], ln[mt], sf[kb]);
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
         if (n >= w) {
           mma32(tacc[n], rw, mm[n]);
         } else {
-          const Frag8<T> rn = ld_frag8<T>(sR + (16 * n + j) * L::DKP + 32 * kb + 8 * g);
+          const Frag8<T> rn = CHANNEL ? ld_frag8<T>(sR + (16 * n + j) * L::DKP + 32 * kb + 8 * g) : ln[n];
           mma32(tacc[n], rn, lw);
         }
       }
