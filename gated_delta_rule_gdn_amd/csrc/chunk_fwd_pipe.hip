@@ -268,7 +268,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
     float* sZ = sZ0 + slot * (L::kZSz / 4);
     float* sR2 = sVec0 + slot * 2 * DK;
     float* sGC = sR2 + DK;
-    // Z^T = (w (.) v)^T for this workgroup's columns
+    // Z^T = (w (.) v)^T for this workgroup's columns: the TPZ = 4
+    // consecutive tokens of a column go out as one 16-byte store
+    static_assert(TPZ == 4, "Z^T store");
+    float zz[4][TPZ];
 #pragma unroll
     for (int i = 0; i < TPZ; ++i) {
       float zv[4];
@@ -284,8 +287,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
         for (int e = 0; e < 4; ++e) zv[e] *= beta;
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sZ[(4 * zc + e) * L::ZP + zt + i] = zv[e];
+      for (int e = 0; e < 4; ++e) zz[e][i] = zv[e];
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      *reinterpret_cast<float4*>(sZ + (4 * zc + e) * L::ZP + zt) = make_float4(zz[e][0], zz[e][1], zz[e][2], zz[e][3]);
     if constexpr (!CHANNEL) {
       // one decay per token: prefix over the 4 tokens of the thread and the
       // 16 token groups of the DPP row; every lane row computes the same.
