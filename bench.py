@@ -171,11 +171,12 @@ def _kernel_key(name):
 
 
 def summarize_profiles(kt_csv, fetch_csv, write_csv, commands):
-    """Turn rocprofv3 output into the committed summaries under profiles/:
-    kernel-trace stats (average launch duration per kernel) and HBM traffic
-    per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
-    what the same counter reads for the plain 1 GiB device copy that
-    `--copy-calibration` runs in the same process."""
+    """Turn rocprofv3 output into profiles/traffic.json: kernel-trace stats
+    (average launch duration per kernel) and HBM traffic per launch from
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the same
+    counter reads for the plain 1 GiB device copy that `--copy-calibration`
+    runs last in the same process.  Profile with `--no-secondary`, so that the
+    only chunk-forward dispatches are those of the headline workload."""
     import csv
 
     def rows(path):
@@ -200,7 +201,9 @@ def summarize_profiles(kt_csv, fetch_csv, write_csv, commands):
             if key:
                 per.setdefault(key, []).append(v)
             elif "copy" in r["Kernel_Name"].lower():
-                copy.append(v)
+                copy.append((int(r["Dispatch_Id"]), v))
+        # the calibration copies are the last dispatches of the process
+        copy = [v for _, v in sorted(copy)[-1:]]
         return per, copy
 
     fetch, copy_f = counter(fetch_csv, "FETCH_SIZE")
