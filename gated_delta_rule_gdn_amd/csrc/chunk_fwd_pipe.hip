@@ -56,6 +56,13 @@ struct PipeLds {
   static constexpr int ES = (int)sizeof(T);
   static constexpr int PADT = 16 / ES;
   static constexpr int DKP = DK + PADT;  // pitch of [64][DK] operand arrays
+  // Element offset of (row, pos) in a [64][DK] operand array.  The 16-byte
+  // column blocks of each row are XOR-swizzled by (row / 8) mod 8: the
+  // producers store rows four tokens apart and the consumers read sixteen
+  // consecutive rows, and both then spread over all banks.
+  __device__ static constexpr int at(int row, int pos) {
+    return row * DKP + (pos ^ (8 * ((row >> 3) & 7)));
+  }
   static constexpr int CP = kC + PADT;   // pitch of [*][64] operand arrays
   static constexpr int TDP = 16 + PADT;  // pitch of the diagonal inverses
   static constexpr int ZP = kC + 4;      // pitch of Z^T (fp32)
@@ -406,8 +413,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
 #pragma unroll
         for (int u = 0; u < CPT / 4; ++u) {
           const int pos = sig(ch0 + 4 * u);
-          *reinterpret_cast<uint2*>(sM + t * L::DKP + pos) = make_uint2(rq[i].w[2 * u], rq[i].w[2 * u + 1]);
-          *reinterpret_cast<uint2*>(sR + t * L::DKP + pos) = make_uint2(rk[i].w[2 * u], rk[i].w[2 * u + 1]);
+          *reinterpret_cast<uint2*>(sM + L::at(t, pos)) = make_uint2(rq[i].w[2 * u], rq[i].w[2 * u + 1]);
+          *reinterpret_cast<uint2*>(sR + L::at(t, pos)) = make_uint2(rk[i].w[2 * u], rk[i].w[2 * u + 1]);
         }
       }
 #pragma unroll
@@ -447,9 +454,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
 #pragma unroll
       for (int u = 0; u < CPT / 4; ++u) {
         const int pos = sig(ch0 + 4 * u);
-        st4<T>(sLn + t * L::DKP + pos, bv[4 * u], bv[4 * u + 1], bv[4 * u + 2], bv[4 * u + 3]);
-        st4<T>(sM + t * L::DKP + pos, qv[4 * u], qv[4 * u + 1], qv[4 * u + 2], qv[4 * u + 3]);
-        st4<T>(sR + t * L::DKP + pos, kv[4 * u], kv[4 * u + 1], kv[4 * u + 2], kv[4 * u + 3]);
+        st4<T>(sLn + L::at(t, pos), bv[4 * u], bv[4 * u + 1], bv[4 * u + 2], bv[4 * u + 3]);
+        st4<T>(sM + L::at(t, pos), qv[4 * u], qv[4 * u + 1], qv[4 * u + 2], qv[4 * u + 3]);
+        st4<T>(sR + L::at(t, pos), kv[4 * u], kv[4 * u + 1], kv[4 * u + 2], kv[4 * u + 3]);
       }
     }
 #pragma unroll
@@ -471,8 +478,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
       f32x4 nrow = {0.f, 0.f, 0.f, 0.f}, ncol = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const Frag8<T> a = ld_frag8<T>(sR + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
-        const Frag8<T> b = ld_frag8<T>(sLn + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
+        const Frag8<T> a = ld_frag8<T>(sR + L::at(16 * pw + j, 32 * kb + 8 * g));
+        const Frag8<T> b = ld_frag8<T>(sLn + L::at(16 * pw + j, 32 * kb + 8 * g));
         mma32(nrow, a, b);  // [4g+i][j] of R Ln^T = N[j][4g+i]
         mma32(ncol, b, a);  // [4g+i][j] of Ln R^T = N[4g+i][j]
       }
@@ -488,7 +495,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
       f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const Frag8<T> a = ld_frag8<T>(sR + (16 * pw + j) * L::DKP + 32 * kb + 8 * g);
+        const Frag8<T> a = ld_frag8<T>(sR + L::at(16 * pw + j, 32 * kb + 8 * g));
         mma32(d, a, a);  // [4g+i][j] = k_(16pw+4g+i) . k_(16pw+j)
       }
       const float4 nb4 = *reinterpret_cast<const float4*>(tok + kFNB * kC + 16 * pw + 4 * g);
@@ -591,12 +598,12 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
       Frag8<T> ln[4], mm[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        ln[mt] = ld_frag8<T>(sL + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
-        mm[mt] = ld_frag8<T>(sM + (16 * mt + j) * L::DKP + 32 * kb + 8 * g);
+        ln[mt] = ld_frag8<T>(sL + L::at(16 * mt + j, 32 * kb + 8 * g));
+        mm[mt] = ld_frag8<T>(sM + L::at(16 * mt + j, 32 * kb + 8 * g));
       }
       // Gram operands: with scalar gates L is raw k, so R(w) and R(n) are
       // the L fragments already loaded; Ln(w) is always ln[w]
-      const Frag8<T> rw = CHANNEL ? ld_frag8<T>(sR + (16 * w + j) * L::DKP + 32 * kb + 8 * g) : ln[w];
+      const Frag8<T> rw = CHANNEL ? ld_frag8<T>(sR + L::at(16 * w + j, 32 * kb + 8 * g)) : ln[w];
       const Frag8<T> lw = ln[w];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -608,7 +615,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
         if (n >= w) {
           mma32(tacc[n], rw, mm[n]);
         } else {
-          const Frag8<T> rn = CHANNEL ? ld_frag8<T>(sR + (16 * n + j) * L::DKP + 32 * kb + 8 * g) : ln[n];
+          const Frag8<T> rn = CHANNEL ? ld_frag8<T>(sR + L::at(16 * n + j, 32 * kb + 8 * g)) : ln[n];
           mma32(tacc[n], rn, lw);
         }
       }
