@@ -621,6 +621,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
       }
     }
     if constexpr (!CHANNEL) {
+      // keep the factor loads below out of the MFMA loop (register budget)
+      __builtin_amdgcn_sched_barrier(0);
       const float* tok = sTok0 + slot * 8 * kC;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
