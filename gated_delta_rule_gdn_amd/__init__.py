@@ -6,5 +6,6 @@ sources under csrc/.  This package holds the thin ctypes binding only.
 from .gdn import (  # noqa: F401
     GDN_BF16, GDN_ERR_HIP, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_F32,
     GDN_GATES_CHANNEL, GDN_GATES_SCALAR, GDN_OK, GdnDecodeDesc, GdnError, GdnFwdDesc,
-    abi_version, gdn_chunk_fwd, gdn_decode_step, lib, status_string,
+    GdnVarlenDesc, abi_version, gdn_chunk_fwd, gdn_chunk_fwd_varlen, gdn_decode_step, lib,
+    status_string,
 )

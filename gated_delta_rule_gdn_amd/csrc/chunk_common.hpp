@@ -170,7 +170,8 @@ __device__ __forceinline__ Frag4<T> frag4_from_acc(const f32x4& a) {
 }
 
 struct Params {
-  int64_t B, T;
+  int64_t B, T;      // sequences, tokens per sequence (packed total when cu is set)
+  const int64_t* cu; // packed sequences: [B + 1] token offsets, or nullptr
   int Hk, Hv;
   float scale;
   const void *q, *k, *v, *b, *w, *g;

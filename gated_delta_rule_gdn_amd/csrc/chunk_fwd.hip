@@ -126,9 +126,30 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
   const int hv = (int)(head - bidx * p.Hv);
   const int hk = hv / (p.Hv / p.Hk);
   const int c0 = split * DVS;  // first value column of this workgroup
-  const int64_t Tn = p.T;  // tokens per sequence
+  // Token range of this sequence: [tok0, tok0 + Tn) in the token-major
+  // tensors.  Packed sequences read their range from cu (clamped into the
+  // tensor, so malformed offsets cannot reach outside it; an empty range only
+  // passes the state through).
+  int64_t tok0 = bidx * p.T, Tn = p.T;
+  if (p.cu) {
+    int64_t a0 = p.cu[bidx], a1 = p.cu[bidx + 1];
+    a0 = a0 < 0 ? 0 : (a0 > p.T ? p.T : a0);
+    a1 = a1 < a0 ? a0 : (a1 > p.T ? p.T : a1);
+    tok0 = a0;
+    Tn = a1 - a0;
+  }
 
   const int tid = threadIdx.x;
+  if (Tn == 0) {  // an empty packed sequence only passes its state through
+    if (p.state_out) {
+      const int64_t base = head * (int64_t)DK * DV + c0;
+      for (int idx = tid; idx < DK * DVS; idx += (int)blockDim.x) {
+        const int64_t e = base + (int64_t)(idx / DVS) * DV + (idx % DVS);
+        p.state_out[e] = p.state_in ? p.state_in[e] : 0.f;
+      }
+    }
+    return;
+  }
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int j = lane & 15;   // MFMA: row/column within a 16x16 tile
@@ -175,15 +196,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
     for (int i = 0; i < 4; ++i) {
       int64_t tok = tc + 4 * tg + i;
       tok = tok < Tn ? tok : Tn - 1;
-      const int64_t qk_off = ((bidx * Tn + tok) * p.Hk + hk) * (int64_t)DK + ch0;
+      const int64_t qk_off = ((tok0 + tok) * p.Hk + hk) * (int64_t)DK + ch0;
       ld_raw<QB>(gq + qk_off, rq[i]);
       ld_raw<QB>(gk + qk_off, rk[i]);
       if constexpr (CHANNEL) {
-        const int64_t g_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DK + ch0;
+        const int64_t g_off = ((tok0 + tok) * p.Hv + hv) * (int64_t)DK + ch0;
         ld_raw<GB>(gb + g_off, rb[i]);
         if constexpr (HAS_G) ld_raw<GB>(gg + g_off, rg[i]);
       } else {
-        const int64_t s_off = (bidx * Tn + tok) * p.Hv + hv;
+        const int64_t s_off = (tok0 + tok) * p.Hv + hv;
         sb[i] = to_f32(gb[s_off]);
         sg[i] = HAS_G ? to_f32(gg[s_off]) : 0.f;
       }
@@ -192,15 +213,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
     for (int i = 0; i < TPZ; ++i) {
       int64_t tok = tc + zt + i;
       tok = tok < Tn ? tok : Tn - 1;
-      const int64_t v_off = ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DV + c0 + 4 * zc;
+      const int64_t v_off = ((tok0 + tok) * p.Hv + hv) * (int64_t)DV + c0 + 4 * zc;
       ld_raw<VB>(gv + v_off, rv[i]);
       if constexpr (CHANNEL) ld_raw<WB>(gw + v_off, rw[i]);
-      else zb[i] = to_f32(gb[(bidx * Tn + tok) * p.Hv + hv]);
+      else zb[i] = to_f32(gb[(tok0 + tok) * p.Hv + hv]);
     }
   };
 
   const int64_t nchunks = (Tn + kC - 1) / kC;
-  load_chunk(0);
+  load_chunk(0);  // nchunks >= 1: empty sequences returned above
   for (int64_t ci = 0; ci < nchunks; ++ci) {
     const int64_t t0 = ci * kC;
     const bool has_next = ci + 1 < nchunks;
@@ -511,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
         for (int nt = 0; nt < 4; ++nt) {
           const int64_t tok = t0 + 16 * nt + j;
           if (tok < Tn) {
-            T* dst = go + ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + 4 * g;
+            T* dst = go + ((tok0 + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + 4 * g;
             st4<T>(dst, p.scale * O[nt][0], p.scale * O[nt][1], p.scale * O[nt][2], p.scale * O[nt][3]);
           }
         }
@@ -569,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
             op += __shfl_xor(op, 16);
             op += __shfl_xor(op, 32);
             if (g == 0)
-              go[((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + j] = from_f32<T>(p.scale * op);
+              go[((tok0 + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + j] = from_f32<T>(p.scale * op);
           }
         }
         __syncthreads();
@@ -591,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
 template <typename T, typename GT, int DK, int DV, int DVS, bool CH, bool HG>
 hipError_t launch_typed(const ChunkArgs& a, hipStream_t stream) {
   Params p;
-  p.B = a.B; p.T = a.T; p.Hk = a.Hk; p.Hv = a.Hv; p.scale = a.scale;
+  p.B = a.B; p.T = a.T; p.cu = a.cu_seqlens; p.Hk = a.Hk; p.Hv = a.Hv; p.scale = a.scale;
   p.q = a.q; p.k = a.k; p.v = a.v; p.b = a.b; p.w = a.w; p.g = a.g;
   p.state_in = a.state_in; p.state_out = a.state_out; p.o = a.o;
   const int64_t nwg = a.B * a.Hv * (DV / DVS);

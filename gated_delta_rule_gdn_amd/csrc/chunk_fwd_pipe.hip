@@ -135,10 +135,31 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   const int hv = (int)(head - bidx * p.Hv);
   const int hk = hv / (p.Hv / p.Hk);
   const int c0 = split * DVS;
-  const int64_t Tn = p.T;
+  // Token range of this sequence: [tok0, tok0 + Tn) in the token-major
+  // tensors.  Packed sequences read their range from cu (clamped into the
+  // tensor, so malformed offsets cannot reach outside it; an empty range only
+  // passes the state through).
+  int64_t tok0 = bidx * p.T, Tn = p.T;
+  if (p.cu) {
+    int64_t a0 = p.cu[bidx], a1 = p.cu[bidx + 1];
+    a0 = a0 < 0 ? 0 : (a0 > p.T ? p.T : a0);
+    a1 = a1 < a0 ? a0 : (a1 > p.T ? p.T : a1);
+    tok0 = a0;
+    Tn = a1 - a0;
+  }
   const int64_t nchunks = (Tn + kC - 1) / kC;
 
   const int tid = threadIdx.x;
+  if (Tn == 0) {  // an empty packed sequence only passes its state through
+    if (p.state_out) {
+      const int64_t base = head * (int64_t)DK * DV + c0;
+      for (int idx = tid; idx < DK * DVS; idx += (int)blockDim.x) {
+        const int64_t e = base + (int64_t)(idx / DVS) * DV + (idx % DVS);
+        p.state_out[e] = p.state_in ? p.state_in[e] : 0.f;
+      }
+    }
+    return;
+  }
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool consumer = wave < 4;
@@ -180,14 +201,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
   const uint32_t gs_tok = (uint32_t)(p.Hv * (int)sizeof(GT));        // scalar gates
   const uint32_t v_tok = (uint32_t)(p.Hv * DV * (int)sizeof(T));
   const uint32_t w_tok = (uint32_t)(p.Hv * DV * (int)sizeof(GT));
-  const char* bq = reinterpret_cast<const char*>(gq) + ((uint64_t)bidx * Tn * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
-  const char* bk = reinterpret_cast<const char*>(gk) + ((uint64_t)bidx * Tn * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
-  const char* bbc = reinterpret_cast<const char*>(gb) + ((uint64_t)bidx * Tn * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
-  const char* bgc = reinterpret_cast<const char*>(gg) + ((uint64_t)bidx * Tn * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
-  const char* bbs = reinterpret_cast<const char*>(gb) + ((uint64_t)bidx * Tn * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
-  const char* bgs = reinterpret_cast<const char*>(gg) + ((uint64_t)bidx * Tn * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
-  const char* bv = reinterpret_cast<const char*>(gv) + ((uint64_t)bidx * Tn * v_tok + (uint32_t)((hv * DV + c0) * (int)sizeof(T)));
-  const char* bw = reinterpret_cast<const char*>(gw) + ((uint64_t)bidx * Tn * w_tok + (uint32_t)((hv * DV + c0) * (int)sizeof(GT)));
+  const char* bq = reinterpret_cast<const char*>(gq) + ((uint64_t)tok0 * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
+  const char* bk = reinterpret_cast<const char*>(gk) + ((uint64_t)tok0 * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
+  const char* bbc = reinterpret_cast<const char*>(gb) + ((uint64_t)tok0 * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
+  const char* bgc = reinterpret_cast<const char*>(gg) + ((uint64_t)tok0 * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
+  const char* bbs = reinterpret_cast<const char*>(gb) + ((uint64_t)tok0 * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
+  const char* bgs = reinterpret_cast<const char*>(gg) + ((uint64_t)tok0 * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
+  const char* bv = reinterpret_cast<const char*>(gv) + ((uint64_t)tok0 * v_tok + (uint32_t)((hv * DV + c0) * (int)sizeof(T)));
+  const char* bw = reinterpret_cast<const char*>(gw) + ((uint64_t)tok0 * w_tok + (uint32_t)((hv * DV + c0) * (int)sizeof(GT)));
   const uint32_t oq = (uint32_t)(ch0 * (int)sizeof(T));
   const uint32_t og = (uint32_t)(ch0 * (int)sizeof(GT));
   const uint32_t ov = (uint32_t)(4 * zc * (int)sizeof(T));
@@ -324,27 +345,31 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
       }
       const bool any_bad = __any(!(worst <= kRange));
       if (lane == 0) sFlag[slot * 4 + pw] = any_bad ? 1 : 0;
-      if (g == 0) {  // lanes 0-15 hold tokens 4 tg .. 4 tg + 3
-        float* tok = sTok0 + slot * 8 * kC;
-        const float r2 = exp2_fast(rr * kLog2e);
-        const float cC = exp2_fast((gc - rr) * kLog2e);
-        float f[6][4];
+      // Every lane computes the factors (the same instructions either way);
+      // only the stores are masked.  Reading beta outside a branch also keeps
+      // the compiler's view of the outstanding loads exact.
+      float* tok = sTok0 + slot * 8 * kC;
+      const float r2 = exp2_fast(rr * kLog2e);
+      const float cC = exp2_fast((gc - rr) * kLog2e);
+      const float gC = exp2_fast(gc * kLog2e);
+      float f[6][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e1 = exp2_fast(xt[i]);
-          const float e2 = exp2_fast(-xt[i]);
-          const float nb = -word_f32<GT>(ub[i]) * e1;
-          f[kFE1][i] = e1;
-          f[kFE2][i] = e2;
-          f[kFNB][i] = nb;
-          f[kFX][i] = nb * r2;
-          f[kFO][i] = e1 * r2;
-          f[kFK][i] = cC * e2;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float e1 = exp2_fast(xt[i]);
+        const float e2 = exp2_fast(-xt[i]);
+        const float nb = -word_f32<GT>(ub[i]) * e1;
+        f[kFE1][i] = e1;
+        f[kFE2][i] = e2;
+        f[kFNB][i] = nb;
+        f[kFX][i] = nb * r2;
+        f[kFO][i] = e1 * r2;
+        f[kFK][i] = cC * e2;
+      }
+      if (g == 0) {  // lanes 0-15 hold tokens 4 tg .. 4 tg + 3
 #pragma unroll
         for (int a = 0; a < 6; ++a)
           *reinterpret_cast<float4*>(tok + a * kC + 4 * tg) = make_float4(f[a][0], f[a][1], f[a][2], f[a][3]);
-        if (tg == 0 && pw == 0) tok[kFG * kC] = exp2_fast(gc * kLog2e);
+        if (tg == 0 && pw == 0) tok[kFG * kC] = gC;
       }
     } else if constexpr (HAS_G) {
       // cumulative log2-decay over the chunk (4 tokens in-thread, then the
@@ -732,7 +757,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
     for (int nt = 0; nt < 4; ++nt) {
       const int64_t tok = t0 + 16 * nt + j;
       if (tok < Tn) {
-        T* dst = go + ((bidx * Tn + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + 4 * g;
+        T* dst = go + ((tok0 + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + 4 * g;
         st4<T>(dst, p.scale * O[nt][0], p.scale * O[nt][1], p.scale * O[nt][2], p.scale * O[nt][3]);
       }
     }
@@ -745,8 +770,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
     for (int tl = 0; tl < kC; ++tl) {
       const int64_t tok = t0 + tl;
       if (tok >= Tn) break;
-      const int64_t qk_off = ((bidx * Tn + tok) * p.Hk + hk) * (int64_t)DK;
-      const int64_t gt = (bidx * Tn + tok) * p.Hv + hv;
+      const int64_t qk_off = ((tok0 + tok) * p.Hk + hk) * (int64_t)DK;
+      const int64_t gt = (tok0 + tok) * p.Hv + hv;
       float sbeta = 0.f, salpha = 1.f;
       if constexpr (!CHANNEL) {
         sbeta = to_f32(gb[gt]);
@@ -833,6 +858,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
         for (int i = 0; i < 4; ++i) sout[(16 * mt + 4 * g + i) * DV + col] = S[mt][i];
     }
   } else {
+    // (nchunks >= 1 here.  The prologue stays unconditional: loads issued
+    // under a branch would leave the compiler unsure of the outstanding
+    // loads at the loop head, and its waits there would drain them.)
     load_gvw(0);
     load_qkb(0);
     produce_decay(0);
@@ -863,7 +891,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void chunk_fwd_pipe_kernel(Params 
 template <typename T, typename GT, int DK, int DV, bool CH, bool HG>
 hipError_t launch_pipe_typed(const ChunkArgs& a, hipStream_t stream) {
   Params p;
-  p.B = a.B; p.T = a.T; p.Hk = a.Hk; p.Hv = a.Hv; p.scale = a.scale;
+  p.B = a.B; p.T = a.T; p.cu = a.cu_seqlens; p.Hk = a.Hk; p.Hv = a.Hv; p.scale = a.scale;
   p.q = a.q; p.k = a.k; p.v = a.v; p.b = a.b; p.w = a.w; p.g = a.g;
   p.state_in = a.state_in; p.state_out = a.state_out; p.o = a.o;
   const int64_t nwg = a.B * a.Hv * (DV / 64);

@@ -164,6 +164,56 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_chunk_fwd_varlen(const gdn_varlen_desc* d, const int64_t* cu_seqlens,
+                                const void* q, const void* k, const void* v,
+                                const void* beta_or_b, const void* w, const void* g,
+                                const float* state_in, float* state_out, void* o,
+                                void* stream) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  if (d->N < 0 || d->total_T < 0) return GDN_ERR_INVALID_ARG;
+  gdn_status st = check_common(d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
+                               d->gate_mode, d->scale);
+  if (st != GDN_OK) return st;
+  if (d->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  const double elems = (double)d->total_T * (double)d->H_v * (double)(d->d_k + d->d_v);
+  if (elems > 9.0e15) return GDN_ERR_INVALID_ARG;
+  if ((double)d->total_T > 2.0e9 || (double)d->N * (double)d->H_v * 2.0 > 2.0e9)
+    return GDN_ERR_UNSUPPORTED;
+  if (d->N == 0) return GDN_OK;
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0) return GDN_ERR_INVALID_ARG;
+  const int64_t heads = d->N * d->H_v;
+  const Span scu = span(cu_seqlens, d->N + 1, 8);
+  const Span so = span(state_out, heads * d->d_k * d->d_v, 4);
+  const Span sO = span(o, d->total_T * d->H_v * d->d_v, dtype_bytes(d->io_dtype));
+  if (overlaps(scu, so) || overlaps(scu, sO)) return GDN_ERR_INVALID_ARG;
+  if (d->total_T == 0) {
+    // Every sequence is empty: only the states pass through.
+    const Span si = span(state_in, heads * d->d_k * d->d_v, 4);
+    if (overlaps(si, so) && !(si.lo == so.lo && si.hi == so.hi)) return GDN_ERR_INVALID_ARG;
+    if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
+      return GDN_ERR_INVALID_ARG;
+    if (!state_out || state_out == state_in) return GDN_OK;
+    hipError_t e = gdn::launch_state_copy(state_in, state_out, heads * d->d_k * d->d_v,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
+  st = check_pointers(d->total_T, heads, d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype,
+                      d->gate_dtype, d->gate_mode, q, k, v, beta_or_b, w, g, state_in, state_out,
+                      o, false);
+  if (st != GDN_OK) return st;
+
+  gdn::ChunkArgs a;
+  a.B = d->N; a.T = d->total_T; a.cu_seqlens = cu_seqlens;
+  a.Hk = d->H_k; a.Hv = d->H_v; a.dk = d->d_k; a.dv = d->d_v;
+  a.io = to_dtype(d->io_dtype); a.gate = to_dtype(d->gate_dtype);
+  a.channel = d->gate_mode == GDN_GATES_CHANNEL; a.scale = d->scale;
+  a.q = q; a.k = k; a.v = v; a.b = beta_or_b; a.w = w; a.g = g;
+  a.state_in = state_in; a.state_out = state_out; a.o = o;
+  hipError_t e = gdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 gdn_status gdn_decode_step(const gdn_decode_desc* d, const void* q, const void* k,
                            const void* v, const void* beta_or_b, const void* w, const void* g,
                            float* state, void* o, void* stream) {

@@ -23,7 +23,8 @@ struct DecodeArgs {
 };
 
 struct ChunkArgs {
-  int64_t B, T;
+  int64_t B, T;                       // sequences; tokens each (packed total with cu_seqlens)
+  const int64_t* cu_seqlens = nullptr;  // device [B + 1] offsets of packed sequences
   int Hk, Hv, dk, dv;
   DType io, gate;
   bool channel;

@@ -19,11 +19,20 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_SCALAR, GDN_GATES_CHANNEL = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class GdnFwdDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
+                ("gate_mode", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class GdnVarlenDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("total_T", ctypes.c_int64),
                 ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
@@ -54,6 +63,9 @@ def _load() -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.gdn_chunk_fwd.argtypes = [ctypes.POINTER(GdnFwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_varlen.argtypes = [ctypes.POINTER(GdnVarlenDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, vp]
+    lib.gdn_chunk_fwd_varlen.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -141,6 +153,52 @@ def gdn_chunk_fwd(q, k, v, beta_or_b, w=None, g=None, state_in=None, state_out=N
                            _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_fwd")
+    return o, state_out
+
+
+def gdn_chunk_fwd_varlen(q, k, v, beta_or_b, cu_seqlens, w=None, g=None, state_in=None,
+                         state_out=None, o=None, scale: float = 1.0, chunk: int = 64,
+                         stream=None):
+    """Chunkwise forward over packed sequences (see include/gdn.h).
+    Returns (o, state_out).
+
+    q, k [total_T,Hk,dk]; v [total_T,Hv,dv]; beta_or_b [total_T,Hv] or
+    [total_T,Hv,dk] (then w [total_T,Hv,dv]); g like beta_or_b or None;
+    cu_seqlens int64 device tensor [N+1] of token offsets; state_in/state_out
+    [N,Hv,dk,dv] fp32 or None.  o is allocated when not given.
+    """
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    io = q.dtype
+    if io not in _DT:
+        raise ValueError("q must be float32 or bfloat16")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    gdt = beta_or_b.dtype
+    channel = w is not None
+    gshape = (T, Hv, dk) if channel else (T, Hv)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int64)
+    _check(q, "q", (T, Hk, dk), io)
+    _check(k, "k", (T, Hk, dk), io)
+    _check(v, "v", (T, Hv, dv), io)
+    _check(beta_or_b, "beta_or_b", gshape, gdt)
+    _check(w, "w", (T, Hv, dv), gdt)
+    _check(g, "g", gshape, gdt)
+    _check(state_in, "state_in", (N, Hv, dk, dv), torch.float32)
+    _check(state_out, "state_out", (N, Hv, dk, dv), torch.float32)
+    if o is None:
+        o = torch.empty((T, Hv, dv), dtype=io, device=q.device)
+    _check(o, "o", (T, Hv, dv), io)
+    if gdt not in _DT:
+        raise ValueError("gates must be float32 or bfloat16")
+    desc = GdnVarlenDesc(N, T, Hk, Hv, dk, dv, _DT[io], _DT[gdt],
+                         GDN_GATES_CHANNEL if channel else GDN_GATES_SCALAR, chunk, float(scale))
+    st = lib.gdn_chunk_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(beta_or_b), _ptr(w), _ptr(g), _ptr(state_in),
+                                  _ptr(state_out), _ptr(o), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_fwd_varlen")
     return o, state_out
 
 

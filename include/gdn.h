@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2  /* 2: adds gdn_chunk_fwd_varlen */
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -107,6 +107,53 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* desc, const void* q, const void* k,
                          const void* v, const void* beta_or_b, const void* w,
                          const void* g, const float* state_in, float* state_out,
                          void* o, void* stream);
+
+/* Chunked forward over packed sequences of different lengths. */
+typedef struct gdn_varlen_desc {
+  int64_t N;          /* sequences, >= 0 (0: nothing to do)                      */
+  int64_t total_T;    /* packed tokens of all sequences, >= 0                    */
+  int32_t H_k, H_v;   /* >= 1, H_v % H_k == 0                                    */
+  int32_t d_k, d_v;   /* each 64 or 128                                          */
+  int32_t io_dtype;   /* gdn_dtype of q, k, v, o                                 */
+  int32_t gate_dtype; /* equal to io_dtype, or F32                               */
+  int32_t gate_mode;  /* gdn_gate_mode                                           */
+  int32_t chunk;      /* must be 64                                              */
+  float scale;        /* finite                                                  */
+} gdn_varlen_desc;
+
+/*
+ * gdn_chunk_fwd_varlen -- gdn_chunk_fwd over N sequences packed along the
+ * token axis (prefill of a serving batch).  Sequence n is the packed tokens
+ * [cu_seqlens[n], cu_seqlens[n+1]); it starts from state_in[n] (or zero) and
+ * leaves its final state in state_out[n], the layout gdn_decode_step updates
+ * in place, so a prefill hands over to decoding without a copy.  The state is
+ * what the recurrence carries from token to token, whatever the context
+ * length (architecture notes page "Gated DeltaNet", §L'etat, en memoire); the
+ * pages describe no batching of sequences, and this entry point is the
+ * packed form of gdn_chunk_fwd with the same per-sequence result.
+ *
+ *   cu_seqlens [N + 1] int64, DEVICE pointer, 8-byte aligned; expected
+ *              non-decreasing with cu_seqlens[0] = 0 and cu_seqlens[N] =
+ *              total_T.  Each range is clamped into [0, total_T] on the
+ *              device, and an empty or reversed range is a sequence of no
+ *              token (its state passes through), so malformed offsets never
+ *              make the kernels touch memory outside the tensors; tokens that
+ *              no range covers keep their previous o.
+ *   q, k       [total_T, H_k, d_k]  io_dtype
+ *   v          [total_T, H_v, d_v]  io_dtype
+ *   beta_or_b  SCALAR: [total_T, H_v]   CHANNEL: [total_T, H_v, d_k]  gate_dtype
+ *   w          SCALAR: NULL             CHANNEL: [total_T, H_v, d_v]  gate_dtype
+ *   g          same shape as beta_or_b; NULL => alpha = 1
+ *   state_in   [N, H_v, d_k, d_v] fp32, or NULL => zero initial states
+ *   state_out  [N, H_v, d_k, d_v] fp32, or NULL; may equal state_in
+ *   o          [total_T, H_v, d_v]  io_dtype (output)
+ *   stream     hipStream_t or NULL
+ */
+gdn_status gdn_chunk_fwd_varlen(const gdn_varlen_desc* desc, const int64_t* cu_seqlens,
+                                const void* q, const void* k, const void* v,
+                                const void* beta_or_b, const void* w, const void* g,
+                                const float* state_in, float* state_out, void* o,
+                                void* stream);
 
 /* Single-token decode step over N independent sequences. */
 typedef struct gdn_decode_desc {

@@ -21,7 +21,8 @@ def _declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
-        ["gdn_chunk_fwd", "gdn_decode_step", "gdn_status_string", "gdn_abi_version"])
+        ["gdn_chunk_fwd", "gdn_chunk_fwd_varlen", "gdn_decode_step", "gdn_status_string",
+         "gdn_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert gdn.abi_version() == 1
+    assert gdn.abi_version() == 2
     for st in range(4):
         s = gdn.status_string(st)
         assert s.startswith("GDN_")
@@ -164,3 +165,65 @@ def test_python_binding_rejects_host_tensors():
     q = torch.zeros(1, 64, 1, 128)
     with pytest.raises(ValueError):
         gdn.gdn_chunk_fwd(q, q, q, torch.zeros(1, 64, 1))
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences (gdn_chunk_fwd_varlen): validation only.
+# ---------------------------------------------------------------------------
+def _varlen_desc(**kw):
+    d = dict(N=3, total_T=300, H_k=2, H_v=4, d_k=128, d_v=128, io_dtype=gdn.GDN_BF16,
+             gate_dtype=gdn.GDN_BF16, gate_mode=gdn.GDN_GATES_CHANNEL, chunk=64, scale=1.0)
+    d.update(kw)
+    return gdn.GdnVarlenDesc(**d)
+
+
+def _varlen(desc, **ptrs):
+    names = ["cu", "q", "k", "v", "b", "w", "g", "s_in", "s_out", "o"]
+    p = {n: _addr(i) for i, n in enumerate(names)}
+    if desc is not None and desc.gate_mode == gdn.GDN_GATES_SCALAR:
+        p["w"] = None
+    p.update(ptrs)
+    return gdn.lib.gdn_chunk_fwd_varlen(ctypes.byref(desc) if desc is not None else None,
+                                        *[p[n] for n in names], None)
+
+
+@pytest.mark.parametrize("field,value,expected", [
+    ("N", -1, 1),
+    ("total_T", -5, 1),
+    ("H_v", 3, 1),
+    ("d_k", 96, 2),
+    ("chunk", 32, 2),
+    ("gate_mode", 9, 1),
+    ("scale", float("inf"), 1),
+])
+def test_varlen_rejects_bad_descriptor(field, value, expected):
+    assert _varlen(_varlen_desc(**{field: value})) == expected
+
+
+def test_varlen_null_descriptor_and_offsets():
+    assert _varlen(None) == gdn.GDN_ERR_INVALID_ARG
+    assert _varlen(_varlen_desc(), cu=None) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_varlen_offsets_must_be_8_byte_aligned():
+    assert _varlen(_varlen_desc(), cu=_addr(0, 4)) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_varlen_offsets_must_not_alias_outputs():
+    assert _varlen(_varlen_desc(), cu=_addr(9)) == gdn.GDN_ERR_INVALID_ARG      # == o
+    assert _varlen(_varlen_desc(), cu=_addr(8)) == gdn.GDN_ERR_INVALID_ARG      # == state_out
+
+
+def test_varlen_pointer_checks_of_the_batched_entry_apply():
+    assert _varlen(_varlen_desc(), q=None) == gdn.GDN_ERR_INVALID_ARG
+    assert _varlen(_varlen_desc(), w=None) == gdn.GDN_ERR_INVALID_ARG          # channel needs w
+    assert _varlen(_varlen_desc(), o=_addr(1)) == gdn.GDN_ERR_INVALID_ARG      # o aliases q
+    assert _varlen(_varlen_desc(gate_mode=gdn.GDN_GATES_SCALAR), w=_addr(5)) == \
+        gdn.GDN_ERR_INVALID_ARG
+
+
+def test_varlen_nothing_to_do_returns_ok_without_launch():
+    assert _varlen(_varlen_desc(N=0), cu=None) == gdn.GDN_OK
+    # no token at all and no state to move
+    assert _varlen(_varlen_desc(total_T=0), s_out=None) == gdn.GDN_OK
+    assert _varlen(_varlen_desc(total_T=0), s_out=_addr(7)) == gdn.GDN_OK    # in place
