@@ -129,6 +129,39 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
                                         (PEAK_FP32_TFLOPS if io_bytes == 4 else PEAK_BF16_TFLOPS), 4)}
         del inp, o, s
         torch.cuda.empty_cache()
+    # packed variable-length prefill (serving): the final states are the
+    # layout the decode step consumes
+    for name, vcfg in synth.VARLEN_CONFIGS.items():
+        inp = synth.varlen_inputs(vcfg, device="cuda")
+        o = torch.empty((vcfg.total_T, vcfg.Hv, vcfg.dv), dtype=vcfg.io_dtype, device=dev)
+        s = torch.empty((vcfg.N, vcfg.Hv, vcfg.dk, vcfg.dv), dtype=torch.float32, device=dev)
+
+        def run():
+            gdn.gdn_chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["beta_or_b"],
+                                     inp["cu_seqlens"], w=inp["w"], g=inp["g"], state_out=s, o=o)
+        for _ in range(warmup):
+            run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            run()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        one = synth.ChunkConfig(name, B=1, T=vcfg.total_T, Hk=vcfg.Hk, Hv=vcfg.Hv, dk=vcfg.dk,
+                                dv=vcfg.dv, channel=vcfg.channel, io_dtype=vcfg.io_dtype,
+                                gate_dtype=vcfg.gate_dtype, seed=vcfg.seed)
+        nbytes, flops = chunk_algorithmic(one, 2)
+        nbytes += (vcfg.N - 1) * vcfg.Hv * vcfg.dk * vcfg.dv * 4   # one final state per sequence
+        res[name] = {"ms": round(ms, 4), "tokens_per_s": round(vcfg.total_T / (ms * 1e-3), 1),
+                     "sequences": vcfg.N, "lengths": inp["lengths"],
+                     "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del inp, o, s
+        torch.cuda.empty_cache()
     return res
 
 

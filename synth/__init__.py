@@ -14,7 +14,12 @@ Transforms (the workload descriptions):
   g     : -softplus(x) = log(alpha)  (alpha = exp(-softplus(x)) in (0, 1))
   state : 0.02 * x                   (decode workload; zeros otherwise)
 
-The gate tensors are handed over in log space (g = log alpha), see the design doc.
+The decay is handed over in log space (g = log alpha), as the library's C
+ABI takes it.
+
+Packed variable-length batches (``varlen_inputs``) draw the sequence lengths
+first, from a generator of their own (log-normal around a mean length,
+rounded, at least 1), then the packed tensors with the same transforms.
 """
 from __future__ import annotations
 
@@ -76,6 +81,60 @@ CONFIGS = {
                                 channel=True, io_dtype=torch.bfloat16,
                                 gate_dtype=torch.bfloat16, seed=5),
 }
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenConfig:
+    name: str
+    N: int                 # sequences
+    total_T: int           # packed tokens (the lengths sum to this)
+    Hk: int
+    Hv: int
+    dk: int
+    dv: int
+    channel: bool
+    io_dtype: torch.dtype
+    gate_dtype: torch.dtype
+    seed: int
+    sigma: float = 0.8     # log-normal spread of the lengths
+
+
+# A serving-style prefill: 16 sequences of mixed lengths, as many tokens as the
+# B8 T4096 training shape, GDN-2 gates.
+VARLEN_CONFIGS = {
+    "gdn2_varlen_mix": VarlenConfig("gdn2_varlen_mix", N=16, total_T=32768, Hk=16, Hv=16, dk=128,
+                                    dv=128, channel=True, io_dtype=torch.bfloat16,
+                                    gate_dtype=torch.bfloat16, seed=6),
+}
+
+
+def varlen_lengths(cfg: VarlenConfig) -> list:
+    """Seeded sequence lengths (each >= 1) summing to cfg.total_T."""
+    gen = torch.Generator().manual_seed(int(cfg.seed) * 1000 + 7)
+    w = torch.exp(cfg.sigma * torch.randn(cfg.N, generator=gen, dtype=torch.float64))
+    raw = torch.clamp(torch.floor(w / w.sum() * cfg.total_T), min=1).to(torch.int64)
+    raw[-1] += cfg.total_T - int(raw.sum())
+    assert int(raw.min()) >= 1 and int(raw.sum()) == cfg.total_T
+    return [int(x) for x in raw]
+
+
+def varlen_inputs(cfg: VarlenConfig, *, device="cpu"):
+    """Packed inputs of a variable-length batch: q, k [total_T, Hk, dk],
+    v [total_T, Hv, dv], gates [total_T, Hv(, d)], cu_seqlens int64 [N + 1]
+    (on ``device``) and the lengths."""
+    lengths = varlen_lengths(cfg)
+    one = ChunkConfig(cfg.name, B=1, T=cfg.total_T, Hk=cfg.Hk, Hv=cfg.Hv, dk=cfg.dk, dv=cfg.dv,
+                      channel=cfg.channel, io_dtype=cfg.io_dtype, gate_dtype=cfg.gate_dtype,
+                      seed=cfg.seed)
+    inp = chunk_inputs(one, device=device)
+    out = {k: (None if v is None else v[0].contiguous())
+           for k, v in inp.items() if k != "state_in"}
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    out["cu_seqlens"] = torch.tensor(cu, dtype=torch.int64, device=device)
+    out["lengths"] = lengths
+    return out
 
 
 def _gen(seed: int, device) -> torch.Generator:
