@@ -16,6 +16,10 @@ Functions (each follows the passages cited in ``gdn_oracle.c``):
   chunkwise  -- naive chunkwise form (same page, §3, decay absorption and
                 (I+T)^{-1} solve).  Used only to check the decomposition.
   decode     -- one token per sequence, state updated in place.
+
+The operations around the recurrence in a Gated DeltaNet block (short causal
+convolution, SiLU, L2 norm, gate activations, output norm and swish gate) are
+in ``oracle.layer`` (numpy, float64).
 """
 from __future__ import annotations
 
