@@ -165,6 +165,60 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
     return res
 
 
+def block_op_workloads(gdn, synth, torch, dev, steps=20, warmup=3):
+    """The operations around the recurrence at the GDN-2 B8 T4096 layer shape
+    (not part of the step): the short conv branch, the gate activations and
+    the output norm x swish(z), each timed with HIP events on the launch
+    stream against the bytes it must move (each operand read once, each
+    output written once)."""
+    cfg = synth.BLOCK_CONFIGS["gdn2_block_train"]
+    inp = synth.block_inputs(cfg, device="cuda", conv_state=False)
+    rows, C, Hv, dk, dv = cfg.rows, cfg.conv_channels, cfg.Hv, cfg.dk, cfg.dv
+    n = Hv * dk if cfg.channel else Hv
+    eb = 2 if cfg.io_dtype == torch.bfloat16 else 4
+    gb = 2 if cfg.gate_dtype == torch.bfloat16 else 4
+    q = torch.empty((rows, cfg.Hk, dk), dtype=cfg.io_dtype, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((rows, Hv, dv), dtype=cfg.io_dtype, device=dev)
+    gshape = (rows, Hv, dk) if cfg.channel else (rows, Hv)
+    g = torch.empty(gshape, dtype=cfg.gate_dtype, device=dev)
+    beta = torch.empty_like(g)
+    w = torch.empty((rows, Hv, dv), dtype=cfg.gate_dtype, device=dev) if cfg.channel else None
+    y = torch.empty_like(inp["o"])
+    ops = {
+        "short_conv": (lambda: gdn.gdn_short_conv(inp["x"], inp["conv_w"], cfg.Hk, Hv, dk, dv,
+                                                  N=cfg.N, q=q, k=k, v=v),
+                       2 * rows * C * eb + C * 16),
+        "gates": (lambda: gdn.gdn_gates(inp["a_raw"], inp["b_raw"], Hv, w_raw=inp["w_raw"],
+                                        A_log=inp["A_log"], dt_bias=inp["dt_bias"], d_k=dk,
+                                        d_v=dv, gate_dtype=cfg.gate_dtype, g=g, beta_or_b=beta,
+                                        w=w),
+                  rows * (2 * n + (Hv * dv if cfg.channel else 0)) * (eb + gb) + 8 * n),
+        "output_gate": (lambda: gdn.gdn_output_gate(inp["o"], inp["z"], inp["norm_w"], y=y),
+                        3 * rows * Hv * dv * eb + 4 * dv),
+    }
+    res = {"workload": f"{cfg.name}: {cfg.N} x {cfg.T} tokens, H_k={cfg.Hk}, H_v={Hv}, "
+                       f"d_k={dk}, d_v={dv}, {'channel' if cfg.channel else 'scalar'} gates, bf16"}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "GBps": round(gbps, 1),
+                     "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(name, nbytes)}
+    del inp, q, k, v, g, beta, w, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(args):
     """The oracle, untuned, on the machine's host cores over the whole prefill
     workload (8 sequences x 16 heads x T=4096: about 15 s of CPU work on 16
@@ -193,7 +247,10 @@ def cpu_baseline(args):
 
 
 KERNEL_KEYS = {"chunk_fwd": ("chunk_fwd_pipe_kernel", "chunk_fwd_kernel"),
-               "decode_step": ("decode_kernel",)}
+               "decode_step": ("decode_kernel",),
+               "short_conv": ("short_conv_kernel",),
+               "gates": ("gates_kernel",),
+               "output_gate": ("output_gate_kernel",)}
 
 
 def _kernel_key(name):
@@ -275,6 +332,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the chunk-forward timings of the other prefill workloads")
+    ap.add_argument("--no-block-ops", action="store_true",
+                    help="skip the timings of the block operations around the recurrence")
     ap.add_argument("--cpu-threads", type=int, default=16,
                     help="cap on oracle threads (the box's CPU share)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -338,13 +397,6 @@ def main():
     chunk_avg = sum(chunk_ms) / len(chunk_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
 
-    if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-
     gate_bytes = 2 if cfg_c.gate_dtype == torch.bfloat16 else 4
     c_bytes, c_flops = chunk_algorithmic(cfg_c, gate_bytes, state_in=inp_c["state_in"] is not None)
     d_bytes, d_flops = decode_algorithmic(cfg_d)
@@ -406,6 +458,15 @@ def main():
     }
     if not args.no_secondary:
         out["secondary"] = secondary_chunk_workloads(gdn, synth, torch, dev)
+    if not args.no_block_ops:
+        out["block_ops"] = block_op_workloads(gdn, synth, torch, dev)
+    if args.copy_calibration:  # the last GPU work of the process
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args)
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}

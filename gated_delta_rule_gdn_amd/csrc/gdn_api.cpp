@@ -214,6 +214,150 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_varlen_desc* d, const int64_t* cu_seql
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_short_conv(const gdn_conv_desc* d, const int64_t* cu_seqlens, const void* x,
+                          const float* conv_w, const void* conv_state_in, void* conv_state_out,
+                          void* q, void* k, void* v, void* stream) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  if (d->N < 0 || d->total_T < 0) return GDN_ERR_INVALID_ARG;
+  if (d->H_k < 1 || d->H_v < 1 || d->d_k < 1 || d->d_v < 1) return GDN_ERR_INVALID_ARG;
+  if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if ((d->d_k != 64 && d->d_k != 128) || (d->d_v != 64 && d->d_v != 128))
+    return GDN_ERR_UNSUPPORTED;
+  if (!std::isfinite(d->eps) || d->eps < 0.f) return GDN_ERR_INVALID_ARG;
+  const int64_t C = 2 * (int64_t)d->H_k * d->d_k + (int64_t)d->H_v * d->d_v;
+  if (d->ld_x < C || d->ld_x % 8 != 0) return GDN_ERR_INVALID_ARG;
+  if ((double)d->total_T * (double)d->ld_x > 9.0e15 || (double)d->N * 3.0 * (double)C > 9.0e15)
+    return GDN_ERR_INVALID_ARG;
+  if (2 * (int64_t)d->H_k + d->H_v > 65535 || (double)d->total_T / 256.0 > 2.0e9)
+    return GDN_ERR_UNSUPPORTED;  // grid limits
+  if (d->N == 0) return GDN_OK;
+  if (!cu_seqlens && d->total_T % d->N != 0) return GDN_ERR_INVALID_ARG;
+  if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0) return GDN_ERR_INVALID_ARG;
+  const bool tokens = d->total_T > 0;
+  if (tokens && (!x || !conv_w || !q || !k || !v)) return GDN_ERR_INVALID_ARG;
+  if (!tokens && !conv_state_out) return GDN_OK;
+  if (conv_state_out && !tokens && conv_state_out == conv_state_in) return GDN_OK;
+  const void* all[] = {x, conv_w, conv_state_in, conv_state_out, q, k, v};
+  for (const void* p : all)
+    if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+
+  const int64_t eb = dtype_bytes(d->io_dtype);
+  const int64_t T = d->total_T;
+  const Span sx = tokens ? span(x, (T - 1) * d->ld_x + C, eb) : Span{0, 0};
+  const Span sw = tokens ? span(conv_w, C * 4, 4) : Span{0, 0};
+  const Span scu = span(cu_seqlens, d->N + 1, 8);
+  const Span si = span(conv_state_in, d->N * 3 * C, eb);
+  const Span so = span(conv_state_out, d->N * 3 * C, eb);
+  const Span sq = tokens ? span(q, T * d->H_k * d->d_k, eb) : Span{0, 0};
+  const Span sk = tokens ? span(k, T * d->H_k * d->d_k, eb) : Span{0, 0};
+  const Span sv = tokens ? span(v, T * d->H_v * d->d_v, eb) : Span{0, 0};
+  const Span outs[] = {sq, sk, sv};
+  const Span ins[] = {sx, sw, scu, si};
+  for (const Span& o : outs) {
+    for (const Span& in : ins)
+      if (overlaps(o, in)) return GDN_ERR_INVALID_ARG;
+    if (overlaps(o, so)) return GDN_ERR_INVALID_ARG;
+  }
+  if (overlaps(sq, sk) || overlaps(sq, sv) || overlaps(sk, sv)) return GDN_ERR_INVALID_ARG;
+  if (overlaps(so, sx) || overlaps(so, sw) || overlaps(so, scu)) return GDN_ERR_INVALID_ARG;
+  if (overlaps(so, si) && !(so.lo == si.lo && so.hi == si.hi)) return GDN_ERR_INVALID_ARG;
+
+  gdn::ConvArgs a;
+  a.N = d->N; a.total_T = T; a.Tseq = cu_seqlens ? 0 : T / d->N; a.cu_seqlens = cu_seqlens;
+  a.Hk = d->H_k; a.Hv = d->H_v; a.dk = d->d_k; a.dv = d->d_v; a.C = C; a.ld_x = d->ld_x;
+  a.io = to_dtype(d->io_dtype); a.eps = d->eps;
+  a.x = x; a.w = conv_w; a.s_in = conv_state_in; a.s_out = conv_state_out;
+  a.q = q; a.k = k; a.v = v;
+  hipError_t e = gdn::launch_short_conv(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_gates(const gdn_gate_desc* d, const void* a_raw, const void* b_raw,
+                     const void* w_raw, const float* A_log, const float* dt_bias, void* g,
+                     void* beta_or_b, void* w, void* stream) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  if (d->rows < 0 || d->H_v < 1) return GDN_ERR_INVALID_ARG;
+  if (d->gate_mode != GDN_GATES_SCALAR && d->gate_mode != GDN_GATES_CHANNEL)
+    return GDN_ERR_INVALID_ARG;
+  if (d->in_dtype != GDN_F32 && d->in_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (d->gate_dtype != GDN_F32 && d->gate_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  const bool ch = d->gate_mode == GDN_GATES_CHANNEL;
+  if (ch && (d->d_k < 1 || d->d_v < 1)) return GDN_ERR_INVALID_ARG;
+  const int64_t n_ab = ch ? (int64_t)d->H_v * d->d_k : d->H_v;
+  const int64_t n_w = ch ? (int64_t)d->H_v * d->d_v : 0;
+  if (d->ld_a < n_ab || d->ld_b < n_ab || (ch && d->ld_w < n_w)) return GDN_ERR_INVALID_ARG;
+  if ((double)d->rows * (double)(n_ab > n_w ? n_ab : n_w) >= 4294967040.0)
+    return GDN_ERR_UNSUPPORTED;  // 32-bit element indices
+  if (!a_raw || !b_raw || !g || !beta_or_b) return GDN_ERR_INVALID_ARG;
+  if (ch != (w_raw != nullptr) || ch != (w != nullptr)) return GDN_ERR_INVALID_ARG;
+  const int64_t ib = dtype_bytes(d->in_dtype), ob = dtype_bytes(d->gate_dtype);
+  const void* in_ptrs[] = {a_raw, b_raw, w_raw};
+  for (const void* p : in_ptrs)
+    if (p && (reinterpret_cast<uintptr_t>(p) % ib) != 0) return GDN_ERR_INVALID_ARG;
+  const void* out_ptrs[] = {g, beta_or_b, w};
+  for (const void* p : out_ptrs)
+    if (p && (reinterpret_cast<uintptr_t>(p) % ob) != 0) return GDN_ERR_INVALID_ARG;
+  if ((A_log && (reinterpret_cast<uintptr_t>(A_log) & 3u)) ||
+      (dt_bias && (reinterpret_cast<uintptr_t>(dt_bias) & 3u)))
+    return GDN_ERR_INVALID_ARG;
+  if (d->rows == 0) return GDN_OK;
+  const int64_t R = d->rows;
+  const Span sa = span(a_raw, (R - 1) * d->ld_a + n_ab, ib);
+  const Span sb = span(b_raw, (R - 1) * d->ld_b + n_ab, ib);
+  const Span swr = ch ? span(w_raw, (R - 1) * d->ld_w + n_w, ib) : Span{0, 0};
+  const Span sA = span(A_log, n_ab, 4), sdt = span(dt_bias, n_ab, 4);
+  const Span sg = span(g, R * n_ab, ob), sbe = span(beta_or_b, R * n_ab, ob);
+  const Span sw = span(w, R * n_w, ob);
+  const Span ins[] = {sa, sb, swr, sA, sdt};
+  const Span outs[] = {sg, sbe, sw};
+  for (const Span& o : outs)
+    for (const Span& in : ins)
+      if (overlaps(o, in)) return GDN_ERR_INVALID_ARG;
+  if (overlaps(sg, sbe) || overlaps(sg, sw) || overlaps(sbe, sw)) return GDN_ERR_INVALID_ARG;
+
+  gdn::GateArgs a;
+  a.n_ab = (uint32_t)n_ab; a.n_w = (uint32_t)n_w;
+  a.n_ab_total = (uint32_t)(R * n_ab); a.n_w_total = (uint32_t)(R * n_w);
+  a.ld_a = d->ld_a; a.ld_b = d->ld_b; a.ld_w = d->ld_w;
+  a.in = to_dtype(d->in_dtype); a.out = to_dtype(d->gate_dtype);
+  a.a = a_raw; a.b = b_raw; a.w_raw = w_raw; a.A_log = A_log; a.dt_bias = dt_bias;
+  a.g = g; a.beta = beta_or_b; a.w = w;
+  hipError_t e = gdn::launch_gates(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_output_gate(const gdn_norm_desc* d, const void* o, const void* z,
+                           const float* weight, void* y, void* stream) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  if (d->rows < 0 || d->H_v < 1 || d->d_v < 1) return GDN_ERR_INVALID_ARG;
+  if (d->io_dtype != GDN_F32 && d->io_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (d->d_v != 64 && d->d_v != 128) return GDN_ERR_UNSUPPORTED;
+  if (!std::isfinite(d->eps) || d->eps < 0.f) return GDN_ERR_INVALID_ARG;
+  const int64_t width = (int64_t)d->H_v * d->d_v;
+  if (d->ld_z < width || d->ld_z % 8 != 0) return GDN_ERR_INVALID_ARG;
+  if ((double)d->rows * (double)d->ld_z > 9.0e15) return GDN_ERR_INVALID_ARG;
+  if ((double)d->rows * (double)d->H_v / 64.0 > 2.0e9) return GDN_ERR_UNSUPPORTED;  // grid
+  if (d->rows == 0) return GDN_OK;
+  if (!o || !z || !weight || !y) return GDN_ERR_INVALID_ARG;
+  const void* all[] = {o, z, weight, y};
+  for (const void* p : all)
+    if (!aligned16(p)) return GDN_ERR_INVALID_ARG;
+  const int64_t eb = dtype_bytes(d->io_dtype);
+  const Span so = span(o, d->rows * width, eb);
+  const Span sz = span(z, (d->rows - 1) * d->ld_z + width, eb);
+  const Span sw = span(weight, d->d_v, 4);
+  const Span sy = span(y, d->rows * width, eb);
+  if (overlaps(sy, sz) || overlaps(sy, sw)) return GDN_ERR_INVALID_ARG;
+  if (overlaps(sy, so) && !(sy.lo == so.lo && sy.hi == so.hi)) return GDN_ERR_INVALID_ARG;
+
+  gdn::NormArgs a;
+  a.rows = d->rows; a.Hv = d->H_v; a.dv = d->d_v; a.ld_z = d->ld_z;
+  a.io = to_dtype(d->io_dtype); a.eps = d->eps;
+  a.o = o; a.z = z; a.weight = weight; a.y = y;
+  hipError_t e = gdn::launch_output_gate(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 gdn_status gdn_decode_step(const gdn_decode_desc* d, const void* q, const void* k,
                            const void* v, const void* beta_or_b, const void* w, const void* g,
                            float* state, void* o, void* stream) {

@@ -35,6 +35,50 @@ struct ChunkArgs {
   void* o;
 };
 
+// Short causal convolution of the q, k, v branch (+ SiLU, L2 norm of q, k).
+struct ConvArgs {
+  int64_t N, total_T;
+  int64_t Tseq;                       // tokens per sequence when cu_seqlens is NULL
+  const int64_t* cu_seqlens;          // device [N + 1] offsets, or NULL
+  int Hk, Hv, dk, dv;
+  int64_t C;                          // 2 Hk dk + Hv dv channels
+  int64_t ld_x;                       // row stride of x (elements)
+  DType io;
+  float eps;
+  const void* x;
+  const float* w;                     // [C, 4]
+  const void* s_in;                   // [N, 3, C] or NULL
+  void* s_out;                        // [N, 3, C] or NULL
+  void *q, *k, *v;
+};
+
+// Gate activations; element totals fit in 32 bits (checked by the caller).
+struct GateArgs {
+  uint32_t n_ab, n_w;                 // columns of a/b and of w (0: no w)
+  uint32_t n_ab_total, n_w_total;     // rows * columns
+  int64_t ld_a, ld_b, ld_w;
+  DType in, out;
+  const void *a, *b, *w_raw;
+  const float *A_log, *dt_bias;       // [n_ab] or NULL
+  void *g, *beta, *w;
+};
+
+// Output RMS norm times swish(z).
+struct NormArgs {
+  int64_t rows;
+  int Hv, dv;
+  int64_t ld_z;
+  DType io;
+  float eps;
+  const void *o, *z;
+  const float* weight;                // [dv]
+  void* y;
+};
+
+hipError_t launch_short_conv(const ConvArgs& a, hipStream_t stream);
+hipError_t launch_gates(const GateArgs& a, hipStream_t stream);
+hipError_t launch_output_gate(const NormArgs& a, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream);
 // bf16-operand producer/consumer variant (called by launch_chunk_fwd).

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_SCALAR, GDN_GATES_CHANNEL = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class GdnFwdDesc(ctypes.Structure):
@@ -48,6 +48,27 @@ class GdnDecodeDesc(ctypes.Structure):
                 ("gate_mode", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
+class GdnConvDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("total_T", ctypes.c_int64), ("ld_x", ctypes.c_int64),
+                ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class GdnGateDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("ld_a", ctypes.c_int64), ("ld_b", ctypes.c_int64),
+                ("ld_w", ctypes.c_int64), ("H_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("gate_mode", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("gate_dtype", ctypes.c_int32)]
+
+
+class GdnNormDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("ld_z", ctypes.c_int64),
+                ("H_v", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
 class GdnError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {status_string(status)}")
@@ -68,6 +89,12 @@ def _load() -> ctypes.CDLL:
     lib.gdn_chunk_fwd_varlen.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_short_conv.argtypes = [ctypes.POINTER(GdnConvDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_short_conv.restype = ctypes.c_int
+    lib.gdn_gates.argtypes = [ctypes.POINTER(GdnGateDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_gates.restype = ctypes.c_int
+    lib.gdn_output_gate.argtypes = [ctypes.POINTER(GdnNormDesc), vp, vp, vp, vp, vp]
+    lib.gdn_output_gate.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_abi_version.argtypes = []
@@ -236,3 +263,135 @@ def gdn_decode_step(q, k, v, beta_or_b, state, w=None, g=None, o=None, scale: fl
     if st != GDN_OK:
         raise GdnError(st, "gdn_decode_step")
     return o
+
+
+def _check_rows(t, name, rows, min_cols, dtype):
+    """A 2-d device tensor of `rows` rows with unit column stride (a column
+    block of a wider buffer is fine).  Returns its row stride in elements."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2 or t.shape[0] != rows or t.shape[1] < min_cols:
+        raise ValueError(f"{name} must be [{rows}, >= {min_cols}], got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.stride(0) if rows > 1 else max(t.stride(0), t.shape[1])
+
+
+def gdn_short_conv(x, conv_w, H_k, H_v, d_k, d_v, N=None, cu_seqlens=None, conv_state_in=None,
+                   conv_state_out=None, q=None, k=None, v=None, eps: float = 1e-6, stream=None):
+    """q, k, v branch: causal conv (kernel 4) + SiLU + L2 norm of q, k (see
+    include/gdn.h).  Returns (q, k, v, conv_state_out).
+
+    x [total_T, >= C] (C = 2 H_k d_k + H_v d_v; a column block of the
+    projection output is fine); conv_w [C, 4] fp32; cu_seqlens int64 device
+    [N+1] or None for N sequences of total_T / N tokens (N defaults to 1);
+    conv states [N, 3, C] in x's dtype or None.  q, k [total_T, H_k, d_k] and
+    v [total_T, H_v, d_v] are allocated when not given.
+    """
+    io = x.dtype
+    if io not in _DT:
+        raise ValueError("x must be float32 or bfloat16")
+    T = x.shape[0]
+    C = 2 * H_k * d_k + H_v * d_v
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-d tensor of N + 1 offsets")
+        N = cu_seqlens.numel() - 1
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int64)
+    elif N is None:
+        N = 1
+    ld_x = _check_rows(x, "x", T, C, io)
+    _check(conv_w, "conv_w", (C, 4), torch.float32)
+    _check(conv_state_in, "conv_state_in", (N, 3, C), io)
+    _check(conv_state_out, "conv_state_out", (N, 3, C), io)
+    dev = x.device
+    if q is None:
+        q = torch.empty((T, H_k, d_k), dtype=io, device=dev)
+    if k is None:
+        k = torch.empty((T, H_k, d_k), dtype=io, device=dev)
+    if v is None:
+        v = torch.empty((T, H_v, d_v), dtype=io, device=dev)
+    _check(q, "q", (T, H_k, d_k), io)
+    _check(k, "k", (T, H_k, d_k), io)
+    _check(v, "v", (T, H_v, d_v), io)
+    desc = GdnConvDesc(N, T, ld_x, H_k, H_v, d_k, d_v, _DT[io], float(eps))
+    st = lib.gdn_short_conv(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(x), _ptr(conv_w),
+                            _ptr(conv_state_in), _ptr(conv_state_out), _ptr(q), _ptr(k), _ptr(v),
+                            _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_short_conv")
+    return q, k, v, conv_state_out
+
+
+def gdn_gates(a_raw, b_raw, H_v, w_raw=None, A_log=None, dt_bias=None, d_k=None, d_v=None,
+              gate_dtype=None, g=None, beta_or_b=None, w=None, stream=None):
+    """Gate activations (see include/gdn.h).  Returns (g, beta_or_b, w).
+
+    Scalar gates (w_raw None): a_raw, b_raw [rows, >= H_v] -> g, beta [rows, H_v].
+    Channel gates: a_raw, b_raw [rows, >= H_v d_k], w_raw [rows, >= H_v d_v] ->
+    g, b [rows, H_v, d_k], w [rows, H_v, d_v].  Raw inputs may be column blocks
+    of one projection output.  A_log, dt_bias fp32 [columns of a] or None.
+    """
+    io = a_raw.dtype
+    if io not in _DT:
+        raise ValueError("a_raw must be float32 or bfloat16")
+    gdt = io if gate_dtype is None else gate_dtype
+    if gdt not in _DT:
+        raise ValueError("gate_dtype must be float32 or bfloat16")
+    rows = a_raw.shape[0]
+    channel = w_raw is not None
+    if channel and (d_k is None or d_v is None):
+        raise ValueError("channel gates need d_k and d_v")
+    n_ab = H_v * d_k if channel else H_v
+    ld_a = _check_rows(a_raw, "a_raw", rows, n_ab, io)
+    ld_b = _check_rows(b_raw, "b_raw", rows, n_ab, io)
+    ld_w = _check_rows(w_raw, "w_raw", rows, H_v * d_v, io) if channel else 0
+    _check(A_log, "A_log", (n_ab,), torch.float32)
+    _check(dt_bias, "dt_bias", (n_ab,), torch.float32)
+    gshape = (rows, H_v, d_k) if channel else (rows, H_v)
+    dev = a_raw.device
+    if g is None:
+        g = torch.empty(gshape, dtype=gdt, device=dev)
+    if beta_or_b is None:
+        beta_or_b = torch.empty(gshape, dtype=gdt, device=dev)
+    if channel and w is None:
+        w = torch.empty((rows, H_v, d_v), dtype=gdt, device=dev)
+    _check(g, "g", gshape, gdt)
+    _check(beta_or_b, "beta_or_b", gshape, gdt)
+    if channel:
+        _check(w, "w", (rows, H_v, d_v), gdt)
+    desc = GdnGateDesc(rows, ld_a, ld_b, ld_w, H_v, d_k or 0, d_v or 0,
+                       GDN_GATES_CHANNEL if channel else GDN_GATES_SCALAR, _DT[io], _DT[gdt])
+    st = lib.gdn_gates(ctypes.byref(desc), _ptr(a_raw), _ptr(b_raw), _ptr(w_raw), _ptr(A_log),
+                       _ptr(dt_bias), _ptr(g), _ptr(beta_or_b), _ptr(w), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_gates")
+    return g, beta_or_b, w
+
+
+def gdn_output_gate(o, z, weight, eps: float = 1e-6, y=None, stream=None):
+    """RMS norm of each value head's output times swish(z) (see include/gdn.h).
+    Returns y.
+
+    o [rows, H_v, d_v]; z [rows, >= H_v d_v] (a column block of the projection
+    output is fine); weight [d_v] fp32; y like o (allocated when not given; may
+    be o itself).
+    """
+    rows, Hv, dv = o.shape
+    io = o.dtype
+    if io not in _DT:
+        raise ValueError("o must be float32 or bfloat16")
+    _check(o, "o", (rows, Hv, dv), io)
+    ld_z = _check_rows(z, "z", rows, Hv * dv, io)
+    _check(weight, "weight", (dv,), torch.float32)
+    if y is None:
+        y = torch.empty_like(o)
+    _check(y, "y", (rows, Hv, dv), io)
+    desc = GdnNormDesc(rows, ld_z, Hv, dv, _DT[io], float(eps))
+    st = lib.gdn_output_gate(ctypes.byref(desc), _ptr(o), _ptr(z), _ptr(weight), _ptr(y),
+                             _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_output_gate")
+    return y

@@ -52,7 +52,8 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2  /* 2: adds gdn_chunk_fwd_varlen */
+#define GDN_ABI_VERSION 3  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
+                              gdn_gates, gdn_output_gate */
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -185,6 +186,132 @@ typedef struct gdn_decode_desc {
 gdn_status gdn_decode_step(const gdn_decode_desc* desc, const void* q, const void* k,
                            const void* v, const void* beta_or_b, const void* w,
                            const void* g, float* state, void* o, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The operations around the recurrence in a Gated DeltaNet block (notes page
+ * "Gated DeltaNet", §Architecture et versions hybrides, Figure 1 right-hand
+ * block): q, k, v pass through a short convolution and SiLU, q and k are
+ * then L2-normalised; alpha and beta come from a plain projection, alpha
+ * with the Mamba-2 parameterisation; the recurrence output is normalised and
+ * multiplied by a gate branch.  The projections themselves are plain GEMMs
+ * and are not part of this library.  The pages leave the exact forms open;
+ * the ones computed here are stated with each entry point.
+ * ------------------------------------------------------------------------ */
+
+/* Short causal convolution of the q, k, v branch. */
+typedef struct gdn_conv_desc {
+  int64_t N;          /* sequences, >= 0 (0: nothing to do)                      */
+  int64_t total_T;    /* packed tokens = rows of x, >= 0                         */
+  int64_t ld_x;       /* elements from one row of x to the next: >= C, % 8 == 0  */
+  int32_t H_k, H_v;   /* >= 1                                                    */
+  int32_t d_k, d_v;   /* each 64 or 128                                          */
+  int32_t io_dtype;   /* gdn_dtype of x, the conv states, q, k, v                */
+  float eps;          /* L2-norm epsilon, finite, >= 0                           */
+} gdn_conv_desc;
+
+/*
+ * gdn_short_conv -- the q, k, v branch: a depthwise causal convolution of
+ * kernel 4 along the tokens of each sequence (architecture notes page "Gated
+ * DeltaNet", §La convolution causale: a token's output combines its own
+ * input with those of the three tokens before it; the notes count 4 weights
+ * per channel, so there is no bias), SiLU, and for q and k an L2
+ * norm over the d_k channels of each head.  With C = 2 H_k d_k + H_v d_v and
+ * u the conv input of one channel,
+ *
+ *   a_t   = w[c][0] u_{t-3} + w[c][1] u_{t-2} + w[c][2] u_{t-1} + w[c][3] u_t
+ *   v_t   = silu(a_t)                        silu(x) = x / (1 + e^-x)
+ *   q_t   = silu(a_t) / sqrt(sum_head silu(a_t)^2 + eps)     (same for k)
+ *
+ * where u_{t-j} before a sequence's first token is the carried conv state
+ * (the sequence's 3 previous inputs) or 0.
+ *
+ *   cu_seqlens      [N + 1] int64 DEVICE offsets of packed sequences (as in
+ *                   gdn_chunk_fwd_varlen, clamped on the device), or NULL for
+ *                   N sequences of total_T / N tokens (total_T % N == 0)
+ *   x               [total_T, ld_x] io_dtype; columns [0, H_k d_k) are q, the
+ *                   next H_k d_k are k, the next H_v d_v are v; later columns
+ *                   (e.g. the output-gate branch) are not read
+ *   conv_w          [C, 4] fp32; tap 3 multiplies the current token
+ *   conv_state_in   [N, 3, C] io_dtype, oldest input first, or NULL (zeros)
+ *   conv_state_out  [N, 3, C] io_dtype, or NULL; receives each sequence's
+ *                   last 3 inputs (the older carried entries where a sequence
+ *                   is shorter); may equal conv_state_in
+ *   q, k            [total_T, H_k, d_k]  io_dtype (outputs)
+ *   v               [total_T, H_v, d_v]  io_dtype (output)
+ *   stream          hipStream_t or NULL
+ * A decode step is the same call with one token per sequence and the state
+ * updated in place.  Pointers are 16-byte aligned (conv_w too).
+ */
+gdn_status gdn_short_conv(const gdn_conv_desc* desc, const int64_t* cu_seqlens,
+                          const void* x, const float* conv_w, const void* conv_state_in,
+                          void* conv_state_out, void* q, void* k, void* v, void* stream);
+
+/* Gate activations. */
+typedef struct gdn_gate_desc {
+  int64_t rows;       /* tokens, >= 0                                            */
+  int64_t ld_a, ld_b; /* row strides (elements) of a_raw and b_raw, >= columns   */
+  int64_t ld_w;       /* row stride of w_raw (CHANNEL), >= H_v d_v               */
+  int32_t H_v;        /* >= 1                                                    */
+  int32_t d_k, d_v;   /* >= 1 (CHANNEL only; ignored for SCALAR)                 */
+  int32_t gate_mode;  /* gdn_gate_mode                                           */
+  int32_t in_dtype;   /* gdn_dtype of the raw projections                        */
+  int32_t gate_dtype; /* gdn_dtype of g, beta_or_b, w                            */
+} gdn_gate_desc;
+
+/*
+ * gdn_gates -- gate activations from the raw projections.  The notes page
+ * "Gated DeltaNet" (§Architecture et versions hybrides) gives alpha the
+ * Mamba-2 parameterisation and the architecture notes page (§La recurrence)
+ * puts alpha and beta in ]0,1[; computed here, per column j:
+ *
+ *   g[r][j]         = log(alpha) = -exp(A_log[j]) * softplus(a_raw[r][j] + dt_bias[j])
+ *   beta_or_b[r][j] = sigmoid(b_raw[r][j])
+ *   w[r][j]         = sigmoid(w_raw[r][j])          (CHANNEL: the GDN-2 write gate)
+ *
+ * in the layouts gdn_chunk_fwd and gdn_decode_step take.  Columns: SCALAR
+ * H_v (a, b); CHANNEL H_v d_k (a, b) and H_v d_v (w).  The raw inputs are
+ * read with row strides, so they may be column blocks of one projection
+ * output; outputs are dense.
+ *
+ *   a_raw, b_raw   [rows, ld_a], [rows, ld_b]  in_dtype
+ *   w_raw          [rows, ld_w] in_dtype (CHANNEL), NULL for SCALAR
+ *   A_log, dt_bias [columns of a] fp32, or NULL (0)
+ *   g, beta_or_b   [rows, columns of a] gate_dtype (outputs)
+ *   w              [rows, H_v d_v] gate_dtype (CHANNEL output), NULL for SCALAR
+ * Pointers are aligned to their element size; rows * columns < 2^32.
+ */
+gdn_status gdn_gates(const gdn_gate_desc* desc, const void* a_raw, const void* b_raw,
+                     const void* w_raw, const float* A_log, const float* dt_bias, void* g,
+                     void* beta_or_b, void* w, void* stream);
+
+/* Output normalisation and gate. */
+typedef struct gdn_norm_desc {
+  int64_t rows;       /* tokens, >= 0                                            */
+  int64_t ld_z;       /* elements from one row of z to the next: >= H_v d_v, % 8 == 0 */
+  int32_t H_v;        /* >= 1                                                    */
+  int32_t d_v;        /* 64 or 128                                               */
+  int32_t io_dtype;   /* gdn_dtype of o, z, y                                    */
+  float eps;          /* finite, >= 0                                            */
+} gdn_norm_desc;
+
+/*
+ * gdn_output_gate -- the block's output: each value head's recurrence output
+ * normalised, then multiplied by swish of the gate branch z (notes page
+ * "Gated DeltaNet", Figure 1; architecture notes page, §La porte de sortie:
+ * y = o (.) swish(z), swish(x) = x sigmoid(x)).  The norm is an RMS norm over
+ * the d_v channels with one weight vector shared by all heads (the
+ * architecture notes count d_v normalisation parameters per layer):
+ *
+ *   y[r][h][:] = o[r][h][:] / sqrt(mean(o[r][h][:]^2) + eps) * weight[:] * swish(z[r][h][:])
+ *
+ *   o       [rows, H_v, d_v] io_dtype
+ *   z       [rows, ld_z] io_dtype; columns [h d_v, (h+1) d_v) gate head h
+ *   weight  [d_v] fp32
+ *   y       [rows, H_v, d_v] io_dtype (output); may equal o
+ * Pointers are 16-byte aligned.
+ */
+gdn_status gdn_output_gate(const gdn_norm_desc* desc, const void* o, const void* z,
+                           const float* weight, void* y, void* stream);
 
 /* Static, never-NULL description of a status code. */
 const char* gdn_status_string(gdn_status s);

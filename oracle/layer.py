@@ -102,8 +102,9 @@ def _ranges(total_T, N, cu_seqlens):
 
 def causal_conv(x, weight, N=1, cu_seqlens=None, state_in=None):
     """Depthwise causal convolution of kernel 4 along the token axis of every
-    sequence (notes "Gated DeltaNet", §La convolution causale: each position is
-    mixed with the three before it).
+    sequence (architecture notes "Gated DeltaNet", §La convolution causale: the
+    output at a token combines that token's input with the inputs of the
+    three tokens before it).
 
     x          [total_T, C]  the packed inputs of N sequences
     weight     [C, 4]        tap 3 multiplies the current token

@@ -206,3 +206,74 @@ def decode_inputs(cfg: DecodeConfig, *, device="cpu", seed=None, N=None, Hv=None
     state = (cfg.state_std * _randn((N, Hv, cfg.dk, cfg.dv), gen, device)).contiguous()
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), beta_or_b=b.contiguous(),
                 w=None if w is None else w.contiguous(), g=g.contiguous(), state=state)
+
+
+@dataclasses.dataclass(frozen=True)
+class BlockConfig:
+    """The operations around the recurrence (short conv branch, gates, output
+    gate) at one layer shape: `rows` packed tokens in N equal sequences."""
+    name: str
+    N: int
+    T: int
+    Hk: int
+    Hv: int
+    dk: int
+    dv: int
+    channel: bool
+    io_dtype: torch.dtype
+    gate_dtype: torch.dtype
+    seed: int
+
+    @property
+    def rows(self) -> int:
+        return self.N * self.T
+
+    @property
+    def conv_channels(self) -> int:
+        return 2 * self.Hk * self.dk + self.Hv * self.dv
+
+
+# The GDN-2 B8 T4096 training shape.
+BLOCK_CONFIGS = {
+    "gdn2_block_train": BlockConfig("gdn2_block_train", N=8, T=4096, Hk=16, Hv=16, dk=128,
+                                    dv=128, channel=True, io_dtype=torch.bfloat16,
+                                    gate_dtype=torch.bfloat16, seed=7),
+}
+
+
+def block_inputs(cfg: BlockConfig, *, device="cpu", seed=None, N=None, T=None, conv_state=True):
+    """Raw inputs of the block operations as a dict of tensors on ``device``.
+
+    x       [rows, C + Hv dv]: the q|k|v|z projection output, N(0, 1); the
+            first C = 2 Hk dk + Hv dv columns feed the short conv, the last
+            Hv dv are the output-gate branch z
+    conv_w  [C, 4] fp32, 0.5 N(0, 1); conv_state [N, 3, C], N(0, 1) (or None)
+    a_raw, b_raw  [rows, n] with n = Hv (scalar gates) or Hv dk (channel),
+            N(0, 1), in one [rows, 2n] buffer (b columns first, then a)
+    w_raw   [rows, Hv dv] (channel gates) or None, N(0, 1)
+    A_log   [n] fp32, log of U(1, 16); dt_bias [n] fp32, N(-2, 0.5^2)
+    norm_w  [dv] fp32, 1 + 0.1 N(0, 1)
+    o       [rows, Hv, dv], N(0, 1): a stand-in recurrence output for the
+            output gate on its own
+    Draw order is the key order above.
+    """
+    N = cfg.N if N is None else N
+    T = cfg.T if T is None else T
+    rows = N * T
+    seed = cfg.seed if seed is None else seed
+    gen = _gen(seed, device)
+    C = cfg.conv_channels
+    n = cfg.Hv * cfg.dk if cfg.channel else cfg.Hv
+    x = _randn((rows, C + cfg.Hv * cfg.dv), gen, device).to(cfg.io_dtype)
+    conv_w = 0.5 * _randn((C, 4), gen, device)
+    cs = _randn((N, 3, C), gen, device).to(cfg.io_dtype) if conv_state else None
+    ba = _randn((rows, 2 * n), gen, device).to(cfg.io_dtype)
+    w_raw = _randn((rows, cfg.Hv * cfg.dv), gen, device).to(cfg.io_dtype) if cfg.channel else None
+    u = torch.rand(n, generator=gen, device=device, dtype=torch.float32)
+    A_log = torch.log(1.0 + 15.0 * u)
+    dt_bias = -2.0 + 0.5 * _randn((n,), gen, device)
+    norm_w = 1.0 + 0.1 * _randn((cfg.dv,), gen, device)
+    o = _randn((rows, cfg.Hv, cfg.dv), gen, device).to(cfg.io_dtype)
+    return dict(x=x.contiguous(), conv_w=conv_w.contiguous(), conv_state=cs, ba=ba.contiguous(),
+                b_raw=ba[:, :n], a_raw=ba[:, n:], w_raw=w_raw, A_log=A_log, dt_bias=dt_bias,
+                norm_w=norm_w, o=o.contiguous(), z=x[:, C:])

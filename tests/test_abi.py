@@ -22,7 +22,7 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["gdn_chunk_fwd", "gdn_chunk_fwd_varlen", "gdn_decode_step", "gdn_status_string",
-         "gdn_abi_version"])
+         "gdn_abi_version", "gdn_short_conv", "gdn_gates", "gdn_output_gate"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert gdn.abi_version() == 2
+    assert gdn.abi_version() == 3
     for st in range(4):
         s = gdn.status_string(st)
         assert s.startswith("GDN_")
@@ -227,3 +227,128 @@ def test_varlen_nothing_to_do_returns_ok_without_launch():
     # no token at all and no state to move
     assert _varlen(_varlen_desc(total_T=0), s_out=None) == gdn.GDN_OK
     assert _varlen(_varlen_desc(total_T=0), s_out=_addr(7)) == gdn.GDN_OK    # in place
+
+
+# ---------------------------------------------------------------------------
+# Block operations around the recurrence: short conv, gates, output gate.
+# ---------------------------------------------------------------------------
+def _conv_desc(**kw):
+    d = dict(N=2, total_T=100, ld_x=2 * 2 * 128 + 4 * 128, H_k=2, H_v=4, d_k=128, d_v=128,
+             io_dtype=gdn.GDN_BF16, eps=1e-6)
+    d.update(kw)
+    return gdn.GdnConvDesc(**d)
+
+
+def _conv(desc, cu=None, **ptrs):
+    names = ["x", "w", "s_in", "s_out", "q", "k", "v"]
+    p = {n: _addr(i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    return gdn.lib.gdn_short_conv(ctypes.byref(desc) if desc is not None else None, cu,
+                                  *[p[n] for n in names], None)
+
+
+@pytest.mark.parametrize("field,value,expected", [
+    ("N", -1, 1), ("total_T", -1, 1), ("H_k", 0, 1), ("d_k", 96, 2), ("d_v", 32, 2),
+    ("io_dtype", 4, 1), ("eps", float("nan"), 1), ("eps", -1.0, 1),
+    ("ld_x", 100, 1),          # narrower than the branch
+    ("ld_x", 1028, 1),         # rows not 16-byte aligned
+    ("total_T", 101, 1),       # equal-length batch needs total_T % N == 0
+])
+def test_short_conv_rejects_bad_descriptor(field, value, expected):
+    assert _conv(_conv_desc(**{field: value})) == expected
+
+
+@pytest.mark.parametrize("name", ["x", "w", "q", "k", "v"])
+def test_short_conv_rejects_null_and_misaligned(name):
+    assert _conv(_conv_desc(), **{name: None}) == gdn.GDN_ERR_INVALID_ARG
+    assert _conv(_conv_desc(), **{name: _addr(9, 8)}) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_short_conv_overlap_rules():
+    # an output inside x
+    assert _conv(_conv_desc(), q=_addr(0, 256)) == gdn.GDN_ERR_INVALID_ARG
+    # k on top of q
+    assert _conv(_conv_desc(), k=_addr(4, 16)) == gdn.GDN_ERR_INVALID_ARG
+    # state_out partly over state_in
+    assert _conv(_conv_desc(), s_out=_addr(2, 32)) == gdn.GDN_ERR_INVALID_ARG
+    # offsets must be 8-byte aligned
+    assert _conv(_conv_desc(), cu=_addr(8, 4)) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_short_conv_nothing_to_do_returns_ok_without_launch():
+    assert _conv(_conv_desc(N=0)) == gdn.GDN_OK
+    assert _conv(_conv_desc(total_T=0), s_out=None) == gdn.GDN_OK
+    assert _conv(_conv_desc(total_T=0), s_out=_addr(2)) == gdn.GDN_OK   # in place, no tokens
+
+
+def _gate_desc(**kw):
+    d = dict(rows=64, ld_a=8, ld_b=8, ld_w=0, H_v=4, d_k=0, d_v=0,
+             gate_mode=gdn.GDN_GATES_SCALAR, in_dtype=gdn.GDN_BF16, gate_dtype=gdn.GDN_F32)
+    d.update(kw)
+    return gdn.GdnGateDesc(**d)
+
+
+def _gates(desc, **ptrs):
+    names = ["a", "b", "w_raw", "A_log", "dt_bias", "g", "beta", "w"]
+    p = {n: _addr(i) for i, n in enumerate(names)}
+    if desc is not None and desc.gate_mode == gdn.GDN_GATES_SCALAR:
+        p["w_raw"] = p["w"] = None
+    p.update(ptrs)
+    return gdn.lib.gdn_gates(ctypes.byref(desc) if desc is not None else None,
+                             *[p[n] for n in names], None)
+
+
+@pytest.mark.parametrize("field,value,expected", [
+    ("rows", -1, 1), ("H_v", 0, 1), ("gate_mode", 3, 1), ("in_dtype", 9, 1),
+    ("gate_dtype", 9, 1), ("ld_a", 3, 1), ("ld_b", 2, 1),
+    ("rows", 1 << 31, 2),      # rows * columns must fit 32-bit indices
+])
+def test_gates_rejects_bad_descriptor(field, value, expected):
+    assert _gates(_gate_desc(**{field: value})) == expected
+
+
+def test_gates_pointer_rules():
+    assert _gates(None) == gdn.GDN_ERR_INVALID_ARG
+    assert _gates(_gate_desc(), a=None) == gdn.GDN_ERR_INVALID_ARG
+    assert _gates(_gate_desc(), w=_addr(7)) == gdn.GDN_ERR_INVALID_ARG     # w in scalar mode
+    ch = dict(gate_mode=gdn.GDN_GATES_CHANNEL, d_k=64, d_v=64, ld_a=256, ld_b=256, ld_w=256)
+    assert _gates(_gate_desc(**ch), w_raw=None) == gdn.GDN_ERR_INVALID_ARG
+    assert _gates(_gate_desc(**{**ch, "ld_w": 100})) == gdn.GDN_ERR_INVALID_ARG
+    assert _gates(_gate_desc(**{**ch, "d_k": 0})) == gdn.GDN_ERR_INVALID_ARG
+    assert _gates(_gate_desc(), a=_addr(0, 1)) == gdn.GDN_ERR_INVALID_ARG  # bf16 needs 2 bytes
+    assert _gates(_gate_desc(), g=_addr(5, 2)) == gdn.GDN_ERR_INVALID_ARG  # fp32 needs 4 bytes
+    assert _gates(_gate_desc(), g=_addr(0, 4)) == gdn.GDN_ERR_INVALID_ARG  # g over a_raw
+    assert _gates(_gate_desc(), beta=_addr(5, 64)) == gdn.GDN_ERR_INVALID_ARG  # beta over g
+    assert _gates(_gate_desc(rows=0)) == gdn.GDN_OK
+
+
+def _norm_desc(**kw):
+    d = dict(rows=64, ld_z=4 * 128, H_v=4, d_v=128, io_dtype=gdn.GDN_BF16, eps=1e-6)
+    d.update(kw)
+    return gdn.GdnNormDesc(**d)
+
+
+def _outgate(desc, **ptrs):
+    names = ["o", "z", "w", "y"]
+    p = {n: _addr(i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    return gdn.lib.gdn_output_gate(ctypes.byref(desc) if desc is not None else None,
+                                   *[p[n] for n in names], None)
+
+
+@pytest.mark.parametrize("field,value,expected", [
+    ("rows", -1, 1), ("H_v", 0, 1), ("d_v", 96, 2), ("io_dtype", 3, 1),
+    ("eps", float("inf"), 1), ("ld_z", 100, 1), ("ld_z", 4 * 128 + 4, 1),
+])
+def test_output_gate_rejects_bad_descriptor(field, value, expected):
+    assert _outgate(_norm_desc(**{field: value})) == expected
+
+
+def test_output_gate_pointer_rules():
+    assert _outgate(None) == gdn.GDN_ERR_INVALID_ARG
+    for name in ["o", "z", "w", "y"]:
+        assert _outgate(_norm_desc(), **{name: None}) == gdn.GDN_ERR_INVALID_ARG
+        assert _outgate(_norm_desc(), **{name: _addr(6, 8)}) == gdn.GDN_ERR_INVALID_ARG
+    assert _outgate(_norm_desc(), y=_addr(1, 64)) == gdn.GDN_ERR_INVALID_ARG   # y over z
+    assert _outgate(_norm_desc(), y=_addr(0, 64)) == gdn.GDN_ERR_INVALID_ARG   # y partly over o
+    assert _outgate(_norm_desc(rows=0)) == gdn.GDN_OK
