@@ -228,8 +228,7 @@ gdn_status gdn_short_conv(const gdn_conv_desc* d, const int64_t* cu_seqlens, con
   if (d->ld_x < C || d->ld_x % 8 != 0) return GDN_ERR_INVALID_ARG;
   if ((double)d->total_T * (double)d->ld_x > 9.0e15 || (double)d->N * 3.0 * (double)C > 9.0e15)
     return GDN_ERR_INVALID_ARG;
-  if (2 * (int64_t)d->H_k + d->H_v > 65535 || (double)d->total_T / 256.0 > 2.0e9)
-    return GDN_ERR_UNSUPPORTED;  // grid limits
+  if (2.0 * d->H_k + d->H_v > 2.0e9) return GDN_ERR_UNSUPPORTED;  // grid limit
   if (d->N == 0) return GDN_OK;
   if (!cu_seqlens && d->total_T % d->N != 0) return GDN_ERR_INVALID_ARG;
   if (cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0) return GDN_ERR_INVALID_ARG;

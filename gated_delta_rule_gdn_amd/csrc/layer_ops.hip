@@ -17,11 +17,13 @@
 #include "gdn_device.hpp"
 #include "gdn_kernels.hpp"
 
+#include <type_traits>
+
 namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kConvTokens = 256;  // tokens per short-conv workgroup
+constexpr int kConvTokens = 128;  // tokens per short-conv workgroup
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* out) {
@@ -40,24 +42,62 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.f + e);
 }
 
-// Sum over the L consecutive lanes (L a power of two dividing 64) that hold
-// one row.
+// Sum over the L consecutive lanes (L = 8 or 16, aligned) that hold one row,
+// as a butterfly of DPP moves inside each 16-lane row: swap neighbours, swap
+// pairs, then fold the 8-lane halves and the 16-lane row onto their mirrors.
 template <int L>
 __device__ __forceinline__ float row_sum(float s) {
-#pragma unroll
-  for (int m = 1; m < L; m <<= 1) s += __shfl_xor(s, m);
+  static_assert(L == 8 || L == 16, "row width");
+  auto dpp = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  s += dpp(s, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  s += dpp(s, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  s += dpp(s, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (L == 16) s += dpp(s, std::integral_constant<int, 0x140>{});  // row_mirror
   return s;
+}
+
+// 8 consecutive elements kept as loaded (converted when used), so that many
+// rows can be in flight at the cost of 4 (bf16) or 8 (fp32) registers each.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> { uint4 u; };
+template <> struct Raw8<float> { float4 a, b; };
+
+__device__ __forceinline__ void ld_raw8(const bf16* p, Raw8<bf16>& r) {
+  r.u = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void ld_raw8(const float* p, Raw8<float>& r) {
+  r.a = reinterpret_cast<const float4*>(p)[0];
+  r.b = reinterpret_cast<const float4*>(p)[1];
+}
+__device__ __forceinline__ void unpack8(const Raw8<bf16>& r, float* out) {
+  const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack8(const Raw8<float>& r, float* out) {
+  out[0] = r.a.x; out[1] = r.a.y; out[2] = r.a.z; out[3] = r.a.w;
+  out[4] = r.b.x; out[5] = r.b.y; out[6] = r.b.z; out[7] = r.b.w;
 }
 
 // ---------------------------------------------------------------------------
 // Short causal convolution.
 //
-// Grid: x = blocks of 256 packed tokens, y = heads of the branch (q heads,
-// then k heads, then v heads).  A head of width D is covered by D/8 lanes
-// with 8 channels each (one 16-byte bf16 access per row); the workgroup's
-// 256 threads form 2048/D streams that each walk D/8 consecutive tokens,
-// keeping the three previous inputs in registers so every input row is read
-// once (plus a 3-row halo per stream, served by L2).  A stream that lies
+// Grid: x = heads of the branch (q heads, then k heads, then v heads), y =
+// blocks of kConvTokens packed tokens, so that the workgroups running
+// together read whole rows of x (all heads of the same tokens) rather than
+// one head's 256-byte piece of many rows (measured 1.4x faster).  A head of
+// width D is covered by D/8 lanes with 8 channels each (one 16-byte bf16
+// access per row); the workgroup's 256 threads form 2048/D streams that each
+// walk kConvTokens*D/2048 consecutive tokens (8 for D = 128, the fastest of
+// 4, 8, 16 and 32), keeping the three previous inputs in registers so every
+// input row is read once from HBM (the 3-row halo of a stream is its
+// neighbour's rows, served by L2).  A stream that lies
 // inside one sequence with its halo takes a branch-free path; a stream that
 // touches a sequence start fetches the history from the carried conv state.
 // ---------------------------------------------------------------------------
@@ -99,8 +139,8 @@ __device__ SeqPos find_seq(const ConvArgs& p, int64_t r) {
 }
 
 template <typename T, int D, bool NORM>
-__device__ __forceinline__ void conv_head(const ConvArgs& p, int64_t col, T* __restrict__ out,
-                                          int64_t out_ld) {
+__device__ __forceinline__ void conv_head(const ConvArgs& p, int64_t blk, int64_t col,
+                                          T* __restrict__ out, int64_t out_ld) {
   constexpr int TPR = D / 8;              // lanes per token row
   constexpr int TB = kConvTokens * TPR / kThreads;  // tokens per stream
   const int tid = threadIdx.x;
@@ -118,7 +158,7 @@ __device__ __forceinline__ void conv_head(const ConvArgs& p, int64_t col, T* __r
     w[0][i] = t.x; w[1][i] = t.y; w[2][i] = t.z; w[3][i] = t.w;
   }
 
-  const int64_t r0 = (int64_t)blockIdx.x * kConvTokens + (int64_t)stream * TB;
+  const int64_t r0 = blk * kConvTokens + (int64_t)stream * TB;
   if (r0 >= p.total_T) return;
 
   auto finish = [&](int64_t r, float* acc) {
@@ -140,20 +180,27 @@ __device__ __forceinline__ void conv_head(const ConvArgs& p, int64_t col, T* __r
 
   SeqPos sp = find_seq(p, r0);
   if (sp.hist && sp.start <= r0 - 3 && r0 + TB <= sp.end) {
-    // Whole stream and its halo inside one sequence.
-    float h[3][8], X[TB][8];
+    // Whole stream and its halo inside one sequence.  Every row load is
+    // issued before any arithmetic (the scheduling barrier keeps the
+    // compiler from spreading them over the token loop).
+    Raw8<T> H[3], X[TB];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) load8<T>(x + (r0 - 3 + j) * p.ld_x + c, h[j]);
+    for (int j = 0; j < 3; ++j) ld_raw8(x + (r0 - 3 + j) * p.ld_x + c, H[j]);
 #pragma unroll
-    for (int t = 0; t < TB; ++t) load8<T>(x + (r0 + t) * p.ld_x + c, X[t]);
+    for (int t = 0; t < TB; ++t) ld_raw8(x + (r0 + t) * p.ld_x + c, X[t]);
+    __builtin_amdgcn_sched_barrier(0);
+    float h[3][8];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) unpack8(H[j], h[j]);
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
-      float acc[8];
+      float xt[8], acc[8];
+      unpack8(X[t], xt);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        acc[i] = w[0][i] * h[0][i] + w[1][i] * h[1][i] + w[2][i] * h[2][i] + w[3][i] * X[t][i];
+        acc[i] = w[0][i] * h[0][i] + w[1][i] * h[1][i] + w[2][i] * h[2][i] + w[3][i] * xt[i];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { h[0][i] = h[1][i]; h[1][i] = h[2][i]; h[2][i] = X[t][i]; }
+      for (int i = 0; i < 8; ++i) { h[0][i] = h[1][i]; h[1][i] = h[2][i]; h[2][i] = xt[i]; }
       finish(r0 + t, acc);
     }
     return;
@@ -187,18 +234,21 @@ __device__ __forceinline__ void conv_head(const ConvArgs& p, int64_t col, T* __r
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kThreads) void short_conv_kernel(ConvArgs p) {
-  const int hh = blockIdx.y;
-  if (hh < p.Hk) {
-    conv_head<T, DK, true>(p, (int64_t)hh * DK, static_cast<T*>(p.q) + (int64_t)hh * DK,
-                           (int64_t)p.Hk * DK);
-  } else if (hh < 2 * p.Hk) {
-    const int h = hh - p.Hk;
-    conv_head<T, DK, true>(p, (int64_t)(p.Hk + h) * DK, static_cast<T*>(p.k) + (int64_t)h * DK,
-                           (int64_t)p.Hk * DK);
-  } else {
-    const int h = hh - 2 * p.Hk;
-    conv_head<T, DV, false>(p, (int64_t)2 * p.Hk * DK + (int64_t)h * DV,
-                            static_cast<T*>(p.v) + (int64_t)h * DV, (int64_t)p.Hv * DV);
+  const int hh = blockIdx.x;
+  const int64_t nblk = (p.total_T + kConvTokens - 1) / kConvTokens;
+  for (int64_t blk = blockIdx.y; blk < nblk; blk += gridDim.y) {
+    if (hh < p.Hk) {
+      conv_head<T, DK, true>(p, blk, (int64_t)hh * DK, static_cast<T*>(p.q) + (int64_t)hh * DK,
+                             (int64_t)p.Hk * DK);
+    } else if (hh < 2 * p.Hk) {
+      const int h = hh - p.Hk;
+      conv_head<T, DK, true>(p, blk, (int64_t)(p.Hk + h) * DK,
+                             static_cast<T*>(p.k) + (int64_t)h * DK, (int64_t)p.Hk * DK);
+    } else {
+      const int h = hh - 2 * p.Hk;
+      conv_head<T, DV, false>(p, blk, (int64_t)2 * p.Hk * DK + (int64_t)h * DV,
+                              static_cast<T*>(p.v) + (int64_t)h * DV, (int64_t)p.Hv * DV);
+    }
   }
 }
 
@@ -238,12 +288,26 @@ __global__ __launch_bounds__(kThreads) void conv_state_kernel(ConvArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Gate activations: one thread per element, flat over rows x columns (32-bit
-// index arithmetic; the launcher checks that the element counts fit).
+// Gate activations, on the hardware exp / log / reciprocal:
+//   sigmoid(x)  = 1 / (1 + 2^(-x log2 e))   (0 and 1 at the saturated ends)
+//   softplus(x) = max(x, 0) + log(1 + t),  t = e^-|x| in (0, 1]; for
+//                 t < 2^-10 the series t - t^2/2 replaces the log, which
+//                 would lose t's low bits in 1 + t.
+// The vector kernel handles 8 consecutive columns per thread (every row
+// stride a multiple of 8 and the pointers 16-byte aligned); the scalar kernel
+// one element.  Flat indices are 32-bit (the host checks the counts fit).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.f + exp2_fast(-x * kLog2e));
+}
 __device__ __forceinline__ float softplus_f(float x) {
-  return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+  const float t = exp2_fast(-fabsf(x) * kLog2e);
+  const float l = t < 0x1p-10f ? t - 0.5f * t * t
+                               : __builtin_amdgcn_logf(1.f + t) * 0.6931471805599453f;
+  return fmaxf(x, 0.f) + l;
+}
+__device__ __forceinline__ float decay_f(float a, float A_log, float dt) {
+  return -exp2_fast(A_log * kLog2e) * softplus_f(a + dt);
 }
 
 template <typename TI, typename TO>
@@ -252,18 +316,69 @@ __global__ __launch_bounds__(kThreads) void gates_kernel(GateArgs p) {
   const TI* a = static_cast<const TI*>(p.a);
   const TI* b = static_cast<const TI*>(p.b);
   if (e < p.n_ab_total) {
-    const uint32_t r = e / (uint32_t)p.n_ab, col = e - r * (uint32_t)p.n_ab;
+    const uint32_t r = e / p.n_ab, col = e - r * p.n_ab;
     const float av = to_f32(a[(int64_t)r * p.ld_a + col]);
     const float bv = to_f32(b[(int64_t)r * p.ld_b + col]);
-    const float A = p.A_log ? expf(p.A_log[col]) : 1.f;
+    const float Al = p.A_log ? p.A_log[col] : 0.f;
     const float dt = p.dt_bias ? p.dt_bias[col] : 0.f;
-    static_cast<TO*>(p.g)[e] = from_f32<TO>(-A * softplus_f(av + dt));
+    static_cast<TO*>(p.g)[e] = from_f32<TO>(decay_f(av, Al, dt));
     static_cast<TO*>(p.beta)[e] = from_f32<TO>(sigmoid_f(bv));
   }
   if (e < p.n_w_total) {
-    const uint32_t r = e / (uint32_t)p.n_w, col = e - r * (uint32_t)p.n_w;
+    const uint32_t r = e / p.n_w, col = e - r * p.n_w;
     const float wv = to_f32(static_cast<const TI*>(p.w_raw)[(int64_t)r * p.ld_w + col]);
     static_cast<TO*>(p.w)[e] = from_f32<TO>(sigmoid_f(wv));
+  }
+}
+
+__device__ __forceinline__ void ld_params8(const float* p, int64_t col, float dflt, float* out) {
+  if (p) {
+    const float4 u = *reinterpret_cast<const float4*>(p + col);
+    const float4 v = *reinterpret_cast<const float4*>(p + col + 4);
+    out[0] = u.x; out[1] = u.y; out[2] = u.z; out[3] = u.w;
+    out[4] = v.x; out[5] = v.y; out[6] = v.z; out[7] = v.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = dflt;
+  }
+}
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(kThreads) void gates_vec_kernel(GateArgs p) {
+  const uint32_t e = blockIdx.x * kThreads + threadIdx.x;   // group of 8 elements
+  const uint32_t nab8 = p.n_ab >> 3, nw8 = p.n_w >> 3;
+  Raw8<TI> ra, rb, rw;
+  uint32_t r = 0, c8 = 0, rw_ = 0, cw8 = 0;
+  const bool ab = e < (p.n_ab_total >> 3), ww = e < (p.n_w_total >> 3);
+  if (ab) {
+    r = e / nab8; c8 = e - r * nab8;
+    ld_raw8(static_cast<const TI*>(p.a) + (int64_t)r * p.ld_a + 8 * c8, ra);
+    ld_raw8(static_cast<const TI*>(p.b) + (int64_t)r * p.ld_b + 8 * c8, rb);
+  }
+  if (ww) {
+    rw_ = e / nw8; cw8 = e - rw_ * nw8;
+    ld_raw8(static_cast<const TI*>(p.w_raw) + (int64_t)rw_ * p.ld_w + 8 * cw8, rw);
+  }
+  if (ab) {
+    float av[8], bv[8], Al[8], dt[8], g[8], be[8];
+    unpack8(ra, av);
+    unpack8(rb, bv);
+    ld_params8(p.A_log, 8 * (int64_t)c8, 0.f, Al);
+    ld_params8(p.dt_bias, 8 * (int64_t)c8, 0.f, dt);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      g[i] = decay_f(av[i], Al[i], dt[i]);
+      be[i] = sigmoid_f(bv[i]);
+    }
+    store8<TO>(static_cast<TO*>(p.g) + 8 * (int64_t)e, g);
+    store8<TO>(static_cast<TO*>(p.beta) + 8 * (int64_t)e, be);
+  }
+  if (ww) {
+    float wv[8];
+    unpack8(rw, wv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wv[i] = sigmoid_f(wv[i]);
+    store8<TO>(static_cast<TO*>(p.w) + 8 * (int64_t)e, wv);
   }
 }
 
@@ -323,7 +438,8 @@ template <typename T>
 hipError_t launch_short_conv_t(const ConvArgs& a, hipStream_t stream) {
   const int heads = 2 * a.Hk + a.Hv;
   if (a.total_T > 0) {
-    const dim3 grid((unsigned)((a.total_T + kConvTokens - 1) / kConvTokens), (unsigned)heads);
+    const int64_t blocks = (a.total_T + kConvTokens - 1) / kConvTokens;
+    const dim3 grid((unsigned)heads, (unsigned)(blocks < 65535 ? blocks : 65535));
     if (a.dk == 128 && a.dv == 128) short_conv_kernel<T, 128, 128><<<grid, kThreads, 0, stream>>>(a);
     else if (a.dk == 128) short_conv_kernel<T, 128, 64><<<grid, kThreads, 0, stream>>>(a);
     else if (a.dv == 128) short_conv_kernel<T, 64, 128><<<grid, kThreads, 0, stream>>>(a);
@@ -343,7 +459,19 @@ hipError_t launch_short_conv_t(const ConvArgs& a, hipStream_t stream) {
 template <typename TI, typename TO>
 hipError_t launch_gates_t(const GateArgs& a, hipStream_t stream) {
   const int64_t n = a.n_ab_total > a.n_w_total ? a.n_ab_total : a.n_w_total;
-  gates_kernel<TI, TO><<<dim3((unsigned)((n + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(a);
+  auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  const bool vec = a.n_ab % 8 == 0 && a.n_w % 8 == 0 && a.ld_a % 8 == 0 && a.ld_b % 8 == 0 &&
+                   a.ld_w % 8 == 0 && al16(a.a) && al16(a.b) && al16(a.g) && al16(a.beta) &&
+                   (!a.w_raw || (al16(a.w_raw) && al16(a.w))) &&
+                   (!a.A_log || al16(a.A_log)) && (!a.dt_bias || al16(a.dt_bias));
+  if (vec) {
+    const int64_t n8 = n / 8;
+    gates_vec_kernel<TI, TO><<<dim3((unsigned)((n8 + kThreads - 1) / kThreads)), kThreads, 0,
+                               stream>>>(a);
+  } else {
+    gates_kernel<TI, TO><<<dim3((unsigned)((n + kThreads - 1) / kThreads)), kThreads, 0,
+                           stream>>>(a);
+  }
   return hipGetLastError();
 }
 
