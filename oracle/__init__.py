@@ -16,6 +16,7 @@ Functions (each follows the passages cited in ``gdn_oracle.c``):
   chunkwise  -- naive chunkwise form (same page, §3, decay absorption and
                 (I+T)^{-1} solve).  Used only to check the decomposition.
   decode     -- one token per sequence, state updated in place.
+  backward   -- gradients of the recurrence (reverse mode, token by token).
 
 The operations around the recurrence in a Gated DeltaNet block (short causal
 convolution, SiLU, L2 norm, gate activations, output norm and swish gate) are
@@ -53,6 +54,9 @@ def _load():
                                    ctypes.c_int, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp,
                                    ctypes.c_double, _dp, _dp, ctypes.c_int]
     lib.gdn_ref_decode.restype = ctypes.c_int
+    lib.gdn_ref_backward.argtypes = common + [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                              ctypes.c_int]
+    lib.gdn_ref_backward.restype = ctypes.c_int
     lib.gdn_oracle_abi.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -139,6 +143,32 @@ def decode(q, k, v, beta_or_b, state, w=None, g=None, scale=1.0, nthreads=None):
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return o, st
+
+
+def backward(q, k, v, beta_or_b, d_o, w=None, g=None, scale=1.0, state_in=None,
+             d_state_out=None, nthreads=None):
+    """Gradients of the token recurrence (reverse mode, fp64).
+
+    Returns a dict with dq, dk [B,T,Hk,dk], dv [B,T,Hv,dv], db (shape of
+    beta_or_b), dw (shape of w, or None), dg (shape of beta_or_b, or None when
+    g is None) and d_state_in [B,Hv,dk,dv], all float64.  Keeps every state
+    of a head, so it is meant for small T.
+    """
+    q, k, v, bb, w, g, s0, do, dsT = map(_f64, (q, k, v, beta_or_b, w, g, state_in, d_o,
+                                                d_state_out))
+    B, T, Hk, Hv, dk, dv, mode = _shapes(q, v, bb, w)
+    out = {"dq": np.zeros(q.shape), "dk": np.zeros(q.shape), "dv": np.zeros(v.shape),
+           "db": np.zeros(bb.shape), "dw": None if w is None else np.zeros(w.shape),
+           "dg": None if g is None else np.zeros(bb.shape),
+           "d_state_in": np.zeros((B, Hv, dk, dv))}
+    rc = _load().gdn_ref_backward(B, T, Hk, Hv, dk, dv, mode, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(bb), _ptr(w), _ptr(g), float(scale), _ptr(s0), _ptr(do),
+                                  _ptr(dsT), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                  _ptr(out["db"]), _ptr(out["dw"]), _ptr(out["dg"]),
+                                  _ptr(out["d_state_in"]), _threads(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
 
 
 def abi_version():

@@ -41,7 +41,7 @@
 #include <omp.h>
 #endif
 
-#define ORACLE_ABI 1
+#define ORACLE_ABI 2
 
 int gdn_oracle_abi(void) { return ORACLE_ABI; }
 
@@ -320,6 +320,191 @@ int gdn_ref_chunkwise(long B, long T, int Hk, int Hv, int dk, int dv, int gate_m
     if (state_out)
       memcpy(state_out + bh * (long)dk * dv, S, sizeof(double) * (size_t)dk * dv);
     free(mem);
+  }
+  return bad ? 1 : 0;
+}
+
+/*
+ * Gradients of the recurrence (reverse mode, token by token) -- the backward
+ * pass that training needs ("Gated DeltaNet-2", §3: the gate-aware gradient
+ * accumulation of the auxiliary matrices; "Gated DeltaNet", §Rendre
+ * l'entrainement parallele).  The pages give no gradient formulas; these
+ * are the chain rule applied to the per-token steps of run_head, taken in
+ * reverse order.  With P_t the state before token t (P_0 = state_in),
+ * abar = exp(g_t), e = b (.) k, z = w (.) v:
+ *
+ *   Sbar = Diag(abar) P_t,  r = Sbar^T e,  u = z - r,
+ *   P_{t+1} = Sbar + k u^T,  o_t = scale P_{t+1}^T q_t.
+ *
+ * Reverse step, with D the gradient w.r.t. P_{t+1} (D = d_state_out after the
+ * last token, or 0):
+ *   D     += scale q_t dO_t^T
+ *   dq_t  += scale P_{t+1} dO_t
+ *   du     = D^T k_t                 (dz = du, dr = -du)
+ *   dv_t   = w (.) du,  dw_t = v (.) du
+ *   de     = -Sbar du
+ *   dk_t  += D u + b (.) de,  db_t = k (.) de
+ *   dSbar  = D - e du^T
+ *   dg_t   = abar (.) rowsum(dSbar (.) P_t)
+ *   D      = Diag(abar) dSbar        (the gradient w.r.t. P_t)
+ * and d_state_in = D after token 0.  In scalar mode b = w = beta_t, so
+ * dbeta_t = sum(k (.) de) + sum(v (.) du), and dg_t is the sum over channels.
+ * dq and dk sum over the value heads that share a key head.
+ *
+ *   d_o          [B, T, Hv, dv]
+ *   d_state_out  [B, Hv, dk, dv] or NULL (no gradient flows into the final state)
+ *   outputs: dq, dk [B,T,Hk,dk]; dv [B,T,Hv,dv]; db like beta_or_b; dw like w
+ *   (NULL in scalar mode); dg like beta_or_b (NULL allowed, and required to be
+ *   NULL when g is NULL); d_state_in [B,Hv,dk,dv] or NULL.
+ * All states of a head are kept (T+1 matrices), so this is for small T.
+ * Returns 0 on success, 1 on bad arguments or allocation failure.
+ */
+int gdn_ref_backward(long B, long T, int Hk, int Hv, int dk, int dv, int gate_mode,
+                     const double* q, const double* k, const double* v,
+                     const double* beta_or_b, const double* w, const double* g,
+                     double scale, const double* state_in, const double* d_o,
+                     const double* d_state_out, double* dq, double* dk_out,
+                     double* dv_out, double* db, double* dw, double* dg,
+                     double* d_state_in, int nthreads) {
+  if (check_dims(B, T, Hk, Hv, dk, dv)) return 1;
+  if (gate_mode != 0 && gate_mode != 1) return 1;
+  if (!q || !k || !v || !beta_or_b || !d_o || !dq || !dk_out || !dv_out || !db) return 1;
+  if (gate_mode == 1 && (!w || !dw)) return 1;
+  if (gate_mode == 0 && (w || dw)) return 1;
+  if (!g && dg) return 1;
+  const int group = Hv / Hk;
+  const int ch = gate_mode == 1;
+  const long n_groups = B * (long)Hk;
+  const size_t SS = (size_t)dk * dv;
+  int bad = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  /* dq, dk are sums over the value heads of a key head: one thread per
+   * (sequence, key head) owns them. */
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (long bg = 0; bg < n_groups; ++bg) {
+    long b = bg / Hk;
+    int hk = (int)(bg % Hk);
+    for (long t = 0; t < T; ++t) {
+      long row = (b * T + t) * Hk + hk;
+      memset(dq + row * dk, 0, sizeof(double) * dk);
+      memset(dk_out + row * dk, 0, sizeof(double) * dk);
+    }
+    double* P = (double*)malloc(sizeof(double) * SS * (size_t)(T + 1));
+    double* U = (double*)malloc(sizeof(double) * (size_t)dv * (size_t)(T > 0 ? T : 1));
+    double* D = (double*)malloc(sizeof(double) * SS);
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)(3 * dk + 3 * dv));
+    if (!P || !U || !D || !tmp) { bad |= 1; free(P); free(U); free(D); free(tmp); continue; }
+    double* a = tmp;             /* abar   [dk] */
+    double* e = a + dk;          /* e      [dk] */
+    double* de = e + dk;         /* de     [dk] */
+    double* z = de + dk;         /* z      [dv] */
+    double* r = z + dv;          /* r      [dv] */
+    double* du = r + dv;         /* du     [dv] */
+    for (int hv = hk * group; hv < (hk + 1) * group; ++hv) {
+      const long bh = b * Hv + hv;
+      /* forward, keeping every state and every u */
+      if (state_in) memcpy(P, state_in + bh * (long)SS, sizeof(double) * SS);
+      else memset(P, 0, sizeof(double) * SS);
+      for (long t = 0; t < T; ++t) {
+        const long bth = (b * T + t) * (long)Hv + hv;
+        const double* kt = k + ((b * T + t) * Hk + hk) * (long)dk;
+        const double* vt = v + bth * (long)dv;
+        const double* Pt = P + (size_t)t * SS;
+        double* Pn = P + (size_t)(t + 1) * SS;
+        for (int i = 0; i < dk; ++i) {
+          a[i] = g ? exp(gate_at(g, ch, bth, dk, i)) : 1.0;
+          e[i] = gate_at(beta_or_b, ch, bth, dk, i) * kt[i];
+        }
+        for (int j = 0; j < dv; ++j) {
+          z[j] = (ch ? w[bth * (long)dv + j] : beta_or_b[bth]) * vt[j];
+          r[j] = 0.0;
+        }
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j) r[j] += a[i] * Pt[(size_t)i * dv + j] * e[i];
+        double* ut = U + (size_t)t * dv;
+        for (int j = 0; j < dv; ++j) ut[j] = z[j] - r[j];
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j)
+            Pn[(size_t)i * dv + j] = a[i] * Pt[(size_t)i * dv + j] + kt[i] * ut[j];
+      }
+      /* reverse */
+      if (d_state_out) memcpy(D, d_state_out + bh * (long)SS, sizeof(double) * SS);
+      else memset(D, 0, sizeof(double) * SS);
+      for (long t = T - 1; t >= 0; --t) {
+        const long bth = (b * T + t) * (long)Hv + hv;
+        const long krow = (b * T + t) * Hk + hk;
+        const double* qt = q + krow * (long)dk;
+        const double* kt = k + krow * (long)dk;
+        const double* vt = v + bth * (long)dv;
+        const double* dot = d_o + bth * (long)dv;
+        const double* Pt = P + (size_t)t * SS;
+        const double* Pn = P + (size_t)(t + 1) * SS;
+        const double* ut = U + (size_t)t * dv;
+        double* dqt = dq + krow * (long)dk;
+        double* dkt = dk_out + krow * (long)dk;
+        double bsum = 0.0, gsum = 0.0;
+        for (int i = 0; i < dk; ++i) {
+          a[i] = g ? exp(gate_at(g, ch, bth, dk, i)) : 1.0;
+          e[i] = gate_at(beta_or_b, ch, bth, dk, i) * kt[i];
+        }
+        /* o_t = scale P_{t+1}^T q_t */
+        for (int i = 0; i < dk; ++i) {
+          double acc = 0.0;
+          for (int j = 0; j < dv; ++j) {
+            D[(size_t)i * dv + j] += scale * qt[i] * dot[j];
+            acc += Pn[(size_t)i * dv + j] * dot[j];
+          }
+          dqt[i] += scale * acc;
+        }
+        /* P_{t+1} = Sbar + k u^T */
+        for (int j = 0; j < dv; ++j) du[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+          for (int j = 0; j < dv; ++j) du[j] += D[(size_t)i * dv + j] * kt[i];
+        for (int j = 0; j < dv; ++j) {
+          const long idx = bth * (long)dv + j;
+          if (ch) {
+            dv_out[idx] = w[idx] * du[j];
+            dw[idx] = vt[j] * du[j];
+          } else {
+            dv_out[idx] = beta_or_b[bth] * du[j];
+            bsum += vt[j] * du[j];
+          }
+        }
+        for (int i = 0; i < dk; ++i) {
+          double s = 0.0, du_dot = 0.0;
+          for (int j = 0; j < dv; ++j) {
+            s += a[i] * Pt[(size_t)i * dv + j] * du[j];
+            du_dot += D[(size_t)i * dv + j] * ut[j];
+          }
+          de[i] = -s;
+          const double bi = gate_at(beta_or_b, ch, bth, dk, i);
+          dkt[i] += du_dot + bi * de[i];
+          if (ch) db[bth * (long)dk + i] = kt[i] * de[i];
+          else bsum += kt[i] * de[i];
+        }
+        /* Sbar = Diag(abar) P_t:  dSbar = D - e du^T */
+        for (int i = 0; i < dk; ++i) {
+          double da = 0.0;
+          for (int j = 0; j < dv; ++j) {
+            const double dsb = D[(size_t)i * dv + j] - e[i] * du[j];
+            da += dsb * Pt[(size_t)i * dv + j];
+            D[(size_t)i * dv + j] = a[i] * dsb;
+          }
+          if (dg && ch) dg[bth * (long)dk + i] = a[i] * da;
+          gsum += a[i] * da;
+        }
+        if (!ch) {
+          db[bth] = bsum;
+          if (dg) dg[bth] = gsum;
+        }
+      }
+      if (d_state_in) memcpy(d_state_in + bh * (long)SS, D, sizeof(double) * SS);
+    }
+    free(P); free(U); free(D); free(tmp);
   }
   return bad ? 1 : 0;
 }
