@@ -75,6 +75,24 @@ struct NormArgs {
   void* y;
 };
 
+// Gradients of the recurrence.  Workspace: ckpt [B*Hv][nblk][dk][dv] states
+// every 16 tokens, u [B*T*Hv][dv], part [dv/64][4][B*T*Hv][dk] per-column-block
+// row gradients followed by [dv/64][B*T*Hv] write-gate sums (scalar gates).
+struct BwdArgs {
+  int64_t B, T;
+  int Hk, Hv, dk, dv;
+  DType io, gate;
+  bool channel;
+  float scale;
+  const void *q, *k, *v, *b, *w, *g, *d_o;
+  const float *state_in, *d_state_out;
+  float *ckpt, *u, *part;
+  int64_t nblk;
+  float *dq_out, *dk_out, *dv_out, *db, *dw, *dg, *d_state_in;
+};
+int64_t bwd_checkpoint_blocks(int64_t T);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_gates(const GateArgs& a, hipStream_t stream);
 hipError_t launch_output_gate(const NormArgs& a, hipStream_t stream);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_SCALAR, GDN_GATES_CHANNEL = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class GdnFwdDesc(ctypes.Structure):
@@ -42,6 +42,14 @@ class GdnVarlenDesc(ctypes.Structure):
 
 class GdnDecodeDesc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64),
+                ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
+                ("gate_mode", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class GdnBwdDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
@@ -89,6 +97,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn_chunk_fwd_varlen.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [ctypes.POINTER(GdnDecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_backward_workspace_size.argtypes = [ctypes.POINTER(GdnBwdDesc)]
+    lib.gdn_backward_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_backward.argtypes = [ctypes.POINTER(GdnBwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 vp, ctypes.c_size_t, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_backward.restype = ctypes.c_int
     lib.gdn_short_conv.argtypes = [ctypes.POINTER(GdnConvDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_short_conv.restype = ctypes.c_int
     lib.gdn_gates.argtypes = [ctypes.POINTER(GdnGateDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -395,3 +408,74 @@ def gdn_output_gate(o, z, weight, eps: float = 1e-6, y=None, stream=None):
     if st != GDN_OK:
         raise GdnError(st, "gdn_output_gate")
     return y
+
+
+def _bwd_desc(q, v, beta_or_b, w, scale):
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if q.dtype not in _DT or beta_or_b.dtype not in _DT:
+        raise ValueError("inputs must be float32 or bfloat16")
+    return GdnBwdDesc(B, T, Hk, Hv, dk, dv, _DT[q.dtype], _DT[beta_or_b.dtype],
+                      GDN_GATES_CHANNEL if w is not None else GDN_GATES_SCALAR, float(scale))
+
+
+def gdn_backward_workspace_size(q, v, beta_or_b, w=None, scale: float = 1.0) -> int:
+    """Workspace bytes gdn_backward needs for these shapes (see include/gdn.h)."""
+    return int(lib.gdn_backward_workspace_size(ctypes.byref(_bwd_desc(q, v, beta_or_b, w, scale))))
+
+
+def gdn_backward(q, k, v, beta_or_b, d_o, w=None, g=None, state_in=None, d_state_out=None,
+                 scale: float = 1.0, workspace=None, need_dg: bool = True,
+                 need_d_state_in: bool = True, grads=None, stream=None):
+    """Gradients of the chunk forward (see include/gdn.h).  Returns a dict of
+    fp32 tensors dq, dk, dv, db, dw (None for scalar gates), dg (None when g
+    is None or need_dg is False), d_state_in (None unless need_d_state_in).
+
+    Shapes as for gdn_chunk_fwd; d_o like o; d_state_out like the state or
+    None.  `workspace` is a device uint8 tensor of at least
+    gdn_backward_workspace_size(...) bytes (allocated when None); `grads` may
+    hold preallocated outputs under the same keys.
+    """
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    io = q.dtype
+    gdt = beta_or_b.dtype
+    channel = w is not None
+    gshape = (B, T, Hv, dk) if channel else (B, T, Hv)
+    _check(q, "q", (B, T, Hk, dk), io)
+    _check(k, "k", (B, T, Hk, dk), io)
+    _check(v, "v", (B, T, Hv, dv), io)
+    _check(beta_or_b, "beta_or_b", gshape, gdt)
+    _check(w, "w", (B, T, Hv, dv), gdt)
+    _check(g, "g", gshape, gdt)
+    _check(state_in, "state_in", (B, Hv, dk, dv), torch.float32)
+    _check(d_o, "d_o", (B, T, Hv, dv), io)
+    _check(d_state_out, "d_state_out", (B, Hv, dk, dv), torch.float32)
+    desc = _bwd_desc(q, v, beta_or_b, w, scale)
+    need = int(lib.gdn_backward_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    shapes = {"dq": (B, T, Hk, dk), "dk": (B, T, Hk, dk), "dv": (B, T, Hv, dv), "db": gshape,
+              "dw": (B, T, Hv, dv) if channel else None,
+              "dg": gshape if (g is not None and need_dg) else None,
+              "d_state_in": (B, Hv, dk, dv) if need_d_state_in else None}
+    out = {} if grads is None else dict(grads)
+    for name, shp in shapes.items():
+        if shp is None:
+            out[name] = None
+            continue
+        if out.get(name) is None:
+            out[name] = torch.empty(shp, **f32)
+        _check(out[name], name, shp, torch.float32)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.gdn_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b),
+                          _ptr(w), _ptr(g), _ptr(state_in), _ptr(d_o), _ptr(d_state_out),
+                          _ptr(workspace), ctypes.c_size_t(nbytes), _ptr(out["dq"]),
+                          _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["db"]), _ptr(out["dw"]),
+                          _ptr(out["dg"]), _ptr(out["d_state_in"]), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_backward")
+    return out

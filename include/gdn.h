@@ -46,14 +46,15 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
-                              gdn_gates, gdn_output_gate */
+#define GDN_ABI_VERSION 4  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
+                              gdn_gates, gdn_output_gate; 4: adds gdn_backward */
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -186,6 +187,63 @@ typedef struct gdn_decode_desc {
 gdn_status gdn_decode_step(const gdn_decode_desc* desc, const void* q, const void* k,
                            const void* v, const void* beta_or_b, const void* w,
                            const void* g, float* state, void* o, void* stream);
+
+/* Gradients of the recurrence over a sequence batch. */
+typedef struct gdn_bwd_desc {
+  int64_t B;          /* batch, >= 0 (0: nothing to do)                          */
+  int64_t T;          /* tokens per sequence, >= 0                               */
+  int32_t H_k, H_v;   /* >= 1, H_v % H_k == 0                                    */
+  int32_t d_k, d_v;   /* each 64 or 128                                          */
+  int32_t io_dtype;   /* gdn_dtype of q, k, v, d_o                               */
+  int32_t gate_dtype; /* gdn_dtype of beta|b, w, g: equal to io_dtype, or F32    */
+  int32_t gate_mode;  /* gdn_gate_mode                                           */
+  float scale;        /* finite; the forward's o = scale * S_t^T q_t             */
+} gdn_bwd_desc;
+
+/*
+ * gdn_backward_workspace_size -- bytes of device workspace gdn_backward needs
+ * for this descriptor (0 for an invalid descriptor or when there is no
+ * token): the states every 16 tokens (B H_v ceil(T/16) d_k d_v fp32), the
+ * per-token vectors u (B T H_v d_v fp32) and per-64-column partial row
+ * gradients (d_v/64 * B T H_v (4 d_k + 1) fp32), each rounded up to 256
+ * bytes.  4.5 GB at B 8, T 4096, H_v 16, d_k = d_v = 128.
+ */
+size_t gdn_backward_workspace_size(const gdn_bwd_desc* desc);
+
+/*
+ * gdn_backward -- gradients of the recurrence of gdn_chunk_fwd for upstream
+ * gradients d_o (of o) and d_state_out (of the final state), i.e. of the
+ * loss L = sum(o * d_o) + sum(S_T * d_state_out).  The pages give the update
+ * ("Gated DeltaNet-2", Methodologie §1) and stress that training needs its
+ * gate-aware gradient (§3); the gradients here are the chain rule through
+ * that update, run in reverse over the tokens (the per-token reverse step is
+ * written out in backward.hip).  The kernels recompute the forward states
+ * from checkpoints kept in the workspace, in fp32.
+ *
+ *   q, k, v, beta_or_b, w, g, state_in   as for gdn_chunk_fwd (inputs)
+ *   d_o          [B, T, H_v, d_v]  io_dtype
+ *   d_state_out  [B, H_v, d_k, d_v] fp32, or NULL (no gradient on S_T)
+ *   workspace    DEVICE, >= gdn_backward_workspace_size(desc) bytes, 16-byte
+ *                aligned; owned by the caller, contents undefined on return
+ *   gradients, all fp32, DEVICE, dense:
+ *     dq, dk     [B, T, H_k, d_k]  (summed over the value heads of a key head)
+ *     dv         [B, T, H_v, d_v]
+ *     db         shape of beta_or_b (SCALAR: d beta, which also collects the
+ *                write side, since b = w = beta there)
+ *     dw         CHANNEL: [B, T, H_v, d_v]; SCALAR: must be NULL
+ *     dg         shape of g (the gradient w.r.t. g = log alpha), or NULL;
+ *                must be NULL when g is NULL
+ *     d_state_in [B, H_v, d_k, d_v], or NULL; may equal d_state_out
+ *   stream     hipStream_t or NULL
+ * Outputs must not overlap the inputs, the workspace or each other (except
+ * d_state_in == d_state_out).
+ */
+gdn_status gdn_backward(const gdn_bwd_desc* desc, const void* q, const void* k, const void* v,
+                        const void* beta_or_b, const void* w, const void* g,
+                        const float* state_in, const void* d_o, const float* d_state_out,
+                        void* workspace, size_t workspace_bytes, float* dq, float* dk,
+                        float* dv, float* db, float* dw, float* dg, float* d_state_in,
+                        void* stream);
 
 /* ------------------------------------------------------------------------
  * The operations around the recurrence in a Gated DeltaNet block (notes page

@@ -22,7 +22,8 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["gdn_chunk_fwd", "gdn_chunk_fwd_varlen", "gdn_decode_step", "gdn_status_string",
-         "gdn_abi_version", "gdn_short_conv", "gdn_gates", "gdn_output_gate"])
+         "gdn_abi_version", "gdn_short_conv", "gdn_gates", "gdn_output_gate", "gdn_backward",
+         "gdn_backward_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert gdn.abi_version() == 3
+    assert gdn.abi_version() == 4
     for st in range(4):
         s = gdn.status_string(st)
         assert s.startswith("GDN_")
@@ -352,3 +353,63 @@ def test_output_gate_pointer_rules():
     assert _outgate(_norm_desc(), y=_addr(1, 64)) == gdn.GDN_ERR_INVALID_ARG   # y over z
     assert _outgate(_norm_desc(), y=_addr(0, 64)) == gdn.GDN_ERR_INVALID_ARG   # y partly over o
     assert _outgate(_norm_desc(rows=0)) == gdn.GDN_OK
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+def _bwd_desc(**kw):
+    d = dict(B=2, T=100, H_k=2, H_v=4, d_k=128, d_v=128, io_dtype=gdn.GDN_BF16,
+             gate_dtype=gdn.GDN_BF16, gate_mode=gdn.GDN_GATES_CHANNEL, scale=1.0)
+    d.update(kw)
+    return gdn.GdnBwdDesc(**d)
+
+
+def _bwd(desc, ws_bytes=None, **ptrs):
+    names = ["q", "k", "v", "b", "w", "g", "s_in", "d_o", "d_sT", "ws", "dq", "dk", "dv", "db",
+             "dw", "dg", "d_s0"]
+    p = {n: _addr(i) for i, n in enumerate(names)}
+    if desc is not None and desc.gate_mode == gdn.GDN_GATES_SCALAR:
+        p["w"] = p["dw"] = None
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = gdn.lib.gdn_backward_workspace_size(ctypes.byref(desc)) if desc else 0
+    args = [p[n] for n in names]
+    return gdn.lib.gdn_backward(ctypes.byref(desc) if desc is not None else None,
+                                *args[:10], ctypes.c_size_t(ws_bytes), *args[10:], None)
+
+
+def test_backward_workspace_size_formula():
+    d = _bwd_desc(B=8, T=4096, H_k=16, H_v=16)
+    got = gdn.lib.gdn_backward_workspace_size(ctypes.byref(d))
+    ck = 8 * 16 * 256 * 128 * 128 * 4
+    u = 8 * 4096 * 16 * 128 * 4
+    part = (2 * 4 * 8 * 4096 * 16 * 128 + 2 * 8 * 4096 * 16) * 4
+    r = lambda x: (x + 255) // 256 * 256
+    assert got == r(ck) + r(u) + r(part)
+    assert gdn.lib.gdn_backward_workspace_size(ctypes.byref(_bwd_desc(T=0))) == 0
+    assert gdn.lib.gdn_backward_workspace_size(ctypes.byref(_bwd_desc(H_v=3))) == 0
+    assert gdn.lib.gdn_backward_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("field,value,expected", [
+    ("H_v", 3, 1), ("d_k", 96, 2), ("io_dtype", 7, 1), ("gate_mode", 5, 1),
+    ("scale", float("nan"), 1), ("B", -1, 1)])
+def test_backward_rejects_bad_descriptor(field, value, expected):
+    assert _bwd(_bwd_desc(**{field: value}), ws_bytes=1 << 40) == expected
+
+
+def test_backward_pointer_rules():
+    assert _bwd(None) == gdn.GDN_ERR_INVALID_ARG
+    for name in ["q", "k", "v", "b", "w", "d_o", "ws", "dq", "dk", "dv", "db", "dw"]:
+        assert _bwd(_bwd_desc(), **{name: None}) == gdn.GDN_ERR_INVALID_ARG, name
+    assert _bwd(_bwd_desc(), ws_bytes=1000) == gdn.GDN_ERR_INVALID_ARG        # too small
+    assert _bwd(_bwd_desc(), dg=_addr(15), g=None) == gdn.GDN_ERR_INVALID_ARG  # dg without g
+    assert _bwd(_bwd_desc(), dq=_addr(10, 8)) == gdn.GDN_ERR_INVALID_ARG      # misaligned
+    assert _bwd(_bwd_desc(), dk=_addr(10, 16)) == gdn.GDN_ERR_INVALID_ARG     # dk over dq
+    assert _bwd(_bwd_desc(), dv=_addr(9, 64)) == gdn.GDN_ERR_INVALID_ARG      # dv in workspace
+    assert _bwd(_bwd_desc(), db=_addr(0, 64)) == gdn.GDN_ERR_INVALID_ARG      # db over q
+    sc = _bwd_desc(gate_mode=gdn.GDN_GATES_SCALAR)
+    assert _bwd(sc, dw=_addr(14)) == gdn.GDN_ERR_INVALID_ARG                  # dw in scalar mode
+    assert _bwd(_bwd_desc(B=0)) == gdn.GDN_OK
+    assert _bwd(_bwd_desc(T=0), d_s0=None) == gdn.GDN_OK
