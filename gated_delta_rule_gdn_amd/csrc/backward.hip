@@ -22,13 +22,15 @@
 //
 // Phase 1 runs the recurrence forward from the initial state, storing the
 // state every kCkpt tokens and every u_t in the workspace.  Phase 2 walks the
-// checkpoint blocks backwards: it rebuilds a block's states from its
-// checkpoint with the stored u (no reduction is needed: P_{t+1} = abar P_t +
-// k u^T), keeps the starts of its sub-blocks in LDS (each thread its own
-// tile) and the states of one sub-block in registers, and runs the reverse
-// step token by token.  The per-row gradients (dq, dk, db, dg) are partial
-// over the column block; they go to the workspace and a second kernel sums
-// them over column blocks and over the value heads of a key head.
+// checkpoint blocks backwards: for each sub-block of kSub tokens it rebuilds
+// the states from the block's checkpoint with the stored u (no reduction is
+// needed: P_{t+1} = abar P_t + k u^T), keeps the sub-block's states in
+// registers and runs the reverse step token by token.  Both phases read a
+// block's token inputs from LDS, where they were staged while the previous
+// block was computed (global loads issued a block ahead, LDS-only barriers in
+// between so they stay in flight).  The per-row gradients (dq, dk, db, dg)
+// are partial over the column block; they go to the workspace and a second
+// kernel sums them over column blocks and over the value heads of a key head.
 #include "gdn_device.hpp"
 #include "gdn_kernels.hpp"
 
@@ -55,59 +57,192 @@ __device__ __forceinline__ float row16_sum(float s) {
   return s;
 }
 
-template <typename T>
-__device__ __forceinline__ void ld4(const T* p, float* o) {
-  if constexpr (sizeof(T) == 2) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
-    o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
-  } else {
-    const float4 f = *reinterpret_cast<const float4*>(p);
-    o[0] = f.x; o[1] = f.y; o[2] = f.z; o[3] = f.w;
-  }
+typedef float Tile[4][4];
+
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not
+// for its global loads, so prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
 __device__ __forceinline__ void st4f(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ void ld4f(const float* p, float* v) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
 
-typedef float Tile[4][4];
+// N consecutive elements of T kept as loaded (converted when stored to LDS,
+// so that the load is not waited for where it is issued).
+template <typename T, int N> struct RawN;
+template <int N> struct RawN<bf16, N> { uint32_t w[N / 2]; };
+template <int N> struct RawN<float, N> { float w[N]; };
 
-// Row-side inputs of token t for a thread's 4 rows: k, e = b (.) k, b, abar.
-template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT>
-__device__ __forceinline__ void load_rows(const BwdArgs& p, int64_t bt, int64_t bth, int hk,
-                                          int r0, float* k, float* e, float* bb, float* a) {
-  ld4<IO>(static_cast<const IO*>(p.k) + (bt * p.Hk + hk) * DK + r0, k);
-  if constexpr (CHANNEL) {
-    ld4<GT>(static_cast<const GT*>(p.b) + bth * DK + r0, bb);
-    if constexpr (HAS_G) {
-      float gg[4];
-      ld4<GT>(static_cast<const GT*>(p.g) + bth * DK + r0, gg);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = exp2_fast(gg[i] * kLog2e);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = 1.f;
-    }
+template <typename T, int N>
+__device__ __forceinline__ void load_raw(const T* p, RawN<T, N>& r) {
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (N == 4) { const uint2 u = *reinterpret_cast<const uint2*>(p); r.w[0] = u.x; r.w[1] = u.y; }
+    else { static_assert(N == 2, "N"); r.w[0] = *reinterpret_cast<const uint32_t*>(p); }
   } else {
-    const float beta = to_f32(static_cast<const GT*>(p.b)[bth]);
-    float av = 1.f;
-    if constexpr (HAS_G) av = exp2_fast(to_f32(static_cast<const GT*>(p.g)[bth]) * kLog2e);
+    if constexpr (N == 4) { const float4 u = *reinterpret_cast<const float4*>(p); r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w; }
+    else { static_assert(N == 2, "N"); const float2 u = *reinterpret_cast<const float2*>(p); r.w[0] = u.x; r.w[1] = u.y; }
+  }
+}
+template <typename T, int N>
+__device__ __forceinline__ void zero_raw(RawN<T, N>& r) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { bb[i] = beta; a[i] = av; }
+  for (int i = 0; i < (sizeof(T) == 2 ? N / 2 : N); ++i) r.w[i] = 0;
+}
+template <typename T, int N>
+__device__ __forceinline__ void unpack_raw(const RawN<T, N>& r, float* o) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w = r.w[i >> 1];
+      o[i] = __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+      o[i] = r.w[i];
+    }
+  }
+}
+
+// One checkpoint block's token inputs in LDS: the row side (q, k, b, abar)
+// over all DK rows and the column side (v, w, dO, u) over the workgroup's 64
+// columns; scalar gates per token.
+template <int DK>
+struct Stage {
+  float k[kCkpt][DK], q[kCkpt][DK], b[kCkpt][DK], a[kCkpt][DK];
+  float v[kCkpt][kCols], w[kCkpt][kCols], dO[kCkpt][kCols], u[kCkpt][kCols];
+  float sb[kCkpt], sa[kCkpt];
+};
+
+// A thread's share of loading one block into a Stage: 4 row elements of one
+// token, CPT column elements of one token.
+template <int DK, bool CHANNEL, bool HAS_G, bool REV, typename IO, typename GT>
+struct BlockLoad {
+  static constexpr int NT = DK * 4;
+  static constexpr int TPR = DK / 4;                // threads per token (rows)
+  static constexpr int CPT = kCkpt * kCols / NT;    // column elements per thread
+  static constexpr int TPC = kCols / CPT;           // threads per token (columns)
+  RawN<IO, 4> k, q;
+  RawN<GT, 4> b, g;
+  RawN<IO, CPT> v, dO;
+  RawN<GT, CPT> w;
+  float u[CPT];
+  float sb, sg;
+  bool rv, cv;   // the row / column token exists (loads past T read token T-1)
+
+  // Every load is issued unconditionally (token index clamped into the
+  // sequence), so the compiler's count of outstanding loads is the same on
+  // every path and nothing waits for them before store().
+  __device__ __forceinline__ void issue(const BwdArgs& p, int64_t bb, int hv, int hk, int cb,
+                                        int64_t t0, int tid) {
+    const int tr = tid / TPR, i0 = 4 * (tid % TPR);
+    const int tc = tid / TPC, j0 = CPT * (tid % TPC);
+    const int64_t trr = t0 + tr, tcc = t0 + tc;
+    rv = trr < p.T;
+    cv = tcc < p.T;
+    {
+      const int64_t t = rv ? trr : p.T - 1;
+      const int64_t bt = bb * p.T + t, bth = bt * p.Hv + hv;
+      load_raw<IO, 4>(static_cast<const IO*>(p.k) + (bt * p.Hk + hk) * DK + i0, k);
+      if constexpr (REV) load_raw<IO, 4>(static_cast<const IO*>(p.q) + (bt * p.Hk + hk) * DK + i0, q);
+      if constexpr (CHANNEL) {
+        load_raw<GT, 4>(static_cast<const GT*>(p.b) + bth * DK + i0, b);
+        if constexpr (HAS_G) load_raw<GT, 4>(static_cast<const GT*>(p.g) + bth * DK + i0, g);
+      } else {
+        sb = to_f32(static_cast<const GT*>(p.b)[bth]);
+        sg = HAS_G ? to_f32(static_cast<const GT*>(p.g)[bth]) : 0.f;
+      }
+    }
+    {
+      const int64_t t = cv ? tcc : p.T - 1;
+      const int64_t bth = (bb * p.T + t) * p.Hv + hv;
+      const int64_t off = bth * p.dv + (int64_t)cb * kCols + j0;
+      load_raw<IO, CPT>(static_cast<const IO*>(p.v) + off, v);
+      if constexpr (CHANNEL) load_raw<GT, CPT>(static_cast<const GT*>(p.w) + off, w);
+      if constexpr (REV) {
+        load_raw<IO, CPT>(static_cast<const IO*>(p.d_o) + off, dO);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) u[j] = p.u[off + j];
+      }
+    }
+  }
+
+  // Writes the block to LDS; tokens past T are stored as zeros.
+  __device__ __forceinline__ void store(Stage<DK>& st, int tid) const {
+    const int tr = tid / TPR, i0 = 4 * (tid % TPR);
+    const int tc = tid / TPC, j0 = CPT * (tid % TPC);
+    const float mr = rv ? 1.f : 0.f, mc = cv ? 1.f : 0.f;
+    float x[4];
+    unpack_raw<IO, 4>(k, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] *= mr;
+    st4f(&st.k[tr][i0], x);
+    if constexpr (REV) {
+      unpack_raw<IO, 4>(q, x);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] *= mr;
+      st4f(&st.q[tr][i0], x);
+    }
+    if constexpr (CHANNEL) {
+      unpack_raw<GT, 4>(b, x);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] *= mr;
+      st4f(&st.b[tr][i0], x);
+      if constexpr (HAS_G) {
+        unpack_raw<GT, 4>(g, x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = exp2_fast(x[i] * kLog2e);
+      } else {
+        x[0] = x[1] = x[2] = x[3] = 1.f;
+      }
+      st4f(&st.a[tr][i0], x);
+    } else if (i0 == 0) {
+      st.sb[tr] = sb * mr;
+      st.sa[tr] = HAS_G ? exp2_fast(sg * kLog2e) : 1.f;
+    }
+    float y[CPT];
+    unpack_raw<IO, CPT>(v, y);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) st.v[tc][j0 + j] = y[j] * mc;
+    if constexpr (CHANNEL) {
+      unpack_raw<GT, CPT>(w, y);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) st.w[tc][j0 + j] = y[j] * mc;
+    }
+    if constexpr (REV) {
+      unpack_raw<IO, CPT>(dO, y);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) { st.dO[tc][j0 + j] = y[j] * mc; st.u[tc][j0 + j] = u[j] * mc; }
+    }
+  }
+};
+
+// Token tl of a staged block, seen by one thread: its 4 rows and 4 columns.
+template <int DK, bool CHANNEL>
+__device__ __forceinline__ void rows_of(const Stage<DK>& st, int tl, int r0, float* k, float* e,
+                                        float* bb, float* a) {
+  ld4f(&st.k[tl][r0], k);
+  if constexpr (CHANNEL) {
+    ld4f(&st.b[tl][r0], bb);
+    ld4f(&st.a[tl][r0], a);
+  } else {
+    const float sb = st.sb[tl], sa = st.sa[tl];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { bb[i] = sb; a[i] = sa; }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) e[i] = bb[i] * k[i];
 }
-
-// Column-side write gate of token t for a thread's 4 columns.
-template <bool CHANNEL, typename GT>
-__device__ __forceinline__ void load_wgate(const BwdArgs& p, int64_t bth, int64_t c0, float* w) {
+template <int DK, bool CHANNEL>
+__device__ __forceinline__ void wgate_of(const Stage<DK>& st, int tl, int cl, float* w) {
   if constexpr (CHANNEL) {
-    ld4<GT>(static_cast<const GT*>(p.w) + bth * p.dv + c0, w);
+    ld4f(&st.w[tl][cl], w);
   } else {
-    const float beta = to_f32(static_cast<const GT*>(p.b)[bth]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = beta;
+    const float sb = st.sb[tl];
+    w[0] = w[1] = w[2] = w[3] = sb;
   }
 }
 
@@ -123,7 +258,7 @@ __device__ __forceinline__ void row_reduce(float* v, float (*red)[NW][kCols], in
     v[j] += __shfl_xor(v[j], 32);
   }
   if (lane < 16) st4f(&red[buf][wave][4 * cg], v);
-  __syncthreads();
+  lds_barrier();
   float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -140,7 +275,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   constexpr int NT = DK * 4;
   constexpr int NW = NT / 64;
   __shared__ float red[2][NW][kCols];
-  __shared__ float4 subs[kSubs][4][NT];     // sub-block start states, private per thread
+  __shared__ Stage<DK> stg[2];
 
   const int64_t head = blockIdx.x;          // b * Hv + hv
   const int cb = blockIdx.y;
@@ -151,55 +286,68 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   const int tid = threadIdx.x;
   const int rg = tid >> 4, cg = tid & 15;
   const int lane = tid & 63, wave = tid >> 6;
-  const int r0 = 4 * rg;
-  const int64_t c0 = (int64_t)cb * kCols + 4 * cg;
+  const int r0 = 4 * rg, cl = 4 * cg;       // first row; first column inside the block
+  const int64_t c0 = (int64_t)cb * kCols + cl;
   const int64_t T = p.T;
   const int64_t NR = p.B * T * p.Hv;        // gradient rows (b, t, hv)
   const float scale = p.scale;
+  const int64_t nblk = p.nblk;
   int buf = 0;
 
-  float* ck = p.ckpt + ((head * ncb + cb) * p.nblk) * (int64_t)DK * kCols;
-  auto ck_at = [&](int64_t m, int i) { return ck + (m * DK + r0 + i) * kCols + 4 * cg; };
+  float* ck = p.ckpt + ((head * ncb + cb) * nblk) * (int64_t)DK * kCols;
+  auto ck_at = [&](int64_t m, int i) { return ck + (m * DK + r0 + i) * kCols + cl; };
 
   // ---- phase 1: forward, storing checkpoints and u ----
   Tile P;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (p.state_in) {
-      const float4 x = *reinterpret_cast<const float4*>(p.state_in + (head * DK + r0 + i) * p.dv + c0);
-      P[i][0] = x.x; P[i][1] = x.y; P[i][2] = x.z; P[i][3] = x.w;
-    } else {
-      P[i][0] = P[i][1] = P[i][2] = P[i][3] = 0.f;
+    if (p.state_in) ld4f(p.state_in + (head * DK + r0 + i) * p.dv + c0, P[i]);
+    else P[i][0] = P[i][1] = P[i][2] = P[i][3] = 0.f;
+  }
+  {
+    BlockLoad<DK, CHANNEL, HAS_G, false, IO, GT> ld;
+    ld.issue(p, b, hv, hk, cb, 0, tid);
+    ld.store(stg[0], tid);
+    lds_barrier();
+    for (int64_t m = 0; m < nblk; ++m) {
+      const int cur = (int)(m & 1);
+      const bool more = m + 1 < nblk;
+      ld.issue(p, b, hv, hk, cb, (more ? m + 1 : m) * kCkpt, tid);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st4f(ck_at(m, i), P[i]);
+      const int64_t t0 = m * kCkpt;
+      const int nt = (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
+      const Stage<DK>& st = stg[cur];
+      for (int tl = 0; tl < nt; ++tl) {
+        float k[4], e[4], bb[4], a[4], w[4], v[4], r[4];
+        rows_of<DK, CHANNEL>(st, tl, r0, k, e, bb, a);
+        wgate_of<DK, CHANNEL>(st, tl, cl, w);
+        ld4f(&st.v[tl][cl], v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float s = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s += a[i] * P[i][j] * e[i];
+          r[j] = s;
+        }
+        row_reduce<NW>(r, red, buf, lane, wave, cg);
+        float u[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = w[j] * v[j] - r[j];
+        if (rg == 0) st4f(p.u + ((b * T + t0 + tl) * p.Hv + hv) * p.dv + c0, u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) P[i][j] = a[i] * P[i][j] + k[i] * u[j];
+      }
+      ld.store(stg[cur ^ 1], tid);   // (the last block stores a copy nobody reads)
+      lds_barrier();
     }
   }
-  for (int64_t t = 0; t < T; ++t) {
-    if (t % kCkpt == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st4f(ck_at(t / kCkpt, i), P[i]);
-    }
-    const int64_t bt = b * T + t, bth = bt * p.Hv + hv;
-    float k[4], e[4], bb[4], a[4], w[4], v[4];
-    load_rows<DK, CHANNEL, HAS_G, IO, GT>(p, bt, bth, hk, r0, k, e, bb, a);
-    load_wgate<CHANNEL, GT>(p, bth, c0, w);
-    ld4<IO>(static_cast<const IO*>(p.v) + bth * p.dv + c0, v);
-    float r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s += a[i] * P[i][j] * e[i];
-      r[j] = s;
-    }
-    row_reduce<NW>(r, red, buf, lane, wave, cg);
-    float u[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) u[j] = w[j] * v[j] - r[j];
-    if (rg == 0) st4f(p.u + bth * p.dv + c0, u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) P[i][j] = a[i] * P[i][j] + k[i] * u[j];
-  }
+  // The u written above is read back below through global memory by other
+  // threads of this workgroup: make the stores visible first.
+  __threadfence_block();
+  __syncthreads();
 
   // ---- phase 2: reverse ----
   Tile D, Pn;
@@ -207,21 +355,15 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) Pn[i][j] = P[i][j];
-    if (p.d_state_out) {
-      const float4 x = *reinterpret_cast<const float4*>(p.d_state_out + (head * DK + r0 + i) * p.dv + c0);
-      D[i][0] = x.x; D[i][1] = x.y; D[i][2] = x.z; D[i][3] = x.w;
-    } else {
-      D[i][0] = D[i][1] = D[i][2] = D[i][3] = 0.f;
-    }
+    if (p.d_state_out) ld4f(p.d_state_out + (head * DK + r0 + i) * p.dv + c0, D[i]);
+    else D[i][0] = D[i][1] = D[i][2] = D[i][3] = 0.f;
   }
 
-  // P_{t+1} = abar P_t + k u^T with the stored u.
-  auto advance = [&](Tile& X, int64_t t) {
-    const int64_t bt = b * T + t, bth = bt * p.Hv + hv;
+  // P_{t+1} = abar P_t + k u^T with the staged u.
+  auto advance = [&](const Stage<DK>& st, Tile& X, int tl) {
     float k[4], e[4], bb[4], a[4], u[4];
-    load_rows<DK, CHANNEL, HAS_G, IO, GT>(p, bt, bth, hk, r0, k, e, bb, a);
-    const float4 uu = *reinterpret_cast<const float4*>(p.u + bth * p.dv + c0);
-    u[0] = uu.x; u[1] = uu.y; u[2] = uu.z; u[3] = uu.w;
+    rows_of<DK, CHANNEL>(st, tl, r0, k, e, bb, a);
+    ld4f(&st.u[tl][cl], u);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -229,18 +371,15 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   };
 
   // Reverse step of token t: Pb = P_t, Pa = P_{t+1}, D = dL/dP_{t+1} -> dL/dP_t.
-  auto reverse = [&](const Tile& Pb, const Tile& Pa, int64_t t) {
-    const int64_t bt = b * T + t, bth = bt * p.Hv + hv;
+  auto reverse = [&](const Stage<DK>& st, const Tile& Pb, const Tile& Pa, int tl, int64_t t) {
+    const int64_t bth = (b * T + t) * p.Hv + hv;
     float k[4], e[4], bb[4], a[4], w[4], v[4], dO[4], q[4], u[4];
-    load_rows<DK, CHANNEL, HAS_G, IO, GT>(p, bt, bth, hk, r0, k, e, bb, a);
-    load_wgate<CHANNEL, GT>(p, bth, c0, w);
-    ld4<IO>(static_cast<const IO*>(p.v) + bth * p.dv + c0, v);
-    ld4<IO>(static_cast<const IO*>(p.d_o) + bth * p.dv + c0, dO);
-    ld4<IO>(static_cast<const IO*>(p.q) + (bt * p.Hk + hk) * DK + r0, q);
-    {
-      const float4 uu = *reinterpret_cast<const float4*>(p.u + bth * p.dv + c0);
-      u[0] = uu.x; u[1] = uu.y; u[2] = uu.z; u[3] = uu.w;
-    }
+    rows_of<DK, CHANNEL>(st, tl, r0, k, e, bb, a);
+    wgate_of<DK, CHANNEL>(st, tl, cl, w);
+    ld4f(&st.v[tl][cl], v);
+    ld4f(&st.dO[tl][cl], dO);
+    ld4f(&st.q[tl][r0], q);
+    ld4f(&st.u[tl][cl], u);
     float dq[4], du[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -313,54 +452,67 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     }
   };
 
-  for (int64_t m = p.nblk - 1; m >= 0; --m) {
-    const int64_t t0 = m * kCkpt;
-    const int64_t t1 = (t0 + kCkpt < T) ? t0 + kCkpt : T;
-    Tile X;
+  {
+    BlockLoad<DK, CHANNEL, HAS_G, true, IO, GT> ld;
+    ld.issue(p, b, hv, hk, cb, (nblk - 1) * kCkpt, tid);
+    ld.store(stg[0], tid);
+    Tile Ck, Cn;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 x = *reinterpret_cast<const float4*>(ck_at(m, i));
-      X[i][0] = x.x; X[i][1] = x.y; X[i][2] = x.z; X[i][3] = x.w;
-    }
-    // starts of the sub-blocks (each thread keeps its own tile)
-    for (int s = 0; s < kSubs; ++s) {
-      const int64_t ts = t0 + s * kSub;
-      if (ts >= t1) break;
+    for (int i = 0; i < 4; ++i) ld4f(ck_at(nblk - 1, i), Ck[i]);
+    // Wait here for everything loaded so far (D, Ck, the first block): the
+    // block loop below then holds no value whose load is still pending on
+    // entry, so the compiler need not drain the prefetches of each block
+    // before its token loop.
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    for (int64_t mm = 0; mm < nblk; ++mm) {
+      const int64_t m = nblk - 1 - mm;
+      const int cur = (int)(mm & 1);
+      const bool more = m > 0;
+      const int64_t mp = more ? m - 1 : m;   // the next block (or this one again)
+      ld.issue(p, b, hv, hk, cb, mp * kCkpt, tid);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) subs[s][i][tid] = make_float4(X[i][0], X[i][1], X[i][2], X[i][3]);
-      if (ts + kSub < t1)
-        for (int j = 0; j < kSub; ++j) advance(X, ts + j);
-    }
-    for (int s = kSubs - 1; s >= 0; --s) {
-      const int64_t ts = t0 + s * kSub;
-      if (ts >= t1) continue;
-      const int n = (int)((t1 - ts) < kSub ? (t1 - ts) : kSub);
-      Tile R[kSub];
+      for (int i = 0; i < 4; ++i) ld4f(ck_at(mp, i), Cn[i]);
+      const Stage<DK>& st = stg[cur];
+      const int64_t t0 = m * kCkpt;
+      const int nt = (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
+      for (int s = kSubs - 1; s >= 0; --s) {
+        const int ts = s * kSub;                // first token of the sub-block (local)
+        if (ts >= nt) continue;
+        const int n = (nt - ts) < kSub ? (nt - ts) : kSub;
+        Tile R[kSub];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 x = subs[s][i][tid];
-        R[0][i][0] = x.x; R[0][i][1] = x.y; R[0][i][2] = x.z; R[0][i][3] = x.w;
-      }
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 1; j < kSub; ++j) {
-        if (j < n) {
+          for (int c = 0; c < 4; ++c) R[0][i][c] = Ck[i][c];
+        for (int tl = 0; tl < ts; ++tl) advance(st, R[0], tl);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+        for (int j = 1; j < kSub; ++j) {
+          if (j < n) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) R[j][i][c] = R[j - 1][i][c];
-          advance(R[j], ts + j - 1);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) R[j][i][c] = R[j - 1][i][c];
+            advance(st, R[j], ts + j - 1);
+          }
+        }
+#pragma unroll
+        for (int j = kSub - 1; j >= 0; --j) {
+          if (j < n) {
+            reverse(st, R[j], Pn, ts + j, t0 + ts + j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) Pn[i][c] = R[j][i][c];
+          }
         }
       }
+      ld.store(stg[cur ^ 1], tid);
 #pragma unroll
-      for (int j = kSub - 1; j >= 0; --j) {
-        if (j < n) {
-          reverse(R[j], Pn, ts + j);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) Pn[i][c] = R[j][i][c];
-        }
-      }
+        for (int c = 0; c < 4; ++c) Ck[i][c] = Cn[i][c];
+      lds_barrier();
     }
   }
   if (p.d_state_in) {
