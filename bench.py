@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3        # MI355X dense fp32 MFMA, published
+PEAK_FP32_VECTOR_TFLOPS = 157.3 # MI355X fp32 vector (FMA = 2 flops), published
 CHUNK = 64
 
 
@@ -61,10 +62,25 @@ def decode_algorithmic(cfg, io_bytes=2, gate_bytes=2):
     return state + qk + vo + gates, flops
 
 
-def source_digest():
+# Sources each profiled kernel is built from; its counter figures stay valid
+# while these files are unchanged.
+KERNEL_SOURCES = {
+    "chunk_fwd": ("chunk_fwd_pipe.hip", "chunk_fwd.hip", "chunk_common.hpp", "gdn_device.hpp"),
+    "decode_step": ("decode.hip", "gdn_device.hpp"),
+    "short_conv": ("layer_ops.hip", "gdn_device.hpp"),
+    "gates": ("layer_ops.hip", "gdn_device.hpp"),
+    "output_gate": ("layer_ops.hip", "gdn_device.hpp"),
+    "backward": ("backward.hip", "gdn_device.hpp"),
+    "backward_reduce": ("backward.hip", "gdn_device.hpp"),
+}
+
+
+def source_digest(names=None):
+    """sha256 prefix over the named files of the kernel sources (all of them
+    when names is None)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_gdn_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(os.listdir(csrc) if names is None else names):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -74,17 +90,17 @@ def source_digest():
 def measured_traffic(kernel_key, per_launch_bytes_alg):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (profiles/traffic.json), or None when it is absent or was taken on other
-    kernel sources."""
+    sources of that kernel."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    if data.get("source_digest") != source_digest():
-        return None
     ent = data.get("kernels", {}).get(kernel_key)
-    if not ent:
+    if not ent or kernel_key not in KERNEL_SOURCES:
+        return None
+    if ent.get("source_digest") != source_digest(KERNEL_SOURCES[kernel_key]):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -219,10 +235,55 @@ def block_op_workloads(gdn, synth, torch, dev, steps=20, warmup=3):
     return res
 
 
+def backward_workload(gdn, synth, torch, dev, steps=5, warmup=2):
+    """gdn_backward on the GDN-2 B8 T4096 shape (not part of the step): the
+    gradients of every input for a random upstream gradient of o.  The
+    kernel works token by token in fp32 on the vector units, so it is judged
+    against the fp32 vector peak: 20 flops per state element per (token,
+    value head) -- 5 to rebuild the forward state (decay, read, rank-1
+    write) and 15 for the reverse step (the seven products of the chain
+    rule and the decay of the state gradient)."""
+    cfg = synth.CONFIGS["gdn2_bf16_train"]
+    inp = synth.chunk_inputs(cfg, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    d_o = torch.randn((cfg.B, cfg.T, cfg.Hv, cfg.dv), generator=gen, device="cuda").to(cfg.io_dtype)
+    nws = gdn.gdn_backward_workspace_size(inp["q"], inp["v"], inp["beta_or_b"], inp["w"])
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    grads = None
+
+    def run(grads):
+        return gdn.gdn_backward(inp["q"], inp["k"], inp["v"], inp["beta_or_b"], d_o, w=inp["w"],
+                                g=inp["g"], workspace=ws, grads=grads)
+    for _ in range(warmup):
+        grads = run(grads)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        run(grads)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    flops = 20.0 * cfg.dk * cfg.dv * cfg.B * cfg.T * cfg.Hv
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"workload": f"{cfg.name} backward: B={cfg.B}, T={cfg.T}, H={cfg.Hv}, d=128, "
+                       "channel gates, bf16 inputs, fp32 gradients",
+           "ms": round(ms, 3), "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+           "workspace_bytes": nws, "vector_tflops": round(tf, 2),
+           "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": PEAK_FP32_VECTOR_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_VECTOR_TFLOPS, 4),
+                        "flops_per_launch": flops,
+                        "traffic": measured_traffic("backward", None)}}
+    del inp, ws, grads, d_o
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(args):
     """The oracle, untuned, on the machine's host cores over the whole prefill
-    workload (8 sequences x 16 heads x T=4096: about 15 s of CPU work on 16
-    cores); the decode leg is not part of the sample."""
+    workload (8 sequences x 16 heads x T=4096; under a second of wall time on
+    16 cores, about 12 s of CPU time); the decode leg is not part of the
+    sample."""
     import torch
 
     import oracle
@@ -249,8 +310,10 @@ def cpu_baseline(args):
 KERNEL_KEYS = {"chunk_fwd": ("chunk_fwd_pipe_kernel", "chunk_fwd_kernel"),
                "decode_step": ("decode_kernel",),
                "short_conv": ("short_conv_kernel",),
-               "gates": ("gates_kernel",),
-               "output_gate": ("output_gate_kernel",)}
+               "gates": ("gates_kernel", "gates_vec_kernel"),
+               "output_gate": ("output_gate_kernel",),
+               "backward": ("bwd_kernel",),
+               "backward_reduce": ("bwd_reduce_kernel",)}
 
 
 def _kernel_key(name):
@@ -313,6 +376,7 @@ def summarize_profiles(kt_csv, fetch_csv, write_csv, commands):
         fk = sum(fetch[key]) / len(fetch[key])
         wk = sum(write[key]) / len(write[key])
         out["kernels"][key] = {
+            "source_digest": source_digest(KERNEL_SOURCES[key]),
             "fetch_kib_raw": fk, "write_kib_raw": wk,
             "hbm_bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024)),
             "dispatches": len(fetch[key]),
@@ -332,6 +396,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the chunk-forward timings of the other prefill workloads")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timing of the backward pass")
     ap.add_argument("--no-block-ops", action="store_true",
                     help="skip the timings of the block operations around the recurrence")
     ap.add_argument("--cpu-threads", type=int, default=16,
@@ -460,6 +526,8 @@ def main():
         out["secondary"] = secondary_chunk_workloads(gdn, synth, torch, dev)
     if not args.no_block_ops:
         out["block_ops"] = block_op_workloads(gdn, synth, torch, dev)
+    if not args.no_backward:
+        out["backward"] = backward_workload(gdn, synth, torch, dev)
     if args.copy_calibration:  # the last GPU work of the process
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         b = torch.empty_like(a)
