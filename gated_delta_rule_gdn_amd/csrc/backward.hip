@@ -21,7 +21,8 @@
 // cross-lane shuffles and one LDS exchange (one barrier).
 //
 // Phase 1 runs the recurrence forward from the initial state, storing the
-// state every kCkpt tokens and every u_t in the workspace.  Phase 2 walks the
+// state every kCkpt tokens, the final state and every u_t in the workspace;
+// it uses a layout of its own in which the read r needs no barrier.  Phase 2 walks the
 // checkpoint blocks backwards: for each sub-block of kSub tokens it rebuilds
 // the states from the block's checkpoint with the stored u (no reduction is
 // needed: P_{t+1} = abar P_t + k u^T), keeps the sub-block's states in
@@ -294,17 +295,47 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   const int64_t nblk = p.nblk;
   int buf = 0;
 
-  float* ck = p.ckpt + ((head * ncb + cb) * nblk) * (int64_t)DK * kCols;
+  // nblk checkpoints (state before each 16-token block) + the final state
+  float* ck = p.ckpt + ((head * ncb + cb) * (nblk + 1)) * (int64_t)DK * kCols;
   auto ck_at = [&](int64_t m, int i) { return ck + (m * DK + r0 + i) * kCols + cl; };
 
   // ---- phase 1: forward, storing checkpoints and u ----
-  Tile P;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (p.state_in) ld4f(p.state_in + (head * DK + r0 + i) * p.dv + c0, P[i]);
-    else P[i][0] = P[i][1] = P[i][2] = P[i][3] = 0.f;
-  }
+  // Its own layout: a wave holds all DK rows of CW columns, a lane RPL rows
+  // x CPL columns (the 16 lanes of a DPP row share the columns), so the read
+  // r = Sbar^T e is an in-wave butterfly and the token loop has no barrier.
   {
+    constexpr int RPL = DK / 16;             // rows per lane
+    constexpr int CPL = 256 / DK;            // columns per lane
+    constexpr int CW = 4 * CPL;              // columns per wave
+    const int rl = lane & 15, dr = lane >> 4;
+    const int pr0 = rl * RPL;                // first row
+    const int pc0 = wave * CW + dr * CPL;    // first column inside the block
+    const int64_t pcg = (int64_t)cb * kCols + pc0;
+    auto ldn = [](const float* src, float* out, int n) {
+      for (int i = 0; i < n; i += 4) ld4f(src + i, out + i);
+    };
+    auto ldc = [](const float* src, float* out) {
+      if constexpr (CPL == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(src);
+        out[0] = x.x; out[1] = x.y;
+      } else {
+        ld4f(src, out);
+      }
+    };
+    auto stc = [](float* dst, const float* v) {
+      if constexpr (CPL == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+      else st4f(dst, v);
+    };
+    float P1[RPL][CPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      if (p.state_in) {
+        ldc(p.state_in + (head * DK + pr0 + i) * p.dv + pcg, P1[i]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) P1[i][j] = 0.f;
+      }
+    }
     BlockLoad<DK, CHANNEL, HAS_G, false, IO, GT> ld;
     ld.issue(p, b, hv, hk, cb, 0, tid);
     ld.store(stg[0], tid);
@@ -314,38 +345,50 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       const bool more = m + 1 < nblk;
       ld.issue(p, b, hv, hk, cb, (more ? m + 1 : m) * kCkpt, tid);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st4f(ck_at(m, i), P[i]);
+      for (int i = 0; i < RPL; ++i) stc(ck + (m * DK + pr0 + i) * kCols + pc0, P1[i]);
       const int64_t t0 = m * kCkpt;
       const int nt = (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
       const Stage<DK>& st = stg[cur];
       for (int tl = 0; tl < nt; ++tl) {
-        float k[4], e[4], bb[4], a[4], w[4], v[4], r[4];
-        rows_of<DK, CHANNEL>(st, tl, r0, k, e, bb, a);
-        wgate_of<DK, CHANNEL>(st, tl, cl, w);
-        ld4f(&st.v[tl][cl], v);
+        float k[RPL], bb[RPL], a[RPL], w[CPL], v[CPL], r[CPL];
+        ldn(&st.k[tl][pr0], k, RPL);
+        if constexpr (CHANNEL) {
+          ldn(&st.b[tl][pr0], bb, RPL);
+          ldn(&st.a[tl][pr0], a, RPL);
+          ldc(&st.w[tl][pc0], w);
+        } else {
+          const float sb = st.sb[tl], sa = st.sa[tl];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float s = 0.f;
+          for (int i = 0; i < RPL; ++i) { bb[i] = sb; a[i] = sa; }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s += a[i] * P[i][j] * e[i];
-          r[j] = s;
+          for (int j = 0; j < CPL; ++j) w[j] = sb;
         }
-        row_reduce<NW>(r, red, buf, lane, wave, cg);
-        float u[4];
+        ldc(&st.v[tl][pc0], v);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) u[j] = w[j] * v[j] - r[j];
-        if (rg == 0) st4f(p.u + ((b * T + t0 + tl) * p.Hv + hv) * p.dv + c0, u);
+        for (int j = 0; j < CPL; ++j) {
+          float sacc = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < RPL; ++i) sacc += a[i] * P1[i][j] * (bb[i] * k[i]);
+          r[j] = row16_sum(sacc);
+        }
+        float u[CPL];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) P[i][j] = a[i] * P[i][j] + k[i] * u[j];
+        for (int j = 0; j < CPL; ++j) u[j] = w[j] * v[j] - r[j];
+        if (rl == 0) stc(p.u + ((b * T + t0 + tl) * p.Hv + hv) * p.dv + pcg, u);
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) P1[i][j] = a[i] * P1[i][j] + k[i] * u[j];
       }
       ld.store(stg[cur ^ 1], tid);   // (the last block stores a copy nobody reads)
       lds_barrier();
     }
+    // the final state, read back below in the reverse layout
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) stc(ck + (nblk * DK + pr0 + i) * kCols + pc0, P1[i]);
   }
-  // The u written above is read back below through global memory by other
-  // threads of this workgroup: make the stores visible first.
+  // The u and the final state written above are read back below through
+  // global memory by other threads of this workgroup: make them visible.
   __threadfence_block();
   __syncthreads();
 
@@ -353,8 +396,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   Tile D, Pn;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Pn[i][j] = P[i][j];
+    ld4f(ck_at(nblk, i), Pn[i]);
     if (p.d_state_out) ld4f(p.d_state_out + (head * DK + r0 + i) * p.dv + c0, D[i]);
     else D[i][0] = D[i][1] = D[i][2] = D[i][3] = 0.f;
   }

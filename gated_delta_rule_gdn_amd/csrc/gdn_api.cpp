@@ -120,7 +120,7 @@ BwdLayout bwd_layout(const gdn_bwd_desc* d) {
   const int64_t rows = d->B * d->T * d->H_v;
   const int64_t ncb = d->d_v / 64;
   L.nblk = gdn::bwd_checkpoint_blocks(d->T);
-  L.ckpt_floats = heads * L.nblk * d->d_k * d->d_v;
+  L.ckpt_floats = heads * (L.nblk + 1) * d->d_k * d->d_v;
   L.u_floats = rows * d->d_v;
   L.part_floats = ncb * 4 * rows * d->d_k + ncb * rows;
   L.ckpt_off = 0;

@@ -75,8 +75,8 @@ struct NormArgs {
   void* y;
 };
 
-// Gradients of the recurrence.  Workspace: ckpt [B*Hv][nblk][dk][dv] states
-// every 16 tokens, u [B*T*Hv][dv], part [dv/64][4][B*T*Hv][dk] per-column-block
+// Gradients of the recurrence.  Workspace: ckpt [B*Hv][nblk+1][dk][dv] states
+// every 16 tokens and the final state, u [B*T*Hv][dv], part [dv/64][4][B*T*Hv][dk] per-column-block
 // row gradients followed by [dv/64][B*T*Hv] write-gate sums (scalar gates).
 struct BwdArgs {
   int64_t B, T;

@@ -203,10 +203,11 @@ typedef struct gdn_bwd_desc {
 /*
  * gdn_backward_workspace_size -- bytes of device workspace gdn_backward needs
  * for this descriptor (0 for an invalid descriptor or when there is no
- * token): the states every 16 tokens (B H_v ceil(T/16) d_k d_v fp32), the
- * per-token vectors u (B T H_v d_v fp32) and per-64-column partial row
- * gradients (d_v/64 * B T H_v (4 d_k + 1) fp32), each rounded up to 256
- * bytes.  4.5 GB at B 8, T 4096, H_v 16, d_k = d_v = 128.
+ * token): the states every 16 tokens and the final state
+ * (B H_v (ceil(T/16) + 1) d_k d_v fp32), the per-token vectors u
+ * (B T H_v d_v fp32) and per-64-column partial row gradients
+ * (d_v/64 * B T H_v (4 d_k + 1) fp32), each rounded up to 256 bytes.
+ * 4.6 GB at B 8, T 4096, H_v 16, d_k = d_v = 128.
  */
 size_t gdn_backward_workspace_size(const gdn_bwd_desc* desc);
 

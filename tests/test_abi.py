@@ -382,7 +382,7 @@ def _bwd(desc, ws_bytes=None, **ptrs):
 def test_backward_workspace_size_formula():
     d = _bwd_desc(B=8, T=4096, H_k=16, H_v=16)
     got = gdn.lib.gdn_backward_workspace_size(ctypes.byref(d))
-    ck = 8 * 16 * 256 * 128 * 128 * 4
+    ck = 8 * 16 * 257 * 128 * 128 * 4
     u = 8 * 4096 * 16 * 128 * 4
     part = (2 * 4 * 8 * 4096 * 16 * 128 + 2 * 8 * 4096 * 16) * 4
     r = lambda x: (x + 255) // 256 * 256
