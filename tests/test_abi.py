@@ -413,3 +413,32 @@ def test_backward_pointer_rules():
     assert _bwd(sc, dw=_addr(14)) == gdn.GDN_ERR_INVALID_ARG                  # dw in scalar mode
     assert _bwd(_bwd_desc(B=0)) == gdn.GDN_OK
     assert _bwd(_bwd_desc(T=0), d_s0=None) == gdn.GDN_OK
+
+
+# ---------------------------------------------------------------------------
+# The product path has no fallback and no dependency on the oracle.
+# ---------------------------------------------------------------------------
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """A copy of the package without libgdn.so cannot be imported."""
+    import shutil
+    import sys
+    pkg = os.path.join(ROOT, "gated_delta_rule_gdn_amd")
+    dst = tmp_path / "gated_delta_rule_gdn_amd"
+    dst.mkdir()
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            shutil.copy(os.path.join(pkg, name), dst / name)
+    r = subprocess.run([sys.executable, "-c", "import gated_delta_rule_gdn_amd"],
+                       cwd=tmp_path, capture_output=True, text=True,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libgdn.so" in r.stderr
+
+
+def test_product_sources_never_reference_the_oracle():
+    pkg = os.path.join(ROOT, "gated_delta_rule_gdn_amd")
+    for base, _, files in os.walk(pkg):
+        for name in files:
+            if name.endswith((".py", ".hip", ".cpp", ".hpp")):
+                text = open(os.path.join(base, name)).read()
+                assert not re.search(r"\boracle\b", text), os.path.join(base, name)
