@@ -1,6 +1,8 @@
 """Build libgdn.so in-tree with hipcc for gfx950.
 
-    python -m gated_delta_rule_gdn_amd.build
+    python gated_delta_rule_gdn_amd/build.py [-v]
+
+(Run as a script: importing the package first would load the library.)
 
 Every HIP source is compiled with packed-fp32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); hipcc's host pass warns

@@ -137,16 +137,16 @@ struct BlockLoad {
   // Every load is issued unconditionally (token index clamped into the
   // sequence), so the compiler's count of outstanding loads is the same on
   // every path and nothing waits for them before store().
-  __device__ __forceinline__ void issue(const BwdArgs& p, int64_t bb, int hv, int hk, int cb,
-                                        int64_t t0, int tid) {
+  __device__ __forceinline__ void issue(const BwdArgs& p, int64_t tok0, int64_t Tn, int hv,
+                                        int hk, int cb, int64_t t0, int tid) {
     const int tr = tid / TPR, i0 = 4 * (tid % TPR);
     const int tc = tid / TPC, j0 = CPT * (tid % TPC);
     const int64_t trr = t0 + tr, tcc = t0 + tc;
-    rv = trr < p.T;
-    cv = tcc < p.T;
+    rv = trr < Tn;
+    cv = tcc < Tn;
     {
-      const int64_t t = rv ? trr : p.T - 1;
-      const int64_t bt = bb * p.T + t, bth = bt * p.Hv + hv;
+      const int64_t t = rv ? trr : Tn - 1;
+      const int64_t bt = tok0 + t, bth = bt * p.Hv + hv;
       load_raw<IO, 4>(static_cast<const IO*>(p.k) + (bt * p.Hk + hk) * DK + i0, k);
       if constexpr (REV) load_raw<IO, 4>(static_cast<const IO*>(p.q) + (bt * p.Hk + hk) * DK + i0, q);
       if constexpr (CHANNEL) {
@@ -158,8 +158,8 @@ struct BlockLoad {
       }
     }
     {
-      const int64_t t = cv ? tcc : p.T - 1;
-      const int64_t bth = (bb * p.T + t) * p.Hv + hv;
+      const int64_t t = cv ? tcc : Tn - 1;
+      const int64_t bth = (tok0 + t) * p.Hv + hv;
       const int64_t off = bth * p.dv + (int64_t)cb * kCols + j0;
       load_raw<IO, CPT>(static_cast<const IO*>(p.v) + off, v);
       if constexpr (CHANNEL) load_raw<GT, CPT>(static_cast<const GT*>(p.w) + off, w);
@@ -289,14 +289,36 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int r0 = 4 * rg, cl = 4 * cg;       // first row; first column inside the block
   const int64_t c0 = (int64_t)cb * kCols + cl;
-  const int64_t T = p.T;
-  const int64_t NR = p.B * T * p.Hv;        // gradient rows (b, t, hv)
+  const int64_t NR = p.rows * p.Hv;         // gradient rows (token, hv)
   const float scale = p.scale;
-  const int64_t nblk = p.nblk;
+  // This workgroup's sequence: tokens [tok0, tok0 + T) of the packed rows,
+  // and its run of checkpoint slots (packed sequences: floor(tok0/16) + 2b,
+  // which leaves room for the ceil(T/16) + 1 slots of every sequence).
+  int64_t tok0 = b * p.T, T = p.T, slot0 = b * (p.nblk + 1);
+  if (p.cu) {
+    int64_t a0 = p.cu[b], a1 = p.cu[b + 1];
+    a0 = a0 < 0 ? 0 : (a0 > p.rows ? p.rows : a0);
+    a1 = a1 < a0 ? a0 : (a1 > p.rows ? p.rows : a1);
+    tok0 = a0;
+    T = a1 - a0;
+    slot0 = a0 / kCkpt + 2 * b;
+  }
+  const int64_t nblk = (T + kCkpt - 1) / kCkpt;
+  if (T == 0) {  // no token: the state gradient passes through
+    if (p.d_state_in) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.d_state_out) ld4f(p.d_state_out + (head * DK + r0 + i) * p.dv + c0, x);
+        st4f(p.d_state_in + (head * DK + r0 + i) * p.dv + c0, x);
+      }
+    }
+    return;
+  }
   int buf = 0;
 
   // nblk checkpoints (state before each 16-token block) + the final state
-  float* ck = p.ckpt + ((head * ncb + cb) * (nblk + 1)) * (int64_t)DK * kCols;
+  float* ck = p.ckpt + (((int64_t)hv * ncb + cb) * p.slots + slot0) * (int64_t)DK * kCols;
   auto ck_at = [&](int64_t m, int i) { return ck + (m * DK + r0 + i) * kCols + cl; };
 
   // ---- phase 1: forward, storing checkpoints and u ----
@@ -337,13 +359,13 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       }
     }
     BlockLoad<DK, CHANNEL, HAS_G, false, IO, GT> ld;
-    ld.issue(p, b, hv, hk, cb, 0, tid);
+    ld.issue(p, tok0, T, hv, hk, cb, 0, tid);
     ld.store(stg[0], tid);
     lds_barrier();
     for (int64_t m = 0; m < nblk; ++m) {
       const int cur = (int)(m & 1);
       const bool more = m + 1 < nblk;
-      ld.issue(p, b, hv, hk, cb, (more ? m + 1 : m) * kCkpt, tid);
+      ld.issue(p, tok0, T, hv, hk, cb, (more ? m + 1 : m) * kCkpt, tid);
 #pragma unroll
       for (int i = 0; i < RPL; ++i) stc(ck + (m * DK + pr0 + i) * kCols + pc0, P1[i]);
       const int64_t t0 = m * kCkpt;
@@ -374,7 +396,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
         float u[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) u[j] = w[j] * v[j] - r[j];
-        if (rl == 0) stc(p.u + ((b * T + t0 + tl) * p.Hv + hv) * p.dv + pcg, u);
+        if (rl == 0) stc(p.u + ((tok0 + t0 + tl) * p.Hv + hv) * p.dv + pcg, u);
 #pragma unroll
         for (int i = 0; i < RPL; ++i)
 #pragma unroll
@@ -414,7 +436,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
 
   // Reverse step of token t: Pb = P_t, Pa = P_{t+1}, D = dL/dP_{t+1} -> dL/dP_t.
   auto reverse = [&](const Stage<DK>& st, const Tile& Pb, const Tile& Pa, int tl, int64_t t) {
-    const int64_t bth = (b * T + t) * p.Hv + hv;
+    const int64_t bth = (tok0 + t) * p.Hv + hv;
     float k[4], e[4], bb[4], a[4], w[4], v[4], dO[4], q[4], u[4];
     rows_of<DK, CHANNEL>(st, tl, r0, k, e, bb, a);
     wgate_of<DK, CHANNEL>(st, tl, cl, w);
@@ -496,7 +518,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
 
   {
     BlockLoad<DK, CHANNEL, HAS_G, true, IO, GT> ld;
-    ld.issue(p, b, hv, hk, cb, (nblk - 1) * kCkpt, tid);
+    ld.issue(p, tok0, T, hv, hk, cb, (nblk - 1) * kCkpt, tid);
     ld.store(stg[0], tid);
     Tile Ck, Cn;
 #pragma unroll
@@ -512,7 +534,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       const int cur = (int)(mm & 1);
       const bool more = m > 0;
       const int64_t mp = more ? m - 1 : m;   // the next block (or this one again)
-      ld.issue(p, b, hv, hk, cb, mp * kCkpt, tid);
+      ld.issue(p, tok0, T, hv, hk, cb, mp * kCkpt, tid);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ld4f(ck_at(mp, i), Cn[i]);
       const Stage<DK>& st = stg[cur];
@@ -571,7 +593,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs p) {
   const int64_t bt = blockIdx.x;
   const int ncb = p.dv / kCols;
   const int G = p.Hv / p.Hk;
-  const int64_t NR = p.B * p.T * p.Hv;
+  const int64_t NR = p.rows * p.Hv;
   auto part = [&](int cb, int vec, int64_t row, int i) {
     return p.part[(((int64_t)cb * 4 + vec) * NR + row) * DK + i];
   };
@@ -614,7 +636,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   bwd_kernel<DK, CHANNEL, HAS_G, IO, GT><<<grid, DK * 4, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_reduce_kernel<DK, CHANNEL><<<dim3((unsigned)(a.B * a.T)), 256, 0, stream>>>(a);
+  bwd_reduce_kernel<DK, CHANNEL><<<dim3((unsigned)a.rows), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

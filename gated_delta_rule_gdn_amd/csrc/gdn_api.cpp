@@ -108,21 +108,31 @@ gdn_status check_pointers(int64_t rows, int64_t heads_state, int32_t Hk, int32_t
 namespace {
 
 struct BwdLayout {
-  int64_t nblk, ckpt_floats, u_floats, part_floats;
+  int64_t nblk, slots, ckpt_floats, u_floats, part_floats;
   size_t ckpt_off, u_off, part_off, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BwdLayout bwd_layout(const gdn_bwd_desc* d) {
+// What the backward runs on: N sequences over `rows` token rows, either of T
+// tokens each (cu == nullptr) or packed by the device offsets cu.
+struct BwdShape {
+  int64_t N, rows, T;
+  const int64_t* cu;
+  int32_t Hk, Hv, dk, dv, io, gate, mode;
+  float scale;
+};
+
+BwdLayout bwd_layout(const BwdShape& d) {
   BwdLayout L;
-  const int64_t heads = d->B * d->H_v;
-  const int64_t rows = d->B * d->T * d->H_v;
-  const int64_t ncb = d->d_v / 64;
-  L.nblk = gdn::bwd_checkpoint_blocks(d->T);
-  L.ckpt_floats = heads * (L.nblk + 1) * d->d_k * d->d_v;
-  L.u_floats = rows * d->d_v;
-  L.part_floats = ncb * 4 * rows * d->d_k + ncb * rows;
+  const int64_t hrows = d.rows * d.Hv;
+  const int64_t ncb = d.dv / 64;
+  L.nblk = d.cu ? 0 : gdn::bwd_checkpoint_blocks(d.T);
+  // packed sequences: sequence n uses slots floor(start/16) + 2n onwards
+  L.slots = d.cu ? d.rows / 16 + 2 * d.N + 2 : d.N * (L.nblk + 1);
+  L.ckpt_floats = (int64_t)d.Hv * L.slots * d.dk * d.dv;
+  L.u_floats = hrows * d.dv;
+  L.part_floats = ncb * 4 * hrows * d.dk + ncb * hrows;
   L.ckpt_off = 0;
   L.u_off = align256((size_t)L.ckpt_floats * 4);
   L.part_off = L.u_off + align256((size_t)L.u_floats * 4);
@@ -130,19 +140,109 @@ BwdLayout bwd_layout(const gdn_bwd_desc* d) {
   return L;
 }
 
-gdn_status check_bwd_desc(const gdn_bwd_desc* d) {
-  if (!d) return GDN_ERR_INVALID_ARG;
-  if (d->B < 0 || d->T < 0) return GDN_ERR_INVALID_ARG;
-  gdn_status st = check_common(d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
-                               d->gate_mode, d->scale);
+gdn_status check_bwd_shape(const BwdShape& d) {
+  if (d.N < 0 || d.rows < 0 || d.T < 0) return GDN_ERR_INVALID_ARG;
+  gdn_status st = check_common(d.Hk, d.Hv, d.dk, d.dv, d.io, d.gate, d.mode, d.scale);
   if (st != GDN_OK) return st;
-  const double elems = (double)d->B * (double)d->T * (double)d->H_v *
-                       (double)(4 * d->d_k + 2 * d->d_v + 2);
-  const double ck = (double)d->B * d->H_v * ((double)d->T / 16.0 + 1.0) * d->d_k * d->d_v;
+  const double elems = (double)d.rows * (double)d.Hv * (double)(4 * d.dk + 2 * d.dv + 2);
+  const double ck = (double)d.Hv * ((double)d.rows / 16.0 + 2.0 * (double)d.N + 2.0) *
+                    (double)d.dk * (double)d.dv;
   if (elems > 2.0e15 || ck > 2.0e15) return GDN_ERR_INVALID_ARG;
-  if ((double)d->B * (double)d->H_v > 2.0e9 || (double)d->B * (double)d->T > 2.0e9)
+  if ((double)d.N * (double)d.Hv > 2.0e9 || (double)d.rows > 2.0e9)
     return GDN_ERR_UNSUPPORTED;  // grid sizes
   return GDN_OK;
+}
+
+BwdShape shape_of(const gdn_bwd_desc* d) {
+  return BwdShape{d->B, d->B * d->T, d->T, nullptr, d->H_k, d->H_v, d->d_k, d->d_v,
+                  d->io_dtype, d->gate_dtype, d->gate_mode, d->scale};
+}
+BwdShape shape_of(const gdn_bwd_varlen_desc* d, const int64_t* cu) {
+  return BwdShape{d->N, d->total_T, 0, cu, d->H_k, d->H_v, d->d_k, d->d_v,
+                  d->io_dtype, d->gate_dtype, d->gate_mode, d->scale};
+}
+
+gdn_status run_backward(const BwdShape& d, const void* q, const void* k, const void* v,
+                        const void* beta_or_b, const void* w, const void* g,
+                        const float* state_in, const void* d_o, const float* d_state_out,
+                        void* workspace, size_t workspace_bytes, float* dq, float* dk,
+                        float* dv, float* db, float* dw, float* dg, float* d_state_in,
+                        void* stream) {
+  gdn_status st = check_bwd_shape(d);
+  if (st != GDN_OK) return st;
+  if (d.N == 0) return GDN_OK;
+  const int64_t heads = d.N * d.Hv;
+  const int64_t S = heads * d.dk * d.dv;
+  const Span sdsi = span(d_state_in, S, 4), sdso = span(d_state_out, S, 4);
+  if ((d_state_in && !aligned16(d_state_in)) || (d_state_out && !aligned16(d_state_out)))
+    return GDN_ERR_INVALID_ARG;
+  if (overlaps(sdsi, sdso) && !(sdsi.lo == sdso.lo && sdsi.hi == sdso.hi))
+    return GDN_ERR_INVALID_ARG;
+  const Span scu = span(d.cu, d.N + 1, 8);
+  if (d.cu && ((reinterpret_cast<uintptr_t>(d.cu) & 7u) != 0 || overlaps(scu, sdsi)))
+    return GDN_ERR_INVALID_ARG;
+  if (d.rows == 0) {
+    // No token: the gradient only passes from the final to the initial state.
+    if (!d_state_in || d_state_in == d_state_out) return GDN_OK;
+    hipError_t e = gdn::launch_state_copy(d_state_out, d_state_in, S,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
+  const int64_t rows = d.rows;
+  st = check_pointers(rows, heads, d.Hk, d.Hv, d.dk, d.dv, d.io, d.gate, d.mode, q, k, v,
+                      beta_or_b, w, g, state_in, nullptr, d_o, false);
+  if (st != GDN_OK) return st;
+  const bool ch = d.mode == GDN_GATES_CHANNEL;
+  if (!dq || !dk || !dv || !db) return GDN_ERR_INVALID_ARG;
+  if (ch != (dw != nullptr)) return GDN_ERR_INVALID_ARG;
+  if (dg && !g) return GDN_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return GDN_ERR_INVALID_ARG;
+  const BwdLayout L = bwd_layout(d);
+  if (workspace_bytes < L.total) return GDN_ERR_INVALID_ARG;
+  const float* outs[] = {dq, dk, dv, db, dw, dg, d_state_in};
+  for (const float* p : outs)
+    if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+  // outputs: no overlap with inputs, the workspace or each other
+  const int64_t ib = dtype_bytes(d.io), gb = dtype_bytes(d.gate);
+  const int64_t gcols = ch ? d.dk : 1;
+  const Span in_sp[] = {
+      span(q, rows * d.Hk * d.dk, ib), span(k, rows * d.Hk * d.dk, ib),
+      span(v, rows * d.Hv * d.dv, ib), span(beta_or_b, rows * d.Hv * gcols, gb),
+      span(w, rows * d.Hv * d.dv, gb), span(g, rows * d.Hv * gcols, gb),
+      span(state_in, S, 4), span(d_o, rows * d.Hv * d.dv, ib), sdso, scu,
+      span(workspace, (int64_t)L.total, 1)};
+  const Span out_sp[] = {
+      span(dq, rows * d.Hk * d.dk, 4), span(dk, rows * d.Hk * d.dk, 4),
+      span(dv, rows * d.Hv * d.dv, 4), span(db, rows * d.Hv * gcols, 4),
+      span(dw, rows * d.Hv * d.dv, 4), span(dg, rows * d.Hv * gcols, 4), sdsi};
+  const int n_out = sizeof(out_sp) / sizeof(out_sp[0]);
+  for (int i = 0; i < n_out; ++i) {
+    for (const Span& in : in_sp) {
+      if (i == n_out - 1 && in.lo == sdso.lo && in.hi == sdso.hi && sdso.valid()) continue;
+      if (overlaps(out_sp[i], in)) return GDN_ERR_INVALID_ARG;
+    }
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(out_sp[i], out_sp[j])) return GDN_ERR_INVALID_ARG;
+  }
+  if (workspace_bytes && overlaps(span(workspace, (int64_t)L.total, 1), scu))
+    return GDN_ERR_INVALID_ARG;
+
+  gdn::BwdArgs a;
+  a.B = d.N; a.T = d.T; a.cu = d.cu; a.rows = rows; a.slots = L.slots;
+  a.Hk = d.Hk; a.Hv = d.Hv; a.dk = d.dk; a.dv = d.dv;
+  a.io = to_dtype(d.io); a.gate = to_dtype(d.gate); a.channel = ch;
+  a.scale = d.scale;
+  a.q = q; a.k = k; a.v = v; a.b = beta_or_b; a.w = w; a.g = g; a.d_o = d_o;
+  a.state_in = state_in; a.d_state_out = d_state_out;
+  char* ws = static_cast<char*>(workspace);
+  a.ckpt = reinterpret_cast<float*>(ws + L.ckpt_off);
+  a.u = reinterpret_cast<float*>(ws + L.u_off);
+  a.part = reinterpret_cast<float*>(ws + L.part_off);
+  a.nblk = L.nblk;
+  a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.db = db; a.dw = dw; a.dg = dg;
+  a.d_state_in = d_state_in;
+  hipError_t e = gdn::launch_backward(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 }  // namespace
@@ -257,9 +357,10 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_varlen_desc* d, const int64_t* cu_seql
 }
 
 size_t gdn_backward_workspace_size(const gdn_bwd_desc* d) {
-  if (check_bwd_desc(d) != GDN_OK) return 0;
-  if (d->B == 0 || d->T == 0) return 0;
-  return bwd_layout(d).total;
+  if (!d) return 0;
+  const BwdShape sh = shape_of(d);
+  if (check_bwd_shape(sh) != GDN_OK || sh.N == 0 || sh.rows == 0) return 0;
+  return bwd_layout(sh).total;
 }
 
 gdn_status gdn_backward(const gdn_bwd_desc* d, const void* q, const void* k, const void* v,
@@ -268,75 +369,31 @@ gdn_status gdn_backward(const gdn_bwd_desc* d, const void* q, const void* k, con
                         void* workspace, size_t workspace_bytes, float* dq, float* dk,
                         float* dv, float* db, float* dw, float* dg, float* d_state_in,
                         void* stream) {
-  gdn_status st = check_bwd_desc(d);
-  if (st != GDN_OK) return st;
-  if (d->B == 0) return GDN_OK;
-  const int64_t heads = d->B * d->H_v;
-  const int64_t S = heads * d->d_k * d->d_v;
-  const Span sdsi = span(d_state_in, S, 4), sdso = span(d_state_out, S, 4);
-  if ((d_state_in && !aligned16(d_state_in)) || (d_state_out && !aligned16(d_state_out)))
-    return GDN_ERR_INVALID_ARG;
-  if (overlaps(sdsi, sdso) && !(sdsi.lo == sdso.lo && sdsi.hi == sdso.hi))
-    return GDN_ERR_INVALID_ARG;
-  if (d->T == 0) {
-    // No token: the gradient only passes from the final to the initial state.
-    if (!d_state_in || d_state_in == d_state_out) return GDN_OK;
-    hipError_t e = gdn::launch_state_copy(d_state_out, d_state_in, S,
-                                          static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
-  }
-  const int64_t rows = d->B * d->T;
-  st = check_pointers(rows, heads, d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
-                      d->gate_mode, q, k, v, beta_or_b, w, g, state_in, nullptr, d_o, false);
-  if (st != GDN_OK) return st;
-  const bool ch = d->gate_mode == GDN_GATES_CHANNEL;
-  if (!dq || !dk || !dv || !db) return GDN_ERR_INVALID_ARG;
-  if (ch != (dw != nullptr)) return GDN_ERR_INVALID_ARG;
-  if (dg && !g) return GDN_ERR_INVALID_ARG;
-  if (!workspace || !aligned16(workspace)) return GDN_ERR_INVALID_ARG;
-  const BwdLayout L = bwd_layout(d);
-  if (workspace_bytes < L.total) return GDN_ERR_INVALID_ARG;
-  const float* outs[] = {dq, dk, dv, db, dw, dg, d_state_in};
-  for (const float* p : outs)
-    if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
-  // outputs: no overlap with inputs, the workspace or each other
-  const int64_t ib = dtype_bytes(d->io_dtype), gb = dtype_bytes(d->gate_dtype);
-  const int64_t gcols = ch ? d->d_k : 1;
-  const Span in_sp[] = {
-      span(q, rows * d->H_k * d->d_k, ib), span(k, rows * d->H_k * d->d_k, ib),
-      span(v, rows * d->H_v * d->d_v, ib), span(beta_or_b, rows * d->H_v * gcols, gb),
-      span(w, rows * d->H_v * d->d_v, gb), span(g, rows * d->H_v * gcols, gb),
-      span(state_in, S, 4), span(d_o, rows * d->H_v * d->d_v, ib), sdso,
-      span(workspace, (int64_t)L.total, 1)};
-  const Span out_sp[] = {
-      span(dq, rows * d->H_k * d->d_k, 4), span(dk, rows * d->H_k * d->d_k, 4),
-      span(dv, rows * d->H_v * d->d_v, 4), span(db, rows * d->H_v * gcols, 4),
-      span(dw, rows * d->H_v * d->d_v, 4), span(dg, rows * d->H_v * gcols, 4), sdsi};
-  const int n_out = sizeof(out_sp) / sizeof(out_sp[0]);
-  for (int i = 0; i < n_out; ++i) {
-    for (const Span& in : in_sp) {
-      if (i == n_out - 1 && in.lo == sdso.lo && in.hi == sdso.hi && sdso.valid()) continue;
-      if (overlaps(out_sp[i], in)) return GDN_ERR_INVALID_ARG;
-    }
-    for (int j = i + 1; j < n_out; ++j)
-      if (overlaps(out_sp[i], out_sp[j])) return GDN_ERR_INVALID_ARG;
-  }
+  if (!d) return GDN_ERR_INVALID_ARG;
+  return run_backward(shape_of(d), q, k, v, beta_or_b, w, g, state_in, d_o, d_state_out,
+                      workspace, workspace_bytes, dq, dk, dv, db, dw, dg, d_state_in, stream);
+}
 
-  gdn::BwdArgs a;
-  a.B = d->B; a.T = d->T; a.Hk = d->H_k; a.Hv = d->H_v; a.dk = d->d_k; a.dv = d->d_v;
-  a.io = to_dtype(d->io_dtype); a.gate = to_dtype(d->gate_dtype); a.channel = ch;
-  a.scale = d->scale;
-  a.q = q; a.k = k; a.v = v; a.b = beta_or_b; a.w = w; a.g = g; a.d_o = d_o;
-  a.state_in = state_in; a.d_state_out = d_state_out;
-  char* ws = static_cast<char*>(workspace);
-  a.ckpt = reinterpret_cast<float*>(ws + L.ckpt_off);
-  a.u = reinterpret_cast<float*>(ws + L.u_off);
-  a.part = reinterpret_cast<float*>(ws + L.part_off);
-  a.nblk = L.nblk;
-  a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.db = db; a.dw = dw; a.dg = dg;
-  a.d_state_in = d_state_in;
-  hipError_t e = gdn::launch_backward(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+size_t gdn_backward_varlen_workspace_size(const gdn_bwd_varlen_desc* d) {
+  if (!d) return 0;
+  const int64_t dummy = 0;
+  const BwdShape sh = shape_of(d, &dummy);
+  if (check_bwd_shape(sh) != GDN_OK || sh.N == 0 || sh.rows == 0) return 0;
+  return bwd_layout(sh).total;
+}
+
+gdn_status gdn_backward_varlen(const gdn_bwd_varlen_desc* d, const int64_t* cu_seqlens,
+                               const void* q, const void* k, const void* v,
+                               const void* beta_or_b, const void* w, const void* g,
+                               const float* state_in, const void* d_o, const float* d_state_out,
+                               void* workspace, size_t workspace_bytes, float* dq, float* dk,
+                               float* dv, float* db, float* dw, float* dg, float* d_state_in,
+                               void* stream) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  if (d->N > 0 && !cu_seqlens) return GDN_ERR_INVALID_ARG;
+  return run_backward(shape_of(d, cu_seqlens), q, k, v, beta_or_b, w, g, state_in, d_o,
+                      d_state_out, workspace, workspace_bytes, dq, dk, dv, db, dw, dg,
+                      d_state_in, stream);
 }
 
 gdn_status gdn_short_conv(const gdn_conv_desc* d, const int64_t* cu_seqlens, const void* x,

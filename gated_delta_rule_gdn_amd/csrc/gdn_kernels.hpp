@@ -75,11 +75,15 @@ struct NormArgs {
   void* y;
 };
 
-// Gradients of the recurrence.  Workspace: ckpt [B*Hv][nblk+1][dk][dv] states
-// every 16 tokens and the final state, u [B*T*Hv][dv], part [dv/64][4][B*T*Hv][dk] per-column-block
-// row gradients followed by [dv/64][B*T*Hv] write-gate sums (scalar gates).
+// Gradients of the recurrence.  Workspace: ckpt [Hv][dv/64][slots][dk][64],
+// the states every 16 tokens and the final state of each sequence;
+// u [rows*Hv][dv]; part [dv/64][4][rows*Hv][dk] per-column-block row
+// gradients followed by [dv/64][rows*Hv] write-gate sums (scalar gates).
 struct BwdArgs {
-  int64_t B, T;
+  int64_t B, T;                       // sequences; tokens each (packed total with cu)
+  const int64_t* cu = nullptr;        // device [B + 1] offsets of packed sequences
+  int64_t rows;                       // token rows of q, k, v, ... (B*T, or packed total)
+  int64_t slots;                      // checkpoint slots per (value head, 64 columns)
   int Hk, Hv, dk, dv;
   DType io, gate;
   bool channel;

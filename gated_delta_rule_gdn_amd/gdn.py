@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_SCALAR, GDN_GATES_CHANNEL = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class GdnFwdDesc(ctypes.Structure):
@@ -56,6 +56,14 @@ class GdnBwdDesc(ctypes.Structure):
                 ("gate_mode", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
+class GdnBwdVarlenDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("total_T", ctypes.c_int64),
+                ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
+                ("gate_mode", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
 class GdnConvDesc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("total_T", ctypes.c_int64), ("ld_x", ctypes.c_int64),
                 ("H_k", ctypes.c_int32), ("H_v", ctypes.c_int32),
@@ -86,7 +94,7 @@ class GdnError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_gdn_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python gated_delta_rule_gdn_amd/build.py` "
             "(there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
     vp = ctypes.c_void_p
@@ -102,6 +110,12 @@ def _load() -> ctypes.CDLL:
     lib.gdn_backward.argtypes = [ctypes.POINTER(GdnBwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  vp, ctypes.c_size_t, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_backward.restype = ctypes.c_int
+    lib.gdn_backward_varlen_workspace_size.argtypes = [ctypes.POINTER(GdnBwdVarlenDesc)]
+    lib.gdn_backward_varlen_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_backward_varlen.argtypes = [ctypes.POINTER(GdnBwdVarlenDesc), vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp, vp, vp,
+                                        vp, vp, vp]
+    lib.gdn_backward_varlen.restype = ctypes.c_int
     lib.gdn_short_conv.argtypes = [ctypes.POINTER(GdnConvDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_short_conv.restype = ctypes.c_int
     lib.gdn_gates.argtypes = [ctypes.POINTER(GdnGateDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -478,4 +492,64 @@ def gdn_backward(q, k, v, beta_or_b, d_o, w=None, g=None, state_in=None, d_state
                           _ptr(out["dg"]), _ptr(out["d_state_in"]), _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_backward")
+    return out
+
+
+def gdn_backward_varlen(q, k, v, beta_or_b, d_o, cu_seqlens, w=None, g=None, state_in=None,
+                        d_state_out=None, scale: float = 1.0, workspace=None,
+                        need_dg: bool = True, need_d_state_in: bool = True, grads=None,
+                        stream=None):
+    """Gradients over packed sequences (see include/gdn.h).  Shapes as for
+    gdn_chunk_fwd_varlen ([total_T, ...] packed, states [N, ...]); returns the
+    same dict of fp32 tensors as gdn_backward."""
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    io = q.dtype
+    gdt = beta_or_b.dtype
+    if io not in _DT or gdt not in _DT:
+        raise ValueError("inputs must be float32 or bfloat16")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    channel = w is not None
+    gshape = (T, Hv, dk) if channel else (T, Hv)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int64)
+    _check(q, "q", (T, Hk, dk), io)
+    _check(k, "k", (T, Hk, dk), io)
+    _check(v, "v", (T, Hv, dv), io)
+    _check(beta_or_b, "beta_or_b", gshape, gdt)
+    _check(w, "w", (T, Hv, dv), gdt)
+    _check(g, "g", gshape, gdt)
+    _check(state_in, "state_in", (N, Hv, dk, dv), torch.float32)
+    _check(d_o, "d_o", (T, Hv, dv), io)
+    _check(d_state_out, "d_state_out", (N, Hv, dk, dv), torch.float32)
+    desc = GdnBwdVarlenDesc(N, T, Hk, Hv, dk, dv, _DT[io], _DT[gdt],
+                            GDN_GATES_CHANNEL if channel else GDN_GATES_SCALAR, float(scale))
+    need = int(lib.gdn_backward_varlen_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    shapes = {"dq": (T, Hk, dk), "dk": (T, Hk, dk), "dv": (T, Hv, dv), "db": gshape,
+              "dw": (T, Hv, dv) if channel else None,
+              "dg": gshape if (g is not None and need_dg) else None,
+              "d_state_in": (N, Hv, dk, dv) if need_d_state_in else None}
+    out = {} if grads is None else dict(grads)
+    for name, shp in shapes.items():
+        if shp is None:
+            out[name] = None
+            continue
+        if out.get(name) is None:
+            out[name] = torch.empty(shp, **f32)
+        _check(out[name], name, shp, torch.float32)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.gdn_backward_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(beta_or_b), _ptr(w), _ptr(g), _ptr(state_in), _ptr(d_o),
+                                 _ptr(d_state_out), _ptr(workspace), ctypes.c_size_t(nbytes),
+                                 _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["db"]),
+                                 _ptr(out["dw"]), _ptr(out["dg"]), _ptr(out["d_state_in"]),
+                                 _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_backward_varlen")
     return out

@@ -53,8 +53,9 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
-                              gdn_gates, gdn_output_gate; 4: adds gdn_backward */
+#define GDN_ABI_VERSION 5  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
+                              gdn_gates, gdn_output_gate; 4: adds gdn_backward;
+                              5: adds gdn_backward_varlen */
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -245,6 +246,49 @@ gdn_status gdn_backward(const gdn_bwd_desc* desc, const void* q, const void* k, 
                         void* workspace, size_t workspace_bytes, float* dq, float* dk,
                         float* dv, float* db, float* dw, float* dg, float* d_state_in,
                         void* stream);
+
+/* Gradients over packed sequences of different lengths. */
+typedef struct gdn_bwd_varlen_desc {
+  int64_t N;          /* sequences, >= 0 (0: nothing to do)                      */
+  int64_t total_T;    /* packed tokens of all sequences, >= 0                    */
+  int32_t H_k, H_v;   /* >= 1, H_v % H_k == 0                                    */
+  int32_t d_k, d_v;   /* each 64 or 128                                          */
+  int32_t io_dtype;   /* gdn_dtype of q, k, v, d_o                               */
+  int32_t gate_dtype; /* equal to io_dtype, or F32                               */
+  int32_t gate_mode;  /* gdn_gate_mode                                           */
+  float scale;        /* finite                                                  */
+} gdn_bwd_varlen_desc;
+
+/*
+ * gdn_backward_varlen_workspace_size -- workspace bytes for gdn_backward_varlen
+ * (0 for an invalid descriptor or when there is no token): as for
+ * gdn_backward with total_T token rows, the checkpoints taking
+ * H_v (floor(total_T/16) + 2 N + 2) d_k d_v fp32.
+ */
+size_t gdn_backward_varlen_workspace_size(const gdn_bwd_varlen_desc* desc);
+
+/*
+ * gdn_backward_varlen -- gdn_backward over the packed sequences of
+ * gdn_chunk_fwd_varlen: sequence n is the tokens [cu_seqlens[n],
+ * cu_seqlens[n+1]) (device offsets, clamped on the device as for the forward;
+ * malformed offsets never make the kernels touch memory outside the tensors
+ * and the workspace, though their gradients are then unspecified).  The
+ * result for each sequence is that of gdn_backward on it alone; an empty
+ * sequence passes d_state_out[n] to d_state_in[n].
+ *
+ *   cu_seqlens        [N + 1] int64, DEVICE, 8-byte aligned
+ *   q, k, v, gates, d_o, dq, dk, dv, db, dw, dg   [total_T, ...] packed, as
+ *                     for gdn_chunk_fwd_varlen
+ *   state_in, d_state_out, d_state_in             [N, H_v, d_k, d_v] fp32
+ *   workspace         >= gdn_backward_varlen_workspace_size(desc) bytes
+ */
+gdn_status gdn_backward_varlen(const gdn_bwd_varlen_desc* desc, const int64_t* cu_seqlens,
+                               const void* q, const void* k, const void* v,
+                               const void* beta_or_b, const void* w, const void* g,
+                               const float* state_in, const void* d_o, const float* d_state_out,
+                               void* workspace, size_t workspace_bytes, float* dq, float* dk,
+                               float* dv, float* db, float* dw, float* dg, float* d_state_in,
+                               void* stream);
 
 /* ------------------------------------------------------------------------
  * The operations around the recurrence in a Gated DeltaNet block (notes page

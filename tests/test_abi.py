@@ -23,7 +23,8 @@ def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["gdn_chunk_fwd", "gdn_chunk_fwd_varlen", "gdn_decode_step", "gdn_status_string",
          "gdn_abi_version", "gdn_short_conv", "gdn_gates", "gdn_output_gate", "gdn_backward",
-         "gdn_backward_workspace_size"])
+         "gdn_backward_workspace_size", "gdn_backward_varlen",
+         "gdn_backward_varlen_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert gdn.abi_version() == 4
+    assert gdn.abi_version() == 5
     for st in range(4):
         s = gdn.status_string(st)
         assert s.startswith("GDN_")
@@ -442,3 +443,28 @@ def test_product_sources_never_reference_the_oracle():
             if name.endswith((".py", ".hip", ".cpp", ".hpp")):
                 text = open(os.path.join(base, name)).read()
                 assert not re.search(r"\boracle\b", text), os.path.join(base, name)
+
+
+def test_backward_varlen_validation():
+    d = gdn.GdnBwdVarlenDesc(N=3, total_T=100, H_k=2, H_v=4, d_k=128, d_v=128,
+                             io_dtype=gdn.GDN_BF16, gate_dtype=gdn.GDN_BF16,
+                             gate_mode=gdn.GDN_GATES_CHANNEL, scale=1.0)
+    n = gdn.lib.gdn_backward_varlen_workspace_size(ctypes.byref(d))
+    r = lambda x: (x + 255) // 256 * 256
+    ck = 4 * (100 // 16 + 2 * 3 + 2) * 128 * 128 * 4
+    u = 100 * 4 * 128 * 4
+    part = (2 * 4 * 100 * 4 * 128 + 2 * 100 * 4) * 4
+    assert n == r(ck) + r(u) + r(part)
+    names = ["q", "k", "v", "b", "w", "g", "s_in", "d_o", "d_sT", "ws", "dq", "dk", "dv", "db",
+             "dw", "dg", "d_s0"]
+
+    def call(cu, **ptrs):
+        p = {nm: _addr(i) for i, nm in enumerate(names)}
+        p.update(ptrs)
+        args = [p[nm] for nm in names]
+        return gdn.lib.gdn_backward_varlen(ctypes.byref(d), cu, *args[:10], ctypes.c_size_t(n),
+                                           *args[10:], None)
+    assert call(None) == gdn.GDN_ERR_INVALID_ARG                    # offsets required
+    assert call(_addr(20, 4)) == gdn.GDN_ERR_INVALID_ARG            # misaligned offsets
+    assert call(_addr(10, 0)) == gdn.GDN_ERR_INVALID_ARG            # offsets inside dq
+    assert call(_addr(9, 64)) == gdn.GDN_ERR_INVALID_ARG            # offsets inside the workspace

@@ -159,3 +159,68 @@ def test_backward_full_size_sampled_heads():
         for n in ["dq", "dk", "dv", "db", "dw", "dg"]:
             assert relerr(got[n][b:b + 1, :, h:h + 1], ref[n]) <= 2e-2, (b, h, n)
         assert relerr(got["d_state_in"][b:b + 1, h:h + 1], ref["d_state_in"]) <= 2e-2
+
+
+# ----------------------------------------------------------------------------
+# packed sequences
+# ----------------------------------------------------------------------------
+VL = [0, 1, 17, 64, 100, 5]
+
+
+def _packed_case(lengths, channel, io=torch.bfloat16, Hk=1, Hv=2, seed=61):
+    total = sum(lengths)
+    inp, d_o, _ = _case(1, total, Hk, Hv, 128, 128, channel, io, seed=seed, state_std=0.0)
+    packed = {k: (None if v is None else v[0].contiguous()) for k, v in inp.items() if k != "state_in"}
+    gen = torch.Generator().manual_seed(seed + 7)
+    N = len(lengths)
+    s0 = 0.3 * torch.randn((N, Hv, 128, 128), generator=gen)
+    dsT = torch.randn((N, Hv, 128, 128), generator=gen)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64)
+    return packed, d_o[0].contiguous(), s0, dsT, cu
+
+
+def _run_packed(packed, d_o, s0, dsT, cu):
+    d = {k: (None if v is None else v.cuda()) for k, v in packed.items()}
+    return gdn.gdn_backward_varlen(d["q"], d["k"], d["v"], d["beta_or_b"], d_o.cuda(), cu.cuda(),
+                                   w=d["w"], g=d["g"], state_in=s0.cuda(), d_state_out=dsT.cuda())
+
+
+@pytest.mark.parametrize("channel", [True, False])
+def test_backward_varlen_matches_oracle_per_sequence(channel):
+    announce(f"backward varlen channel={channel}")
+    packed, d_o, s0, dsT, cu = _packed_case(VL, channel)
+    got = _run_packed(packed, d_o, s0, dsT, cu)
+    torch.cuda.synchronize()
+    for n in range(len(VL)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b == a:
+            assert torch.equal(got["d_state_in"][n].cpu(), dsT[n]), n
+            continue
+        sl = lambda x: None if x is None else x[a:b].unsqueeze(0)
+        ref = oracle.backward(sl(packed["q"]), sl(packed["k"]), sl(packed["v"]),
+                              sl(packed["beta_or_b"]), sl(d_o), w=sl(packed["w"]),
+                              g=sl(packed["g"]), state_in=s0[n:n + 1], d_state_out=dsT[n:n + 1])
+        for name in ["dq", "dk", "dv", "db", "dw", "dg"]:
+            if ref[name] is None:
+                continue
+            assert relerr(got[name][a:b].unsqueeze(0), ref[name]) <= 2e-2, (n, name)
+        assert relerr(got["d_state_in"][n:n + 1], ref["d_state_in"]) <= 2e-2, n
+
+
+def test_backward_varlen_equals_separate_calls_bitwise():
+    announce("backward varlen vs separate calls")
+    packed, d_o, s0, dsT, cu = _packed_case(VL, True)
+    got = _run_packed(packed, d_o, s0, dsT, cu)
+    for n in range(len(VL)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b == a:
+            continue
+        sub = {k: (None if v is None else v[a:b].unsqueeze(0).contiguous().cuda())
+               for k, v in packed.items()}
+        one = gdn.gdn_backward(sub["q"], sub["k"], sub["v"], sub["beta_or_b"],
+                               d_o[a:b].unsqueeze(0).contiguous().cuda(), w=sub["w"], g=sub["g"],
+                               state_in=s0[n:n + 1].cuda(), d_state_out=dsT[n:n + 1].cuda())
+        torch.cuda.synchronize()
+        for name in ["dq", "dk", "dv", "db", "dw", "dg"]:
+            assert torch.equal(one[name][0], got[name][a:b]), (n, name)
+        assert torch.equal(one["d_state_in"], got["d_state_in"][n:n + 1]), n
