@@ -1,49 +1,61 @@
 // backward.hip -- gradients of the gated delta rule on gfx950 (reverse mode
-// through the token recurrence).
+// through the recurrence, in 16-token blocks on MFMA).
 //
 // With P_t the state before token t, abar = exp(g_t), e = b (.) k,
 // z = w (.) v, the forward step is
 //   Sbar = Diag(abar) P_t,  r = Sbar^T e,  u = z - r,
-//   P_{t+1} = Sbar + k u^T,  o_t = scale P_{t+1}^T q_t,
-// and the reverse step, with D the gradient w.r.t. P_{t+1}:
-//   D += scale q dO^T;  dq = scale P_{t+1} dO;  du = D^T k;
-//   dv = w (.) du;  dw = v (.) du;  de = -Sbar du;
-//   dk = D u + b (.) de;  db = k (.) de;  dSbar = D - e du^T;
-//   dg = abar (.) rowsum(dSbar (.) P_t);  D <- Diag(abar) dSbar.
+//   P_{t+1} = Sbar + k u^T,  o_t = scale P_{t+1}^T q_t.
 // The pages give the forward update ("Gated DeltaNet-2", Methodologie §1)
 // and name the gate-aware gradient as what makes training work (§3); the
-// formulas above are the chain rule through that update.
+// gradients below are the chain rule through that update, gathered over a
+// block of C = 16 tokens so that they become matrix products.
+//
+// Block form.  For a block with entry state S, exit-state gradient D and,
+// per channel i, the inclusive cumulative log-decay G_s (from the block
+// start), write Gamma_st = exp(G_s - G_t) (s >= t; <= 1), gs = exp(G_s),
+// ge = exp(G_end - G_s), gend = exp(G_end).  With
+//   A[s][t] = sum_i e_s Gamma_st k_t (s > t),  Pm[s][t] = sum_i q_s Gamma_st k_t (s >= t),
+//   RHS = (k ge) D + scale Pm^T dO,  DU = (I + A^T)^{-1} RHS   (du per token),
+//   M3 = U dO^T,  M4 = U DU^T                                  (over columns),
+// the gradients are
+//   dq = scale (gs (.) dO S^T + [sum_{t<=s} M3[t][s] Gamma_st k_t])
+//   de = -(gs (.) DU S^T + [sum_{t<s} M4[t][s] Gamma_st k_t])
+//   dk = ge (.) U D^T + [sum_{s>=t} (scale M3[t][s] q_s - [s>t] M4[t][s] e_s) Gamma_st] + b (.) de
+//   db = k (.) de,  dv = w (.) DU,  dw = v (.) DU,
+//   dG_s = q dq + e de - k dk1 (+ rowsum(D (.) P_end) at the last token),
+//   dg = reverse cumulative sum of dG over the block,
+//   D <- Diag(gend) D + scale (gs q)^T dO - (gs e)^T DU.
+// The bracketed sums are intra-block.  They and A, Pm are products over the
+// channel with a per-channel decay; they factor as exp(G_s - ref) exp(ref - G_t)
+// around a per-channel reference (the block's 8th token) and then run on the
+// MFMA.  A block whose decay range would take the factors out of the fp32
+// range computes them term by term on the vector units instead.  With scalar
+// gates the decay is a 16 x 16 mask and the factors are 1.
 //
 // Layout: one workgroup per (sequence, value head, block of 64 value
-// columns); the fp32 state slice is DK x 64, 4 rows x 4 columns per thread
-// (DK * 4 threads).  The 16 lanes of a DPP row hold the 64 columns of 4 rows,
-// so sums over columns are DPP butterflies; sums over rows take two
-// cross-lane shuffles and one LDS exchange (one barrier).
-//
-// Phase 1 runs the recurrence forward from the initial state, storing the
-// state every kCkpt tokens, the final state and every u_t in the workspace;
-// it uses a layout of its own in which the read r needs no barrier.  Phase 2 walks the
-// checkpoint blocks backwards: for each sub-block of kSub tokens it rebuilds
-// the states from the block's checkpoint with the stored u (no reduction is
-// needed: P_{t+1} = abar P_t + k u^T), keeps the sub-block's states in
-// registers and runs the reverse step token by token.  Both phases read a
-// block's token inputs from LDS, where they were staged while the previous
-// block was computed (global loads issued a block ahead, LDS-only barriers in
-// between so they stay in flight).  The per-row gradients (dq, dk, db, dg)
-// are partial over the column block; they go to the workspace and a second
-// kernel sums them over column blocks and over the value heads of a key head.
-#include "gdn_device.hpp"
-#include "gdn_kernels.hpp"
+// columns), DK * 4 threads.  Phase 1 runs the recurrence forward from the
+// initial state, storing the state every 16 tokens, the final state and every
+// u_t in the workspace (a wave holds all DK rows of a few columns, so the read
+// r is an in-wave butterfly).  Phase 2 walks the blocks backwards with the
+// exit-state gradient in MFMA accumulators -- wave w holds D rows
+// 16w..16w+15 as D^T tiles, waves 0-3 also D columns 16w..16w+15 over all
+// rows as D tiles -- and evaluates the block form above.  The per-row
+// gradients (dq, dk, db, dg) are partial over the column block; they go to
+// the workspace and a second kernel sums them over column blocks and over the
+// value heads of a key head.
+#include "chunk_common.hpp"
 
 #include <type_traits>
 
 namespace gdn {
 namespace {
 
-constexpr int kCkpt = 16;            // tokens between stored states
-constexpr int kSub = 4;              // tokens per register-resident sub-block
-constexpr int kSubs = kCkpt / kSub;  // sub-blocks per checkpoint block
+constexpr int kCkpt = 16;            // tokens per block (and between stored states)
 constexpr int kCols = 64;            // value columns per workgroup
+// Largest |G_s - ref| (log2 units) for which the factored operands, their
+// products with the intra-block matrices and the masked-out entries stay
+// finite in fp32.
+constexpr float kSafeLog2 = 96.f;
 
 // Sum over the 16 lanes of a DPP row (all lanes get the sum).
 __device__ __forceinline__ float row16_sum(float s) {
@@ -57,8 +69,6 @@ __device__ __forceinline__ float row16_sum(float s) {
   s += dpp(s, std::integral_constant<int, 0x140>{});  // row_mirror
   return s;
 }
-
-typedef float Tile[4][4];
 
 // Barrier for LDS traffic only: waits for this wave's LDS operations, not
 // for its global loads, so prefetches stay in flight across it.
@@ -91,11 +101,6 @@ __device__ __forceinline__ void load_raw(const T* p, RawN<T, N>& r) {
   }
 }
 template <typename T, int N>
-__device__ __forceinline__ void zero_raw(RawN<T, N>& r) {
-#pragma unroll
-  for (int i = 0; i < (sizeof(T) == 2 ? N / 2 : N); ++i) r.w[i] = 0;
-}
-template <typename T, int N>
 __device__ __forceinline__ void unpack_raw(const RawN<T, N>& r, float* o) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
@@ -108,35 +113,34 @@ __device__ __forceinline__ void unpack_raw(const RawN<T, N>& r, float* o) {
   }
 }
 
-// One checkpoint block's token inputs in LDS: the row side (q, k, b, abar)
-// over all DK rows and the column side (v, w, dO, u) over the workgroup's 64
-// columns; scalar gates per token.
+// ---------------------------------------------------------------------------
+// Phase 1: one block's token inputs (row side k, b, abar over all DK rows;
+// column side v, w over the workgroup's 64 columns; scalar gates per token).
+// ---------------------------------------------------------------------------
 template <int DK>
-struct Stage {
-  float k[kCkpt][DK], q[kCkpt][DK], b[kCkpt][DK], a[kCkpt][DK];
-  float v[kCkpt][kCols], w[kCkpt][kCols], dO[kCkpt][kCols], u[kCkpt][kCols];
+struct FwdStage {
+  float k[kCkpt][DK], b[kCkpt][DK], a[kCkpt][DK];
+  float v[kCkpt][kCols], w[kCkpt][kCols];
   float sb[kCkpt], sa[kCkpt];
 };
 
-// A thread's share of loading one block into a Stage: 4 row elements of one
-// token, CPT column elements of one token.
-template <int DK, bool CHANNEL, bool HAS_G, bool REV, typename IO, typename GT>
-struct BlockLoad {
+// A thread's share of loading one block: 4 row elements of one token, CPT
+// column elements of one token.  Every load is issued unconditionally (token
+// index clamped into the sequence), so the compiler's count of outstanding
+// loads is the same on every path and nothing waits for them before store().
+template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT>
+struct FwdLoad {
   static constexpr int NT = DK * 4;
   static constexpr int TPR = DK / 4;                // threads per token (rows)
   static constexpr int CPT = kCkpt * kCols / NT;    // column elements per thread
   static constexpr int TPC = kCols / CPT;           // threads per token (columns)
-  RawN<IO, 4> k, q;
+  RawN<IO, 4> k;
   RawN<GT, 4> b, g;
-  RawN<IO, CPT> v, dO;
+  RawN<IO, CPT> v;
   RawN<GT, CPT> w;
-  float u[CPT];
   float sb, sg;
   bool rv, cv;   // the row / column token exists (loads past T read token T-1)
 
-  // Every load is issued unconditionally (token index clamped into the
-  // sequence), so the compiler's count of outstanding loads is the same on
-  // every path and nothing waits for them before store().
   __device__ __forceinline__ void issue(const BwdArgs& p, int64_t tok0, int64_t Tn, int hv,
                                         int hk, int cb, int64_t t0, int tid) {
     const int tr = tid / TPR, i0 = 4 * (tid % TPR);
@@ -148,7 +152,6 @@ struct BlockLoad {
       const int64_t t = rv ? trr : Tn - 1;
       const int64_t bt = tok0 + t, bth = bt * p.Hv + hv;
       load_raw<IO, 4>(static_cast<const IO*>(p.k) + (bt * p.Hk + hk) * DK + i0, k);
-      if constexpr (REV) load_raw<IO, 4>(static_cast<const IO*>(p.q) + (bt * p.Hk + hk) * DK + i0, q);
       if constexpr (CHANNEL) {
         load_raw<GT, 4>(static_cast<const GT*>(p.b) + bth * DK + i0, b);
         if constexpr (HAS_G) load_raw<GT, 4>(static_cast<const GT*>(p.g) + bth * DK + i0, g);
@@ -159,20 +162,14 @@ struct BlockLoad {
     }
     {
       const int64_t t = cv ? tcc : Tn - 1;
-      const int64_t bth = (tok0 + t) * p.Hv + hv;
-      const int64_t off = bth * p.dv + (int64_t)cb * kCols + j0;
+      const int64_t off = ((tok0 + t) * p.Hv + hv) * p.dv + (int64_t)cb * kCols + j0;
       load_raw<IO, CPT>(static_cast<const IO*>(p.v) + off, v);
       if constexpr (CHANNEL) load_raw<GT, CPT>(static_cast<const GT*>(p.w) + off, w);
-      if constexpr (REV) {
-        load_raw<IO, CPT>(static_cast<const IO*>(p.d_o) + off, dO);
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) u[j] = p.u[off + j];
-      }
     }
   }
 
   // Writes the block to LDS; tokens past T are stored as zeros.
-  __device__ __forceinline__ void store(Stage<DK>& st, int tid) const {
+  __device__ __forceinline__ void store(FwdStage<DK>& st, int tid) const {
     const int tr = tid / TPR, i0 = 4 * (tid % TPR);
     const int tc = tid / TPC, j0 = CPT * (tid % TPC);
     const float mr = rv ? 1.f : 0.f, mc = cv ? 1.f : 0.f;
@@ -181,12 +178,6 @@ struct BlockLoad {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] *= mr;
     st4f(&st.k[tr][i0], x);
-    if constexpr (REV) {
-      unpack_raw<IO, 4>(q, x);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] *= mr;
-      st4f(&st.q[tr][i0], x);
-    }
     if constexpr (CHANNEL) {
       unpack_raw<GT, 4>(b, x);
 #pragma unroll
@@ -213,70 +204,155 @@ struct BlockLoad {
 #pragma unroll
       for (int j = 0; j < CPT; ++j) st.w[tc][j0 + j] = y[j] * mc;
     }
-    if constexpr (REV) {
-      unpack_raw<IO, CPT>(dO, y);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Phase 2: one block in LDS.  Fragment layouts (lane = 16 g + n): rowL(X)
+// holds X[n][4g .. 4g+3], accL(X) holds X[4g .. 4g+3][n]; mma16(acc,
+// rowL(X), accL(Y)) adds accL(X Y), and accL(X) = rowL(X^T).  Operands read
+// with the channel as the contraction index are [token][channel] arrays;
+// those read with the token as the contraction index are [channel][token]
+// arrays (names ending in T).
+// ---------------------------------------------------------------------------
+template <int DK, typename T>
+struct RevLds {
+  static constexpr int RP = DK + 4;                    // fp32 [16][DK] pitch
+  static constexpr int OP = DK + 16 / (int)sizeof(T);  // T [16][DK] pitch
+  static constexpr int CPd = kCols + 16 / (int)sizeof(T);
+  static constexpr int TP = 20;                        // [*][16] pitch
+  float k[kCkpt][RP], q[kCkpt][RP], b[kCkpt][RP], gl[kCkpt][RP];  // inputs (fp32)
+  T Kg[kCkpt][OP], Kf[kCkpt][OP], Qf[kCkpt][OP], Ef[kCkpt][OP];
+  T KfT[DK][TP], QfT[DK][TP], EfT[DK][TP], QgT[DK][TP], EgT[DK][TP];
+  T dOr[kCkpt][CPd], Ur[kCkpt][CPd], DUr[kCkpt][CPd];  // [token][column]
+  T dOt[kCols][TP], DUt[kCols][TP];                     // [column][token]
+  float Gl[DK][TP];                                     // cumulative log2-decay
+  float ref[DK], lend[DK], gend[DK];
+  float A[kCkpt][kCkpt + 1], P[kCkpt][kCkpt + 1];       // exact Gram matrices
+  float M3[kCkpt][kCkpt + 1], M4[kCkpt][kCkpt + 1];
+  float vs[4][kCkpt];                                   // scalar gates: sum_j v du per tile
+  float sb[kCkpt], sgl[kCkpt];
+  int unsafe;
+};
+
+// A thread's share of one block's row inputs (4 channels of one token) and
+// column inputs (CPT columns of one token), issued a block ahead.
+template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT>
+struct RevLoad {
+  static constexpr int NT = DK * 4;
+  static constexpr int TPR = DK / 4;
+  static constexpr int CPT = kCkpt * kCols / NT;
+  static constexpr int TPC = kCols / CPT;
+  RawN<IO, 4> k, q;
+  RawN<GT, 4> b, g;
+  RawN<IO, CPT> dO;
+  float u[CPT];
+  float sb, sg;
+  bool rv, cv;
+
+  __device__ __forceinline__ void issue(const BwdArgs& p, int64_t tok0, int64_t Tn, int hv,
+                                        int hk, int cb, int64_t t0, int tid) {
+    const int tr = tid / TPR, i0 = 4 * (tid % TPR);
+    const int tc = tid / TPC, j0 = CPT * (tid % TPC);
+    const int64_t trr = t0 + tr, tcc = t0 + tc;
+    rv = trr < Tn;
+    cv = tcc < Tn;
+    {
+      const int64_t t = rv ? trr : Tn - 1;
+      const int64_t bt = tok0 + t, bth = bt * p.Hv + hv;
+      load_raw<IO, 4>(static_cast<const IO*>(p.k) + (bt * p.Hk + hk) * DK + i0, k);
+      load_raw<IO, 4>(static_cast<const IO*>(p.q) + (bt * p.Hk + hk) * DK + i0, q);
+      if constexpr (CHANNEL) {
+        load_raw<GT, 4>(static_cast<const GT*>(p.b) + bth * DK + i0, b);
+        if constexpr (HAS_G) load_raw<GT, 4>(static_cast<const GT*>(p.g) + bth * DK + i0, g);
+      } else {
+        sb = to_f32(static_cast<const GT*>(p.b)[bth]);
+        sg = HAS_G ? to_f32(static_cast<const GT*>(p.g)[bth]) : 0.f;
+      }
+    }
+    {
+      const int64_t t = cv ? tcc : Tn - 1;
+      const int64_t off = ((tok0 + t) * p.Hv + hv) * p.dv + (int64_t)cb * kCols + j0;
+      load_raw<IO, CPT>(static_cast<const IO*>(p.d_o) + off, dO);
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) { st.dO[tc][j0 + j] = y[j] * mc; st.u[tc][j0 + j] = u[j] * mc; }
+      for (int j = 0; j < CPT; ++j) u[j] = p.u[off + j];
+    }
+  }
+
+  // Writes the block to LDS; tokens past T are stored as zeros, with zero
+  // log-decay so that the cumulative decay stays put past the end.
+  template <typename T>
+  __device__ __forceinline__ void store(RevLds<DK, T>& L, int tid) const {
+    const int tr = tid / TPR, i0 = 4 * (tid % TPR);
+    const int tc = tid / TPC, j0 = CPT * (tid % TPC);
+    const float mr = rv ? 1.f : 0.f, mc = cv ? 1.f : 0.f;
+    float x[4];
+    unpack_raw<IO, 4>(k, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] *= mr;
+    st4f(&L.k[tr][i0], x);
+    unpack_raw<IO, 4>(q, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] *= mr;
+    st4f(&L.q[tr][i0], x);
+    if constexpr (CHANNEL) {
+      unpack_raw<GT, 4>(b, x);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] *= mr;
+      st4f(&L.b[tr][i0], x);
+      if constexpr (HAS_G) {
+        unpack_raw<GT, 4>(g, x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] *= kLog2e * mr;
+      } else {
+        x[0] = x[1] = x[2] = x[3] = 0.f;
+      }
+      st4f(&L.gl[tr][i0], x);
+    } else if (i0 == 0) {
+      L.sb[tr] = sb * mr;
+      L.sgl[tr] = HAS_G ? sg * kLog2e * mr : 0.f;
+    }
+    float y[CPT];
+    unpack_raw<IO, CPT>(dO, y);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const T d = from_f32<T>(y[j] * mc);
+      L.dOr[tc][j0 + j] = d;
+      L.dOt[j0 + j][tc] = d;
+      L.Ur[tc][j0 + j] = from_f32<T>(u[j] * mc);
     }
   }
 };
 
-// Token tl of a staged block, seen by one thread: its 4 rows and 4 columns.
-template <int DK, bool CHANNEL>
-__device__ __forceinline__ void rows_of(const Stage<DK>& st, int tl, int r0, float* k, float* e,
-                                        float* bb, float* a) {
-  ld4f(&st.k[tl][r0], k);
-  if constexpr (CHANNEL) {
-    ld4f(&st.b[tl][r0], bb);
-    ld4f(&st.a[tl][r0], a);
-  } else {
-    const float sb = st.sb[tl], sa = st.sa[tl];
+template <typename T>
+__device__ __forceinline__ Frag4<T> frag4_of(const float* x) {
+  Frag4<T> f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { bb[i] = sb; a[i] = sa; }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) e[i] = bb[i] * k[i];
+  for (int i = 0; i < 4; ++i) f.v[i] = from_f32<T>(x[i]);
+  return f;
 }
-template <int DK, bool CHANNEL>
-__device__ __forceinline__ void wgate_of(const Stage<DK>& st, int tl, int cl, float* w) {
-  if constexpr (CHANNEL) {
-    ld4f(&st.w[tl][cl], w);
-  } else {
-    const float sb = st.sb[tl];
-    w[0] = w[1] = w[2] = w[3] = sb;
-  }
+__device__ __forceinline__ Frag4<float> f32frag(const f32x4& a) {
+  Frag4<float> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.v[i] = a[i];
+  return f;
 }
 
-// Sum of v[4] over all DK rows of the workgroup for each of the thread's 4
-// columns: across the 4 row groups of a wave by shuffles, then across the
-// waves through LDS (double-buffered, so one barrier per call).
-template <int NW>
-__device__ __forceinline__ void row_reduce(float* v, float (*red)[NW][kCols], int& buf, int lane,
-                                           int wave, int cg) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[j] += __shfl_xor(v[j], 16);
-    v[j] += __shfl_xor(v[j], 32);
-  }
-  if (lane < 16) st4f(&red[buf][wave][4 * cg], v);
-  lds_barrier();
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const float4 x = *reinterpret_cast<const float4*>(&red[buf][w][4 * cg]);
-    s[0] += x.x; s[1] += x.y; s[2] += x.z; s[3] += x.w;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = s[j];
-  buf ^= 1;
+// 2^(Gl_s - Gl_t) for scalar gates (the per-token cumulative log2-decay is
+// the same in every channel's row of Gl).
+template <int DK, typename T>
+__device__ __forceinline__ float token_decay(const RevLds<DK, T>& L, int s, int t) {
+  return exp2_fast(L.Gl[0][s] - L.Gl[0][t]);
 }
 
 template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT>
 __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
-  constexpr int NT = DK * 4;
-  constexpr int NW = NT / 64;
-  __shared__ float red[2][NW][kCols];
-  __shared__ Stage<DK> stg[2];
+  constexpr int RB = DK / 16;               // 16-row blocks of the state
+  union Smem {
+    FwdStage<DK> fwd[2];
+    RevLds<DK, IO> rev;
+  };
+  __shared__ Smem sm;
 
   const int64_t head = blockIdx.x;          // b * Hv + hv
   const int cb = blockIdx.y;
@@ -285,10 +361,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   const int hv = (int)(head - b * p.Hv);
   const int hk = hv / (p.Hv / p.Hk);
   const int tid = threadIdx.x;
-  const int rg = tid >> 4, cg = tid & 15;
   const int lane = tid & 63, wave = tid >> 6;
-  const int r0 = 4 * rg, cl = 4 * cg;       // first row; first column inside the block
-  const int64_t c0 = (int64_t)cb * kCols + cl;
   const int64_t NR = p.rows * p.Hv;         // gradient rows (token, hv)
   const float scale = p.scale;
   // This workgroup's sequence: tokens [tok0, tok0 + T) of the packed rows,
@@ -306,6 +379,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   const int64_t nblk = (T + kCkpt - 1) / kCkpt;
   if (T == 0) {  // no token: the state gradient passes through
     if (p.d_state_in) {
+      const int r0 = 4 * (tid >> 4), c0 = cb * kCols + 4 * (tid & 15);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x[4] = {0.f, 0.f, 0.f, 0.f};
@@ -315,16 +389,14 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     }
     return;
   }
-  int buf = 0;
 
   // nblk checkpoints (state before each 16-token block) + the final state
   float* ck = p.ckpt + (((int64_t)hv * ncb + cb) * p.slots + slot0) * (int64_t)DK * kCols;
-  auto ck_at = [&](int64_t m, int i) { return ck + (m * DK + r0 + i) * kCols + cl; };
 
   // ---- phase 1: forward, storing checkpoints and u ----
-  // Its own layout: a wave holds all DK rows of CW columns, a lane RPL rows
-  // x CPL columns (the 16 lanes of a DPP row share the columns), so the read
-  // r = Sbar^T e is an in-wave butterfly and the token loop has no barrier.
+  // A wave holds all DK rows of CW columns, a lane RPL rows x CPL columns
+  // (the 16 lanes of a DPP row share the columns), so the read r = Sbar^T e
+  // is an in-wave butterfly and the token loop has no barrier.
   {
     constexpr int RPL = DK / 16;             // rows per lane
     constexpr int CPL = 256 / DK;            // columns per lane
@@ -358,9 +430,9 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
         for (int j = 0; j < CPL; ++j) P1[i][j] = 0.f;
       }
     }
-    BlockLoad<DK, CHANNEL, HAS_G, false, IO, GT> ld;
+    FwdLoad<DK, CHANNEL, HAS_G, IO, GT> ld;
     ld.issue(p, tok0, T, hv, hk, cb, 0, tid);
-    ld.store(stg[0], tid);
+    ld.store(sm.fwd[0], tid);
     lds_barrier();
     for (int64_t m = 0; m < nblk; ++m) {
       const int cur = (int)(m & 1);
@@ -370,7 +442,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       for (int i = 0; i < RPL; ++i) stc(ck + (m * DK + pr0 + i) * kCols + pc0, P1[i]);
       const int64_t t0 = m * kCkpt;
       const int nt = (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
-      const Stage<DK>& st = stg[cur];
+      const FwdStage<DK>& st = sm.fwd[cur];
       for (int tl = 0; tl < nt; ++tl) {
         float k[RPL], bb[RPL], a[RPL], w[CPL], v[CPL], r[CPL];
         ldn(&st.k[tl][pr0], k, RPL);
@@ -402,186 +474,436 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
 #pragma unroll
           for (int j = 0; j < CPL; ++j) P1[i][j] = a[i] * P1[i][j] + k[i] * u[j];
       }
-      ld.store(stg[cur ^ 1], tid);   // (the last block stores a copy nobody reads)
+      ld.store(sm.fwd[cur ^ 1], tid);   // (the last block stores a copy nobody reads)
       lds_barrier();
     }
-    // the final state, read back below in the reverse layout
+    // the final state
 #pragma unroll
     for (int i = 0; i < RPL; ++i) stc(ck + (nblk * DK + pr0 + i) * kCols + pc0, P1[i]);
   }
-  // The u and the final state written above are read back below through
-  // global memory by other threads of this workgroup: make them visible.
+  // The u and the states written above are read back below through global
+  // memory by other threads of this workgroup: make them visible.
   __threadfence_block();
   __syncthreads();
 
-  // ---- phase 2: reverse ----
-  Tile D, Pn;
+  // ---- phase 2: reverse, one block at a time in matrix form ----
+  using TO = IO;                             // MFMA operand type
+  RevLds<DK, TO>& L = sm.rev;
+  const int g4 = lane >> 4, n = lane & 15;
+  const bool colw = wave < 4;                // column waves own D tiles of columns 16 wave..
+  const int ct = wave & 3;                   // a column wave's column tile
+  const int ch = 16 * wave + n;              // this lane's channel in the row-gradient tiles
+  const int64_t colg = (int64_t)cb * kCols;  // first value column of the workgroup
+
+  // Dt[c]: accL(D^T) tile (columns 16c.., rows 16 wave..): D[ch][16c + 4 g4 + ii].
+  // Dc[rb]: accL(D) tile (rows 16rb.., columns 16 ct..): D[16rb + 4 g4 + ii][16 ct + n].
+  f32x4 Dt[4], Dc[RB];
+  float Sf[4][4], Sn[4][4];                  // S[ch][16c + 4 g4 + ii]: block entry states
+  {
+    const float* dso = p.d_state_out ? p.d_state_out + head * (int64_t)DK * p.dv + colg : nullptr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ld4f(ck_at(nblk, i), Pn[i]);
-    if (p.d_state_out) ld4f(p.d_state_out + (head * DK + r0 + i) * p.dv + c0, D[i]);
-    else D[i][0] = D[i][1] = D[i][2] = D[i][3] = 0.f;
+    for (int c = 0; c < 4; ++c) {
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (dso) ld4f(dso + (int64_t)ch * p.dv + 16 * c + 4 * g4, x);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) Dt[c][ii] = x[ii];
+      ld4f(ck + ((nblk - 1) * DK + ch) * kCols + 16 * c + 4 * g4, Sn[c]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        Dc[rb][ii] = (dso && colw) ? dso[(int64_t)(16 * rb + 4 * g4 + ii) * p.dv + 16 * ct + n] : 0.f;
   }
-
-  // P_{t+1} = abar P_t + k u^T with the staged u.
-  auto advance = [&](const Stage<DK>& st, Tile& X, int tl) {
-    float k[4], e[4], bb[4], a[4], u[4];
-    rows_of<DK, CHANNEL>(st, tl, r0, k, e, bb, a);
-    ld4f(&st.u[tl][cl], u);
+  // A column wave's own v, w of its column tile (4 tokens per lane), a block ahead.
+  IO vr[4];
+  GT wr[4];
+  auto issue_vw = [&](int64_t t0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) X[i][j] = a[i] * X[i][j] + k[i] * u[j];
+    for (int ii = 0; ii < 4; ++ii) {
+      int64_t t = t0 + 4 * g4 + ii;
+      t = t < T ? t : T - 1;
+      const int64_t off = ((tok0 + t) * p.Hv + hv) * p.dv + colg + 16 * ct + n;
+      vr[ii] = static_cast<const IO*>(p.v)[off];
+      if constexpr (CHANNEL) wr[ii] = static_cast<const GT*>(p.w)[off];
+    }
   };
+  RevLoad<DK, CHANNEL, HAS_G, IO, GT> ld;
+  ld.issue(p, tok0, T, hv, hk, cb, (nblk - 1) * kCkpt, tid);
+  issue_vw((nblk - 1) * kCkpt);
+  // Wait here for everything loaded so far: the block loop then holds no
+  // value whose load is still pending on entry, so the compiler need not
+  // drain each block's prefetches at its top.
+  __builtin_amdgcn_s_waitcnt(0);
 
-  // Reverse step of token t: Pb = P_t, Pa = P_{t+1}, D = dL/dP_{t+1} -> dL/dP_t.
-  auto reverse = [&](const Stage<DK>& st, const Tile& Pb, const Tile& Pa, int tl, int64_t t) {
-    const int64_t bth = (tok0 + t) * p.Hv + hv;
-    float k[4], e[4], bb[4], a[4], w[4], v[4], dO[4], q[4], u[4];
-    rows_of<DK, CHANNEL>(st, tl, r0, k, e, bb, a);
-    wgate_of<DK, CHANNEL>(st, tl, cl, w);
-    ld4f(&st.v[tl][cl], v);
-    ld4f(&st.dO[tl][cl], dO);
-    ld4f(&st.q[tl][r0], q);
-    ld4f(&st.u[tl][cl], u);
-    float dq[4], du[4];
+  for (int64_t mm = 0; mm < nblk; ++mm) {
+    const int64_t m = nblk - 1 - mm;
+    const int64_t t0 = m * kCkpt;
+    const int nt = (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
+    const int64_t mp = m > 0 ? m - 1 : 0;    // the next block (or this one again)
+
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s = 0.f;
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        D[i][j] += scale * q[i] * dO[j];
-        s += Pa[i][j] * dO[j];
+      for (int ii = 0; ii < 4; ++ii) Sf[c][ii] = Sn[c][ii];
+    // rowsum(D (.) S) of the incoming D with the entry state
+    float dps = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) dps += Dt[c][ii] * Sf[c][ii];
+    dps += __shfl_xor(dps, 16);
+    dps += __shfl_xor(dps, 32);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ld4f(ck + (mp * DK + ch) * kCols + 16 * c + 4 * g4, Sn[c]);
+
+    ld.store(L, tid);
+    if (tid == 0) L.unsafe = 0;
+    float vv[4], wv[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      vv[ii] = to_f32(vr[ii]);
+      wv[ii] = CHANNEL ? to_f32(wr[ii]) : 0.f;
+    }
+    lds_barrier();
+    ld.issue(p, tok0, T, hv, hk, cb, mp * kCkpt, tid);
+    if (colw) issue_vw(mp * kCkpt);
+
+    // ---- cumulative decay, factors and gated operands (thread: channel i, tokens 4 qt..) ----
+    {
+      const int i = tid % DK, qt = tid / DK;
+      float acc = 0.f, ref = 0.f, G[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < kCkpt; ++r) {
+        acc += CHANNEL ? L.gl[r][i] : L.sgl[r];
+        if (r == 7) ref = acc;
+        if ((r >> 2) == qt) G[r & 3] = acc;
       }
-      dq[i] = scale * s;
+      const float lend = acc;
+      if (qt == 0) {
+        L.ref[i] = ref;
+        L.lend[i] = lend;
+        L.gend[i] = exp2_fast(lend);
+      }
+      st4f(&L.Gl[i][4 * qt], G);
+      float kf[4], qf[4], ef[4], qg[4], eg[4];
+      bool bad = false;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int s = 4 * qt + ii;
+        const float kk = L.k[s][i], qq = L.q[s][i];
+        const float e = (CHANNEL ? L.b[s][i] : L.sb[s]) * kk;
+        const float gs = exp2_fast(G[ii]), ge = exp2_fast(lend - G[ii]);
+        const float fq = CHANNEL ? exp2_fast(G[ii] - ref) : 1.f;
+        const float fk = CHANNEL ? exp2_fast(ref - G[ii]) : 1.f;
+        if (CHANNEL) bad |= fabsf(G[ii] - ref) > kSafeLog2;
+        kf[ii] = kk * fk;
+        qf[ii] = qq * fq;
+        ef[ii] = e * fq;
+        qg[ii] = scale * qq * gs;
+        eg[ii] = -e * gs;
+        L.Kg[s][i] = from_f32<TO>(kk * ge);
+        L.Kf[s][i] = from_f32<TO>(kf[ii]);
+        L.Qf[s][i] = from_f32<TO>(qf[ii]);
+        L.Ef[s][i] = from_f32<TO>(ef[ii]);
+      }
+      st4<TO>(&L.KfT[i][4 * qt], kf[0], kf[1], kf[2], kf[3]);
+      st4<TO>(&L.QfT[i][4 * qt], qf[0], qf[1], qf[2], qf[3]);
+      st4<TO>(&L.EfT[i][4 * qt], ef[0], ef[1], ef[2], ef[3]);
+      st4<TO>(&L.QgT[i][4 * qt], qg[0], qg[1], qg[2], qg[3]);
+      st4<TO>(&L.EgT[i][4 * qt], eg[0], eg[1], eg[2], eg[3]);
+      if (bad) L.unsafe = 1;
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s += D[i][j] * k[i];
-      du[j] = s;
+    lds_barrier();
+    const bool exact = CHANNEL && L.unsafe != 0;   // uniform over the workgroup
+
+    if (exact) {
+      // Gram matrices term by term: A[s][t] = sum_i e_s k_t 2^(Gl_s - Gl_t).
+      if (tid < kCkpt * kCkpt) {
+        const int s = tid >> 4, t = tid & 15;
+        float sa = 0.f, sp = 0.f;
+        if (s >= t) {
+          for (int i = 0; i < DK; ++i) {
+            const float kt = L.k[t][i] * exp2_fast(L.Gl[i][s] - L.Gl[i][t]);
+            sa += L.b[s][i] * L.k[s][i] * kt;
+            sp += L.q[s][i] * kt;
+          }
+        }
+        L.A[s][t] = s > t ? sa : 0.f;
+        L.P[s][t] = s >= t ? sp : 0.f;
+      }
+      lds_barrier();
     }
-    row_reduce<NW>(du, red, buf, lane, wave, cg);
-    if (rg == 0) {
-      float dvv[4];
+
+    // ---- column waves: DU tile = (I + A^T)^{-1} RHS, dv, dw, D tiles ----
+    f32x4 du = {0.f, 0.f, 0.f, 0.f};
+    if (colw) {
+      Frag4<float> nr, nc;   // rowL(N), accL(N), N = -A
+      Frag4<TO> pT;          // rowL(scale Pm^T) = scale accL(Pm)
+      if (!exact) {
+        f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aAt = aA, aP = aA;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dvv[j] = w[j] * du[j];
-      st4f(p.dv_out + bth * p.dv + c0, dvv);
-      if constexpr (CHANNEL) {
-        float dww[4];
+        for (int kb = 0; kb < RB; ++kb) {
+          const Frag4<TO> ef = ld_frag4<TO>(&L.Ef[n][16 * kb + 4 * g4]);
+          const Frag4<TO> kf = ld_frag4<TO>(&L.Kf[n][16 * kb + 4 * g4]);
+          const Frag4<TO> qf = ld_frag4<TO>(&L.Qf[n][16 * kb + 4 * g4]);
+          mma16(aA, ef, kf);    // A[4g+ii][n]
+          mma16(aAt, kf, ef);   // A[n][4g+ii]
+          mma16(aP, qf, kf);    // Pm[4g+ii][n]
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dww[j] = v[j] * du[j];
-        st4f(p.dw + bth * p.dv + c0, dww);
+        for (int ii = 0; ii < 4; ++ii) {
+          const int r = 4 * g4 + ii;
+          float grn = 1.f, gnr = 1.f;
+          if constexpr (!CHANNEL) {
+            grn = r >= n ? token_decay(L, r, n) : 0.f;
+            gnr = n >= r ? token_decay(L, n, r) : 0.f;
+          }
+          nc.v[ii] = n < r ? -aA[ii] * grn : 0.f;
+          nr.v[ii] = r < n ? -aAt[ii] * gnr : 0.f;
+          pT.v[ii] = from_f32<TO>(r >= n ? scale * aP[ii] * grn : 0.f);
+        }
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int r = 4 * g4 + ii;
+          nc.v[ii] = -L.A[r][n];
+          nr.v[ii] = -L.A[n][r];
+          pT.v[ii] = from_f32<TO>(scale * L.P[r][n]);
+        }
+      }
+      // (I + A)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0), as accL.
+      auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        mma16(a, x, y);
+        return f32frag(a);
+      };
+      const Frag4<float> n2c = prod(nr, nc), n2r = prod(nc, nr);
+      const Frag4<float> n4c = prod(n2r, n2c), n4r = prod(n2c, n2r);
+      const Frag4<float> n8c = prod(n4r, n4c);
+      f32x4 tinv;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) tinv[ii] = n8c.v[ii] + (4 * g4 + ii == n ? 1.f : 0.f);
+      mma16(tinv, n4r, f32frag(tinv));
+      mma16(tinv, n2r, f32frag(tinv));
+      mma16(tinv, nr, f32frag(tinv));
+      // RHS = (k ge) D + scale Pm^T dO for this column tile
+      f32x4 rhs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        mma16(rhs, ld_frag4<TO>(&L.Kg[n][16 * rb + 4 * g4]), frag4_from_acc<TO>(Dc[rb]));
+      const Frag4<TO> dot = ld_frag4<TO>(&L.dOt[16 * ct + n][4 * g4]);   // accL(dO tile)
+      mma16(rhs, pT, dot);
+      mma16(du, f32frag(tinv), f32frag(rhs));   // DU = Tinv^T RHS
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) L.DUr[4 * g4 + ii][16 * ct + n] = from_f32<TO>(du[ii]);
+      st4<TO>(&L.DUt[16 * ct + n][4 * g4], du[0], du[1], du[2], du[3]);
+      // dv = w du, dw = v du (scalar gates: w = beta, and sum_j v du goes to dbeta)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int s = 4 * g4 + ii;
+        const float wgt = CHANNEL ? wv[ii] : L.sb[s];
+        if (s < nt) {
+          const int64_t o = ((tok0 + t0 + s) * p.Hv + hv) * p.dv + colg + 16 * ct + n;
+          p.dv_out[o] = wgt * du[ii];
+          if constexpr (CHANNEL) p.dw[o] = vv[ii] * du[ii];
+        }
+        if constexpr (!CHANNEL) {
+          const float x = row16_sum(vv[ii] * du[ii]);
+          if (n == 0) L.vs[ct][s] = x;
+        }
+      }
+      // D tiles: D <- Diag(gend) D + (scale gs q)^T dO - (gs e)^T DU
+      const Frag4<TO> duf = frag4_from_acc<TO>(du);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float4 ge4 = *reinterpret_cast<const float4*>(&L.gend[16 * rb + 4 * g4]);
+        Dc[rb][0] *= ge4.x; Dc[rb][1] *= ge4.y; Dc[rb][2] *= ge4.z; Dc[rb][3] *= ge4.w;
+        mma16(Dc[rb], ld_frag4<TO>(&L.QgT[16 * rb + n][4 * g4]), dot);
+        mma16(Dc[rb], ld_frag4<TO>(&L.EgT[16 * rb + n][4 * g4]), duf);
+      }
+    }
+
+    // ---- every wave: row-gradient tiles of channels 16 wave .. (tokens 4 g4 + ii) ----
+    Frag4<TO> sfr[4], ua[4], doa[4];
+    f32x4 dQi = {0.f, 0.f, 0.f, 0.f}, dKi = dQi, m3 = dQi, m3t = dQi, dQa = dQi, dKa = dQi;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sfr[c] = frag4_of<TO>(Sf[c]);                        // accL(S^T) tile
+      ua[c] = ld_frag4<TO>(&L.Ur[n][16 * c + 4 * g4]);     // rowL(U)
+      doa[c] = ld_frag4<TO>(&L.dOr[n][16 * c + 4 * g4]);   // rowL(dO)
+      mma16(dQi, doa[c], sfr[c]);                          // dO S^T
+      mma16(dKi, ua[c], frag4_from_acc<TO>(Dt[c]));        // U D^T
+      mma16(m3, ua[c], doa[c]);                            // M3[4g+ii][n]
+      mma16(m3t, doa[c], ua[c]);                           // M3[n][4g+ii]
+    }
+    // M3[s][s] for this lane's tokens (the diagonal pairs are added apart)
+    float d3[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) d3[ii] = __shfl(m3[ii], 20 * g4 + ii);
+    const Frag4<TO> kfb = ld_frag4<TO>(&L.KfT[ch][4 * g4]);   // accL(Kf) tile
+    const Frag4<TO> qfb = ld_frag4<TO>(&L.QfT[ch][4 * g4]);
+    const Frag4<TO> efb = ld_frag4<TO>(&L.EfT[ch][4 * g4]);
+    if (!exact) {
+      Frag4<TO> a1, a2;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = 4 * g4 + ii;
+        float gnr = 1.f, grn = 1.f;
+        if constexpr (!CHANNEL) {
+          gnr = n >= r ? token_decay(L, n, r) : 0.f;
+          grn = r >= n ? token_decay(L, r, n) : 0.f;
+        }
+        a1.v[ii] = from_f32<TO>(r < n ? m3[ii] * gnr : 0.f);            // X[s=n][t=r]
+        a2.v[ii] = from_f32<TO>(r > n ? scale * m3t[ii] * grn : 0.f);   // Y[t=n][s=r]
+      }
+      mma16(dQa, a1, kfb);
+      mma16(dKa, a2, qfb);
+    } else if (wave == 0) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) L.M3[4 * g4 + ii][n] = m3[ii];
+    }
+    lds_barrier();   // DU tiles (and the exact path's M3) visible
+
+    f32x4 dEi = {0.f, 0.f, 0.f, 0.f}, m4 = dEi, m4t = dEi, dEa = dEi;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const Frag4<TO> dua = ld_frag4<TO>(&L.DUr[n][16 * c + 4 * g4]);
+      mma16(dEi, dua, sfr[c]);     // DU S^T
+      mma16(m4, ua[c], dua);       // M4[4g+ii][n]
+      mma16(m4t, dua, ua[c]);      // M4[n][4g+ii]
+    }
+    if (!exact) {
+      Frag4<TO> a3, a4;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = 4 * g4 + ii;
+        float gnr = 1.f, grn = 1.f;
+        if constexpr (!CHANNEL) {
+          gnr = n >= r ? token_decay(L, n, r) : 0.f;
+          grn = r >= n ? token_decay(L, r, n) : 0.f;
+        }
+        a3.v[ii] = from_f32<TO>(r < n ? m4[ii] * gnr : 0.f);     // X[s=n][t=r]
+        a4.v[ii] = from_f32<TO>(r > n ? -m4t[ii] * grn : 0.f);   // Y[t=n][s=r]
+      }
+      mma16(dEa, a3, kfb);
+      mma16(dKa, a4, efb);
+    }
+    // D^T tiles: D^T <- D^T Diag(gend) + dO^T (scale gs q) - DU^T (gs e)
+    {
+      const Frag4<TO> qgb = ld_frag4<TO>(&L.QgT[ch][4 * g4]);
+      const Frag4<TO> egb = ld_frag4<TO>(&L.EgT[ch][4 * g4]);
+      const float gi = L.gend[ch];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) Dt[c][ii] *= gi;
+        mma16(Dt[c], ld_frag4<TO>(&L.dOt[16 * c + n][4 * g4]), qgb);
+        mma16(Dt[c], ld_frag4<TO>(&L.DUt[16 * c + n][4 * g4]), egb);
+      }
+    }
+    if (exact) {
+      if (wave == 0) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) L.M4[4 * g4 + ii][n] = m4[ii];
+      }
+      lds_barrier();
+      // intra-block terms term by term, with 2^(Gl_s - Gl_t) for s > t
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int s = 4 * g4 + ii;
+        const float Gs = L.Gl[ch][s];
+        float aq = 0.f, ae = 0.f, ak = 0.f;
+        for (int t2 = 0; t2 < kCkpt; ++t2) {
+          const float Gt = L.Gl[ch][t2];
+          if (t2 < s) {
+            const float kg = L.k[t2][ch] * exp2_fast(Gs - Gt);
+            aq += L.M3[t2][s] * kg;
+            ae += L.M4[t2][s] * kg;
+          }
+          if (t2 > s) {
+            const float x = scale * L.M3[s][t2] * L.q[t2][ch] -
+                            L.M4[s][t2] * L.b[t2][ch] * L.k[t2][ch];
+            ak += x * exp2_fast(Gt - Gs);
+          }
+        }
+        dQa[ii] = aq;
+        dEa[ii] = ae;
+        dKa[ii] = ak;
+      }
+    }
+
+    // ---- combine and write the partial row gradients ----
+    {
+      const float4 G4 = *reinterpret_cast<const float4*>(&L.Gl[ch][4 * g4]);
+      const float Gv[4] = {G4.x, G4.y, G4.z, G4.w};
+      const float ref = L.ref[ch], lend = L.lend[ch];
+      const bool fac = CHANNEL && !exact;
+      const int send = nt - 1;   // the block's last token
+      // dG: every pair of terms that share a decay factor contributes once
+      // at each end, so the pairs whose factor is identically 1 -- the
+      // diagonal (s, s) and the last token's own share of the exit state --
+      // are left out of both ends; with them in, dG would be a difference
+      // of O(1) terms where the true value underflows.
+      float dq[4], dk[4], db[4], dG[4], pend = 0.f;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int s = 4 * g4 + ii;
+        const float G = Gv[ii];
+        const float gs = exp2_fast(G), ge = exp2_fast(lend - G);
+        const float fq = fac ? exp2_fast(G - ref) : 1.f;
+        const float fk = fac ? exp2_fast(ref - G) : 1.f;
+        const float kk = L.k[s][ch], qq = L.q[s][ch];
+        const float bb = CHANNEL ? L.b[s][ch] : L.sb[s];
+        const float dQo = scale * (gs * dQi[ii] + fq * dQa[ii]);   // off-diagonal part
+        const float dE = -(gs * dEi[ii] + fq * dEa[ii]);
+        const float K1i = ge * dKi[ii], K1a = fk * dKa[ii];
+        const float dgn = scale * d3[ii];                          // diagonal: scale M3[s][s]
+        dq[ii] = dQo + dgn * kk;
+        dk[ii] = K1i + K1a + dgn * qq + bb * dE;
+        db[ii] = kk * dE;
+        dG[ii] = qq * dQo + bb * kk * dE - kk * (K1a + (s == send ? 0.f : K1i));
+        if (s < send) pend += kk * K1i;   // the exit state's k u^T terms
+      }
+      pend += __shfl_xor(pend, 16);
+      pend += __shfl_xor(pend, 32);
+      if (g4 == 3) dG[3] += L.gend[ch] * dps + pend;
+      // dg = reverse cumulative sum of dG over the block's tokens
+      dG[2] += dG[3];
+      dG[1] += dG[2];
+      dG[0] += dG[1];
+      const float t1 = __shfl(dG[0], n + 16), t2 = __shfl(dG[0], n + 32);
+      const float t3 = __shfl(dG[0], n + 48);
+      const float after = (g4 < 1 ? t1 : 0.f) + (g4 < 2 ? t2 : 0.f) + (g4 < 3 ? t3 : 0.f);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int s = 4 * g4 + ii;
+        if (s < nt) {
+          const int64_t row = (tok0 + t0 + s) * p.Hv + hv;
+          float* pp = p.part + ((int64_t)cb * 4 * NR + row) * DK + ch;
+          pp[0] = dq[ii];
+          pp[NR * DK] = dk[ii];
+          pp[2 * NR * DK] = db[ii];
+          pp[3 * NR * DK] = dG[ii] + after;
+        }
       }
     }
     if constexpr (!CHANNEL) {
-      float ws = v[0] * du[0] + v[1] * du[1] + v[2] * du[2] + v[3] * du[3];
-      ws = row16_sum(ws);
-      if (tid == 0) p.part[(int64_t)ncb * 4 * NR * DK + (int64_t)cb * NR + bth] = ws;
-    }
-    float de[4], dk[4], da[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s = 0.f, sk = 0.f, sa = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s += Pb[i][j] * du[j];
-        sk += D[i][j] * u[j];
-        const float dsb = D[i][j] - e[i] * du[j];
-        sa += dsb * Pb[i][j];
-        D[i][j] = a[i] * dsb;
+      if (tid < nt) {
+        const int64_t row = (tok0 + t0 + tid) * p.Hv + hv;
+        p.part[(int64_t)ncb * 4 * NR * DK + (int64_t)cb * NR + row] =
+            L.vs[0][tid] + L.vs[1][tid] + L.vs[2][tid] + L.vs[3][tid];
       }
-      de[i] = -a[i] * s;
-      dk[i] = sk;
-      da[i] = sa;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dq[i] = row16_sum(dq[i]);
-      de[i] = row16_sum(de[i]);
-      dk[i] = row16_sum(dk[i]);
-      da[i] = row16_sum(da[i]);
-    }
-    if (cg < 4) {
-      float out[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        out[i] = cg == 0 ? dq[i]
-               : cg == 1 ? dk[i] + bb[i] * de[i]
-               : cg == 2 ? k[i] * de[i]
-                         : a[i] * da[i];
-      }
-      st4f(p.part + (((int64_t)cb * 4 + cg) * NR + bth) * DK + r0, out);
-    }
-  };
-
-  {
-    BlockLoad<DK, CHANNEL, HAS_G, true, IO, GT> ld;
-    ld.issue(p, tok0, T, hv, hk, cb, (nblk - 1) * kCkpt, tid);
-    ld.store(stg[0], tid);
-    Tile Ck, Cn;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ld4f(ck_at(nblk - 1, i), Ck[i]);
-    // Wait here for everything loaded so far (D, Ck, the first block): the
-    // block loop below then holds no value whose load is still pending on
-    // entry, so the compiler need not drain the prefetches of each block
-    // before its token loop.
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_barrier();
-    for (int64_t mm = 0; mm < nblk; ++mm) {
-      const int64_t m = nblk - 1 - mm;
-      const int cur = (int)(mm & 1);
-      const bool more = m > 0;
-      const int64_t mp = more ? m - 1 : m;   // the next block (or this one again)
-      ld.issue(p, tok0, T, hv, hk, cb, mp * kCkpt, tid);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ld4f(ck_at(mp, i), Cn[i]);
-      const Stage<DK>& st = stg[cur];
-      const int64_t t0 = m * kCkpt;
-      const int nt = (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
-      for (int s = kSubs - 1; s >= 0; --s) {
-        const int ts = s * kSub;                // first token of the sub-block (local)
-        if (ts >= nt) continue;
-        const int n = (nt - ts) < kSub ? (nt - ts) : kSub;
-        Tile R[kSub];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) R[0][i][c] = Ck[i][c];
-        for (int tl = 0; tl < ts; ++tl) advance(st, R[0], tl);
-#pragma unroll
-        for (int j = 1; j < kSub; ++j) {
-          if (j < n) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int c = 0; c < 4; ++c) R[j][i][c] = R[j - 1][i][c];
-            advance(st, R[j], ts + j - 1);
-          }
-        }
-#pragma unroll
-        for (int j = kSub - 1; j >= 0; --j) {
-          if (j < n) {
-            reverse(st, R[j], Pn, ts + j, t0 + ts + j);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int c = 0; c < 4; ++c) Pn[i][c] = R[j][i][c];
-          }
-        }
-      }
-      ld.store(stg[cur ^ 1], tid);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) Ck[i][c] = Cn[i][c];
-      lds_barrier();
-    }
+    lds_barrier();   // the block's LDS is rewritten by the next one
   }
   if (p.d_state_in) {
+    float* dsi = p.d_state_in + head * (int64_t)DK * p.dv + colg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st4f(p.d_state_in + (head * DK + r0 + i) * p.dv + c0, D[i]);
+    for (int c = 0; c < 4; ++c) {
+      const float x[4] = {Dt[c][0], Dt[c][1], Dt[c][2], Dt[c][3]};
+      st4f(dsi + (int64_t)ch * p.dv + 16 * c + 4 * g4, x);
+    }
   }
 }
 

@@ -1,10 +1,11 @@
 """GPU parity of gdn_backward (gradients of the recurrence) against the CPU
 oracle's reverse-mode pass, through the C ABI.
 
-Both sides see the same input values (bf16 inputs are widened exactly); the
-GPU works in fp32 throughout, so the bar is the fp32 tolerance for fp32
-inputs and the bf16 one otherwise, on every gradient tensor (normwise
-max-relative error, as for the forward).
+Both sides see the same input values (bf16 inputs are widened exactly).  The
+GPU's matrix products take bf16 operands for bf16 inputs and fp32 operands
+for fp32 inputs (state and accumulation in fp32), so the bar is the fp32
+tolerance for fp32 inputs and the bf16 one otherwise, on every gradient
+tensor (normwise max-relative error, as for the forward).
 """
 import numpy as np
 import pytest
@@ -86,6 +87,37 @@ def test_backward_without_decay_state_or_final_gradient(channel):
     got = _run(inp, d_o, d_sT, with_g=False, use_dsT=False)
     torch.cuda.synchronize()
     _compare(got, _ref(inp, d_o, d_sT, with_g=False, use_dsT=False), TOL_FP32, "plain")
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("channel", [True, False])
+def test_backward_strong_decay(io, channel):
+    """Log-decay of -30 per token: with per-channel gates every block is
+    outside the range of the factored operands and takes the term-by-term
+    path; with scalar gates the decay mask underflows to zero off the
+    diagonal.  Both must stay finite and match."""
+    announce(f"backward g=-30 channel={channel} io={io}")
+    inp, d_o, d_sT = _case(1, 45, 1, 2, 128, 128, channel, io)
+    inp["g"] = torch.full_like(inp["g"], -30.0)
+    got = _run(inp, d_o, d_sT, scale=0.9)
+    torch.cuda.synchronize()
+    _compare(got, _ref(inp, d_o, d_sT, scale=0.9), tol_for(io), "g=-30")
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_backward_mixed_decay_blocks(io):
+    """Per-channel gates with a strong decay in some channels of the second
+    block only (that block takes the term-by-term path, the others the
+    factored one) and a decay of -5 per token elsewhere (near the edge of the
+    factored range)."""
+    announce(f"backward mixed decay io={io}")
+    inp, d_o, d_sT = _case(2, 70, 1, 2, 128, 128, True, io)
+    g = torch.full_like(inp["g"], -5.0)
+    g[:, 16:32, :, ::7] = -40.0
+    inp["g"] = g.to(inp["g"].dtype)
+    got = _run(inp, d_o, d_sT)
+    torch.cuda.synchronize()
+    _compare(got, _ref(inp, d_o, d_sT), tol_for(io), "mixed")
 
 
 def test_backward_grouped_heads_sum_dq_dk():
