@@ -23,7 +23,9 @@
 //   dk = ge (.) U D^T + [sum_{s>=t} (scale M3[t][s] q_s - [s>t] M4[t][s] e_s) Gamma_st] + b (.) de
 //   db = k (.) de,  dv = w (.) DU,  dw = v (.) DU,
 //   dG_s = q dq + e de - k dk1 (+ rowsum(D (.) P_end) at the last token),
-//   dg = reverse cumulative sum of dG over the block,
+//   dg = reverse cumulative sum of dG over the block
+//   (evaluated without the pairs of terms that cancel identically; see the
+//   combine step),
 //   D <- Diag(gend) D + scale (gs q)^T dO - (gs e)^T DU.
 // The bracketed sums are intra-block.  They and A, Pm are products over the
 // channel with a per-channel decay; they factor as exp(G_s - ref) exp(ref - G_t)
@@ -33,16 +35,19 @@
 // gates the decay is a 16 x 16 mask and the factors are 1.
 //
 // Layout: one workgroup per (sequence, value head, block of 64 value
-// columns), DK * 4 threads.  Phase 1 runs the recurrence forward from the
-// initial state, storing the state every 16 tokens, the final state and every
-// u_t in the workspace (a wave holds all DK rows of a few columns, so the read
-// r is an in-wave butterfly).  Phase 2 walks the blocks backwards with the
-// exit-state gradient in MFMA accumulators -- wave w holds D rows
-// 16w..16w+15 as D^T tiles, waves 0-3 also D columns 16w..16w+15 over all
-// rows as D tiles -- and evaluates the block form above.  The per-row
-// gradients (dq, dk, db, dg) are partial over the column block; they go to
-// the workspace and a second kernel sums them over column blocks and over the
-// value heads of a key head.
+// columns), DK * 4 threads; waves 0-3 are "column waves", one per 16-column
+// tile.  Phase 1 runs the forward in the same 16-token blocks from the
+// initial state -- U = (I + A)^{-1} (Z - (gs e) S), S' = Diag(gend) S +
+// (ge k)^T U, the state tiles in the column waves' MFMA accumulators -- and
+// stores the entry state of every block, the final state and every u_t in
+// the workspace.  Phase 2 walks the blocks backwards with the exit-state
+// gradient D held by every wave w as D^T tiles of rows 16w..16w+15 (bf16
+// operands: also as a bf16 copy in LDS for the column waves' (k ge) D) and
+// evaluates the block form above.  The per-row gradients (dq, dk, db, dg) are
+// partial over the column block; they go to the workspace and a second
+// kernel sums them over column blocks and over the value heads of a key head.
+// Only the first block walked in each phase can be short, so the others are
+// compiled without per-token guards.
 #include "chunk_common.hpp"
 
 #include <type_traits>
@@ -114,95 +119,78 @@ __device__ __forceinline__ void unpack_raw(const RawN<T, N>& r, float* o) {
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1: one block's token inputs (row side k, b, abar over all DK rows;
-// column side v, w over the workgroup's 64 columns; scalar gates per token).
+// Phase 1 (forward rebuild) in LDS: one block's row inputs, the gated
+// operands of U = (I + A)^{-1} (Z - (gs e) S) and S' = Diag(gend) S +
+// (ge k)^T U, and the cumulative decay.  Fragment layouts as in phase 2
+// (below).
 // ---------------------------------------------------------------------------
-template <int DK>
-struct FwdStage {
-  float k[kCkpt][DK], b[kCkpt][DK], a[kCkpt][DK];
-  float v[kCkpt][kCols], w[kCkpt][kCols];
-  float sb[kCkpt], sa[kCkpt];
+template <int DK, typename T>
+struct FwdLds {
+  static constexpr int RP = DK + 4;
+  static constexpr int OP = DK + 16 / (int)sizeof(T);
+  static constexpr int TP = 20;
+  float k[kCkpt][RP], b[kCkpt][RP], gl[kCkpt][RP];   // inputs (fp32)
+  T Kf[kCkpt][OP], Ef[kCkpt][OP], Egm[kCkpt][OP];    // k fk, e fq, -e gs  [token][channel]
+  T KgT[DK][TP];                                     // k ge  [channel][token]
+  float Gl[DK][TP];                                  // cumulative log2-decay
+  float gend[DK];
+  float A[kCkpt][kCkpt + 1];                         // exact Gram matrix
+  float sb[kCkpt], sgl[kCkpt];
+  int unsafe;
 };
 
-// A thread's share of loading one block: 4 row elements of one token, CPT
-// column elements of one token.  Every load is issued unconditionally (token
-// index clamped into the sequence), so the compiler's count of outstanding
-// loads is the same on every path and nothing waits for them before store().
+// A thread's share of one block's row inputs (4 channels of one token).
 template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT>
 struct FwdLoad {
-  static constexpr int NT = DK * 4;
-  static constexpr int TPR = DK / 4;                // threads per token (rows)
-  static constexpr int CPT = kCkpt * kCols / NT;    // column elements per thread
-  static constexpr int TPC = kCols / CPT;           // threads per token (columns)
+  static constexpr int TPR = DK / 4;
   RawN<IO, 4> k;
   RawN<GT, 4> b, g;
-  RawN<IO, CPT> v;
-  RawN<GT, CPT> w;
   float sb, sg;
-  bool rv, cv;   // the row / column token exists (loads past T read token T-1)
+  bool rv;
 
   __device__ __forceinline__ void issue(const BwdArgs& p, int64_t tok0, int64_t Tn, int hv,
-                                        int hk, int cb, int64_t t0, int tid) {
+                                        int hk, int64_t t0, int tid) {
     const int tr = tid / TPR, i0 = 4 * (tid % TPR);
-    const int tc = tid / TPC, j0 = CPT * (tid % TPC);
-    const int64_t trr = t0 + tr, tcc = t0 + tc;
+    const int64_t trr = t0 + tr;
     rv = trr < Tn;
-    cv = tcc < Tn;
-    {
-      const int64_t t = rv ? trr : Tn - 1;
-      const int64_t bt = tok0 + t, bth = bt * p.Hv + hv;
-      load_raw<IO, 4>(static_cast<const IO*>(p.k) + (bt * p.Hk + hk) * DK + i0, k);
-      if constexpr (CHANNEL) {
-        load_raw<GT, 4>(static_cast<const GT*>(p.b) + bth * DK + i0, b);
-        if constexpr (HAS_G) load_raw<GT, 4>(static_cast<const GT*>(p.g) + bth * DK + i0, g);
-      } else {
-        sb = to_f32(static_cast<const GT*>(p.b)[bth]);
-        sg = HAS_G ? to_f32(static_cast<const GT*>(p.g)[bth]) : 0.f;
-      }
-    }
-    {
-      const int64_t t = cv ? tcc : Tn - 1;
-      const int64_t off = ((tok0 + t) * p.Hv + hv) * p.dv + (int64_t)cb * kCols + j0;
-      load_raw<IO, CPT>(static_cast<const IO*>(p.v) + off, v);
-      if constexpr (CHANNEL) load_raw<GT, CPT>(static_cast<const GT*>(p.w) + off, w);
+    const int64_t t = rv ? trr : Tn - 1;
+    const int64_t bt = tok0 + t, bth = bt * p.Hv + hv;
+    load_raw<IO, 4>(static_cast<const IO*>(p.k) + (bt * p.Hk + hk) * DK + i0, k);
+    if constexpr (CHANNEL) {
+      load_raw<GT, 4>(static_cast<const GT*>(p.b) + bth * DK + i0, b);
+      if constexpr (HAS_G) load_raw<GT, 4>(static_cast<const GT*>(p.g) + bth * DK + i0, g);
+    } else {
+      sb = to_f32(static_cast<const GT*>(p.b)[bth]);
+      sg = HAS_G ? to_f32(static_cast<const GT*>(p.g)[bth]) : 0.f;
     }
   }
 
-  // Writes the block to LDS; tokens past T are stored as zeros.
-  __device__ __forceinline__ void store(FwdStage<DK>& st, int tid) const {
+  // Tokens past T are stored as zeros with zero log-decay.
+  template <typename T>
+  __device__ __forceinline__ void store(FwdLds<DK, T>& F, int tid) const {
     const int tr = tid / TPR, i0 = 4 * (tid % TPR);
-    const int tc = tid / TPC, j0 = CPT * (tid % TPC);
-    const float mr = rv ? 1.f : 0.f, mc = cv ? 1.f : 0.f;
+    const float mr = rv ? 1.f : 0.f;
     float x[4];
     unpack_raw<IO, 4>(k, x);
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] *= mr;
-    st4f(&st.k[tr][i0], x);
+    st4f(&F.k[tr][i0], x);
     if constexpr (CHANNEL) {
       unpack_raw<GT, 4>(b, x);
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] *= mr;
-      st4f(&st.b[tr][i0], x);
+      st4f(&F.b[tr][i0], x);
       if constexpr (HAS_G) {
         unpack_raw<GT, 4>(g, x);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = exp2_fast(x[i] * kLog2e);
+        for (int i = 0; i < 4; ++i) x[i] *= kLog2e * mr;
       } else {
-        x[0] = x[1] = x[2] = x[3] = 1.f;
+        x[0] = x[1] = x[2] = x[3] = 0.f;
       }
-      st4f(&st.a[tr][i0], x);
+      st4f(&F.gl[tr][i0], x);
     } else if (i0 == 0) {
-      st.sb[tr] = sb * mr;
-      st.sa[tr] = HAS_G ? exp2_fast(sg * kLog2e) : 1.f;
-    }
-    float y[CPT];
-    unpack_raw<IO, CPT>(v, y);
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) st.v[tc][j0 + j] = y[j] * mc;
-    if constexpr (CHANNEL) {
-      unpack_raw<GT, CPT>(w, y);
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) st.w[tc][j0 + j] = y[j] * mc;
+      F.sb[tr] = sb * mr;
+      F.sgl[tr] = HAS_G ? sg * kLog2e * mr : 0.f;
     }
   }
 };
@@ -233,6 +221,10 @@ struct RevLds {
   float vs[4][kCkpt];                                   // scalar gates: sum_j v du per tile
   float sb[kCkpt], sgl[kCkpt];
   int unsafe;
+  // bf16 operands: the exit-state gradient as D^T [column][row], the X1
+  // operand of the column waves (fp32 operands keep D tiles in registers).
+  static constexpr bool kDl = sizeof(T) == 2;
+  T Dl[kDl ? kCols : 1][DK + 8];
 };
 
 // A thread's share of one block's row inputs (4 channels of one token) and
@@ -340,17 +332,18 @@ __device__ __forceinline__ Frag4<float> f32frag(const f32x4& a) {
 
 // 2^(Gl_s - Gl_t) for scalar gates (the per-token cumulative log2-decay is
 // the same in every channel's row of Gl).
-template <int DK, typename T>
-__device__ __forceinline__ float token_decay(const RevLds<DK, T>& L, int s, int t) {
+template <typename Lds>
+__device__ __forceinline__ float token_decay(const Lds& L, int s, int t) {
   return exp2_fast(L.Gl[0][s] - L.Gl[0][t]);
 }
 
 template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT>
 __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   constexpr int RB = DK / 16;               // 16-row blocks of the state
+  using TO = IO;                            // MFMA operand type
   union Smem {
-    FwdStage<DK> fwd[2];
-    RevLds<DK, IO> rev;
+    FwdLds<DK, TO> fwd;
+    RevLds<DK, TO> rev;
   };
   __shared__ Smem sm;
 
@@ -393,129 +386,11 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   // nblk checkpoints (state before each 16-token block) + the final state
   float* ck = p.ckpt + (((int64_t)hv * ncb + cb) * p.slots + slot0) * (int64_t)DK * kCols;
 
-  // ---- phase 1: forward, storing checkpoints and u ----
-  // A wave holds all DK rows of CW columns, a lane RPL rows x CPL columns
-  // (the 16 lanes of a DPP row share the columns), so the read r = Sbar^T e
-  // is an in-wave butterfly and the token loop has no barrier.
-  {
-    constexpr int RPL = DK / 16;             // rows per lane
-    constexpr int CPL = 256 / DK;            // columns per lane
-    constexpr int CW = 4 * CPL;              // columns per wave
-    const int rl = lane & 15, dr = lane >> 4;
-    const int pr0 = rl * RPL;                // first row
-    const int pc0 = wave * CW + dr * CPL;    // first column inside the block
-    const int64_t pcg = (int64_t)cb * kCols + pc0;
-    auto ldn = [](const float* src, float* out, int n) {
-      for (int i = 0; i < n; i += 4) ld4f(src + i, out + i);
-    };
-    auto ldc = [](const float* src, float* out) {
-      if constexpr (CPL == 2) {
-        const float2 x = *reinterpret_cast<const float2*>(src);
-        out[0] = x.x; out[1] = x.y;
-      } else {
-        ld4f(src, out);
-      }
-    };
-    auto stc = [](float* dst, const float* v) {
-      if constexpr (CPL == 2) *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
-      else st4f(dst, v);
-    };
-    float P1[RPL][CPL];
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      if (p.state_in) {
-        ldc(p.state_in + (head * DK + pr0 + i) * p.dv + pcg, P1[i]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) P1[i][j] = 0.f;
-      }
-    }
-    FwdLoad<DK, CHANNEL, HAS_G, IO, GT> ld;
-    ld.issue(p, tok0, T, hv, hk, cb, 0, tid);
-    ld.store(sm.fwd[0], tid);
-    lds_barrier();
-    for (int64_t m = 0; m < nblk; ++m) {
-      const int cur = (int)(m & 1);
-      const bool more = m + 1 < nblk;
-      ld.issue(p, tok0, T, hv, hk, cb, (more ? m + 1 : m) * kCkpt, tid);
-#pragma unroll
-      for (int i = 0; i < RPL; ++i) stc(ck + (m * DK + pr0 + i) * kCols + pc0, P1[i]);
-      const int64_t t0 = m * kCkpt;
-      const int nt = (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
-      const FwdStage<DK>& st = sm.fwd[cur];
-      for (int tl = 0; tl < nt; ++tl) {
-        float k[RPL], bb[RPL], a[RPL], w[CPL], v[CPL], r[CPL];
-        ldn(&st.k[tl][pr0], k, RPL);
-        if constexpr (CHANNEL) {
-          ldn(&st.b[tl][pr0], bb, RPL);
-          ldn(&st.a[tl][pr0], a, RPL);
-          ldc(&st.w[tl][pc0], w);
-        } else {
-          const float sb = st.sb[tl], sa = st.sa[tl];
-#pragma unroll
-          for (int i = 0; i < RPL; ++i) { bb[i] = sb; a[i] = sa; }
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) w[j] = sb;
-        }
-        ldc(&st.v[tl][pc0], v);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          float sacc = 0.f;
-#pragma unroll
-          for (int i = 0; i < RPL; ++i) sacc += a[i] * P1[i][j] * (bb[i] * k[i]);
-          r[j] = row16_sum(sacc);
-        }
-        float u[CPL];
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) u[j] = w[j] * v[j] - r[j];
-        if (rl == 0) stc(p.u + ((tok0 + t0 + tl) * p.Hv + hv) * p.dv + pcg, u);
-#pragma unroll
-        for (int i = 0; i < RPL; ++i)
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) P1[i][j] = a[i] * P1[i][j] + k[i] * u[j];
-      }
-      ld.store(sm.fwd[cur ^ 1], tid);   // (the last block stores a copy nobody reads)
-      lds_barrier();
-    }
-    // the final state
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) stc(ck + (nblk * DK + pr0 + i) * kCols + pc0, P1[i]);
-  }
-  // The u and the states written above are read back below through global
-  // memory by other threads of this workgroup: make them visible.
-  __threadfence_block();
-  __syncthreads();
-
-  // ---- phase 2: reverse, one block at a time in matrix form ----
-  using TO = IO;                             // MFMA operand type
-  RevLds<DK, TO>& L = sm.rev;
   const int g4 = lane >> 4, n = lane & 15;
-  const bool colw = wave < 4;                // column waves own D tiles of columns 16 wave..
+  const bool colw = wave < 4;                // column waves own state tiles of columns 16 wave..
   const int ct = wave & 3;                   // a column wave's column tile
-  const int ch = 16 * wave + n;              // this lane's channel in the row-gradient tiles
   const int64_t colg = (int64_t)cb * kCols;  // first value column of the workgroup
-
-  // Dt[c]: accL(D^T) tile (columns 16c.., rows 16 wave..): D[ch][16c + 4 g4 + ii].
-  // Dc[rb]: accL(D) tile (rows 16rb.., columns 16 ct..): D[16rb + 4 g4 + ii][16 ct + n].
-  f32x4 Dt[4], Dc[RB];
-  float Sf[4][4], Sn[4][4];                  // S[ch][16c + 4 g4 + ii]: block entry states
-  {
-    const float* dso = p.d_state_out ? p.d_state_out + head * (int64_t)DK * p.dv + colg : nullptr;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
-      if (dso) ld4f(dso + (int64_t)ch * p.dv + 16 * c + 4 * g4, x);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Dt[c][ii] = x[ii];
-      ld4f(ck + ((nblk - 1) * DK + ch) * kCols + 16 * c + 4 * g4, Sn[c]);
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        Dc[rb][ii] = (dso && colw) ? dso[(int64_t)(16 * rb + 4 * g4 + ii) * p.dv + 16 * ct + n] : 0.f;
-  }
-  // A column wave's own v, w of its column tile (4 tokens per lane), a block ahead.
+  // A column wave's v, w of its column tile (4 tokens per lane), a block ahead.
   IO vr[4];
   GT wr[4];
   auto issue_vw = [&](int64_t t0) {
@@ -528,6 +403,217 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       if constexpr (CHANNEL) wr[ii] = static_cast<const GT*>(p.w)[off];
     }
   };
+
+  // ---- phase 1: forward in blocks, storing checkpoints and u ----
+  // Column wave ct holds the state's columns 16 ct.. over all rows as accL
+  // tiles Sc[rb] (S[16rb + 4 g4 + ii][16 ct + n]) and per block solves
+  // U = (I + A)^{-1} (Z - (gs e) S) and updates S' = Diag(gend) S + (ge k)^T U.
+  {
+    FwdLds<DK, TO>& F = sm.fwd;
+    f32x4 Sc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        Sc[rb][ii] = (colw && p.state_in)
+                         ? p.state_in[(head * DK + 16 * rb + 4 * g4 + ii) * p.dv + colg + 16 * ct + n]
+                         : 0.f;
+    FwdLoad<DK, CHANNEL, HAS_G, IO, GT> ld;
+    ld.issue(p, tok0, T, hv, hk, 0, tid);
+    issue_vw(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    // One block of the forward walk (FULL: all 16 tokens; only the last can be short).
+    auto fwd_block = [&](auto full_tag, int64_t m) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      const int64_t t0 = m * kCkpt;
+      const int nt = FULL ? kCkpt : (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
+      const int64_t mn = m + 1 < nblk ? m + 1 : m;   // the next block (or this one again)
+      ld.store(F, tid);
+      if (tid == 0) F.unsafe = 0;
+      float vv[4], wv[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        vv[ii] = to_f32(vr[ii]);
+        wv[ii] = CHANNEL ? to_f32(wr[ii]) : 0.f;
+      }
+      lds_barrier();
+      ld.issue(p, tok0, T, hv, hk, mn * kCkpt, tid);
+      if (colw) issue_vw(mn * kCkpt);
+      {
+        const int i = tid % DK, qt = tid / DK;
+        float acc = 0.f, ref = 0.f, G[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < kCkpt; ++r) {
+          acc += CHANNEL ? F.gl[r][i] : F.sgl[r];
+          if (r == 7) ref = acc;
+          if ((r >> 2) == qt) G[r & 3] = acc;
+        }
+        const float lend = acc;
+        if (qt == 0) F.gend[i] = exp2_fast(lend);
+        st4f(&F.Gl[i][4 * qt], G);
+        float kg[4];
+        bool bad = false;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int s = 4 * qt + ii;
+          const float kk = F.k[s][i];
+          const float e = (CHANNEL ? F.b[s][i] : F.sb[s]) * kk;
+          const float fq = CHANNEL ? exp2_fast(G[ii] - ref) : 1.f;
+          const float fk = CHANNEL ? exp2_fast(ref - G[ii]) : 1.f;
+          if (CHANNEL) bad |= fabsf(G[ii] - ref) > kSafeLog2;
+          kg[ii] = kk * exp2_fast(lend - G[ii]);
+          F.Kf[s][i] = from_f32<TO>(kk * fk);
+          F.Ef[s][i] = from_f32<TO>(e * fq);
+          F.Egm[s][i] = from_f32<TO>(-e * exp2_fast(G[ii]));
+        }
+        st4<TO>(&F.KgT[i][4 * qt], kg[0], kg[1], kg[2], kg[3]);
+        if (bad) F.unsafe = 1;
+      }
+      lds_barrier();
+      const bool exact = CHANNEL && F.unsafe != 0;   // uniform over the workgroup
+      if (exact) {
+        if (tid < kCkpt * kCkpt) {
+          const int s = tid >> 4, t = tid & 15;
+          float sa = 0.f;
+          if (s > t) {
+            for (int i = 0; i < DK; ++i)
+              sa += F.b[s][i] * F.k[s][i] * F.k[t][i] * exp2_fast(F.Gl[i][s] - F.Gl[i][t]);
+          }
+          F.A[s][t] = sa;
+        }
+        lds_barrier();
+      }
+      if (colw) {
+        // the block's entry state
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            ck[(m * DK + 16 * rb + 4 * g4 + ii) * kCols + 16 * ct + n] = Sc[rb][ii];
+        Frag4<float> nr, nc;   // rowL(N), accL(N), N = -A
+        if (!exact) {
+          f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aAt = aA;
+#pragma unroll
+          for (int kb = 0; kb < RB; ++kb) {
+            const Frag4<TO> ef = ld_frag4<TO>(&F.Ef[n][16 * kb + 4 * g4]);
+            const Frag4<TO> kf = ld_frag4<TO>(&F.Kf[n][16 * kb + 4 * g4]);
+            mma16(aA, ef, kf);    // A[4g+ii][n]
+            mma16(aAt, kf, ef);   // A[n][4g+ii]
+          }
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int r = 4 * g4 + ii;
+            float grn = 1.f, gnr = 1.f;
+            if constexpr (!CHANNEL) {
+              grn = r >= n ? token_decay(F, r, n) : 0.f;
+              gnr = n >= r ? token_decay(F, n, r) : 0.f;
+            }
+            nc.v[ii] = n < r ? -aA[ii] * grn : 0.f;
+            nr.v[ii] = r < n ? -aAt[ii] * gnr : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int r = 4 * g4 + ii;
+            nc.v[ii] = -F.A[r][n];
+            nr.v[ii] = -F.A[n][r];
+          }
+        }
+        // rowL((I + A)^{-1}) = accL(T^T), T = (I + N)(I + N^2)(I + N^4)(I + N^8)
+        auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+          mma16(a, x, y);
+          return f32frag(a);
+        };
+        const Frag4<float> n2c = prod(nr, nc), n2r = prod(nc, nr);
+        const Frag4<float> n4c = prod(n2r, n2c), n4r = prod(n2c, n2r);
+        const Frag4<float> n8r = prod(n4c, n4r);
+        f32x4 trow;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) trow[ii] = n8r.v[ii] + (4 * g4 + ii == n ? 1.f : 0.f);
+        mma16(trow, n4c, f32frag(trow));
+        mma16(trow, n2c, f32frag(trow));
+        mma16(trow, nc, f32frag(trow));
+        // W = Z - (gs e) S, U = T W
+        f32x4 wt;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int s = 4 * g4 + ii;
+          wt[ii] = s < nt ? (CHANNEL ? wv[ii] : F.sb[s]) * vv[ii] : 0.f;
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          mma16(wt, ld_frag4<TO>(&F.Egm[n][16 * rb + 4 * g4]), frag4_from_acc<TO>(Sc[rb]));
+        f32x4 ut = {0.f, 0.f, 0.f, 0.f};
+        mma16(ut, f32frag(trow), f32frag(wt));
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int s = 4 * g4 + ii;
+          if (s < nt) p.u[((tok0 + t0 + s) * p.Hv + hv) * p.dv + colg + 16 * ct + n] = ut[ii];
+        }
+        const Frag4<TO> uf = frag4_from_acc<TO>(ut);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float4 ge4 = *reinterpret_cast<const float4*>(&F.gend[16 * rb + 4 * g4]);
+          Sc[rb][0] *= ge4.x; Sc[rb][1] *= ge4.y; Sc[rb][2] *= ge4.z; Sc[rb][3] *= ge4.w;
+          mma16(Sc[rb], ld_frag4<TO>(&F.KgT[16 * rb + n][4 * g4]), uf);
+        }
+      }
+      lds_barrier();   // the block's LDS is rewritten by the next one
+    };
+    for (int64_t m = 0; m + 1 < nblk; ++m) fwd_block(std::true_type{}, m);
+    fwd_block(std::false_type{}, nblk - 1);
+    // the final state
+    if (colw) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          ck[(nblk * DK + 16 * rb + 4 * g4 + ii) * kCols + 16 * ct + n] = Sc[rb][ii];
+    }
+  }
+  // The u and the states written above are read back below through global
+  // memory by other threads of this workgroup: make them visible.
+  __threadfence_block();
+  __syncthreads();
+
+  // ---- phase 2: reverse, one block at a time in matrix form ----
+  RevLds<DK, TO>& L = sm.rev;
+  const int ch = 16 * wave + n;              // this lane's channel in the row-gradient tiles
+
+  // Dt[c]: accL(D^T) tile (columns 16c.., rows 16 wave..): D[ch][16c + 4 g4 + ii].
+  // Dc[rb]: accL(D) tile (rows 16rb.., columns 16 ct..): D[16rb + 4 g4 + ii][16 ct + n]
+  // (fp32 operands; with bf16 operands the column waves read D from LDS).
+  constexpr bool DL = RevLds<DK, TO>::kDl;
+  f32x4 Dt[4], Dc[DL ? 1 : RB];
+  float Sf[4][4];                            // S[ch][16c + 4 g4 + ii]: the block's entry state
+  {
+    const float* dso = p.d_state_out ? p.d_state_out + head * (int64_t)DK * p.dv + colg : nullptr;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (dso) ld4f(dso + (int64_t)ch * p.dv + 16 * c + 4 * g4, x);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) Dt[c][ii] = x[ii];
+      ld4f(ck + ((nblk - 1) * DK + ch) * kCols + 16 * c + 4 * g4, Sf[c]);
+    }
+    if constexpr (!DL) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          Dc[rb][ii] = (dso && colw) ? dso[(int64_t)(16 * rb + 4 * g4 + ii) * p.dv + 16 * ct + n] : 0.f;
+    }
+  }
+  auto put_dl = [&]() {   // D^T into LDS for the next block's X1 (bf16 operands)
+    if constexpr (DL) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) L.Dl[16 * c + 4 * g4 + ii][ch] = from_f32<TO>(Dt[c][ii]);
+    }
+  };
+  put_dl();
   RevLoad<DK, CHANNEL, HAS_G, IO, GT> ld;
   ld.issue(p, tok0, T, hv, hk, cb, (nblk - 1) * kCkpt, tid);
   issue_vw((nblk - 1) * kCkpt);
@@ -536,16 +622,15 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   // drain each block's prefetches at its top.
   __builtin_amdgcn_s_waitcnt(0);
 
-  for (int64_t mm = 0; mm < nblk; ++mm) {
+  // One block of the reverse walk; FULL blocks have all 16 tokens, so none
+  // of their stores is conditional (only the first block walked can be short).
+  auto rev_block = [&](auto full_tag, int64_t mm) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int64_t m = nblk - 1 - mm;
     const int64_t t0 = m * kCkpt;
-    const int nt = (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
+    const int nt = FULL ? kCkpt : (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
     const int64_t mp = m > 0 ? m - 1 : 0;    // the next block (or this one again)
 
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Sf[c][ii] = Sn[c][ii];
     // rowsum(D (.) S) of the incoming D with the entry state
     float dps = 0.f;
 #pragma unroll
@@ -554,8 +639,6 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       for (int ii = 0; ii < 4; ++ii) dps += Dt[c][ii] * Sf[c][ii];
     dps += __shfl_xor(dps, 16);
     dps += __shfl_xor(dps, 32);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ld4f(ck + (mp * DK + ch) * kCols + 16 * c + 4 * g4, Sn[c]);
 
     ld.store(L, tid);
     if (tid == 0) L.unsafe = 0;
@@ -690,37 +773,24 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       // RHS = (k ge) D + scale Pm^T dO for this column tile
       f32x4 rhs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        mma16(rhs, ld_frag4<TO>(&L.Kg[n][16 * rb + 4 * g4]), frag4_from_acc<TO>(Dc[rb]));
+      for (int rb = 0; rb < RB; ++rb) {
+        Frag4<TO> dfr;
+        if constexpr (DL) dfr = ld_frag4<TO>(&L.Dl[16 * ct + n][16 * rb + 4 * g4]);
+        else dfr = frag4_from_acc<TO>(Dc[rb]);
+        mma16(rhs, ld_frag4<TO>(&L.Kg[n][16 * rb + 4 * g4]), dfr);
+      }
       const Frag4<TO> dot = ld_frag4<TO>(&L.dOt[16 * ct + n][4 * g4]);   // accL(dO tile)
       mma16(rhs, pT, dot);
       mma16(du, f32frag(tinv), f32frag(rhs));   // DU = Tinv^T RHS
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) L.DUr[4 * g4 + ii][16 * ct + n] = from_f32<TO>(du[ii]);
       st4<TO>(&L.DUt[16 * ct + n][4 * g4], du[0], du[1], du[2], du[3]);
-      // dv = w du, dw = v du (scalar gates: w = beta, and sum_j v du goes to dbeta)
+      if constexpr (!CHANNEL) {   // sum_j v du of the tile goes to dbeta
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int s = 4 * g4 + ii;
-        const float wgt = CHANNEL ? wv[ii] : L.sb[s];
-        if (s < nt) {
-          const int64_t o = ((tok0 + t0 + s) * p.Hv + hv) * p.dv + colg + 16 * ct + n;
-          p.dv_out[o] = wgt * du[ii];
-          if constexpr (CHANNEL) p.dw[o] = vv[ii] * du[ii];
-        }
-        if constexpr (!CHANNEL) {
+        for (int ii = 0; ii < 4; ++ii) {
           const float x = row16_sum(vv[ii] * du[ii]);
-          if (n == 0) L.vs[ct][s] = x;
+          if (n == 0) L.vs[ct][4 * g4 + ii] = x;
         }
-      }
-      // D tiles: D <- Diag(gend) D + (scale gs q)^T dO - (gs e)^T DU
-      const Frag4<TO> duf = frag4_from_acc<TO>(du);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float4 ge4 = *reinterpret_cast<const float4*>(&L.gend[16 * rb + 4 * g4]);
-        Dc[rb][0] *= ge4.x; Dc[rb][1] *= ge4.y; Dc[rb][2] *= ge4.z; Dc[rb][3] *= ge4.w;
-        mma16(Dc[rb], ld_frag4<TO>(&L.QgT[16 * rb + n][4 * g4]), dot);
-        mma16(Dc[rb], ld_frag4<TO>(&L.EgT[16 * rb + n][4 * g4]), duf);
       }
     }
 
@@ -728,8 +798,12 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     Frag4<TO> sfr[4], ua[4], doa[4];
     f32x4 dQi = {0.f, 0.f, 0.f, 0.f}, dKi = dQi, m3 = dQi, m3t = dQi, dQa = dQi, dKa = dQi;
 #pragma unroll
+    for (int c = 0; c < 4; ++c) sfr[c] = frag4_of<TO>(Sf[c]);   // accL(S^T) tile
+#pragma unroll
+    for (int c = 0; c < 4; ++c)   // the next block's entry state
+      ld4f(ck + (mp * DK + ch) * kCols + 16 * c + 4 * g4, Sf[c]);
+#pragma unroll
     for (int c = 0; c < 4; ++c) {
-      sfr[c] = frag4_of<TO>(Sf[c]);                        // accL(S^T) tile
       ua[c] = ld_frag4<TO>(&L.Ur[n][16 * c + 4 * g4]);     // rowL(U)
       doa[c] = ld_frag4<TO>(&L.dOr[n][16 * c + 4 * g4]);   // rowL(dO)
       mma16(dQi, doa[c], sfr[c]);                          // dO S^T
@@ -764,6 +838,32 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       for (int ii = 0; ii < 4; ++ii) L.M3[4 * g4 + ii][n] = m3[ii];
     }
     lds_barrier();   // DU tiles (and the exact path's M3) visible
+
+    if (colw) {
+      // dv = w du, dw = v du (scalar gates: w = beta)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int s = 4 * g4 + ii;
+        const float wgt = CHANNEL ? wv[ii] : L.sb[s];
+        if (s < nt) {
+          const int64_t o = ((tok0 + t0 + s) * p.Hv + hv) * p.dv + colg + 16 * ct + n;
+          p.dv_out[o] = wgt * du[ii];
+          if constexpr (CHANNEL) p.dw[o] = vv[ii] * du[ii];
+        }
+      }
+      if constexpr (!DL) {
+        // D tiles: D <- Diag(gend) D + (scale gs q)^T dO - (gs e)^T DU
+        const Frag4<TO> dot = ld_frag4<TO>(&L.dOt[16 * ct + n][4 * g4]);
+        const Frag4<TO> duf = ld_frag4<TO>(&L.DUt[16 * ct + n][4 * g4]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float4 ge4 = *reinterpret_cast<const float4*>(&L.gend[16 * rb + 4 * g4]);
+          Dc[rb][0] *= ge4.x; Dc[rb][1] *= ge4.y; Dc[rb][2] *= ge4.z; Dc[rb][3] *= ge4.w;
+          mma16(Dc[rb], ld_frag4<TO>(&L.QgT[16 * rb + n][4 * g4]), dot);
+          mma16(Dc[rb], ld_frag4<TO>(&L.EgT[16 * rb + n][4 * g4]), duf);
+        }
+      }
+    }
 
     f32x4 dEi = {0.f, 0.f, 0.f, 0.f}, m4 = dEi, m4t = dEi, dEa = dEi;
 #pragma unroll
@@ -801,6 +901,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
         mma16(Dt[c], ld_frag4<TO>(&L.dOt[16 * c + n][4 * g4]), qgb);
         mma16(Dt[c], ld_frag4<TO>(&L.DUt[16 * c + n][4 * g4]), egb);
       }
+      put_dl();   // read by the next block's column waves, after the end barrier
     }
     if (exact) {
       if (wave == 0) {
@@ -896,7 +997,9 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       }
     }
     lds_barrier();   // the block's LDS is rewritten by the next one
-  }
+  };
+  rev_block(std::false_type{}, 0);
+  for (int64_t mm = 1; mm < nblk; ++mm) rev_block(std::true_type{}, mm);
   if (p.d_state_in) {
     float* dsi = p.d_state_in + head * (int64_t)DK * p.dv + colg;
 #pragma unroll
