@@ -72,7 +72,7 @@ def test_backward_matches_oracle(channel, dk, dv, io, gate):
 
 @pytest.mark.parametrize("T", [1, 3, 4, 5, 15, 16, 17, 64, 100])
 def test_backward_ragged_lengths(T):
-    """Every position of the last checkpoint block and sub-block."""
+    """Every position of the last 16-token block."""
     announce(f"backward T={T}")
     inp, d_o, d_sT = _case(1, T, 1, 1, 128, 128, True, torch.float32)
     got = _run(inp, d_o, d_sT)
