@@ -218,9 +218,10 @@ size_t gdn_backward_workspace_size(const gdn_bwd_desc* desc);
  * loss L = sum(o * d_o) + sum(S_T * d_state_out).  The pages give the update
  * ("Gated DeltaNet-2", Methodologie §1) and stress that training needs its
  * gate-aware gradient (§3); the gradients here are the chain rule through
- * that update, run in reverse over the tokens (the per-token reverse step is
+ * that update, run in reverse over blocks of 16 tokens (the block form is
  * written out in backward.hip).  The kernels recompute the forward states
- * from checkpoints kept in the workspace, in fp32.
+ * from checkpoints kept in the workspace: states and accumulation in fp32,
+ * matrix-product operands in io_dtype.
  *
  *   q, k, v, beta_or_b, w, g, state_in   as for gdn_chunk_fwd (inputs)
  *   d_o          [B, T, H_v, d_v]  io_dtype
