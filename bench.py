@@ -69,8 +69,8 @@ KERNEL_SOURCES = {
     "short_conv": ("layer_ops.hip", "gdn_device.hpp"),
     "gates": ("layer_ops.hip", "gdn_device.hpp"),
     "output_gate": ("layer_ops.hip", "gdn_device.hpp"),
-    "backward": ("backward.hip", "gdn_device.hpp"),
-    "backward_reduce": ("backward.hip", "gdn_device.hpp"),
+    "backward": ("backward.hip", "chunk_common.hpp", "gdn_device.hpp"),
+    "backward_reduce": ("backward.hip", "chunk_common.hpp", "gdn_device.hpp"),
 }
 
 
