@@ -64,7 +64,7 @@ def decode_algorithmic(cfg, io_bytes=2, gate_bytes=2):
 # Sources each profiled kernel is built from; its counter figures stay valid
 # while these files are unchanged.
 KERNEL_SOURCES = {
-    "chunk_fwd": ("chunk_fwd_pipe.hip", "chunk_fwd.hip", "chunk_common.hpp", "gdn_device.hpp"),
+    "chunk_fwd": ("chunk_fwd_sb.hip", "chunk_fwd.hip", "chunk_common.hpp", "gdn_device.hpp"),
     "decode_step": ("decode.hip", "gdn_device.hpp"),
     "short_conv": ("layer_ops.hip", "gdn_device.hpp"),
     "gates": ("layer_ops.hip", "gdn_device.hpp"),
@@ -104,30 +104,110 @@ def measured_traffic(kernel_key, per_launch_bytes_alg):
     return ent.get("hbm_bytes_per_launch")
 
 
+def time_cold(fn, torch, flush, steps, warmup):
+    """Per-repetition launch times (ms) with HIP events on the launch stream,
+    each repetition after a 512 MB write that evicts L2 and the Infinity
+    Cache; returns (median, min) over the repetitions and the warm mean of as
+    many back-to-back launches."""
+    for _ in range(warmup):
+        fn()
+    times = []
+    for _ in range(steps):
+        flush.zero_()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        times.append(ev[0].elapsed_time(ev[1]))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        fn()
+    ev[1].record()
+    torch.cuda.synchronize()
+    warm = ev[0].elapsed_time(ev[1]) / steps
+    times.sort()
+    return times[len(times) // 2], times[0], warm
+
+
+def exact_path_fraction(g, channel, torch, sub=16, limit=110.0):
+    """Fraction of (sequence, value head, 16-token sub-block) units the chunk
+    kernel runs on its exact token path, from the log-decay tensor g
+    ([B, T, H_v, d_k] or [B, T, H_v]) and the kernel's own criterion: with G
+    the cumulative log2-decay from the sub-block start, the factored form
+    needs |G - m_h| <= limit (m_h = G at token 3 for the first half, at token
+    11 for the second) with channel gates, and no rise G_t - min_{s<=t} G_s,
+    G_t or G_15 - G_t above it with scalar gates."""
+    B, T = g.shape[0], g.shape[1]
+    Tb = (T // sub) * sub
+    x = g[:, :Tb].float() * 1.4426950408889634
+    if not channel:
+        x = x.unsqueeze(-1)
+    x = x.reshape(B, Tb // sub, sub, x.shape[2], x.shape[3])
+    G = torch.cumsum(x, dim=2)
+    g15 = G[:, :, 15:16]
+    if channel:
+        m0, m1 = G[:, :, 3:4], G[:, :, 11:12]
+        mh = torch.cat([m0.expand(-1, -1, 8, -1, -1), m1.expand(-1, -1, 8, -1, -1)], dim=2)
+        worst = torch.maximum((G - mh).abs(), torch.maximum(mh, g15 - mh))
+        worst = torch.maximum(worst, torch.maximum(m1 - m0, g15))
+    else:
+        rise = G - torch.cummin(G, dim=2).values
+        worst = torch.maximum(torch.maximum(G, g15 - G), rise)
+    flagged = (worst.amax(dim=(2, 4)) > limit)
+    return float(flagged.float().mean())
+
+
+def realistic_gates(gdn, synth, torch, cfg):
+    """g, beta or b, w for the shape of cfg from gdn_gates over the Mamba-2
+    recipe of the block inputs (A_log = log U(1, 16), dt_bias ~ N(-2, 0.5^2),
+    raw projections N(0, 1); seed 7)."""
+    bcfg = synth.BlockConfig("gates", N=cfg.B, T=cfg.T, Hk=cfg.Hk, Hv=cfg.Hv, dk=cfg.dk,
+                             dv=cfg.dv, channel=cfg.channel, io_dtype=torch.bfloat16,
+                             gate_dtype=torch.bfloat16, seed=7)
+    blk = synth.block_inputs(bcfg, device="cuda", conv_state=False)
+    g, beta, w = gdn.gdn_gates(blk["a_raw"], blk["b_raw"], cfg.Hv, w_raw=blk["w_raw"],
+                               A_log=blk["A_log"], dt_bias=blk["dt_bias"], d_k=cfg.dk, d_v=cfg.dv)
+    torch.cuda.synchronize()
+    del blk
+    return g, beta, w
+
+
 def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
     """Chunk-forward timings of the other prefill workloads (not part of the
-    step): launch time from HIP events on the launch stream, against the same
-    algorithmic bytes and flops as the headline workload."""
+    step): HIP events on the launch stream, cold caches per repetition
+    (median and min) and warm, against the same algorithmic bytes and flops
+    as the headline workload.  The rows "*_mamba2_gates" run the B8 T4096
+    shapes on gates from gdn_gates over the Mamba-2 recipe and report the
+    fraction of sub-blocks on the exact path."""
     res = {}
-    for name in ("gdn1_fp32_small", "gdn1_bf16_train", "gdn1_grouped_long"):
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)   # 512 MB
+    rows = [("gdn1_fp32_small", None, None), ("gdn1_bf16_train", None, None),
+            ("gdn2_bf16_train", "fp32_gates", None), ("gdn1_grouped_long", None, None),
+            ("gdn2_bf16_train", "mamba2_gates", None), ("gdn1_bf16_train", "mamba2_gates", None)]
+    for name, variant, _ in rows:
         cfg = synth.CONFIGS[name]
+        if variant == "fp32_gates":
+            cfg = synth.ChunkConfig(name, B=cfg.B, T=cfg.T, Hk=cfg.Hk, Hv=cfg.Hv, dk=cfg.dk,
+                                    dv=cfg.dv, channel=cfg.channel, io_dtype=cfg.io_dtype,
+                                    gate_dtype=torch.float32, seed=cfg.seed)
         inp = synth.chunk_inputs(cfg, device="cuda")
+        frac = None
+        if variant == "mamba2_gates":
+            g, beta, w = realistic_gates(gdn, synth, torch, cfg)
+            inp["g"], inp["beta_or_b"] = g.reshape(inp["g"].shape), beta.reshape(inp["g"].shape)
+            if cfg.channel:
+                inp["w"] = w.reshape(inp["v"].shape)
+            frac = exact_path_fraction(inp["g"], cfg.channel, torch)
         o = torch.empty((cfg.B, cfg.T, cfg.Hv, cfg.dv), dtype=cfg.io_dtype, device=dev)
         s = torch.empty((cfg.B, cfg.Hv, cfg.dk, cfg.dv), dtype=torch.float32, device=dev)
 
         def run():
             gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta_or_b"], w=inp["w"], g=inp["g"],
                               state_in=inp["state_in"], state_out=s, o=o)
-        for _ in range(warmup):
-            run()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for _ in range(steps):
-            run()
-        ev[1].record()
-        torch.cuda.synchronize()
-        ms = ev[0].elapsed_time(ev[1]) / steps
+        ms, ms_min, ms_warm = time_cold(run, torch, flush, steps, warmup)
         io_bytes = 4 if cfg.io_dtype == torch.float32 else 2
         gate_bytes = 4 if cfg.gate_dtype == torch.float32 else 2
         nbytes, flops = chunk_algorithmic(cfg, gate_bytes, io_bytes=io_bytes,
@@ -136,12 +216,16 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
             G = cfg.Hv // cfg.Hk
             flops = 2.0 * (CHUNK / 2 * (cfg.dk + 2 * cfg.dv) + 3 * cfg.dk * cfg.dv
                            + CHUNK * cfg.dk / G) * cfg.B * cfg.T * cfg.Hv
-        res[name] = {"ms": round(ms, 4), "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
-                     "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                     "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
-                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
-                                        (PEAK_FP32_TFLOPS if io_bytes == 4 else PEAK_BF16_TFLOPS), 4)}
+        key = name if variant is None else f"{name}_{variant}"
+        res[key] = {"ms": round(ms, 4), "ms_min": round(ms_min, 4), "ms_warm": round(ms_warm, 4),
+                    "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+                    "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                    "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
+                                       (PEAK_FP32_TFLOPS if io_bytes == 4 else PEAK_BF16_TFLOPS), 4)}
+        if frac is not None:
+            res[key]["exact_path_fraction"] = round(frac, 6)
         del inp, o, s
         torch.cuda.empty_cache()
     # packed variable-length prefill (serving): the final states are the
@@ -154,22 +238,14 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
         def run():
             gdn.gdn_chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["beta_or_b"],
                                      inp["cu_seqlens"], w=inp["w"], g=inp["g"], state_out=s, o=o)
-        for _ in range(warmup):
-            run()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for _ in range(steps):
-            run()
-        ev[1].record()
-        torch.cuda.synchronize()
-        ms = ev[0].elapsed_time(ev[1]) / steps
+        ms, ms_min, ms_warm = time_cold(run, torch, flush, steps, warmup)
         one = synth.ChunkConfig(name, B=1, T=vcfg.total_T, Hk=vcfg.Hk, Hv=vcfg.Hv, dk=vcfg.dk,
                                 dv=vcfg.dv, channel=vcfg.channel, io_dtype=vcfg.io_dtype,
                                 gate_dtype=vcfg.gate_dtype, seed=vcfg.seed)
         nbytes, flops = chunk_algorithmic(one, 2)
         nbytes += (vcfg.N - 1) * vcfg.Hv * vcfg.dk * vcfg.dv * 4   # one final state per sequence
-        res[name] = {"ms": round(ms, 4), "tokens_per_s": round(vcfg.total_T / (ms * 1e-3), 1),
+        res[name] = {"ms": round(ms, 4), "ms_min": round(ms_min, 4), "ms_warm": round(ms_warm, 4),
+                     "tokens_per_s": round(vcfg.total_T / (ms * 1e-3), 1),
                      "sequences": vcfg.N, "lengths": inp["lengths"],
                      "algorithmic_bytes": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
@@ -177,7 +253,29 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
                      "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del inp, o, s
         torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
     return res
+
+
+def copy_bandwidth(torch, dev):
+    """A plain 2 GiB device-to-device copy through torch: read + write bytes
+    per second, the practical streaming rate beside the 8 TB/s nominal peak."""
+    a = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(5):
+        b.copy_(a)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / 5
+    del a, b
+    torch.cuda.empty_cache()
+    return round(2 * (1 << 31) / (ms * 1e-3) / 1e9, 1)
 
 
 def block_op_workloads(gdn, synth, torch, dev, steps=20, warmup=3):
@@ -303,13 +401,22 @@ def cpu_baseline(args):
     oracle.recurrent(args64["q"], args64["k"], args64["v"], args64["beta_or_b"], args64["w"],
                      args64["g"], nthreads=cores)
     dt = time.perf_counter() - t0
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": B * cfg.T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"GDN-2 prefill chunk forward only, all {B} sequences x {cfg.Hv} heads x "
                       f"T={cfg.T} (fp64 token recurrence, OpenMP over heads); {dt:.2f} s wall",
-            "seconds": dt}
+            "cpu_model": model, "seconds": dt}
 
 
-KERNEL_KEYS = {"chunk_fwd": ("chunk_fwd_pipe_kernel", "chunk_fwd_kernel"),
+KERNEL_KEYS = {"chunk_fwd": ("chunk_fwd_sb_kernel", "chunk_fwd_kernel"),
                "decode_step": ("decode_kernel",),
                "short_conv": ("short_conv_kernel",),
                "gates": ("gates_kernel", "gates_vec_kernel"),
@@ -524,6 +631,7 @@ def main():
         "rooflines": {"chunk_fwd": roof_c, "decode_step": roof_d},
         "source_digest": source_digest(),
     }
+    out["device_copy_GBps"] = copy_bandwidth(torch, dev)
     if not args.no_secondary:
         out["secondary"] = secondary_chunk_workloads(gdn, synth, torch, dev)
     if not args.no_block_ops:
@@ -539,7 +647,8 @@ def main():
         del a, b
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args)
-        out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample",
+                                                  "cpu_model")}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gdn_api.cpp", "decode.hip", "chunk_fwd.hip", "chunk_fwd_pipe.hip", "layer_ops.hip",
+SOURCES = ["gdn_api.cpp", "decode.hip", "chunk_fwd.hip", "chunk_fwd_sb.hip", "layer_ops.hip",
            "backward.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 

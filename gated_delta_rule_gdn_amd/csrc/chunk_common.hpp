@@ -1,6 +1,7 @@
 // chunk_common.hpp -- helpers shared by the chunkwise forward kernels
-// (chunk_fwd.hip: sequential-phase kernel; chunk_fwd_pipe.hip: producer /
-// consumer kernel).  Device code only; internal linkage in each unit.
+// (chunk_fwd.hip: sequential-phase kernel, fp32 operands; chunk_fwd_sb.hip:
+// sub-block kernel, bf16 operands) and the backward.  Device code only;
+// internal linkage in each unit.
 #pragma once
 
 #include "gdn_device.hpp"

@@ -648,10 +648,10 @@ __global__ void state_copy_kernel(const float* __restrict__ src, float* __restri
 
 }  // namespace
 
-// bf16 operands run the producer/consumer kernel (chunk_fwd_pipe.hip); fp32
+// bf16 operands run the sub-block kernel (chunk_fwd_sb.hip); fp32
 // operands run the sequential-phase kernel of this file.
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream) {
-  if (a.io == DType::BF16) return launch_chunk_fwd_pipe(a, stream);
+  if (a.io == DType::BF16) return launch_chunk_fwd_sb(a, stream);
   return pick_dims<float, float>(a, stream);
 }
 

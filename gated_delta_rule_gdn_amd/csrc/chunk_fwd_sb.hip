@@ -1,0 +1,885 @@
+// chunk_fwd_sb.hip -- chunkwise forward on bf16 MFMA operands, each 64-token
+// chunk solved in four 16-token sub-blocks.
+//
+// Method ("Gated DeltaNet-2", Methodologie §3 "Entrainement Parallele Efficace
+// par Blocs"; "Gated DeltaNet", §Rendre l'entrainement parallele).  Inside a
+// chunk of C = 64 tokens the unit lower-triangular system (I + A) U = Z - E S
+// is solved by block forward substitution over four 16x16 diagonal blocks.
+// The off-diagonal blocks A_bb' (b' < b) are applied in factored form through
+// the running state: with S_b the state entering sub-block b and G the
+// cumulative log-decay counted from the first token of the sub-block,
+//
+//   X_b     = Z_b + Ln_b S_b          Ln_t = -(b_t (.) k_t) exp(G_t)
+//   U_b     = (I + A_bb)^{-1} X_b
+//   O_b     = Qb_b S_b + P_bb U_b     Qb_t = q_t (.) exp(G_t)
+//   S_{b+1} = Diag(exp(G_15)) S_b + Kh_b^T U_b,   Kh_s = k_s (.) exp(G_15 - G_s)
+//
+// which is the chunk's block substitution (A_bb' U_b' enters through
+// Ln_b S_b).  For alpha <= 1 every exponential above is at most 1, so the
+// state-side operands never overflow however strong the decay.
+//
+// Inside a diagonal block, A[t,s] = sum_c e_t,c k_s,c exp(G_t,c - G_s,c)
+// (s < t) and P[t,s] (s <= t) are MFMA products of factored operands.  Each
+// 8-token half uses its own reference, the cumulative log-decay at its 4th
+// token (m0 = G_3, m1 = G_11), so a factor spans at most four tokens of decay:
+//   L = -e exp(G - m_h),  M = q exp(G - m_h),  R = k exp(m_h - G)
+// gives the two diagonal 8x8 quadrants; the lower-left quadrant (t >= 8 > s)
+// uses L'' = L exp(m1 - m0) = -e exp(G - m0) against R (exp(G_t - m0) <= 1
+// there).  A sub-block where some |G - m_h| exceeds kRange (log2 units) runs
+// the exact token recurrence instead; on realistic Mamba-2 gates this is
+// about one sub-block in a thousand.
+//
+// With scalar gates (Gated DeltaNet, DeltaNet) the decay factors out of the
+// Gram matrices exactly: A[t,s] = beta_t exp(G_t - G_s) (k_t . k_s), applied
+// as an element-wise mask, and as row scales of K S, Q S and U, so the
+// operands are the raw q and k and no sub-block ever leaves the MFMA path
+// when alpha <= 1.
+//
+// Workgroup: 512 threads per (sequence, value head, 64 columns of d_v).
+//   Consumer waves 0-3 own 16 state columns each (all d_k rows, fp32, in MFMA
+//     accumulator registers for the whole sequence) and walk the sub-blocks.
+//   Producer wave 4 + p prepares sub-block p of the next chunk on its own:
+//     loads, decay prefix, gated operands, the 16x16 Gram blocks, the inverse
+//     (I + A_bb)^{-1} and the flags.  Nothing crosses producer waves, so
+//     one workgroup barrier per chunk hands a whole chunk over.
+// State rows in registers: accumulator tile 2kb + h, row 4g + i holds channel
+// 32kb + 8g + 4h + i.  With that order the B fragment of a 32-channel block
+// is 8 consecutive channels per lane, so every operand is stored with its
+// channels in natural order: X and O read 16-byte fragments, and the state
+// update reads Kh^T with the gfx950 transposing LDS read (ds_read_b64_tr_b16).
+#include "chunk_common.hpp"
+
+namespace gdn {
+namespace {
+
+template <int N>
+struct IntTag {
+  static constexpr int value = N;
+};
+
+constexpr int kSB = 16;           // tokens per sub-block
+constexpr int kSbThreads = 512;   // 4 consumer + 4 producer waves
+constexpr float kRange = 110.f;   // largest |G - m_h| (log2) of the factored form
+
+// One [16][DK] bf16 operand block.  Rows are DK contiguous channels; the
+// 16-byte chunks of a row are XOR-swizzled by the row so that a fragment read
+// (16 rows, one chunk) and a producer store (4 rows, all chunks) both spread
+// over every bank.
+template <int DK>
+struct Blk {
+  static constexpr int NCH = DK / 8;
+  static constexpr int RPB = NCH >= 16 ? 1 : 16 / NCH;
+  static constexpr int BYTES = 16 * DK * 2;
+  __device__ static int at(int r, int c) {
+    const int sw = (r / RPB) % NCH;
+    return r * DK + ((((c >> 3) ^ sw)) << 3) + (c & 7);
+  }
+};
+
+template <int DK, bool CHANNEL>
+struct SbLds {
+  static constexpr int NOPS = CHANNEL ? 3 : 2;  // Ln|k, Qb|q, Kh (channel)
+  static constexpr int BLK = Blk<DK>::BYTES;
+  static constexpr int TPB = 16 * 16 * 2;       // one 16x16 bf16 block
+  static constexpr int kOps = 0;                 // [NOPS][4 sub-blocks] blocks
+  static constexpr int kT = kOps + NOPS * 4 * BLK;
+  static constexpr int kP = kT + 4 * TPB;
+  static constexpr int kVec = kP + 4 * TPB;      // channel: D [4][DK]; scalar: [4][6][16]
+  static constexpr int VEC = CHANNEL ? 4 * DK * 4 : 4 * 6 * 16 * 4;
+  static constexpr int kFlag = kVec + VEC;
+  static constexpr int SLOT = kFlag + 16;
+  static constexpr int kPriv = 2 * SLOT;         // channel: per producer wave LM, R, L2|M2
+  static constexpr int PRIV = CHANNEL ? 3 * BLK : 0;
+  static constexpr int kTotal = kPriv + 4 * PRIV;
+  static_assert(kTotal <= 160 * 1024, "LDS budget");
+};
+
+// Scalar-gate factor arrays of one sub-block, [6][16] floats.
+constexpr int kFX = 0;    // -beta_t exp(G_t):   X = Z + diag(FX) K S
+constexpr int kFO = 1;    // exp(G_t):           O = diag(FO) Q S + P U
+constexpr int kFK = 2;    // exp(G_15 - G_t):    S' = D S + K^T diag(FK) U
+constexpr int kFB = 3;    // beta_t:             Z = diag(beta) V
+constexpr int kFG = 4;    // G_t (log2)
+constexpr int kFD = 5;    // [0] = D = exp(G_15)
+
+__device__ __forceinline__ float quad_perm(float x, int pat) {
+  int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (pat) {
+    case 0x00: r = __builtin_amdgcn_update_dpp(0, v, 0x00, 0xf, 0xf, false); break;
+    case 0x90: r = __builtin_amdgcn_update_dpp(0, v, 0x90, 0xf, 0xf, false); break;
+    case 0x44: r = __builtin_amdgcn_update_dpp(0, v, 0x44, 0xf, 0xf, false); break;
+    case 0xAA: r = __builtin_amdgcn_update_dpp(0, v, 0xAA, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_update_dpp(0, v, 0xFF, 0xf, 0xf, false); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// Row shift right by n inside 16-lane rows; lanes shifted in take +inf.
+__device__ __forceinline__ float dpp_row_shr_inf(float x, int n) {
+  const int inf = 0x7f800000;
+  int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (n) {
+    case 1: r = __builtin_amdgcn_update_dpp(inf, v, 0x111, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(inf, v, 0x112, 0xf, 0xf, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(inf, v, 0x114, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_update_dpp(inf, v, 0x118, 0xf, 0xf, false); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+typedef short sb_v4s __attribute__((ext_vector_type(4)));
+
+// Four 16-bit elements of one row read transposed: within each 16-lane group
+// the lanes' 8-byte reads of 4 rows x 16 columns come back as lane l holding
+// column l of the 4 rows.
+__device__ __forceinline__ Frag4<bf16> ld_tr16(const bf16* p) {
+  const sb_v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) sb_v4s*)(p));
+  Frag4<bf16> f;
+  f.v = __builtin_bit_cast(bf16x4, r);
+  return f;
+}
+
+// (I + A)^{-1} of a 16x16 unit lower-triangular matrix from N = -A (strictly
+// lower, N^16 = 0):  (I + A)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8), on the
+// fp32 MFMA.  Layouts (lane = 16 g + j):
+//   rowL(X): X[j][4g + i]      accL(X): X[4g + i][j]
+// mma16(acc, rowL(X), accL(Y)) adds accL(X Y); accL(X) = rowL(X^T).
+// In: nr = rowL(N), nc = accL(N).  Out: rowL(T), T = (I + A)^{-1}.
+__device__ __forceinline__ Frag4<float> unit_lower_inverse(const Frag4<float>& nr,
+                                                           const Frag4<float>& nc, int g, int j) {
+  auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    mma16(acc, x, y);
+    Frag4<float> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.v[i] = acc[i];
+    return f;
+  };
+  const Frag4<float> n2c = prod(nr, nc);    // accL(N^2)
+  const Frag4<float> n2r = prod(nc, nr);    // rowL(N^2)
+  const Frag4<float> n4c = prod(n2r, n2c);  // accL(N^4)
+  const Frag4<float> n4r = prod(n2c, n2r);  // rowL(N^4)
+  const Frag4<float> n8c = prod(n4r, n4c);  // accL(N^8)
+  // accL(T^T), T^T = (I + N^8)^T (I + N^4)^T (I + N^2)^T (I + N)^T, by left
+  // products starting from accL((I + N)^T) = rowL(I + N).
+  Frag4<float> t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t.v[i] = nr.v[i] + ((4 * g + i == j) ? 1.f : 0.f);
+  auto step = [](const Frag4<float>& x, const Frag4<float>& c) {  // accL(C + X C), x = rowL(X)
+    f32x4 acc = {c.v[0], c.v[1], c.v[2], c.v[3]};
+    mma16(acc, x, c);
+    Frag4<float> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.v[i] = acc[i];
+    return f;
+  };
+  t = step(n2c, t);
+  t = step(n4c, t);
+  t = step(n8c, t);
+  return t;  // accL(T^T) = rowL(T)
+}
+
+template <typename GT, int DK, int DV, bool CHANNEL, bool HAS_G>
+__global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
+  using T = bf16;
+  using L = SbLds<DK, CHANNEL>;
+  using B = Blk<DK>;
+  constexpr int DVS = 64;
+  constexpr int NSPLIT = DV / DVS;
+  constexpr int KB = DK / 32;
+  constexpr int MT = DK / 16;
+  constexpr int CPL = DK / 16;   // channels per producer lane (channel gates)
+  constexpr int NSB = kC / kSB;  // 4
+
+  __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+
+  const T* __restrict__ gq = static_cast<const T*>(p.q);
+  const T* __restrict__ gk = static_cast<const T*>(p.k);
+  const T* __restrict__ gv = static_cast<const T*>(p.v);
+  const GT* __restrict__ gb = static_cast<const GT*>(p.b);
+  const GT* __restrict__ gw = static_cast<const GT*>(p.w);
+  const GT* __restrict__ gg = static_cast<const GT*>(p.g);
+  T* __restrict__ go = static_cast<T*>(p.o);
+
+  // Workgroup -> (head, d_v slice), XCD-aware (workgroup i runs on XCD i % 8;
+  // the slices of one head land on the same XCD and share its L2).
+  const int64_t nwg = (int64_t)gridDim.x;
+  int64_t lid = blockIdx.x;
+  if ((nwg & 7) == 0) lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
+  const int64_t head = lid / NSPLIT;
+  const int split = (int)(lid - head * NSPLIT);
+  const int64_t bidx = head / p.Hv;
+  const int hv = (int)(head - bidx * p.Hv);
+  const int hk = hv / (p.Hv / p.Hk);
+  const int c0 = split * DVS;
+  int64_t tok0 = bidx * p.T, Tn = p.T;
+  if (p.cu) {  // packed sequences: clamped range, so malformed offsets stay inside
+    int64_t a0 = p.cu[bidx], a1 = p.cu[bidx + 1];
+    a0 = a0 < 0 ? 0 : (a0 > p.T ? p.T : a0);
+    a1 = a1 < a0 ? a0 : (a1 > p.T ? p.T : a1);
+    tok0 = a0;
+    Tn = a1 - a0;
+  }
+  const int64_t nchunks = (Tn + kC - 1) / kC;
+  const int tid = threadIdx.x;
+  if (Tn == 0) {  // an empty sequence only passes its state through
+    if (p.state_out) {
+      const int64_t base = head * (int64_t)DK * DV + c0;
+      for (int idx = tid; idx < DK * DVS; idx += (int)blockDim.x) {
+        const int64_t e = base + (int64_t)(idx / DVS) * DV + (idx % DVS);
+        p.state_out[e] = p.state_in ? p.state_in[e] : 0.f;
+      }
+    }
+    return;
+  }
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15;
+  const int g = lane >> 4;
+
+  auto opblk = [&](int slot, int op, int sb) -> T* {
+    return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kOps + (op * NSB + sb) * L::BLK);
+  };
+  auto tblk = [&](int slot, int sb) -> T* {
+    return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kT + sb * L::TPB);
+  };
+  auto pblk = [&](int slot, int sb) -> T* {
+    return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kP + sb * L::TPB);
+  };
+  auto vecp = [&](int slot) -> float* {
+    return reinterpret_cast<float*>(smem + slot * L::SLOT + L::kVec);
+  };
+  auto flagp = [&](int slot) -> int* {
+    return reinterpret_cast<int*>(smem + slot * L::SLOT + L::kFlag);
+  };
+
+  const uint32_t qk_tok = (uint32_t)(p.Hk * DK * (int)sizeof(T));   // bytes per token
+  const uint32_t gc_tok = (uint32_t)(p.Hv * DK * (int)sizeof(GT));
+  const uint32_t gs_tok = (uint32_t)(p.Hv * (int)sizeof(GT));
+  const char* bq = reinterpret_cast<const char*>(gq) + ((uint64_t)tok0 * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
+  const char* bk = reinterpret_cast<const char*>(gk) + ((uint64_t)tok0 * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
+  const char* bbc = reinterpret_cast<const char*>(gb) + ((uint64_t)tok0 * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
+  const char* bgc = reinterpret_cast<const char*>(gg) + ((uint64_t)tok0 * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
+  const char* bbs = reinterpret_cast<const char*>(gb) + ((uint64_t)tok0 * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
+  const char* bgs = reinterpret_cast<const char*>(gg) + ((uint64_t)tok0 * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
+
+  if (wave >= 4) {
+    // =================================================================
+    // Producer wave 4 + pw: sub-block pw of every chunk.
+    // =================================================================
+    const int pw = wave - 4;
+    if constexpr (CHANNEL) {
+      // lane = 4 cg + qd: tokens 4 qd .. 4 qd + 3 of the sub-block,
+      // channels cg * CPL .. cg * CPL + CPL - 1
+      const int qd = lane & 3;
+      const int cg = lane >> 2;
+      const int ch0 = cg * CPL;
+      constexpr int QB = CPL * 2;
+      constexpr int GB = CPL * (int)sizeof(GT);
+      Raw<QB> rq[4], rk[4];
+      Raw<GB> rb[4], rg[4];
+      const uint32_t oq = (uint32_t)(ch0 * 2);
+      const uint32_t og = (uint32_t)(ch0 * (int)sizeof(GT));
+      auto load = [&](int64_t ci) {
+        const int64_t tb = ci * kC + kSB * pw + 4 * qd;  // first token of this lane
+        const int64_t last = Tn - 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int64_t t = tb + i;
+          t = t < last ? t : last;
+          const uint64_t tu = (uint64_t)t;
+          ld_raw<QB>(bq + (tu * qk_tok + oq), rq[i]);
+          ld_raw<QB>(bk + (tu * qk_tok + oq), rk[i]);
+          ld_raw<GB>(bbc + (tu * gc_tok + og), rb[i]);
+          if constexpr (HAS_G) ld_raw<GB>(bgc + (tu * gc_tok + og), rg[i]);
+        }
+      };
+      T* priv = reinterpret_cast<T*>(smem + L::kPriv + pw * L::PRIV);
+      T* sLM = priv;
+      T* sR = priv + 16 * DK;
+      T* sL2 = priv + 32 * DK;   // rows 8..15 of L'' as rows 0..7
+      T* sM2 = priv + 40 * DK;   // rows 8..15 of M'' as rows 0..7
+
+      auto produce = [&](int64_t ci) {
+        const int slot = (int)(ci & 1);
+        const int64_t tb = ci * kC + kSB * pw + 4 * qd;
+        // absent tokens (past the end): q = k = b = 0, g = 0
+        bool present[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) present[i] = tb + i < Tn;
+        // cumulative log2-decay over the sub-block: 4 tokens in-thread, then
+        // an exclusive scan over the 4 token quads of the lane quad
+        float G[4][CPL];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (HAS_G) {
+            unpack<GT, CPL>(rg[i], G[i]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) G[i][e] = 0.f;
+          }
+          if (!present[i]) {
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) G[i][e] = 0.f;
+          }
+        }
+        float mh[CPL], fln[CPL], fkh[CPL], c01[CPL];
+        float worst = 0.f;
+        float* dvec = vecp(slot) + pw * DK + ch0;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          G[0][e] *= kLog2e;
+#pragma unroll
+          for (int i = 1; i < 4; ++i) G[i][e] = fmaf(G[i][e], kLog2e, G[i - 1][e]);
+          // (every lane evaluates the DPP reads: a read under a branch
+          // would see the lanes that took the other side as inactive)
+          const float tot = G[3][e];
+          const float sh1 = quad_perm(tot, 0x90);
+          float s = tot + (qd >= 1 ? sh1 : 0.f);
+          const float sh2 = quad_perm(s, 0x44);
+          s = s + (qd >= 2 ? sh2 : 0.f);
+          const float excl = s - tot;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) G[i][e] += excl;
+          const float m0 = quad_perm(G[3][e], 0x00);   // G at token 3
+          const float m1 = quad_perm(G[3][e], 0xAA);   // G at token 11
+          const float g15 = quad_perm(G[3][e], 0xFF);
+          mh[e] = qd < 2 ? m0 : m1;
+          fln[e] = exp2_fast(mh[e]);
+          fkh[e] = exp2_fast(g15 - mh[e]);
+          c01[e] = exp2_fast(m1 - m0);
+          // channel decay of the whole sub-block (one lane per channel group)
+          if (qd == 0) dvec[e] = exp2_fast(g15);
+          // exponents that could overflow only when some g > 0
+          worst = fmaxf(worst, fmaxf(fmaxf(mh[e], g15 - mh[e]), fmaxf(m1 - m0, g15)));
+        }
+        // gated operands, token by token and 4 channels at a time; M waits in
+        // registers until the L rows it shares storage with have been read by
+        // the Gram products
+        T* sLn = opblk(slot, 0, pw);
+        T* sQb = opblk(slot, 1, pw);
+        T* sKh = opblk(slot, 2, pw);
+        uint32_t mpk[4][CPL / 2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float qv[CPL], kv[CPL], bv[CPL];
+          unpack<T, CPL>(rq[i], qv);
+          unpack<T, CPL>(rk[i], kv);
+          unpack<GT, CPL>(rb[i], bv);
+          const int r = 4 * qd + i;
+#pragma unroll
+          for (int u = 0; u < CPL / 4; ++u) {
+            float Lv[4], Mv[4], Rv[4], Lnv[4], Qbv[4], Khv[4], L2v[4], M2v[4];
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int e = 4 * u + e4;
+              const float qq = present[i] ? qv[e] : 0.f;
+              const float kk = present[i] ? kv[e] : 0.f;
+              const float bb = present[i] ? bv[e] : 0.f;
+              const float x = G[i][e] - mh[e];
+              worst = fmaxf(worst, fabsf(x));
+              const float e1 = exp2_fast(x);
+              const float e2 = exp2_fast(-x);
+              Lv[e4] = -(bb * kk) * e1;
+              Mv[e4] = qq * e1;
+              Rv[e4] = kk * e2;
+              Lnv[e4] = Lv[e4] * fln[e];
+              Qbv[e4] = Mv[e4] * fln[e];
+              Khv[e4] = Rv[e4] * fkh[e];
+              L2v[e4] = Lv[e4] * c01[e];
+              M2v[e4] = Mv[e4] * c01[e];
+            }
+            const int c = ch0 + 4 * u;
+            st4<T>(sLn + B::at(r, c), Lnv[0], Lnv[1], Lnv[2], Lnv[3]);
+            st4<T>(sQb + B::at(r, c), Qbv[0], Qbv[1], Qbv[2], Qbv[3]);
+            st4<T>(sKh + B::at(r, c), Khv[0], Khv[1], Khv[2], Khv[3]);
+            st4<T>(sLM + B::at(r, c), Lv[0], Lv[1], Lv[2], Lv[3]);
+            st4<T>(sR + B::at(r, c), Rv[0], Rv[1], Rv[2], Rv[3]);
+            if (qd >= 2) {
+              st4<T>(sL2 + B::at(r - 8, c), L2v[0], L2v[1], L2v[2], L2v[3]);
+              st4<T>(sM2 + B::at(r - 8, c), M2v[0], M2v[1], M2v[2], M2v[3]);
+            }
+            bf16x2 h0 = {(bf16)Mv[0], (bf16)Mv[1]};
+            bf16x2 h1 = {(bf16)Mv[2], (bf16)Mv[3]};
+            mpk[i][2 * u] = __builtin_bit_cast(uint32_t, h0);
+            mpk[i][2 * u + 1] = __builtin_bit_cast(uint32_t, h1);
+          }
+        }
+        const bool bad = __any(!(worst <= kRange));
+        if (lane == 0) flagp(slot)[pw] = bad ? 1 : 0;
+        // next chunk's raw inputs (the last chunk re-reads itself)
+        load(ci + 1 < nchunks ? ci + 1 : ci);
+
+        // Gram blocks; L carries the sign, so L . R = -A = N.  Layouts
+        // (lane = 16 g + j):
+        //   ac = L_{4g+i} . R_j     = N[t][s], t = 4g+i, s = j
+        //   ar = R_{4g+i} . L_j     = N[t][s], t = j, s = 4g+i
+        //   a2c, a2r: the same with L'' (lower-left quadrant only)
+        //   p1 = R_{4g+i} . M_j, p2 = R_{4g+i} . M''_j = P[t][s], t = j, s = 4g+i
+        Frag8<T> rf[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) rf[kb] = ld_frag8<T>(sR + B::at(j, 32 * kb + 8 * g));
+        f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ar = ac, a2c = ac, a2r = ac, p1 = ac, p2 = ac;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const Frag8<T> lf = ld_frag8<T>(sLM + B::at(j, 32 * kb + 8 * g));
+          const Frag8<T> l2f = ld_frag8<T>(sL2 + B::at(j & 7, 32 * kb + 8 * g));
+          const Frag8<T> m2f = ld_frag8<T>(sM2 + B::at(j & 7, 32 * kb + 8 * g));
+          mma32(ac, lf, rf[kb]);
+          mma32(ar, rf[kb], lf);
+          mma32(a2c, l2f, rf[kb]);
+          mma32(a2r, rf[kb], l2f);
+          mma32(p2, rf[kb], m2f);
+        }
+        // M replaces L in the shared rows (this wave's LDS operations run in
+        // order, so the L fragment reads above complete first)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * qd + i;
+#pragma unroll
+          for (int u = 0; u < CPL / 4; ++u)
+            *reinterpret_cast<uint2*>(sLM + B::at(r, ch0 + 4 * u)) = make_uint2(mpk[i][2 * u], mpk[i][2 * u + 1]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const Frag8<T> mf = ld_frag8<T>(sLM + B::at(j, 32 * kb + 8 * g));
+          mma32(p1, rf[kb], mf);
+        }
+        // N strictly lower in both layouts; P lower incl. diagonal.  Selects
+        // (not products) drop the unused quadrants, which may hold inf or NaN
+        // from the factors' products.
+        Frag4<float> nr, nc;
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tc = 4 * g + i;  // t of ac, s of ar
+          const float av = (tc >= 8 && j < 8) ? a2c[i] : ac[i];
+          nc.v[i] = (j < tc) ? av : 0.f;
+          const float bvv = (j >= 8 && tc < 8) ? a2r[i] : ar[i];
+          nr.v[i] = (tc < j) ? bvv : 0.f;
+          const float pp = (j >= 8 && tc < 8) ? p2[i] : p1[i];
+          pv[i] = (tc <= j) ? pp : 0.f;
+        }
+        const Frag4<float> tt = unit_lower_inverse(nr, nc, g, j);
+        st4<T>(tblk(slot, pw) + j * 16 + 4 * g, tt.v[0], tt.v[1], tt.v[2], tt.v[3]);
+        st4<T>(pblk(slot, pw) + j * 16 + 4 * g, pv[0], pv[1], pv[2], pv[3]);
+      };
+
+      load(0);
+      produce(0);
+      __syncthreads();
+      for (int64_t ci = 0; ci < nchunks; ++ci) {
+        if (ci + 1 < nchunks) produce(ci + 1);
+        __syncthreads();
+      }
+    } else {
+      // Scalar gates.  lane (g, j): token j of the sub-block, channels
+      // 32 kb + 8 g .. + 7 of every 32-channel block (the MFMA fragment).
+      Raw<16> rq[KB], rk[KB];
+      uint32_t ub = 0u, ug = 0u;
+      auto load = [&](int64_t ci) {
+        int64_t t = ci * kC + kSB * pw + j;
+        t = t < Tn - 1 ? t : Tn - 1;
+        const uint64_t tu = (uint64_t)t;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          ld_raw<16>(bq + (tu * qk_tok + (uint32_t)((32 * kb + 8 * g) * 2)), rq[kb]);
+          ld_raw<16>(bk + (tu * qk_tok + (uint32_t)((32 * kb + 8 * g) * 2)), rk[kb]);
+        }
+        ub = ld_word<GT>(bbs + tu * gs_tok);
+        if constexpr (HAS_G) ug = ld_word<GT>(bgs + tu * gs_tok);
+      };
+      auto produce = [&](int64_t ci) {
+        const int slot = (int)(ci & 1);
+        const bool present = ci * kC + kSB * pw + j < Tn;
+        Frag8<T> kf[KB], qf[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          if (!present) { zero_raw(rq[kb]); zero_raw(rk[kb]); }
+          kf[kb].v = __builtin_bit_cast(bf16x8, make_uint4(rk[kb].w[0], rk[kb].w[1], rk[kb].w[2], rk[kb].w[3]));
+          qf[kb].v = __builtin_bit_cast(bf16x8, make_uint4(rq[kb].w[0], rq[kb].w[1], rq[kb].w[2], rq[kb].w[3]));
+        }
+        const float beta = present ? word_f32<GT>(ub) : 0.f;
+        float x = (HAS_G && present) ? word_f32<GT>(ug) * kLog2e : 0.f;
+        // inclusive prefix over the 16 tokens of the row
+        x += dpp_row_shr(x, 1);
+        x += dpp_row_shr(x, 2);
+        x += dpp_row_shr(x, 4);
+        x += dpp_row_shr(x, 8);
+        const float G = x;
+        const float g15 = dpp_row_bcast<15>(G);
+        // largest rise G_t - min_{s<=t} G_s (0 when alpha <= 1)
+        float mn = G;
+        mn = fminf(mn, dpp_row_shr_inf(mn, 1));
+        mn = fminf(mn, dpp_row_shr_inf(mn, 2));
+        mn = fminf(mn, dpp_row_shr_inf(mn, 4));
+        mn = fminf(mn, dpp_row_shr_inf(mn, 8));
+        const float worst = fmaxf(fmaxf(G, g15 - G), G - mn);
+        const bool bad = __any(!(worst <= kRange));
+        const float fo = exp2_fast(G);
+        float* fv = vecp(slot) + pw * 6 * 16;
+        if (g == 0) {
+          fv[kFX * 16 + j] = -beta * fo;
+          fv[kFO * 16 + j] = fo;
+          fv[kFK * 16 + j] = exp2_fast(g15 - G);
+          fv[kFB * 16 + j] = beta;
+          fv[kFG * 16 + j] = G;
+          if (j == 0) fv[kFD * 16] = exp2_fast(g15);
+        }
+        if (lane == 0) flagp(slot)[pw] = bad ? 1 : 0;
+        // raw k and q rows for the consumers
+        T* sK = opblk(slot, 0, pw);
+        T* sQ = opblk(slot, 1, pw);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          *reinterpret_cast<uint4*>(sK + B::at(j, 32 * kb + 8 * g)) =
+              make_uint4(rk[kb].w[0], rk[kb].w[1], rk[kb].w[2], rk[kb].w[3]);
+          *reinterpret_cast<uint4*>(sQ + B::at(j, 32 * kb + 8 * g)) =
+              make_uint4(rq[kb].w[0], rq[kb].w[1], rq[kb].w[2], rq[kb].w[3]);
+        }
+        load(ci + 1 < nchunks ? ci + 1 : ci);
+        // Gram blocks: kk[4g+i][j] = k_{4g+i} . k_j, pq[4g+i][j] = k_{4g+i} . q_j
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f}, pq = kk;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          mma32(kk, kf[kb], kf[kb]);
+          mma32(pq, kf[kb], qf[kb]);
+        }
+        const float4 G4 = *reinterpret_cast<const float4*>(fv + kFG * 16 + 4 * g);
+        const float4 B4 = *reinterpret_cast<const float4*>(fv + kFB * 16 + 4 * g);
+        const float Gs[4] = {G4.x, G4.y, G4.z, G4.w};
+        const float Bs[4] = {B4.x, B4.y, B4.z, B4.w};
+        Frag4<float> nr, nc;
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tc = 4 * g + i;
+          // exponents are taken only where t >= s, so they are <= the rise
+          const float dcol = exp2_fast((j < tc) ? Gs[i] - G : 0.f);   // t = tc, s = j
+          const float drow = exp2_fast((tc <= j) ? G - Gs[i] : 0.f);  // t = j, s = tc
+          nc.v[i] = (j < tc) ? -Bs[i] * dcol * kk[i] : 0.f;
+          nr.v[i] = (tc < j) ? -beta * drow * kk[i] : 0.f;
+          pv[i] = (tc <= j) ? drow * pq[i] : 0.f;
+        }
+        const Frag4<float> tt = unit_lower_inverse(nr, nc, g, j);
+        st4<T>(tblk(slot, pw) + j * 16 + 4 * g, tt.v[0], tt.v[1], tt.v[2], tt.v[3]);
+        st4<T>(pblk(slot, pw) + j * 16 + 4 * g, pv[0], pv[1], pv[2], pv[3]);
+      };
+      load(0);
+      produce(0);
+      __syncthreads();
+      for (int64_t ci = 0; ci < nchunks; ++ci) {
+        if (ci + 1 < nchunks) produce(ci + 1);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+
+  // ===================================================================
+  // Consumer wave w: state columns col = c0 + 16 w + j; accumulator tile
+  // 2kb + h, row 4g + i <-> channel 32kb + 8g + 4h + i.
+  // ===================================================================
+  const int col = c0 + 16 * wave + j;
+  f32x4 S[MT];
+  {
+    const float* sin = p.state_in ? p.state_in + head * (int64_t)DK * DV : nullptr;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + i;
+        S[t][i] = sin ? sin[row * DV + col] : 0.f;
+      }
+  }
+  const uint32_t v_tok = (uint32_t)(p.Hv * DV * 2);
+  const uint32_t w_tok = (uint32_t)(p.Hv * DV * (int)sizeof(GT));
+  const char* bv = reinterpret_cast<const char*>(gv) + ((uint64_t)tok0 * v_tok + (uint32_t)((hv * DV + col) * 2));
+  const char* bw = reinterpret_cast<const char*>(gw) + ((uint64_t)tok0 * w_tok + (uint32_t)((hv * DV + col) * (int)sizeof(GT)));
+  // v (and w) of the 16 tokens 16 sb + 4 g + i of a chunk for this column,
+  // two tokens per register (d16 loads): zv/zw are prefetched a chunk ahead,
+  // cv/cw hold the chunk being consumed.  fp32 write gates keep one per word.
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  constexpr int WPW = sizeof(GT) == 2 ? 2 : 1;  // w tokens per word
+  u16x2 zv[NSB][2], cv[NSB][2];
+  uint32_t zw[NSB][4 / WPW], cw[NSB][4 / WPW];
+  auto load_z = [&](int64_t ci) {
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int64_t t0 = ci * kC + kSB * sb + 4 * g + 2 * h;
+        int64_t t1 = t0 + 1;
+        t0 = t0 < Tn - 1 ? t0 : Tn - 1;
+        t1 = t1 < Tn - 1 ? t1 : Tn - 1;
+        u16x2 pv;
+        pv.x = *reinterpret_cast<const unsigned short*>(bv + (uint64_t)t0 * v_tok);
+        pv.y = *reinterpret_cast<const unsigned short*>(bv + (uint64_t)t1 * v_tok);
+        zv[sb][h] = pv;
+        if constexpr (CHANNEL) {
+          if constexpr (WPW == 2) {
+            u16x2 pw2;
+            pw2.x = *reinterpret_cast<const unsigned short*>(bw + (uint64_t)t0 * w_tok);
+            pw2.y = *reinterpret_cast<const unsigned short*>(bw + (uint64_t)t1 * w_tok);
+            zw[sb][h] = __builtin_bit_cast(uint32_t, pw2);
+          } else {
+            zw[sb][2 * h] = *reinterpret_cast<const uint32_t*>(bw + (uint64_t)t0 * w_tok);
+            zw[sb][2 * h + 1] = *reinterpret_cast<const uint32_t*>(bw + (uint64_t)t1 * w_tok);
+          }
+        }
+      }
+  };
+  // value of token 4g + i of sub-block sb from the packed words
+  auto zval = [&](int sb, int i) -> float {
+    const u16x2 pv = cv[sb][i >> 1];
+    return __uint_as_float(((uint32_t)((i & 1) ? pv.y : pv.x)) << 16);
+  };
+  auto wval = [&](int sb, int i) -> float {
+    if constexpr (WPW == 2) {
+      const uint32_t w = cw[sb][i >> 1];
+      return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+      return __uint_as_float(cw[sb][i]);
+    }
+  };
+
+  // Exact token-by-token recurrence for tokens [tb, min(tb + 16, Tn)).
+  auto tokens_path = [&](int64_t tb) {
+    for (int tl = 0; tl < kSB; ++tl) {
+      const int64_t tok = tb + tl;
+      if (tok >= Tn) break;
+      const int64_t qk_off = ((tok0 + tok) * p.Hk + hk) * (int64_t)DK;
+      const int64_t gt = (tok0 + tok) * p.Hv + hv;
+      float sbeta = 0.f, salpha = 1.f;
+      if constexpr (!CHANNEL) {
+        sbeta = to_f32(gb[gt]);
+        if constexpr (HAS_G) salpha = exp2_fast(to_f32(gg[gt]) * kLog2e);
+      }
+      float rp = 0.f;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int row = 32 * (t >> 1) + 8 * g + 4 * (t & 1);
+        float kr[4], er[4], ar[4];
+        load_f32<4, T>(gk + qk_off + row, kr);
+        if constexpr (CHANNEL) {
+          load_f32<4, GT>(gb + gt * DK + row, er);
+          if constexpr (HAS_G) {
+            load_f32<4, GT>(gg + gt * DK + row, ar);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ar[i] = exp2_fast(ar[i] * kLog2e);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ar[i] = 1.f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { er[i] = sbeta; ar[i] = salpha; }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          S[t][i] *= ar[i];
+          rp += er[i] * kr[i] * S[t][i];
+        }
+      }
+      rp += __shfl_xor(rp, 16);
+      rp += __shfl_xor(rp, 32);
+      float z = to_f32(gv[gt * DV + col]);
+      if constexpr (CHANNEL) z *= to_f32(gw[gt * DV + col]);
+      else z *= sbeta;
+      const float d = z - rp;
+      float op = 0.f;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int row = 32 * (t >> 1) + 8 * g + 4 * (t & 1);
+        float kr[4], qr[4];
+        load_f32<4, T>(gk + qk_off + row, kr);
+        load_f32<4, T>(gq + qk_off + row, qr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          S[t][i] += kr[i] * d;
+          op += qr[i] * S[t][i];
+        }
+      }
+      op += __shfl_xor(op, 16);
+      op += __shfl_xor(op, 32);
+      if (g == 0) go[gt * DV + col] = from_f32<T>(p.scale * op);
+    }
+  };
+
+  // One sub-block on the MFMA path.  zpre: take v (and w) from the
+  // prefetched words (the unrolled common loop) or load them here (the loop
+  // of a chunk that holds a sub-block on the exact path).
+  auto sub_block = [&](int slot, int sb, int64_t tb, auto zpre) {
+    const T* sA = opblk(slot, 0, sb);                    // Ln | k
+    const T* sQ = opblk(slot, 1, sb);                    // Qb | q
+    const T* sK = opblk(slot, CHANNEL ? 2 : 0, sb);      // Kh | k
+    const float* fv = vecp(slot) + (CHANNEL ? sb * DK : sb * 6 * 16);
+    Frag8<T> sf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sf[kb] = frag8_from_acc<T>(S[2 * kb], S[2 * kb + 1]);
+    f32x4 X, O = {0.f, 0.f, 0.f, 0.f};
+    float zz[4], ww[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = tb + 4 * g + i;
+      if constexpr (decltype(zpre)::value) {
+        zz[i] = zval(sb, i);
+        ww[i] = CHANNEL ? wval(sb, i) : 0.f;
+      } else {
+        const int64_t tc = t < Tn - 1 ? t : Tn - 1;
+        zz[i] = to_f32(gv[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]);
+        ww[i] = CHANNEL ? to_f32(gw[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]) : 0.f;
+      }
+      if (t >= Tn) zz[i] = 0.f;
+    }
+    if constexpr (CHANNEL) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[i] = zz[i] * ww[i];
+    } else {
+      X = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const Frag8<T> af = ld_frag8<T>(sA + B::at(j, 32 * kb + 8 * g));
+      const Frag8<T> qf = ld_frag8<T>(sQ + B::at(j, 32 * kb + 8 * g));
+      mma32(X, af, sf[kb]);   // X[4g+i][j]: token 4g+i, column j
+      mma32(O, sf[kb], qf);   // O[4g+i][j]: column 4g+i, token j
+    }
+    float fk[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (!CHANNEL) {
+      const float4 fx = *reinterpret_cast<const float4*>(fv + kFX * 16 + 4 * g);
+      const float4 fb = *reinterpret_cast<const float4*>(fv + kFB * 16 + 4 * g);
+      const float4 f4 = *reinterpret_cast<const float4*>(fv + kFK * 16 + 4 * g);
+      const float fo = fv[kFO * 16 + j];
+      X[0] = fmaf(fx.x, X[0], fb.x * zz[0]);
+      X[1] = fmaf(fx.y, X[1], fb.y * zz[1]);
+      X[2] = fmaf(fx.z, X[2], fb.z * zz[2]);
+      X[3] = fmaf(fx.w, X[3], fb.w * zz[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[i] *= fo;
+      fk[0] = f4.x; fk[1] = f4.y; fk[2] = f4.z; fk[3] = f4.w;
+    }
+    const Frag4<T> xf = frag4_from_acc<T>(X);
+    const Frag4<T> td = ld_frag4<T>(tblk(slot, sb) + j * 16 + 4 * g);
+    f32x4 U = {0.f, 0.f, 0.f, 0.f};
+    mma16(U, td, xf);  // U[4g+i][j]
+    const Frag4<T> uo = frag4_from_acc<T>(U);
+    Frag4<T> uk = uo;
+    if constexpr (!CHANNEL) {
+      f32x4 us = {U[0] * fk[0], U[1] * fk[1], U[2] * fk[2], U[3] * fk[3]};
+      uk = frag4_from_acc<T>(us);
+    }
+    const Frag4<T> pf = ld_frag4<T>(pblk(slot, sb) + j * 16 + 4 * g);
+    mma16(O, uo, pf);
+    // state: S = Diag(D) S + Kh^T U
+    if constexpr (CHANNEL) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const float4 d4 = *reinterpret_cast<const float4*>(fv + 32 * (t >> 1) + 8 * g + 4 * (t & 1));
+        S[t][0] *= d4.x; S[t][1] *= d4.y; S[t][2] *= d4.z; S[t][3] *= d4.w;
+      }
+    } else if constexpr (HAS_G) {
+      const float dsc = fv[kFD * 16];
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][i] *= dsc;
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const Frag4<T> kt = ld_tr16(sK + B::at(4 * g + (j >> 2), 32 * (t >> 1) + 8 * (j & 3) + 4 * (t & 1)));
+      mma16(S[t], kt, uk);
+    }
+    const int64_t tok = tb + j;
+    if (tok < Tn) {
+      T* dst = go + ((tok0 + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + 4 * g;
+      st4<T>(dst, p.scale * O[0], p.scale * O[1], p.scale * O[2], p.scale * O[3]);
+    }
+  };
+
+  load_z(0);
+  __syncthreads();  // chunk 0 is ready
+  for (int64_t ci = 0; ci < nchunks; ++ci) {
+    const int slot = (int)(ci & 1);
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) cv[sb][h] = zv[sb][h];
+#pragma unroll
+      for (int h = 0; h < 4 / WPW; ++h) cw[sb][h] = zw[sb][h];
+    }
+    load_z(ci + 1 < nchunks ? ci + 1 : ci);
+    const int* fl = flagp(slot);
+    if ((fl[0] | fl[1] | fl[2] | fl[3]) == 0) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int64_t tb = ci * kC + kSB * sb;
+        if (tb < Tn) sub_block(slot, sb, tb, IntTag<1>{});
+      }
+    } else {
+      // a chunk with a sub-block whose decay range the factored form cannot
+      // hold: that sub-block runs the exact recurrence, the others as usual
+#pragma unroll 1
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int64_t tb = ci * kC + kSB * sb;
+        if (tb < Tn) {
+          if (fl[sb]) tokens_path(tb);
+          else sub_block(slot, sb, tb, IntTag<0>{});
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (p.state_out) {
+    float* sout = p.state_out + head * (int64_t)DK * DV;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + i;
+        sout[row * DV + col] = S[t][i];
+      }
+  }
+}
+
+template <typename GT, int DK, int DV, bool CH, bool HG>
+hipError_t launch_sb_typed(const ChunkArgs& a, hipStream_t stream) {
+  Params p;
+  p.B = a.B; p.T = a.T; p.cu = a.cu_seqlens; p.Hk = a.Hk; p.Hv = a.Hv; p.scale = a.scale;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.b = a.b; p.w = a.w; p.g = a.g;
+  p.state_in = a.state_in; p.state_out = a.state_out; p.o = a.o;
+  const int64_t nwg = a.B * a.Hv * (DV / 64);
+  chunk_fwd_sb_kernel<GT, DK, DV, CH, HG><<<dim3((unsigned)nwg), dim3(kSbThreads), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <typename GT, int DK, int DV>
+hipError_t sb_gates(const ChunkArgs& a, hipStream_t s) {
+  const bool hg = a.g != nullptr;
+  if (a.channel) return hg ? launch_sb_typed<GT, DK, DV, true, true>(a, s)
+                           : launch_sb_typed<GT, DK, DV, true, false>(a, s);
+  return hg ? launch_sb_typed<GT, DK, DV, false, true>(a, s)
+            : launch_sb_typed<GT, DK, DV, false, false>(a, s);
+}
+
+template <typename GT>
+hipError_t sb_dims(const ChunkArgs& a, hipStream_t s) {
+  if (a.dk == 128 && a.dv == 128) return sb_gates<GT, 128, 128>(a, s);
+  if (a.dk == 128 && a.dv == 64) return sb_gates<GT, 128, 64>(a, s);
+  if (a.dk == 64 && a.dv == 128) return sb_gates<GT, 64, 128>(a, s);
+  return sb_gates<GT, 64, 64>(a, s);
+}
+
+}  // namespace
+
+// bf16 operands: sub-block producer/consumer kernel.
+hipError_t launch_chunk_fwd_sb(const ChunkArgs& a, hipStream_t stream) {
+  if (a.gate == DType::F32) return sb_dims<float>(a, stream);
+  return sb_dims<bf16>(a, stream);
+}
+
+}  // namespace gdn

@@ -103,8 +103,8 @@ hipError_t launch_output_gate(const NormArgs& a, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream);
-// bf16-operand producer/consumer variant (called by launch_chunk_fwd).
-hipError_t launch_chunk_fwd_pipe(const ChunkArgs& a, hipStream_t stream);
+// bf16-operand sub-block variant (called by launch_chunk_fwd).
+hipError_t launch_chunk_fwd_sb(const ChunkArgs& a, hipStream_t stream);
 // state_out = state_in (or 0 when state_in is NULL) for n floats; used when
 // there are no tokens to process.
 hipError_t launch_state_copy(const float* state_in, float* state_out, int64_t n,
