@@ -258,6 +258,36 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
     return res
 
 
+def single_workload(gdn, synth, torch, dev, name, steps, warmup):
+    """gdn_chunk_fwd alone on one workload, warm back-to-back launches."""
+    base = name[:-len("_mamba2_gates")] if name.endswith("_mamba2_gates") else name
+    cfg = synth.CONFIGS[base]
+    inp = synth.chunk_inputs(cfg, device="cuda")
+    if base != name:
+        g, beta, w = realistic_gates(gdn, synth, torch, cfg)
+        inp["g"], inp["beta_or_b"] = g.reshape(inp["g"].shape), beta.reshape(inp["g"].shape)
+        if cfg.channel:
+            inp["w"] = w.reshape(inp["v"].shape)
+    o = torch.empty((cfg.B, cfg.T, cfg.Hv, cfg.dv), dtype=cfg.io_dtype, device=dev)
+    s = torch.empty((cfg.B, cfg.Hv, cfg.dk, cfg.dv), dtype=torch.float32, device=dev)
+
+    def run():
+        gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta_or_b"], w=inp["w"], g=inp["g"],
+                          state_in=inp["state_in"], state_out=s, o=o)
+    for _ in range(warmup):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        run()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    return {"workload": name, "ms": round(ms, 4),
+            "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1)}
+
+
 def copy_bandwidth(torch, dev):
     """A plain 2 GiB device-to-device copy through torch: read + write bytes
     per second, the practical streaming rate beside the 8 TB/s nominal peak."""
@@ -511,6 +541,10 @@ def main():
                     help="skip the timings of the block operations around the recurrence")
     ap.add_argument("--cpu-threads", type=int, default=16,
                     help="cap on oracle threads (the box's CPU share)")
+    ap.add_argument("--workload", default=None,
+                    help="time only gdn_chunk_fwd on this workload (a key of synth.CONFIGS, "
+                         "optionally with the suffix _mamba2_gates) and print its timing; "
+                         "for profiling one kernel in isolation")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KERNEL_STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
@@ -536,6 +570,10 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.workload:
+        print(json.dumps(single_workload(gdn, synth, torch, dev, args.workload, args.steps,
+                                         args.warmup)), flush=True)
+        return
     cfg_c = synth.CONFIGS["gdn2_bf16_train"]
     cfg_d = synth.CONFIGS["gdn2_decode"]
     inp_c = synth.chunk_inputs(cfg_c, device="cuda")
