@@ -62,16 +62,20 @@ constexpr int kSbThreads = 512;   // 4 consumer + 4 producer waves
 constexpr float kRange = 110.f;   // largest |G - m_h| (log2) of the factored form
 
 // One [16][DK] bf16 operand block.  Rows are DK contiguous channels; the
-// 16-byte chunks of a row are XOR-swizzled by the row so that a fragment read
-// (16 rows, one chunk) and a producer store (4 rows, all chunks) both spread
-// over every bank.
+// 16-byte chunks of a row are XOR-swizzled by the row.  For DK = 128 (16
+// chunks per row, one 256-byte bank period) row r = 4x + y flips the chunk
+// index by s = 4 (x ^ y) + x: a fragment read (16 rows, one chunk), the
+// transposing read (rows 4x .. 4x + 3, four chunks) and a producer store
+// (rows 4x + y over x, all chunks of a lane quad) each reach 16 distinct
+// 16-byte bank groups.  DK = 64 shares a bank period between two rows.
 template <int DK>
 struct Blk {
   static constexpr int NCH = DK / 8;
-  static constexpr int RPB = NCH >= 16 ? 1 : 16 / NCH;
   static constexpr int BYTES = 16 * DK * 2;
   __device__ static int at(int r, int c) {
-    const int sw = (r / RPB) % NCH;
+    int sw;
+    if constexpr (NCH >= 16) sw = 4 * ((r >> 2) ^ (r & 3)) + (r >> 2);
+    else sw = (r >> 1) % NCH;
     return r * DK + ((((c >> 3) ^ sw)) << 3) + (c & 7);
   }
 };
@@ -88,8 +92,8 @@ struct SbLds {
   static constexpr int VEC = CHANNEL ? 4 * DK * 4 : 4 * 6 * 16 * 4;
   static constexpr int kFlag = kVec + VEC;
   static constexpr int SLOT = kFlag + 16;
-  static constexpr int kPriv = 2 * SLOT;         // channel: per producer wave LM, R, L2|M2
-  static constexpr int PRIV = CHANNEL ? 3 * BLK : 0;
+  static constexpr int kPriv = 2 * SLOT;         // channel: per producer wave L|M, R, R'
+  static constexpr int PRIV = CHANNEL ? 5 * BLK / 2 : 0;
   static constexpr int kTotal = kPriv + 4 * PRIV;
   static_assert(kTotal <= 160 * 1024, "LDS budget");
 };
@@ -127,6 +131,19 @@ __device__ __forceinline__ float dpp_row_shr_inf(float x, int n) {
     default: r = __builtin_amdgcn_update_dpp(inf, v, 0x118, 0xf, 0xf, false); break;
   }
   return __builtin_bit_cast(float, r);
+}
+
+// Two fp32 values rounded to bf16 (nearest even) in one 32-bit word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 h = {(bf16)a, (bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// N packed words to LDS in one store (16 or 8 bytes).
+template <int N>
+__device__ __forceinline__ void st_words(bf16* p, const uint32_t* w) {
+  if constexpr (N == 4) *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  else *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
 }
 
 typedef short sb_v4s __attribute__((ext_vector_type(4)));
@@ -283,33 +300,56 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       Raw<GB> rb[4], rg[4];
       const uint32_t oq = (uint32_t)(ch0 * 2);
       const uint32_t og = (uint32_t)(ch0 * (int)sizeof(GT));
+      // addressing: a wave-uniform 64-bit base per sub-block plus a per-lane
+      // 32-bit offset.  A sub-block that is not whole (the last chunk; it may
+      // even start past the end) clamps absolute token indices to the last
+      // token instead.
       auto load = [&](int64_t ci) {
-        const int64_t tb = ci * kC + kSB * pw + 4 * qd;  // first token of this lane
-        const int64_t last = Tn - 1;
+        const int64_t t0 = ci * kC + kSB * pw;          // first token of the sub-block
+        if (t0 + kSB <= Tn) {                           // wave-uniform
+          const uint64_t tu = (uint64_t)t0;
+          const char* cq = bq + tu * qk_tok;
+          const char* ck = bk + tu * qk_tok;
+          const char* cb = bbc + tu * gc_tok;
+          const char* cg2 = bgc + tu * gc_tok;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int64_t t = tb + i;
-          t = t < last ? t : last;
-          const uint64_t tu = (uint64_t)t;
-          ld_raw<QB>(bq + (tu * qk_tok + oq), rq[i]);
-          ld_raw<QB>(bk + (tu * qk_tok + oq), rk[i]);
-          ld_raw<GB>(bbc + (tu * gc_tok + og), rb[i]);
-          if constexpr (HAS_G) ld_raw<GB>(bgc + (tu * gc_tok + og), rg[i]);
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t tl = (uint32_t)(4 * qd + i);
+            ld_raw<QB>(cq + (tl * qk_tok + oq), rq[i]);
+            ld_raw<QB>(ck + (tl * qk_tok + oq), rk[i]);
+            ld_raw<GB>(cb + (tl * gc_tok + og), rb[i]);
+            if constexpr (HAS_G) ld_raw<GB>(cg2 + (tl * gc_tok + og), rg[i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            int64_t t = t0 + 4 * qd + i;
+            t = t < Tn - 1 ? t : Tn - 1;
+            const uint64_t tu = (uint64_t)t;
+            ld_raw<QB>(bq + (tu * qk_tok + oq), rq[i]);
+            ld_raw<QB>(bk + (tu * qk_tok + oq), rk[i]);
+            ld_raw<GB>(bbc + (tu * gc_tok + og), rb[i]);
+            if constexpr (HAS_G) ld_raw<GB>(bgc + (tu * gc_tok + og), rg[i]);
+          }
         }
       };
       T* priv = reinterpret_cast<T*>(smem + L::kPriv + pw * L::PRIV);
-      T* sLM = priv;
-      T* sR = priv + 16 * DK;
-      T* sL2 = priv + 32 * DK;   // rows 8..15 of L'' as rows 0..7
-      T* sM2 = priv + 40 * DK;   // rows 8..15 of M'' as rows 0..7
+      T* sLM = priv;              // L, then M (rows 0..15)
+      T* sR = priv + 16 * DK;     // R (rows 0..15)
+      T* sR2 = priv + 32 * DK;    // R' = R exp(m1 - m0), rows 0..7
 
       auto produce = [&](int64_t ci) {
         const int slot = (int)(ci & 1);
-        const int64_t tb = ci * kC + kSB * pw + 4 * qd;
-        // absent tokens (past the end): q = k = b = 0, g = 0
-        bool present[4];
+        // absent tokens of a partial last chunk: q = k = b = 0, g = 0
+        if (ci * kC + kSB * pw + kSB > Tn) {
+          const int64_t tb = ci * kC + kSB * pw + 4 * qd;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) present[i] = tb + i < Tn;
+          for (int i = 0; i < 4; ++i)
+            if (tb + i >= Tn) {
+              zero_raw(rq[i]); zero_raw(rk[i]); zero_raw(rb[i]);
+              if constexpr (HAS_G) zero_raw(rg[i]);
+            }
+        }
         // cumulative log2-decay over the sub-block: 4 tokens in-thread, then
         // an exclusive scan over the 4 token quads of the lane quad
         float G[4][CPL];
@@ -318,10 +358,6 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           if constexpr (HAS_G) {
             unpack<GT, CPL>(rg[i], G[i]);
           } else {
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) G[i][e] = 0.f;
-          }
-          if (!present[i]) {
 #pragma unroll
             for (int e = 0; e < CPL; ++e) G[i][e] = 0.f;
           }
@@ -353,12 +389,14 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           c01[e] = exp2_fast(m1 - m0);
           // channel decay of the whole sub-block (one lane per channel group)
           if (qd == 0) dvec[e] = exp2_fast(g15);
-          // exponents that could overflow only when some g > 0
-          worst = fmaxf(worst, fmaxf(fmaxf(mh[e], g15 - mh[e]), fmaxf(m1 - m0, g15)));
+          // per-channel factors that exceed 1 only when some g > 0; each
+          // may reach 2^10 so that no product of two factors overflows
+          worst = fmaxf(worst, fmaxf(fmaxf(mh[e], g15 - mh[e]), fmaxf(m1 - m0, g15)) +
+                                   (kRange - 10.f));
         }
-        // gated operands, token by token and 4 channels at a time; M waits in
-        // registers until the L rows it shares storage with have been read by
-        // the Gram products
+        // gated operands, token by token; each operand row of the lane's
+        // CPL channels goes out as one store.  M waits in registers until the
+        // L rows it shares storage with have been read by the Gram products.
         T* sLn = opblk(slot, 0, pw);
         T* sQb = opblk(slot, 1, pw);
         T* sKh = opblk(slot, 2, pw);
@@ -369,44 +407,37 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           unpack<T, CPL>(rq[i], qv);
           unpack<T, CPL>(rk[i], kv);
           unpack<GT, CPL>(rb[i], bv);
-          const int r = 4 * qd + i;
+          uint32_t wLn[CPL / 2], wQb[CPL / 2], wKh[CPL / 2], wL[CPL / 2], wR[CPL / 2], wR2[CPL / 2];
 #pragma unroll
-          for (int u = 0; u < CPL / 4; ++u) {
-            float Lv[4], Mv[4], Rv[4], Lnv[4], Qbv[4], Khv[4], L2v[4], M2v[4];
+          for (int e2 = 0; e2 < CPL / 2; ++e2) {
+            float Lv[2], Mv[2], Rv[2];
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-              const int e = 4 * u + e4;
-              const float qq = present[i] ? qv[e] : 0.f;
-              const float kk = present[i] ? kv[e] : 0.f;
-              const float bb = present[i] ? bv[e] : 0.f;
+            for (int h = 0; h < 2; ++h) {
+              const int e = 2 * e2 + h;
               const float x = G[i][e] - mh[e];
               worst = fmaxf(worst, fabsf(x));
               const float e1 = exp2_fast(x);
-              const float e2 = exp2_fast(-x);
-              Lv[e4] = -(bb * kk) * e1;
-              Mv[e4] = qq * e1;
-              Rv[e4] = kk * e2;
-              Lnv[e4] = Lv[e4] * fln[e];
-              Qbv[e4] = Mv[e4] * fln[e];
-              Khv[e4] = Rv[e4] * fkh[e];
-              L2v[e4] = Lv[e4] * c01[e];
-              M2v[e4] = Mv[e4] * c01[e];
+              const float e2v = exp2_fast(-x);
+              Lv[h] = -(bv[e] * kv[e]) * e1;
+              Mv[h] = qv[e] * e1;
+              Rv[h] = kv[e] * e2v;
             }
-            const int c = ch0 + 4 * u;
-            st4<T>(sLn + B::at(r, c), Lnv[0], Lnv[1], Lnv[2], Lnv[3]);
-            st4<T>(sQb + B::at(r, c), Qbv[0], Qbv[1], Qbv[2], Qbv[3]);
-            st4<T>(sKh + B::at(r, c), Khv[0], Khv[1], Khv[2], Khv[3]);
-            st4<T>(sLM + B::at(r, c), Lv[0], Lv[1], Lv[2], Lv[3]);
-            st4<T>(sR + B::at(r, c), Rv[0], Rv[1], Rv[2], Rv[3]);
-            if (qd >= 2) {
-              st4<T>(sL2 + B::at(r - 8, c), L2v[0], L2v[1], L2v[2], L2v[3]);
-              st4<T>(sM2 + B::at(r - 8, c), M2v[0], M2v[1], M2v[2], M2v[3]);
-            }
-            bf16x2 h0 = {(bf16)Mv[0], (bf16)Mv[1]};
-            bf16x2 h1 = {(bf16)Mv[2], (bf16)Mv[3]};
-            mpk[i][2 * u] = __builtin_bit_cast(uint32_t, h0);
-            mpk[i][2 * u + 1] = __builtin_bit_cast(uint32_t, h1);
+            const int e = 2 * e2;
+            wLn[e2] = pack_bf16x2(Lv[0] * fln[e], Lv[1] * fln[e + 1]);
+            wQb[e2] = pack_bf16x2(Mv[0] * fln[e], Mv[1] * fln[e + 1]);
+            wKh[e2] = pack_bf16x2(Rv[0] * fkh[e], Rv[1] * fkh[e + 1]);
+            wR2[e2] = pack_bf16x2(Rv[0] * c01[e], Rv[1] * c01[e + 1]);
+            wL[e2] = pack_bf16x2(Lv[0], Lv[1]);
+            wR[e2] = pack_bf16x2(Rv[0], Rv[1]);
+            mpk[i][e2] = pack_bf16x2(Mv[0], Mv[1]);
           }
+          const int r = 4 * qd + i;
+          st_words<CPL / 2>(sLn + B::at(r, ch0), wLn);
+          st_words<CPL / 2>(sQb + B::at(r, ch0), wQb);
+          st_words<CPL / 2>(sKh + B::at(r, ch0), wKh);
+          st_words<CPL / 2>(sLM + B::at(r, ch0), wL);
+          st_words<CPL / 2>(sR + B::at(r, ch0), wR);
+          if (qd < 2) st_words<CPL / 2>(sR2 + B::at(r, ch0), wR2);
         }
         const bool bad = __any(!(worst <= kRange));
         if (lane == 0) flagp(slot)[pw] = bad ? 1 : 0;
@@ -417,37 +448,34 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         // (lane = 16 g + j):
         //   ac = L_{4g+i} . R_j     = N[t][s], t = 4g+i, s = j
         //   ar = R_{4g+i} . L_j     = N[t][s], t = j, s = 4g+i
-        //   a2c, a2r: the same with L'' (lower-left quadrant only)
-        //   p1 = R_{4g+i} . M_j, p2 = R_{4g+i} . M''_j = P[t][s], t = j, s = 4g+i
-        Frag8<T> rf[KB];
+        //   a2c, a2r: the same with R' (lower-left quadrant t >= 8 > s:
+        //     L there has the reference m1, and R' = k exp(m1 - G) <= 1)
+        //   p1 = R_{4g+i} . M_j, p2 = R'_{4g+i} . M_j = P[t][s], t = j, s = 4g+i
+        Frag8<T> rf[KB], r2f[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) rf[kb] = ld_frag8<T>(sR + B::at(j, 32 * kb + 8 * g));
+        for (int kb = 0; kb < KB; ++kb) {
+          rf[kb] = ld_frag8<T>(sR + B::at(j, 32 * kb + 8 * g));
+          r2f[kb] = ld_frag8<T>(sR2 + B::at(j & 7, 32 * kb + 8 * g));
+        }
         f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ar = ac, a2c = ac, a2r = ac, p1 = ac, p2 = ac;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const Frag8<T> lf = ld_frag8<T>(sLM + B::at(j, 32 * kb + 8 * g));
-          const Frag8<T> l2f = ld_frag8<T>(sL2 + B::at(j & 7, 32 * kb + 8 * g));
-          const Frag8<T> m2f = ld_frag8<T>(sM2 + B::at(j & 7, 32 * kb + 8 * g));
           mma32(ac, lf, rf[kb]);
           mma32(ar, rf[kb], lf);
-          mma32(a2c, l2f, rf[kb]);
-          mma32(a2r, rf[kb], l2f);
-          mma32(p2, rf[kb], m2f);
+          mma32(a2c, lf, r2f[kb]);
+          mma32(a2r, r2f[kb], lf);
         }
         // M replaces L in the shared rows (this wave's LDS operations run in
         // order, so the L fragment reads above complete first)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * qd + i;
-#pragma unroll
-          for (int u = 0; u < CPL / 4; ++u)
-            *reinterpret_cast<uint2*>(sLM + B::at(r, ch0 + 4 * u)) = make_uint2(mpk[i][2 * u], mpk[i][2 * u + 1]);
-        }
+        for (int i = 0; i < 4; ++i) st_words<CPL / 2>(sLM + B::at(4 * qd + i, ch0), mpk[i]);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const Frag8<T> mf = ld_frag8<T>(sLM + B::at(j, 32 * kb + 8 * g));
           mma32(p1, rf[kb], mf);
+          mma32(p2, r2f[kb], mf);
         }
         // N strictly lower in both layouts; P lower incl. diagonal.  Selects
         // (not products) drop the unused quadrants, which may hold inf or NaN
@@ -584,6 +612,10 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   // Consumer wave w: state columns col = c0 + 16 w + j; accumulator tile
   // 2kb + h, row 4g + i <-> channel 32kb + 8g + 4h + i.
   // ===================================================================
+  // The consumers' state chain is the latency-critical path; at a higher
+  // issue priority their instructions go first and the producer wave on the
+  // same SIMD fills the gaps.
+  __builtin_amdgcn_s_setprio(3);
   const int col = c0 + 16 * wave + j;
   f32x4 S[MT];
   {
@@ -608,30 +640,51 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   u16x2 zv[NSB][2], cv[NSB][2];
   uint32_t zw[NSB][4 / WPW], cw[NSB][4 / WPW];
   auto load_z = [&](int64_t ci) {
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int64_t t0 = ci * kC + kSB * sb + 4 * g + 2 * h;
-        int64_t t1 = t0 + 1;
-        t0 = t0 < Tn - 1 ? t0 : Tn - 1;
-        t1 = t1 < Tn - 1 ? t1 : Tn - 1;
-        u16x2 pv;
-        pv.x = *reinterpret_cast<const unsigned short*>(bv + (uint64_t)t0 * v_tok);
-        pv.y = *reinterpret_cast<const unsigned short*>(bv + (uint64_t)t1 * v_tok);
-        zv[sb][h] = pv;
-        if constexpr (CHANNEL) {
-          if constexpr (WPW == 2) {
-            u16x2 pw2;
-            pw2.x = *reinterpret_cast<const unsigned short*>(bw + (uint64_t)t0 * w_tok);
-            pw2.y = *reinterpret_cast<const unsigned short*>(bw + (uint64_t)t1 * w_tok);
-            zw[sb][h] = __builtin_bit_cast(uint32_t, pw2);
-          } else {
-            zw[sb][2 * h] = *reinterpret_cast<const uint32_t*>(bw + (uint64_t)t0 * w_tok);
-            zw[sb][2 * h + 1] = *reinterpret_cast<const uint32_t*>(bw + (uint64_t)t1 * w_tok);
-          }
+    const int64_t t0 = ci * kC;
+    const char* cvb = bv + (uint64_t)t0 * v_tok;
+    const char* cwb = bw + (uint64_t)t0 * w_tok;
+    // token (4g + lt) of the chunk; lt = 16 sb + 2 h (+1).  Full chunks: a
+    // wave-uniform offset plus one per-lane term.  The partial last chunk
+    // clamps every token to the last one.
+    auto fetch = [&](int sb, int h, uint32_t ov0, uint32_t ov1, uint32_t ow0, uint32_t ow1) {
+      u16x2 pv;
+      pv.x = *reinterpret_cast<const unsigned short*>(cvb + ov0);
+      pv.y = *reinterpret_cast<const unsigned short*>(cvb + ov1);
+      zv[sb][h] = pv;
+      if constexpr (CHANNEL) {
+        if constexpr (WPW == 2) {
+          u16x2 pw2;
+          pw2.x = *reinterpret_cast<const unsigned short*>(cwb + ow0);
+          pw2.y = *reinterpret_cast<const unsigned short*>(cwb + ow1);
+          zw[sb][h] = __builtin_bit_cast(uint32_t, pw2);
+        } else {
+          zw[sb][2 * h] = *reinterpret_cast<const uint32_t*>(cwb + ow0);
+          zw[sb][2 * h + 1] = *reinterpret_cast<const uint32_t*>(cwb + ow1);
         }
       }
+    };
+    if (t0 + kC <= Tn) {
+      const uint32_t lv = (uint32_t)(4 * g) * v_tok, lw = (uint32_t)(4 * g) * w_tok;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t u = (uint32_t)(kSB * sb + 2 * h);
+          fetch(sb, h, lv + u * v_tok, lv + (u + 1) * v_tok, lw + u * w_tok, lw + (u + 1) * w_tok);
+        }
+    } else {
+      const int lastl = (int)(Tn - 1 - t0);
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int l0 = kSB * sb + 4 * g + 2 * h, l1 = l0 + 1;
+          l0 = l0 < lastl ? l0 : lastl;
+          l1 = l1 < lastl ? l1 : lastl;
+          fetch(sb, h, (uint32_t)l0 * v_tok, (uint32_t)l1 * v_tok, (uint32_t)l0 * w_tok,
+                (uint32_t)l1 * w_tok);
+        }
+    }
   };
   // value of token 4g + i of sub-block sb from the packed words
   auto zval = [&](int sb, int i) -> float {
@@ -718,11 +771,35 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
     const T* sQ = opblk(slot, 1, sb);                    // Qb | q
     const T* sK = opblk(slot, CHANNEL ? 2 : 0, sb);      // Kh | k
     const float* fv = vecp(slot) + (CHANNEL ? sb * DK : sb * 6 * 16);
+    // every operand read is issued first: none depends on the state, so
+    // their LDS latency overlaps the conversions and the first products
+    Frag8<T> af[KB], qf[KB];
+    Frag4<T> kt[MT];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      af[kb] = ld_frag8<T>(sA + B::at(j, 32 * kb + 8 * g));
+      qf[kb] = ld_frag8<T>(sQ + B::at(j, 32 * kb + 8 * g));
+    }
+    const Frag4<T> td = ld_frag4<T>(tblk(slot, sb) + j * 16 + 4 * g);
+    const Frag4<T> pf = ld_frag4<T>(pblk(slot, sb) + j * 16 + 4 * g);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      kt[t] = ld_tr16(sK + B::at(4 * g + (j >> 2), 32 * (t >> 1) + 8 * (j & 3) + 4 * (t & 1)));
+    float4 fx, fb, f4;
+    float fo = 1.f, dsc = 1.f;
+    if constexpr (!CHANNEL) {
+      fx = *reinterpret_cast<const float4*>(fv + kFX * 16 + 4 * g);
+      fb = *reinterpret_cast<const float4*>(fv + kFB * 16 + 4 * g);
+      f4 = *reinterpret_cast<const float4*>(fv + kFK * 16 + 4 * g);
+      fo = fv[kFO * 16 + j];
+      dsc = fv[kFD * 16];
+    }
     Frag8<T> sf[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sf[kb] = frag8_from_acc<T>(S[2 * kb], S[2 * kb + 1]);
     f32x4 X, O = {0.f, 0.f, 0.f, 0.f};
     float zz[4], ww[4];
+    const bool full_sb = tb + kSB <= Tn;  // wave-uniform
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t t = tb + 4 * g + i;
@@ -734,7 +811,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         zz[i] = to_f32(gv[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]);
         ww[i] = CHANNEL ? to_f32(gw[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]) : 0.f;
       }
-      if (t >= Tn) zz[i] = 0.f;
+      if (!full_sb && t >= Tn) zz[i] = 0.f;
     }
     if constexpr (CHANNEL) {
 #pragma unroll
@@ -744,17 +821,24 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const Frag8<T> af = ld_frag8<T>(sA + B::at(j, 32 * kb + 8 * g));
-      const Frag8<T> qf = ld_frag8<T>(sQ + B::at(j, 32 * kb + 8 * g));
-      mma32(X, af, sf[kb]);   // X[4g+i][j]: token 4g+i, column j
-      mma32(O, sf[kb], qf);   // O[4g+i][j]: column 4g+i, token j
+      mma32(X, af[kb], sf[kb]);   // X[4g+i][j]: token 4g+i, column j
+      mma32(O, sf[kb], qf[kb]);   // O[4g+i][j]: column 4g+i, token j
+    }
+    // the state decays while the products run: S = Diag(D) S + Kh^T U
+    if constexpr (CHANNEL) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const float4 d4 = *reinterpret_cast<const float4*>(fv + 32 * (t >> 1) + 8 * g + 4 * (t & 1));
+        S[t][0] *= d4.x; S[t][1] *= d4.y; S[t][2] *= d4.z; S[t][3] *= d4.w;
+      }
+    } else if constexpr (HAS_G) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t][i] *= dsc;
     }
     float fk[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (!CHANNEL) {
-      const float4 fx = *reinterpret_cast<const float4*>(fv + kFX * 16 + 4 * g);
-      const float4 fb = *reinterpret_cast<const float4*>(fv + kFB * 16 + 4 * g);
-      const float4 f4 = *reinterpret_cast<const float4*>(fv + kFK * 16 + 4 * g);
-      const float fo = fv[kFO * 16 + j];
       X[0] = fmaf(fx.x, X[0], fb.x * zz[0]);
       X[1] = fmaf(fx.y, X[1], fb.y * zz[1]);
       X[2] = fmaf(fx.z, X[2], fb.z * zz[2]);
@@ -764,7 +848,6 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       fk[0] = f4.x; fk[1] = f4.y; fk[2] = f4.z; fk[3] = f4.w;
     }
     const Frag4<T> xf = frag4_from_acc<T>(X);
-    const Frag4<T> td = ld_frag4<T>(tblk(slot, sb) + j * 16 + 4 * g);
     f32x4 U = {0.f, 0.f, 0.f, 0.f};
     mma16(U, td, xf);  // U[4g+i][j]
     const Frag4<T> uo = frag4_from_acc<T>(U);
@@ -773,27 +856,9 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       f32x4 us = {U[0] * fk[0], U[1] * fk[1], U[2] * fk[2], U[3] * fk[3]};
       uk = frag4_from_acc<T>(us);
     }
-    const Frag4<T> pf = ld_frag4<T>(pblk(slot, sb) + j * 16 + 4 * g);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) mma16(S[t], kt[t], uk);
     mma16(O, uo, pf);
-    // state: S = Diag(D) S + Kh^T U
-    if constexpr (CHANNEL) {
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float4 d4 = *reinterpret_cast<const float4*>(fv + 32 * (t >> 1) + 8 * g + 4 * (t & 1));
-        S[t][0] *= d4.x; S[t][1] *= d4.y; S[t][2] *= d4.z; S[t][3] *= d4.w;
-      }
-    } else if constexpr (HAS_G) {
-      const float dsc = fv[kFD * 16];
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[t][i] *= dsc;
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const Frag4<T> kt = ld_tr16(sK + B::at(4 * g + (j >> 2), 32 * (t >> 1) + 8 * (j & 3) + 4 * (t & 1)));
-      mma16(S[t], kt, uk);
-    }
     const int64_t tok = tb + j;
     if (tok < Tn) {
       T* dst = go + ((tok0 + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + 4 * g;

@@ -179,11 +179,13 @@ def test_sub_block_transitions_bf16(channel):
 
 @pytest.mark.parametrize("channel", [True, False])
 def test_growing_state_within_range(channel):
-    """alpha > 1 (g = +0.5 per token) stays on the factored path and matches."""
-    cfg = _cfg(io=torch.bfloat16, T=100, channel=channel)
-    inp = to_dev(synth.chunk_inputs(cfg))
-    inp["g"] = torch.full_like(inp["g"], 0.5)
-    _check(inp, TOL_BF16, label=f"g=+0.5 ch={channel}")
+    """alpha > 1 (g = +0.1 per token) stays on the factored path and matches;
+    g = +0.5 per token leaves it (channel gates) and still matches."""
+    for gv in (0.1, 0.5):
+        cfg = _cfg(io=torch.bfloat16, T=100, channel=channel)
+        inp = to_dev(synth.chunk_inputs(cfg))
+        inp["g"] = torch.full_like(inp["g"], gv)
+        _check(inp, TOL_BF16, label=f"g=+{gv} ch={channel}")
 
 
 # ---------------------------------------------------------------------------
