@@ -149,24 +149,37 @@ __device__ __forceinline__ Frag4<T> ld_frag4(const T* p) {
   return f;
 }
 
-// K=32 fragment from two accumulator tiles (rows 0-15 and 16-31 of a block),
-// optionally scaled per element.
+// K=32 fragment from two accumulator tiles (rows 0-15 and 16-31 of a block).
+// bf16 values are rounded in pairs (one v_cvt_pk_bf16_f32 per two).
 template <typename T>
 __device__ __forceinline__ Frag8<T> frag8_from_acc(const f32x4& lo, const f32x4& hi) {
   Frag8<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const bf16x2 a = {(bf16)lo[0], (bf16)lo[1]}, b = {(bf16)lo[2], (bf16)lo[3]};
+    const bf16x2 c = {(bf16)hi[0], (bf16)hi[1]}, d = {(bf16)hi[2], (bf16)hi[3]};
+    const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    f.v = __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f.v[i] = from_f32<T>(lo[i]);
-    f.v[4 + i] = from_f32<T>(hi[i]);
+    for (int i = 0; i < 4; ++i) {
+      f.v[i] = lo[i];
+      f.v[4 + i] = hi[i];
+    }
   }
   return f;
 }
 
 template <typename T>
-__device__ __forceinline__ Frag4<T> frag4_from_acc(const f32x4& a) {
+__device__ __forceinline__ Frag4<T> frag4_from_acc(const f32x4& x) {
   Frag4<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const bf16x2 a = {(bf16)x[0], (bf16)x[1]}, b = {(bf16)x[2], (bf16)x[3]};
+    f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.v[i] = from_f32<T>(a[i]);
+    for (int i = 0; i < 4; ++i) f.v[i] = x[i];
+  }
   return f;
 }
 

@@ -61,28 +61,56 @@ constexpr int kSB = 16;           // tokens per sub-block
 constexpr int kSbThreads = 512;   // 4 consumer + 4 producer waves
 constexpr float kRange = 110.f;   // largest |G - m_h| (log2) of the factored form
 
-// One [16][DK] bf16 operand block.  Rows are DK contiguous channels; the
-// 16-byte chunks of a row are XOR-swizzled by the row.  For DK = 128 (16
-// chunks per row, one 256-byte bank period) row r = 4x + y flips the chunk
-// index by s = 4 (x ^ y) + x: a fragment read (16 rows, one chunk), the
-// transposing read (rows 4x .. 4x + 3, four chunks) and a producer store
-// (rows 4x + y over x, all chunks of a lane quad) each reach 16 distinct
-// 16-byte bank groups.  DK = 64 shares a bank period between two rows.
+// One [16][DK] bf16 operand block.  Rows are DK contiguous channels in
+// 16-byte chunks of 8; the chunks of a row are XOR-permuted by the row, in
+// one of three placements, each chosen for the LDS accesses that touch the
+// block (on gfx950, measured with the bank-conflict counter; for DK = 128):
+//   ax:  chunk ^ r.  Fragment reads (lane 16 g + j: row j, chunk 4 kb + g)
+//        and stores of that shape are conflict free.
+//   at:  chunk ^ s(r), s(4x + y) = 4 (x ^ y) + x.  Row-quad stores (lane
+//        4 cg + qd: row 4 qd + i, chunk cg) are conflict free.
+//   ath: at, with the two 8-byte halves of each chunk exchanged in rows
+//        4..7 and 12..15; the transposing reads (lane 16 g + j: row
+//        4 g + j / 4, a half chunk) are then conflict free.
+// DK = 64 (two rows per bank period) keeps one placement, chunk ^ (r/2) % 8.
 template <int DK>
 struct Blk {
   static constexpr int NCH = DK / 8;
   static constexpr int BYTES = 16 * DK * 2;
-  __device__ static int at(int r, int c) {
-    int sw;
-    if constexpr (NCH >= 16) sw = 4 * ((r >> 2) ^ (r & 3)) + (r >> 2);
-    else sw = (r >> 1) % NCH;
-    return r * DK + ((((c >> 3) ^ sw)) << 3) + (c & 7);
+  static constexpr bool kWide = NCH >= 16;
+  __device__ static int sw(int r) {
+    if constexpr (kWide) return 4 * ((r >> 2) ^ (r & 3)) + (r >> 2);
+    else return (r >> 1) % NCH;
   }
+  __device__ static int at(int r, int c) { return r * DK + ((((c >> 3) ^ sw(r))) << 3) + (c & 7); }
+  __device__ static int ax(int r, int c) {
+    if constexpr (kWide) return r * DK + ((((c >> 3) ^ r)) << 3) + (c & 7);
+    else return at(r, c);
+  }
+  __device__ static int ath(int r, int c) {
+    if constexpr (kWide) return at(r, c) ^ (((r >> 2) & 1) << 2);
+    else return at(r, c);
+  }
+  // does row r hold its chunks' halves exchanged (ath)?
+  __device__ static bool half_swapped(int r) { return kWide && ((r >> 2) & 1); }
 };
+
+// Element (r, c) of a [64][64] bf16 tile of v or o rows (token r, column c
+// of the workgroup's slice): the 32-byte column segments of a row are
+// XOR-permuted by r / 2, so that accesses of 4 rows x 16 columns (the
+// transposing reads of v, the output fragments) spread over the banks.
+__device__ __forceinline__ int vo_at(int r, int c) {
+  return r * 64 + (((c >> 4) ^ ((r >> 1) & 3)) << 4) + (c & 15);
+}
+
+// Element (r, c) of a 16x16 bf16 block (T, P), read and written as four
+// consecutive columns per lane: the 4-column group is XOR-permuted by r / 4
+// (conflict-free 8-byte accesses for lane 16 g + j at row j, group g).
+__device__ __forceinline__ int tp_at(int r, int c) { return r * 16 + (((c >> 2) ^ ((r >> 2) & 3)) << 2) + (c & 3); }
 
 template <int DK, bool CHANNEL>
 struct SbLds {
-  static constexpr int NOPS = CHANNEL ? 3 : 2;  // Ln|k, Qb|q, Kh (channel)
+  static constexpr int NOPS = 3;                 // Ln|k, Qb|q, Kh|k (transposing placement)
   static constexpr int BLK = Blk<DK>::BYTES;
   static constexpr int TPB = 16 * 16 * 2;       // one 16x16 bf16 block
   static constexpr int kOps = 0;                 // [NOPS][4 sub-blocks] blocks
@@ -91,7 +119,12 @@ struct SbLds {
   static constexpr int kVec = kP + 4 * TPB;      // channel: D [4][DK]; scalar: [4][6][16]
   static constexpr int VEC = CHANNEL ? 4 * DK * 4 : 4 * 6 * 16 * 4;
   static constexpr int kFlag = kVec + VEC;
-  static constexpr int SLOT = kFlag + 16;
+  // scalar gates: the v rows and the o rows of the chunk's 64 tokens for the
+  // workgroup's 64 columns, [64][64] bf16 each
+  static constexpr int VO = CHANNEL ? 0 : 64 * 64 * 2;
+  static constexpr int kVt = kFlag + 16;
+  static constexpr int kOt = kVt + VO;
+  static constexpr int SLOT = kOt + VO;
   static constexpr int kPriv = 2 * SLOT;         // channel: per producer wave L|M, R, R'
   static constexpr int PRIV = CHANNEL ? 5 * BLK / 2 : 0;
   static constexpr int kTotal = kPriv + 4 * PRIV;
@@ -159,44 +192,61 @@ __device__ __forceinline__ Frag4<bf16> ld_tr16(const bf16* p) {
   return f;
 }
 
+typedef _Float16 sb_h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 sb_h2 __attribute__((ext_vector_type(2)));
+typedef float sb_f2 __attribute__((ext_vector_type(2)));
+
+// Largest entry of N the fp16 inverse accepts.  With |N| <= m entrywise, an
+// entry of N^k is at most m^k C(14, k - 1) (paths of k strictly descending
+// steps), so every power and partial product below stays under
+// m (1 + m)^14 = 4.3e4 for m = 1.125, inside fp16's 65504; a sub-block above
+// it takes the exact path.  Unit keys with gates in [0, 1] and decay <= 1
+// give |N| <= 1.
+constexpr float kNBig = 1.125f;
+
 // (I + A)^{-1} of a 16x16 unit lower-triangular matrix from N = -A (strictly
 // lower, N^16 = 0):  (I + A)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8), on the
-// fp32 MFMA.  Layouts (lane = 16 g + j):
+// fp16 MFMA with fp32 accumulation (one v_mfma_f32_16x16x16_f16 per product;
+// fp16 operands carry 11 significant bits, finer than the bf16 in which T is
+// stored).  Layouts (lane = 16 g + j):
 //   rowL(X): X[j][4g + i]      accL(X): X[4g + i][j]
-// mma16(acc, rowL(X), accL(Y)) adds accL(X Y); accL(X) = rowL(X^T).
-// In: nr = rowL(N), nc = accL(N).  Out: rowL(T), T = (I + A)^{-1}.
+// mma(acc, rowL(X), accL(Y)) adds accL(X Y); accL(X) = rowL(X^T).
+// In: nr = rowL(N), nc = accL(N).  Out: rowL(T), T = (I + A)^{-1}, and nmax =
+// the lane's largest |N| entry.
 __device__ __forceinline__ Frag4<float> unit_lower_inverse(const Frag4<float>& nr,
-                                                           const Frag4<float>& nc, int g, int j) {
-  auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma16(acc, x, y);
-    Frag4<float> f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.v[i] = acc[i];
-    return f;
+                                                           const Frag4<float>& nc, int g, int j,
+                                                           float& nmax) {
+  auto h = [](float a, float b, float c, float d) {
+    const sb_h2 lo = __builtin_convertvector((sb_f2){a, b}, sb_h2);
+    const sb_h2 hi = __builtin_convertvector((sb_f2){c, d}, sb_h2);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
   };
-  const Frag4<float> n2c = prod(nr, nc);    // accL(N^2)
-  const Frag4<float> n2r = prod(nc, nr);    // rowL(N^2)
-  const Frag4<float> n4c = prod(n2r, n2c);  // accL(N^4)
-  const Frag4<float> n4r = prod(n2c, n2r);  // rowL(N^4)
-  const Frag4<float> n8c = prod(n4r, n4c);  // accL(N^8)
+  nmax = fmaxf(fmaxf(fabsf(nr.v[0]), fabsf(nr.v[1])), fmaxf(fabsf(nr.v[2]), fabsf(nr.v[3])));
+  auto hv = [&h](const f32x4& x) { return h(x[0], x[1], x[2], x[3]); };
+  auto mma = [](const sb_h4& a, const sb_h4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  };
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const sb_h4 hr = h(nr.v[0], nr.v[1], nr.v[2], nr.v[3]);
+  const sb_h4 hc = h(nc.v[0], nc.v[1], nc.v[2], nc.v[3]);
+  const sb_h4 n2c = hv(mma(hr, hc, z));    // accL(N^2)
+  const sb_h4 n2r = hv(mma(hc, hr, z));    // rowL(N^2)
+  const sb_h4 n4c = hv(mma(n2r, n2c, z));  // accL(N^4)
+  const sb_h4 n4r = hv(mma(n2c, n2r, z));  // rowL(N^4)
+  const sb_h4 n8c = hv(mma(n4r, n4c, z));  // accL(N^8)
   // accL(T^T), T^T = (I + N^8)^T (I + N^4)^T (I + N^2)^T (I + N)^T, by left
-  // products starting from accL((I + N)^T) = rowL(I + N).
-  Frag4<float> t;
+  // products C + X C starting from accL((I + N)^T) = rowL(I + N); C enters
+  // the accumulator in fp32 and only the product X C is rounded
+  f32x4 t;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) t.v[i] = nr.v[i] + ((4 * g + i == j) ? 1.f : 0.f);
-  auto step = [](const Frag4<float>& x, const Frag4<float>& c) {  // accL(C + X C), x = rowL(X)
-    f32x4 acc = {c.v[0], c.v[1], c.v[2], c.v[3]};
-    mma16(acc, x, c);
-    Frag4<float> f;
+  for (int i = 0; i < 4; ++i) t[i] = nr.v[i] + ((4 * g + i == j) ? 1.f : 0.f);
+  t = mma(n2c, hv(t), t);
+  t = mma(n4c, hv(t), t);
+  t = mma(n8c, hv(t), t);
+  Frag4<float> r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.v[i] = acc[i];
-    return f;
-  };
-  t = step(n2c, t);
-  t = step(n4c, t);
-  t = step(n8c, t);
-  return t;  // accL(T^T) = rowL(T)
+  for (int i = 0; i < 4; ++i) r.v[i] = t[i];
+  return r;  // accL(T^T) = rowL(T)
 }
 
 template <typename GT, int DK, int DV, bool CHANNEL, bool HAS_G>
@@ -272,6 +322,9 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   auto flagp = [&](int slot) -> int* {
     return reinterpret_cast<int*>(smem + slot * L::SLOT + L::kFlag);
   };
+  auto vtile = [&](int slot) -> T* { return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kVt); };
+  auto otile = [&](int slot) -> T* { return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kOt); };
+  const uint32_t v_tok = (uint32_t)(p.Hv * DV * 2);   // bytes per token of v (and o)
 
   const uint32_t qk_tok = (uint32_t)(p.Hk * DK * (int)sizeof(T));   // bytes per token
   const uint32_t gc_tok = (uint32_t)(p.Hv * DK * (int)sizeof(GT));
@@ -432,15 +485,17 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
             mpk[i][e2] = pack_bf16x2(Mv[0], Mv[1]);
           }
           const int r = 4 * qd + i;
-          st_words<CPL / 2>(sLn + B::at(r, ch0), wLn);
-          st_words<CPL / 2>(sQb + B::at(r, ch0), wQb);
+          st_words<CPL / 2>(sLn + B::ax(r, ch0), wLn);
+          st_words<CPL / 2>(sQb + B::ax(r, ch0), wQb);
+          if (B::half_swapped(r)) {
+            const uint32_t a0 = wKh[0], a1 = wKh[1];
+            wKh[0] = wKh[2]; wKh[1] = wKh[3]; wKh[2] = a0; wKh[3] = a1;
+          }
           st_words<CPL / 2>(sKh + B::at(r, ch0), wKh);
           st_words<CPL / 2>(sLM + B::at(r, ch0), wL);
           st_words<CPL / 2>(sR + B::at(r, ch0), wR);
           if (qd < 2) st_words<CPL / 2>(sR2 + B::at(r, ch0), wR2);
         }
-        const bool bad = __any(!(worst <= kRange));
-        if (lane == 0) flagp(slot)[pw] = bad ? 1 : 0;
         // next chunk's raw inputs (the last chunk re-reads itself)
         load(ci + 1 < nchunks ? ci + 1 : ci);
 
@@ -492,9 +547,12 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           const float pp = (j >= 8 && tc < 8) ? p2[i] : p1[i];
           pv[i] = (tc <= j) ? pp : 0.f;
         }
-        const Frag4<float> tt = unit_lower_inverse(nr, nc, g, j);
-        st4<T>(tblk(slot, pw) + j * 16 + 4 * g, tt.v[0], tt.v[1], tt.v[2], tt.v[3]);
-        st4<T>(pblk(slot, pw) + j * 16 + 4 * g, pv[0], pv[1], pv[2], pv[3]);
+        float nmax;
+        const Frag4<float> tt = unit_lower_inverse(nr, nc, g, j, nmax);
+        st4<T>(tblk(slot, pw) + tp_at(j, 4 * g), tt.v[0], tt.v[1], tt.v[2], tt.v[3]);
+        st4<T>(pblk(slot, pw) + tp_at(j, 4 * g), pv[0], pv[1], pv[2], pv[3]);
+        const bool bad = __any(!(worst <= kRange) || !(nmax <= kNBig));
+        if (lane == 0) flagp(slot)[pw] = bad ? 1 : 0;
       };
 
       load(0);
@@ -507,9 +565,18 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
     } else {
       // Scalar gates.  lane (g, j): token j of the sub-block, channels
       // 32 kb + 8 g .. + 7 of every 32-channel block (the MFMA fragment).
-      Raw<16> rq[KB], rk[KB];
+      Raw<16> rq[KB], rk[KB], rv[2];
       uint32_t ub = 0u, ug = 0u;
+      // v rows of the sub-block for the consumers, whole 16-byte pieces:
+      // lane l takes token 8 h + l / 8 and columns 8 (l % 8) .. + 7
+      const char* bvs = reinterpret_cast<const char*>(gv) + ((uint64_t)tok0 * v_tok + (uint32_t)((hv * DV + c0) * 2));
       auto load = [&](int64_t ci) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int64_t tv = ci * kC + kSB * pw + 8 * h + (lane >> 3);
+          tv = tv < Tn - 1 ? tv : Tn - 1;
+          ld_raw<16>(bvs + ((uint64_t)tv * v_tok + (uint32_t)((lane & 7) * 16)), rv[h]);
+        }
         int64_t t = ci * kC + kSB * pw + j;
         t = t < Tn - 1 ? t : Tn - 1;
         const uint64_t tu = (uint64_t)t;
@@ -547,7 +614,6 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         mn = fminf(mn, dpp_row_shr_inf(mn, 4));
         mn = fminf(mn, dpp_row_shr_inf(mn, 8));
         const float worst = fmaxf(fmaxf(G, g15 - G), G - mn);
-        const bool bad = __any(!(worst <= kRange));
         const float fo = exp2_fast(G);
         float* fv = vecp(slot) + pw * 6 * 16;
         if (g == 0) {
@@ -558,16 +624,28 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           fv[kFG * 16 + j] = G;
           if (j == 0) fv[kFD * 16] = exp2_fast(g15);
         }
-        if (lane == 0) flagp(slot)[pw] = bad ? 1 : 0;
-        // raw k and q rows for the consumers
+        // raw k and q rows for the consumers: k twice, in the fragment
+        // placement and in the transposing one
         T* sK = opblk(slot, 0, pw);
         T* sQ = opblk(slot, 1, pw);
+        T* sKt = opblk(slot, 2, pw);
+        const bool hs = B::half_swapped(j);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          *reinterpret_cast<uint4*>(sK + B::at(j, 32 * kb + 8 * g)) =
+          *reinterpret_cast<uint4*>(sK + B::ax(j, 32 * kb + 8 * g)) =
               make_uint4(rk[kb].w[0], rk[kb].w[1], rk[kb].w[2], rk[kb].w[3]);
-          *reinterpret_cast<uint4*>(sQ + B::at(j, 32 * kb + 8 * g)) =
+          *reinterpret_cast<uint4*>(sQ + B::ax(j, 32 * kb + 8 * g)) =
               make_uint4(rq[kb].w[0], rq[kb].w[1], rq[kb].w[2], rq[kb].w[3]);
+          *reinterpret_cast<uint4*>(sKt + B::at(j, 32 * kb + 8 * g)) =
+              hs ? make_uint4(rk[kb].w[2], rk[kb].w[3], rk[kb].w[0], rk[kb].w[1])
+                 : make_uint4(rk[kb].w[0], rk[kb].w[1], rk[kb].w[2], rk[kb].w[3]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = kSB * pw + 8 * h + (lane >> 3);
+          const bool pres = ci * kC + r < Tn;   // absent tokens: v = 0
+          *reinterpret_cast<uint4*>(vtile(slot) + vo_at(r, 8 * (lane & 7))) =
+              pres ? make_uint4(rv[h].w[0], rv[h].w[1], rv[h].w[2], rv[h].w[3]) : make_uint4(0u, 0u, 0u, 0u);
         }
         load(ci + 1 < nchunks ? ci + 1 : ci);
         // Gram blocks: kk[4g+i][j] = k_{4g+i} . k_j, pq[4g+i][j] = k_{4g+i} . q_j
@@ -593,9 +671,12 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           nr.v[i] = (tc < j) ? -beta * drow * kk[i] : 0.f;
           pv[i] = (tc <= j) ? drow * pq[i] : 0.f;
         }
-        const Frag4<float> tt = unit_lower_inverse(nr, nc, g, j);
-        st4<T>(tblk(slot, pw) + j * 16 + 4 * g, tt.v[0], tt.v[1], tt.v[2], tt.v[3]);
-        st4<T>(pblk(slot, pw) + j * 16 + 4 * g, pv[0], pv[1], pv[2], pv[3]);
+        float nmax;
+        const Frag4<float> tt = unit_lower_inverse(nr, nc, g, j, nmax);
+        st4<T>(tblk(slot, pw) + tp_at(j, 4 * g), tt.v[0], tt.v[1], tt.v[2], tt.v[3]);
+        st4<T>(pblk(slot, pw) + tp_at(j, 4 * g), pv[0], pv[1], pv[2], pv[3]);
+        const bool bad = __any(!(worst <= kRange) || !(nmax <= kNBig));
+        if (lane == 0) flagp(slot)[pw] = bad ? 1 : 0;
       };
       load(0);
       produce(0);
@@ -628,61 +709,80 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         S[t][i] = sin ? sin[row * DV + col] : 0.f;
       }
   }
-  const uint32_t v_tok = (uint32_t)(p.Hv * DV * 2);
   const uint32_t w_tok = (uint32_t)(p.Hv * DV * (int)sizeof(GT));
-  const char* bv = reinterpret_cast<const char*>(gv) + ((uint64_t)tok0 * v_tok + (uint32_t)((hv * DV + col) * 2));
-  const char* bw = reinterpret_cast<const char*>(gw) + ((uint64_t)tok0 * w_tok + (uint32_t)((hv * DV + col) * (int)sizeof(GT)));
   // v (and w) of the 16 tokens 16 sb + 4 g + i of a chunk for this column,
-  // two tokens per register (d16 loads): zv/zw are prefetched a chunk ahead,
-  // cv/cw hold the chunk being consumed.  fp32 write gates keep one per word.
+  // two tokens per register: zv/zw are prefetched a chunk ahead, cv/cw hold
+  // the chunk being consumed (fp32 write gates keep one per word).  The reads
+  // go through buffer descriptors based at the chunk's first token: one
+  // 32-bit lane offset (the lane's column) and the token offset as a scalar.
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   constexpr int WPW = sizeof(GT) == 2 ? 2 : 1;  // w tokens per word
   u16x2 zv[NSB][2], cv[NSB][2];
   uint32_t zw[NSB][4 / WPW], cw[NSB][4 / WPW];
+  const char* bv0 = reinterpret_cast<const char*>(gv) + (uint64_t)tok0 * v_tok;
+  const char* bw0 = reinterpret_cast<const char*>(gw) + (uint64_t)tok0 * w_tok;
+  const int cvo = (hv * DV + col) * 2;
+  const int cwo = (hv * DV + col) * (int)sizeof(GT);
+  auto rsrc = [](const char* base, uint32_t bytes) {
+    // the base is the same in every lane; say so, so that it stays scalar
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    char* u = reinterpret_cast<char*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)bytes, 0x00020000);
+  };
   auto load_z = [&](int64_t ci) {
     const int64_t t0 = ci * kC;
-    const char* cvb = bv + (uint64_t)t0 * v_tok;
-    const char* cwb = bw + (uint64_t)t0 * w_tok;
-    // token (4g + lt) of the chunk; lt = 16 sb + 2 h (+1).  Full chunks: a
-    // wave-uniform offset plus one per-lane term.  The partial last chunk
-    // clamps every token to the last one.
-    auto fetch = [&](int sb, int h, uint32_t ov0, uint32_t ov1, uint32_t ow0, uint32_t ow1) {
+    const auto rv = rsrc(bv0 + (uint64_t)t0 * v_tok, (uint32_t)kC * v_tok);
+    const auto rw = rsrc(CHANNEL ? bw0 + (uint64_t)t0 * w_tok : bv0, CHANNEL ? (uint32_t)kC * w_tok : 0u);
+    // tokens a and b (chunk-relative) of the pair (sb, h): lane term la / lb
+    // plus scalar term sa / sb (bytes of v); w likewise
+    auto fetch = [&](int sb, int h, int lva, int lvb, int sva, int svb, int lwa, int lwb, int swa,
+                     int swb) {
       u16x2 pv;
-      pv.x = *reinterpret_cast<const unsigned short*>(cvb + ov0);
-      pv.y = *reinterpret_cast<const unsigned short*>(cvb + ov1);
+      pv.x = __builtin_amdgcn_raw_buffer_load_b16(rv, lva, sva, 0);
+      pv.y = __builtin_amdgcn_raw_buffer_load_b16(rv, lvb, svb, 0);
       zv[sb][h] = pv;
       if constexpr (CHANNEL) {
         if constexpr (WPW == 2) {
           u16x2 pw2;
-          pw2.x = *reinterpret_cast<const unsigned short*>(cwb + ow0);
-          pw2.y = *reinterpret_cast<const unsigned short*>(cwb + ow1);
+          pw2.x = __builtin_amdgcn_raw_buffer_load_b16(rw, lwa, swa, 0);
+          pw2.y = __builtin_amdgcn_raw_buffer_load_b16(rw, lwb, swb, 0);
           zw[sb][h] = __builtin_bit_cast(uint32_t, pw2);
         } else {
-          zw[sb][2 * h] = *reinterpret_cast<const uint32_t*>(cwb + ow0);
-          zw[sb][2 * h + 1] = *reinterpret_cast<const uint32_t*>(cwb + ow1);
+          zw[sb][2 * h] = __builtin_amdgcn_raw_buffer_load_b32(rw, lwa, swa, 0);
+          zw[sb][2 * h + 1] = __builtin_amdgcn_raw_buffer_load_b32(rw, lwb, swb, 0);
         }
       }
     };
     if (t0 + kC <= Tn) {
-      const uint32_t lv = (uint32_t)(4 * g) * v_tok, lw = (uint32_t)(4 * g) * w_tok;
+      // full chunk: token 16 sb + 4 g + 2 h (+1); the 4g term is the lane's
+      const int lv = cvo + 4 * g * (int)v_tok, lw = cwo + 4 * g * (int)w_tok;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint32_t u = (uint32_t)(kSB * sb + 2 * h);
-          fetch(sb, h, lv + u * v_tok, lv + (u + 1) * v_tok, lw + u * w_tok, lw + (u + 1) * w_tok);
+          const int u = kSB * sb + 2 * h;
+          fetch(sb, h, lv, lv, u * (int)v_tok, (u + 1) * (int)v_tok, lw, lw, u * (int)w_tok,
+                (u + 1) * (int)w_tok);
         }
     } else {
+      // the partial last chunk clamps every token to the last one and zeroes
+      // the values of tokens past the end, so that their rows of X (and U)
+      // vanish
       const int lastl = (int)(Tn - 1 - t0);
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           int l0 = kSB * sb + 4 * g + 2 * h, l1 = l0 + 1;
-          l0 = l0 < lastl ? l0 : lastl;
-          l1 = l1 < lastl ? l1 : lastl;
-          fetch(sb, h, (uint32_t)l0 * v_tok, (uint32_t)l1 * v_tok, (uint32_t)l0 * w_tok,
-                (uint32_t)l1 * w_tok);
+          const bool p0 = l0 <= lastl, p1 = l1 <= lastl;
+          l0 = p0 ? l0 : lastl;
+          l1 = p1 ? l1 : lastl;
+          fetch(sb, h, cvo + l0 * (int)v_tok, cvo + l1 * (int)v_tok, 0, 0, cwo + l0 * (int)w_tok,
+                cwo + l1 * (int)w_tok, 0, 0);
+          if (!p0) zv[sb][h].x = 0;
+          if (!p1) zv[sb][h].y = 0;
         }
     }
   };
@@ -700,8 +800,9 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
     }
   };
 
-  // Exact token-by-token recurrence for tokens [tb, min(tb + 16, Tn)).
-  auto tokens_path = [&](int64_t tb) {
+  // Exact token-by-token recurrence for tokens [tb, min(tb + 16, Tn)) of the
+  // chunk in the given slot that starts at token cb.
+  auto tokens_path = [&](int slot, int64_t cb, int64_t tb) {
     for (int tl = 0; tl < kSB; ++tl) {
       const int64_t tok = tb + tl;
       if (tok >= Tn) break;
@@ -759,59 +860,87 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       }
       op += __shfl_xor(op, 16);
       op += __shfl_xor(op, 32);
-      if (g == 0) go[gt * DV + col] = from_f32<T>(p.scale * op);
+      if (g == 0) {
+        if constexpr (CHANNEL) go[gt * DV + col] = from_f32<T>(p.scale * op);
+        else otile(slot)[vo_at((int)(tok - cb), 16 * wave + j)] = from_f32<T>(p.scale * op);
+      }
     }
+    (void)slot; (void)cb;
+  };
+
+  // The state-independent operands of one sub-block, read from LDS ahead of
+  // their use (the common loop reads sub-block sb + 1 while sb computes).
+  struct Ops {
+    Frag8<T> af[KB], qf[KB];
+    Frag4<T> td, pf;
+    float4 fx, fb, f4;
+    float fo, dsc;
+  };
+  auto ld_ops = [&](int slot, int sb) {
+    Ops o;
+    const T* sA = opblk(slot, 0, sb);   // Ln | k
+    const T* sQ = opblk(slot, 1, sb);   // Qb | q
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      o.af[kb] = ld_frag8<T>(sA + B::ax(j, 32 * kb + 8 * g));
+      o.qf[kb] = ld_frag8<T>(sQ + B::ax(j, 32 * kb + 8 * g));
+    }
+    o.td = ld_frag4<T>(tblk(slot, sb) + tp_at(j, 4 * g));
+    o.pf = ld_frag4<T>(pblk(slot, sb) + tp_at(j, 4 * g));
+    o.fo = 1.f;
+    o.dsc = 1.f;
+    if constexpr (!CHANNEL) {
+      const float* fv = vecp(slot) + sb * 6 * 16;
+      o.fx = *reinterpret_cast<const float4*>(fv + kFX * 16 + 4 * g);
+      o.fb = *reinterpret_cast<const float4*>(fv + kFB * 16 + 4 * g);
+      o.f4 = *reinterpret_cast<const float4*>(fv + kFK * 16 + 4 * g);
+      o.fo = fv[kFO * 16 + j];
+      o.dsc = fv[kFD * 16];
+    }
+    return o;
   };
 
   // One sub-block on the MFMA path.  zpre: take v (and w) from the
   // prefetched words (the unrolled common loop) or load them here (the loop
   // of a chunk that holds a sub-block on the exact path).
-  auto sub_block = [&](int slot, int sb, int64_t tb, auto zpre) {
-    const T* sA = opblk(slot, 0, sb);                    // Ln | k
-    const T* sQ = opblk(slot, 1, sb);                    // Qb | q
-    const T* sK = opblk(slot, CHANNEL ? 2 : 0, sb);      // Kh | k
+  auto sub_block = [&](int slot, int sb, int64_t tb, auto zpre, const Ops& op) {
+    const T* sK = opblk(slot, 2, sb);   // Kh | k, transposing placement
     const float* fv = vecp(slot) + (CHANNEL ? sb * DK : sb * 6 * 16);
-    // every operand read is issued first: none depends on the state, so
-    // their LDS latency overlaps the conversions and the first products
-    Frag8<T> af[KB], qf[KB];
     Frag4<T> kt[MT];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      af[kb] = ld_frag8<T>(sA + B::at(j, 32 * kb + 8 * g));
-      qf[kb] = ld_frag8<T>(sQ + B::at(j, 32 * kb + 8 * g));
-    }
-    const Frag4<T> td = ld_frag4<T>(tblk(slot, sb) + j * 16 + 4 * g);
-    const Frag4<T> pf = ld_frag4<T>(pblk(slot, sb) + j * 16 + 4 * g);
-#pragma unroll
     for (int t = 0; t < MT; ++t)
-      kt[t] = ld_tr16(sK + B::at(4 * g + (j >> 2), 32 * (t >> 1) + 8 * (j & 3) + 4 * (t & 1)));
-    float4 fx, fb, f4;
-    float fo = 1.f, dsc = 1.f;
-    if constexpr (!CHANNEL) {
-      fx = *reinterpret_cast<const float4*>(fv + kFX * 16 + 4 * g);
-      fb = *reinterpret_cast<const float4*>(fv + kFB * 16 + 4 * g);
-      f4 = *reinterpret_cast<const float4*>(fv + kFK * 16 + 4 * g);
-      fo = fv[kFO * 16 + j];
-      dsc = fv[kFD * 16];
-    }
+      kt[t] = ld_tr16(sK + B::ath(4 * g + (j >> 2), 32 * (t >> 1) + 8 * (j & 3) + 4 * (t & 1)));
+    const Frag8<T>* af = op.af;
+    const Frag8<T>* qf = op.qf;
+    const Frag4<T>& td = op.td;
+    const Frag4<T>& pf = op.pf;
+    const float4 fx = op.fx, fb = op.fb, f4 = op.f4;
+    const float fo = op.fo, dsc = op.dsc;
     Frag8<T> sf[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sf[kb] = frag8_from_acc<T>(S[2 * kb], S[2 * kb + 1]);
     f32x4 X, O = {0.f, 0.f, 0.f, 0.f};
     float zz[4], ww[4];
     const bool full_sb = tb + kSB <= Tn;  // wave-uniform
+    Frag4<T> vz;
+    if constexpr (!CHANNEL)  // v rows 16 sb + 4 g + i, column 16 wave + j
+      vz = ld_tr16(vtile(slot) + vo_at(16 * sb + 4 * g + (j >> 2), 16 * wave + 4 * (j & 3)));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t t = tb + 4 * g + i;
-      if constexpr (decltype(zpre)::value) {
+      if constexpr (!CHANNEL) {
+        // absent tokens hold zero in the tile
+        zz[i] = (float)vz.v[i];
+        ww[i] = 0.f;
+      } else if constexpr (decltype(zpre)::value) {
+        // prefetched words: tokens past the end already hold zero
         zz[i] = zval(sb, i);
-        ww[i] = CHANNEL ? wval(sb, i) : 0.f;
+        ww[i] = wval(sb, i);
       } else {
+        const int64_t t = tb + 4 * g + i;
         const int64_t tc = t < Tn - 1 ? t : Tn - 1;
-        zz[i] = to_f32(gv[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]);
+        zz[i] = t < Tn ? to_f32(gv[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]) : 0.f;
         ww[i] = CHANNEL ? to_f32(gw[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]) : 0.f;
       }
-      if (!full_sb && t >= Tn) zz[i] = 0.f;
     }
     if constexpr (CHANNEL) {
 #pragma unroll
@@ -859,31 +988,60 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) mma16(S[t], kt[t], uk);
     mma16(O, uo, pf);
-    const int64_t tok = tb + j;
-    if (tok < Tn) {
-      T* dst = go + ((tok0 + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + 4 * g;
-      st4<T>(dst, p.scale * O[0], p.scale * O[1], p.scale * O[2], p.scale * O[3]);
+    if constexpr (CHANNEL) {
+      const int64_t tok = tb + j;
+      if (full_sb || tok < Tn) {
+        T* dst = go + ((tok0 + tok) * p.Hv + hv) * (int64_t)DV + c0 + 16 * wave + 4 * g;
+        st4<T>(dst, p.scale * O[0], p.scale * O[1], p.scale * O[2], p.scale * O[3]);
+      }
+    } else {
+      // token 16 sb + j, columns 16 wave + 4 g .. + 3, into the o tile
+      st4<T>(otile(slot) + vo_at(16 * sb + j, 16 * wave + 4 * g), p.scale * O[0], p.scale * O[1],
+             p.scale * O[2], p.scale * O[3]);
     }
   };
 
-  load_z(0);
+  // Scalar gates: o rows of a finished chunk from its tile to memory, whole
+  // 16-byte pieces (consumer wave w: tokens 16 w .. 16 w + 15).
+  auto flush_o = [&](int64_t ci) {
+    const int slot = (int)(ci & 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 16 * wave + 8 * h + (lane >> 3);
+      const int64_t tok = ci * kC + r;
+      if (tok < Tn) {
+        const uint4 val = *reinterpret_cast<const uint4*>(otile(slot) + vo_at(r, 8 * (lane & 7)));
+        *reinterpret_cast<uint4*>(go + ((tok0 + tok) * p.Hv + hv) * (int64_t)DV + c0 + 8 * (lane & 7)) = val;
+      }
+    }
+  };
+
+  if constexpr (CHANNEL) load_z(0);
   __syncthreads();  // chunk 0 is ready
   for (int64_t ci = 0; ci < nchunks; ++ci) {
     const int slot = (int)(ci & 1);
+    if constexpr (CHANNEL) {
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
+      for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) cv[sb][h] = zv[sb][h];
+        for (int h = 0; h < 2; ++h) cv[sb][h] = zv[sb][h];
 #pragma unroll
-      for (int h = 0; h < 4 / WPW; ++h) cw[sb][h] = zw[sb][h];
+        for (int h = 0; h < 4 / WPW; ++h) cw[sb][h] = zw[sb][h];
+      }
+      load_z(ci + 1 < nchunks ? ci + 1 : ci);
+    } else if (ci > 0) {
+      flush_o(ci - 1);  // the previous chunk's rows, complete since the barrier
     }
-    load_z(ci + 1 < nchunks ? ci + 1 : ci);
     const int* fl = flagp(slot);
     if ((fl[0] | fl[1] | fl[2] | fl[3]) == 0) {
+      Ops cur = ld_ops(slot, 0);
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
         const int64_t tb = ci * kC + kSB * sb;
-        if (tb < Tn) sub_block(slot, sb, tb, IntTag<1>{});
+        Ops nxt;
+        if (sb + 1 < NSB) nxt = ld_ops(slot, sb + 1);
+        if (tb < Tn) sub_block(slot, sb, tb, IntTag<1>{}, cur);
+        if (sb + 1 < NSB) cur = nxt;
       }
     } else {
       // a chunk with a sub-block whose decay range the factored form cannot
@@ -892,13 +1050,14 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       for (int sb = 0; sb < NSB; ++sb) {
         const int64_t tb = ci * kC + kSB * sb;
         if (tb < Tn) {
-          if (fl[sb]) tokens_path(tb);
-          else sub_block(slot, sb, tb, IntTag<0>{});
+          if (fl[sb]) tokens_path(slot, ci * kC, tb);
+          else sub_block(slot, sb, tb, IntTag<0>{}, ld_ops(slot, sb));
         }
       }
     }
     __syncthreads();
   }
+  if constexpr (!CHANNEL) flush_o(nchunks - 1);
   if (p.state_out) {
     float* sout = p.state_out + head * (int64_t)DK * DV;
 #pragma unroll
