@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libgdn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["gdn_api.cpp", "decode.hip", "chunk_fwd.hip", "chunk_fwd_sb.hip", "layer_ops.hip",
-           "backward.hip"]
+           "backward.hip", "noalloc.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_SCALAR, GDN_GATES_CHANNEL = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class GdnFwdDesc(ctypes.Structure):
@@ -110,6 +110,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn_backward.argtypes = [ctypes.POINTER(GdnBwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  vp, ctypes.c_size_t, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_backward.restype = ctypes.c_int
+    lib.gdn_backward_noalloc.argtypes = [ctypes.POINTER(GdnBwdDesc), vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_backward_noalloc.restype = ctypes.c_int
+    lib.gdn_backward_noalloc_max_bytes.argtypes = []
+    lib.gdn_backward_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.gdn_backward_varlen_workspace_size.argtypes = [ctypes.POINTER(GdnBwdVarlenDesc)]
     lib.gdn_backward_varlen_workspace_size.restype = ctypes.c_size_t
     lib.gdn_backward_varlen.argtypes = [ctypes.POINTER(GdnBwdVarlenDesc), vp, vp, vp, vp, vp, vp,
@@ -438,18 +443,8 @@ def gdn_backward_workspace_size(q, v, beta_or_b, w=None, scale: float = 1.0) -> 
     return int(lib.gdn_backward_workspace_size(ctypes.byref(_bwd_desc(q, v, beta_or_b, w, scale))))
 
 
-def gdn_backward(q, k, v, beta_or_b, d_o, w=None, g=None, state_in=None, d_state_out=None,
-                 scale: float = 1.0, workspace=None, need_dg: bool = True,
-                 need_d_state_in: bool = True, grads=None, stream=None):
-    """Gradients of the chunk forward (see include/gdn.h).  Returns a dict of
-    fp32 tensors dq, dk, dv, db, dw (None for scalar gates), dg (None when g
-    is None or need_dg is False), d_state_in (None unless need_d_state_in).
-
-    Shapes as for gdn_chunk_fwd; d_o like o; d_state_out like the state or
-    None.  `workspace` is a device uint8 tensor of at least
-    gdn_backward_workspace_size(...) bytes (allocated when None); `grads` may
-    hold preallocated outputs under the same keys.
-    """
+def _bwd_outputs(q, k, v, beta_or_b, d_o, w, g, state_in, d_state_out, need_dg,
+                 need_d_state_in, grads):
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     io = q.dtype
@@ -465,12 +460,6 @@ def gdn_backward(q, k, v, beta_or_b, d_o, w=None, g=None, state_in=None, d_state
     _check(state_in, "state_in", (B, Hv, dk, dv), torch.float32)
     _check(d_o, "d_o", (B, T, Hv, dv), io)
     _check(d_state_out, "d_state_out", (B, Hv, dk, dv), torch.float32)
-    desc = _bwd_desc(q, v, beta_or_b, w, scale)
-    need = int(lib.gdn_backward_workspace_size(ctypes.byref(desc)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
     f32 = dict(dtype=torch.float32, device=q.device)
     shapes = {"dq": (B, T, Hk, dk), "dk": (B, T, Hk, dk), "dv": (B, T, Hv, dv), "db": gshape,
               "dw": (B, T, Hv, dv) if channel else None,
@@ -484,6 +473,29 @@ def gdn_backward(q, k, v, beta_or_b, d_o, w=None, g=None, state_in=None, d_state
         if out.get(name) is None:
             out[name] = torch.empty(shp, **f32)
         _check(out[name], name, shp, torch.float32)
+    return out
+
+
+def gdn_backward(q, k, v, beta_or_b, d_o, w=None, g=None, state_in=None, d_state_out=None,
+                 scale: float = 1.0, workspace=None, need_dg: bool = True,
+                 need_d_state_in: bool = True, grads=None, stream=None):
+    """Gradients of the chunk forward (see include/gdn.h).  Returns a dict of
+    fp32 tensors dq, dk, dv, db, dw (None for scalar gates), dg (None when g
+    is None or need_dg is False), d_state_in (None unless need_d_state_in).
+
+    Shapes as for gdn_chunk_fwd; d_o like o; d_state_out like the state or
+    None.  `workspace` is a device uint8 tensor of at least
+    gdn_backward_workspace_size(...) bytes (allocated when None); `grads` may
+    hold preallocated outputs under the same keys.
+    """
+    out = _bwd_outputs(q, k, v, beta_or_b, d_o, w, g, state_in, d_state_out, need_dg,
+                       need_d_state_in, grads)
+    desc = _bwd_desc(q, v, beta_or_b, w, scale)
+    need = int(lib.gdn_backward_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
     st = lib.gdn_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b),
                           _ptr(w), _ptr(g), _ptr(state_in), _ptr(d_o), _ptr(d_state_out),
@@ -492,6 +504,31 @@ def gdn_backward(q, k, v, beta_or_b, d_o, w=None, g=None, state_in=None, d_state
                           _ptr(out["dg"]), _ptr(out["d_state_in"]), _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_backward")
+    return out
+
+
+def gdn_backward_noalloc_max_bytes() -> int:
+    """Bytes of the static workspace gdn_backward_noalloc uses on each GPU."""
+    return int(lib.gdn_backward_noalloc_max_bytes())
+
+
+def gdn_backward_noalloc(q, k, v, beta_or_b, d_o, w=None, g=None, state_in=None,
+                         d_state_out=None, scale: float = 1.0, need_dg: bool = True,
+                         need_d_state_in: bool = True, grads=None, stream=None):
+    """gdn_backward on the library's static workspace (see include/gdn.h): no
+    workspace argument; with every output passed in `grads`, the library
+    allocates nothing.  Raises GdnError(GDN_ERR_UNSUPPORTED) when the shapes
+    need more than gdn_backward_noalloc_max_bytes() of workspace."""
+    out = _bwd_outputs(q, k, v, beta_or_b, d_o, w, g, state_in, d_state_out, need_dg,
+                       need_d_state_in, grads)
+    desc = _bwd_desc(q, v, beta_or_b, w, scale)
+    st = lib.gdn_backward_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b),
+                                  _ptr(w), _ptr(g), _ptr(state_in), _ptr(d_o), _ptr(d_state_out),
+                                  _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                  _ptr(out["db"]), _ptr(out["dw"]), _ptr(out["dg"]),
+                                  _ptr(out["d_state_in"]), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_backward_noalloc")
     return out
 
 

@@ -53,9 +53,10 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
+#define GDN_ABI_VERSION 6  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
                               gdn_gates, gdn_output_gate; 4: adds gdn_backward;
-                              5: adds gdn_backward_varlen */
+                              5: adds gdn_backward_varlen; 6: adds
+                              gdn_backward_noalloc */
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -247,6 +248,29 @@ gdn_status gdn_backward(const gdn_bwd_desc* desc, const void* q, const void* k, 
                         void* workspace, size_t workspace_bytes, float* dq, float* dk,
                         float* dv, float* db, float* dw, float* dg, float* d_state_in,
                         void* stream);
+
+/*
+ * gdn_backward_noalloc -- gdn_backward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments and results, without the
+ * workspace.  The workspace is a static device array inside the library,
+ * gdn_backward_noalloc_max_bytes() bytes (64 MiB) on each GPU it runs on,
+ * held until the process ends; the call allocates nothing.  A descriptor
+ * whose gdn_backward_workspace_size exceeds that returns GDN_ERR_UNSUPPORTED
+ * (for example B 1, T 384, H_v 16, d_k = d_v = 128 fits; the B 8, T 4096
+ * training shape does not).  All calls on one GPU share its array: calls that
+ * overlap on one GPU (other streams or host threads) race, and must be
+ * serialised by the caller.
+ */
+gdn_status gdn_backward_noalloc(const gdn_bwd_desc* desc, const void* q, const void* k,
+                                const void* v, const void* beta_or_b, const void* w,
+                                const void* g, const float* state_in, const void* d_o,
+                                const float* d_state_out, float* dq, float* dk, float* dv,
+                                float* db, float* dw, float* dg, float* d_state_in,
+                                void* stream);
+
+/* Bytes of the static workspace gdn_backward_noalloc uses on each GPU. */
+size_t gdn_backward_noalloc_max_bytes(void);
 
 /* Gradients over packed sequences of different lengths. */
 typedef struct gdn_bwd_varlen_desc {

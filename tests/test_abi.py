@@ -24,7 +24,8 @@ def test_header_declares_expected_entry_points():
         ["gdn_chunk_fwd", "gdn_chunk_fwd_varlen", "gdn_decode_step", "gdn_status_string",
          "gdn_abi_version", "gdn_short_conv", "gdn_gates", "gdn_output_gate", "gdn_backward",
          "gdn_backward_workspace_size", "gdn_backward_varlen",
-         "gdn_backward_varlen_workspace_size"])
+         "gdn_backward_varlen_workspace_size", "gdn_backward_noalloc",
+         "gdn_backward_noalloc_max_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert gdn.abi_version() == 5
+    assert gdn.abi_version() == 6
     for st in range(4):
         s = gdn.status_string(st)
         assert s.startswith("GDN_")
