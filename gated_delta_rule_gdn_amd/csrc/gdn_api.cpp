@@ -47,6 +47,10 @@ gdn_status check_common(int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, int32_t 
   if (!std::isfinite(scale)) return GDN_ERR_INVALID_ARG;
   if (dk < 1 || dv < 1) return GDN_ERR_INVALID_ARG;
   if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return GDN_ERR_UNSUPPORTED;
+  // Token rows of at most 2^22 elements (the kernels address a 64-token chunk
+  // of any tensor with 32-bit byte offsets).
+  if ((int64_t)Hk * dk > (int64_t(1) << 22) || (int64_t)Hv * dv > (int64_t(1) << 22))
+    return GDN_ERR_UNSUPPORTED;
   // Gate storage must match the io type or be fp32; fp32 io with bf16 gates
   // is not built.
   if (!(gate == io || gate == GDN_F32)) return GDN_ERR_UNSUPPORTED;
@@ -142,6 +146,7 @@ BwdLayout bwd_layout(const BwdShape& d) {
 
 gdn_status check_bwd_shape(const BwdShape& d) {
   if (d.N < 0 || d.rows < 0 || d.T < 0) return GDN_ERR_INVALID_ARG;
+  if ((double)d.T > 2.0e9 || (double)d.rows > 2.0e9) return GDN_ERR_UNSUPPORTED;
   gdn_status st = check_common(d.Hk, d.Hv, d.dk, d.dv, d.io, d.gate, d.mode, d.scale);
   if (st != GDN_OK) return st;
   const double elems = (double)d.rows * (double)d.Hv * (double)(4 * d.dk + 2 * d.dv + 2);
@@ -154,7 +159,12 @@ gdn_status check_bwd_shape(const BwdShape& d) {
 }
 
 BwdShape shape_of(const gdn_bwd_desc* d) {
-  return BwdShape{d->B, d->B * d->T, d->T, nullptr, d->H_k, d->H_v, d->d_k, d->d_v,
+  // rows = B T, or -1 (rejected by check_bwd_shape) when a factor is negative
+  // or the product overflows
+  int64_t rows = -1;
+  if (d->B >= 0 && d->T >= 0 && __builtin_mul_overflow(d->B, d->T, &rows)) rows = -1;
+  if (d->B < 0 || d->T < 0) rows = -1;
+  return BwdShape{d->B, rows, d->T, nullptr, d->H_k, d->H_v, d->d_k, d->d_v,
                   d->io_dtype, d->gate_dtype, d->gate_mode, d->scale};
 }
 BwdShape shape_of(const gdn_bwd_varlen_desc* d, const int64_t* cu) {
@@ -274,6 +284,7 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
   const double elems = (double)d->B * (double)d->T * (double)d->H_v * (double)(d->d_k + d->d_v);
   if (elems > 9.0e15) return GDN_ERR_INVALID_ARG;
   if ((double)d->T > 2.0e9) return GDN_ERR_UNSUPPORTED;
+  if ((double)d->B * (double)d->H_v * 2.0 > 2.0e9) return GDN_ERR_UNSUPPORTED;  // grid size
   if (d->B == 0) return GDN_OK;  // nothing to read or write
   const int64_t rows = d->B * d->T;
   const int64_t heads = d->B * d->H_v;

@@ -21,5 +21,17 @@ def build(verbose=False):
     return out
 
 
+def build_sanitize_check(out, verbose=False):
+    """Compile sanitize_check.c with the oracle into the executable `out`,
+    with AddressSanitizer and UndefinedBehaviorSanitizer (host code; gcc)."""
+    srcs = [os.path.join(_HERE, "sanitize_check.c"), os.path.join(_HERE, "gdn_oracle.c")]
+    cmd = ["gcc", "-O1", "-g", "-std=c99", "-Wall", "-Wextra", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-o", out, *srcs, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -85,6 +85,9 @@ def _fwd(desc, **ptrs):
     ("T", -5, 1),
     ("scale", float("nan"), 1),
     ("scale", float("inf"), 1),
+    ("B", 2 ** 30, 2),        # more workgroups than a grid holds
+    ("T", 3 * 10 ** 9, 2),    # token index beyond 32 bits of chunk arithmetic
+    ("H_v", 2 ** 16, 2),      # a token row of v beyond 2^22 elements
 ])
 def test_fwd_rejects_bad_descriptor(field, value, expected):
     assert _fwd(_fwd_desc(**{field: value})) == expected
@@ -149,6 +152,7 @@ def _dec(desc, **ptrs):
 
 @pytest.mark.parametrize("field,value,expected", [
     ("H_v", 5, 1), ("d_k", 32, 2), ("N", -1, 1), ("io_dtype", 3, 1), ("scale", float("nan"), 1),
+    ("N", 2 ** 31, 2),        # more workgroups than a grid holds
 ])
 def test_decode_rejects_bad_descriptor(field, value, expected):
     assert _dec(_dec_desc(**{field: value})) == expected
@@ -396,9 +400,16 @@ def test_backward_workspace_size_formula():
 
 @pytest.mark.parametrize("field,value,expected", [
     ("H_v", 3, 1), ("d_k", 96, 2), ("io_dtype", 7, 1), ("gate_mode", 5, 1),
-    ("scale", float("nan"), 1), ("B", -1, 1)])
+    ("scale", float("nan"), 1), ("B", -1, 1), ("T", -3, 1), ("T", 3 * 10 ** 9, 2)])
 def test_backward_rejects_bad_descriptor(field, value, expected):
     assert _bwd(_bwd_desc(**{field: value}), ws_bytes=1 << 40) == expected
+
+
+def test_backward_rejects_overflowing_token_count():
+    """B T beyond int64 is rejected before any arithmetic on it."""
+    d = _bwd_desc(B=2 ** 62, T=2 ** 62)
+    assert gdn.lib.gdn_backward_workspace_size(ctypes.byref(d)) == 0
+    assert _bwd(d, ws_bytes=1 << 40) == gdn.GDN_ERR_INVALID_ARG
 
 
 def test_backward_pointer_rules():
