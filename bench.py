@@ -362,6 +362,20 @@ def block_op_workloads(gdn, synth, torch, dev, steps=20, warmup=3):
     return res
 
 
+def backward_exact_fraction(g, torch, block=16, limit=96.0):
+    """Fraction of (sequence, 16-token block, value head) units the backward
+    runs term by term, from channel log-decays g [B, T, H_v, d_k] and the
+    kernel's criterion: with G the inclusive cumulative log2-decay from the
+    block start and m the midpoint of each channel's range of G over the
+    block, some |G - m| above the limit."""
+    B, T = g.shape[0], g.shape[1]
+    Tb = (T // block) * block
+    x = g[:, :Tb].float() * 1.4426950408889634
+    G = torch.cumsum(x.reshape(B, Tb // block, block, g.shape[2], g.shape[3]), dim=2)
+    mid = 0.5 * (G.amax(dim=2, keepdim=True) + G.amin(dim=2, keepdim=True))
+    return float(((G - mid).abs().amax(dim=(2, 4)) > limit).float().mean())
+
+
 def backward_workload(gdn, synth, torch, dev, steps=5, warmup=2):
     """gdn_backward on the GDN-2 B8 T4096 shape (not part of the step): the
     gradients of every input for a random upstream gradient of o.  The
@@ -404,6 +418,23 @@ def backward_workload(gdn, synth, torch, dev, steps=5, warmup=2):
                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                         "flops_per_launch": flops,
                         "traffic": measured_traffic("backward", None)}}
+    # the same shape on gates from gdn_gates over the Mamba-2 recipe: the
+    # blocks whose decay range exceeds the factored form's run term by term
+    g, beta, w = realistic_gates(gdn, synth, torch, cfg)
+    inp["g"], inp["beta_or_b"], inp["w"] = (g.reshape(inp["g"].shape), beta.reshape(inp["g"].shape),
+                                           w.reshape(inp["v"].shape))
+    del g, beta, w
+    for _ in range(warmup):
+        run(grads)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        run(grads)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms2 = ev[0].elapsed_time(ev[1]) / steps
+    res["mamba2_gates"] = {"ms": round(ms2, 3),
+                           "term_by_term_fraction": round(backward_exact_fraction(inp["g"], torch), 4)}
     del inp, ws, grads, d_o
     torch.cuda.empty_cache()
     return res

@@ -29,9 +29,11 @@
 //   D <- Diag(gend) D + scale (gs q)^T dO - (gs e)^T DU.
 // The bracketed sums are intra-block.  They and A, Pm are products over the
 // channel with a per-channel decay; they factor as exp(G_s - ref) exp(ref - G_t)
-// around a per-channel reference (the block's 8th token) and then run on the
-// MFMA.  A block whose decay range would take the factors out of the fp32
-// range computes them term by term on the vector units instead.  With scalar
+// around a per-channel reference and then run on the
+// MFMA.  The reference is the midpoint of the channel's range of G over the
+// block, which makes max |G_s - ref| half that range; a block whose range
+// would still take the factors past the bound below computes them term by
+// term on the vector units instead.  With scalar
 // gates the decay is a 16 x 16 mask and the factors are 1.
 //
 // Layout: one workgroup per (sequence, value head, block of 64 value
@@ -57,9 +59,15 @@ namespace {
 
 constexpr int kCkpt = 16;            // tokens per block (and between stored states)
 constexpr int kCols = 64;            // value columns per workgroup
-// Largest |G_s - ref| (log2 units) for which the factored operands, their
-// products with the intra-block matrices and the masked-out entries stay
-// finite in fp32.
+// Largest |G_s - ref| (log2 units) on the MFMA path.  The factored operands
+// are at most 2^96 |k| (and 2^96 |q|, |e|), well inside fp32 and bf16.  An
+// intra-block bracketed sum adds 16 terms M[t][s] Kf_t with |Kf_t| <= 2^96
+// before the 2^(G_s - ref) factor brings it back, so it stays finite while
+// |M| < 2^28: M3 and M4 are products of per-token vectors (U dO^T, U DU^T)
+// and reach large values when a slowly decaying channel lets the state
+// gradient D grow over a long sequence, so the bound is kept well below
+// 2^127 / 16.  The masked-out entries of A and Pm (s < t) can overflow to
+// inf; they are dropped with selects, never multiplied by zero.
 constexpr float kSafeLog2 = 96.f;
 
 // Sum over the 16 lanes of a DPP row (all lanes get the sum).
@@ -441,13 +449,15 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       if (colw) issue_vw(mn * kCkpt);
       {
         const int i = tid % DK, qt = tid / DK;
-        float acc = 0.f, ref = 0.f, G[4] = {0.f, 0.f, 0.f, 0.f};
+        float acc = 0.f, gmax = -INFINITY, gmin = INFINITY, G[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < kCkpt; ++r) {
           acc += CHANNEL ? F.gl[r][i] : F.sgl[r];
-          if (r == 7) ref = acc;
+          gmax = fmaxf(gmax, acc);
+          gmin = fminf(gmin, acc);
           if ((r >> 2) == qt) G[r & 3] = acc;
         }
+        const float ref = 0.5f * (gmax + gmin);   // midpoint of the block's range
         const float lend = acc;
         if (qt == 0) F.gend[i] = exp2_fast(lend);
         st4f(&F.Gl[i][4 * qt], G);
@@ -655,13 +665,15 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     // ---- cumulative decay, factors and gated operands (thread: channel i, tokens 4 qt..) ----
     {
       const int i = tid % DK, qt = tid / DK;
-      float acc = 0.f, ref = 0.f, G[4] = {0.f, 0.f, 0.f, 0.f};
+      float acc = 0.f, gmax = -INFINITY, gmin = INFINITY, G[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < kCkpt; ++r) {
         acc += CHANNEL ? L.gl[r][i] : L.sgl[r];
-        if (r == 7) ref = acc;
+        gmax = fmaxf(gmax, acc);
+        gmin = fminf(gmin, acc);
         if ((r >> 2) == qt) G[r & 3] = acc;
       }
+      const float ref = 0.5f * (gmax + gmin);   // midpoint of the block's range
       const float lend = acc;
       if (qt == 0) {
         L.ref[i] = ref;
