@@ -259,7 +259,29 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
 
 
 def single_workload(gdn, synth, torch, dev, name, steps, warmup):
-    """gdn_chunk_fwd alone on one workload, warm back-to-back launches."""
+    """gdn_chunk_fwd (or gdn_chunk_fwd_varlen for a packed mix) alone on one
+    workload, warm back-to-back launches."""
+    if name in synth.VARLEN_CONFIGS:
+        vcfg = synth.VARLEN_CONFIGS[name]
+        inp = synth.varlen_inputs(vcfg, device="cuda")
+        o = torch.empty((vcfg.total_T, vcfg.Hv, vcfg.dv), dtype=vcfg.io_dtype, device=dev)
+        s = torch.empty((vcfg.N, vcfg.Hv, vcfg.dk, vcfg.dv), dtype=torch.float32, device=dev)
+
+        def run_v():
+            gdn.gdn_chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["beta_or_b"],
+                                     inp["cu_seqlens"], w=inp["w"], g=inp["g"], state_out=s, o=o)
+        for _ in range(warmup):
+            run_v()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            run_v()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        return {"workload": name, "ms": round(ms, 4),
+                "tokens_per_s": round(vcfg.total_T / (ms * 1e-3), 1)}
     base = name[:-len("_mamba2_gates")] if name.endswith("_mamba2_gates") else name
     cfg = synth.CONFIGS[base]
     inp = synth.chunk_inputs(cfg, device="cuda")

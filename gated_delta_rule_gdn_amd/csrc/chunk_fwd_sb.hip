@@ -58,6 +58,7 @@ struct IntTag {
 };
 
 constexpr int kSB = 16;           // tokens per sub-block
+constexpr int kRankMax = 256;     // packed sequences ranked by length in the kernel
 constexpr int kSbThreads = 512;   // 4 consumer + 4 producer waves
 constexpr float kRange = 110.f;   // largest |G - m_h| (log2) of the factored form
 
@@ -271,27 +272,62 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   const GT* __restrict__ gg = static_cast<const GT*>(p.g);
   T* __restrict__ go = static_cast<T*>(p.o);
 
-  // Workgroup -> (head, d_v slice), XCD-aware (workgroup i runs on XCD i % 8;
-  // the slices of one head land on the same XCD and share its L2).
+  const int tid = threadIdx.x;
+  // packed sequences: clamped token range of sequence n, so malformed offsets
+  // stay inside the tensors
+  auto seq_range = [&](int64_t n, int64_t& a0, int64_t& a1) {
+    a0 = p.cu[n];
+    a1 = p.cu[n + 1];
+    a0 = a0 < 0 ? 0 : (a0 > p.T ? p.T : a0);
+    a1 = a1 < a0 ? a0 : (a1 > p.T ? p.T : a1);
+  };
+  // Workgroup -> (sequence, value head, d_v slice).  Equal-length sequences:
+  // XCD-aware (workgroup i runs on XCD i % 8; the slices of one head, and
+  // the value heads that share a key head, land on the same XCD and share its
+  // L2).  Packed sequences: workgroups start in dispatch order with the
+  // longest sequence first (ties by index), so that the short ones fill in
+  // behind; the rank is computed here when there are at most kRankMax
+  // sequences.
   const int64_t nwg = (int64_t)gridDim.x;
   int64_t lid = blockIdx.x;
-  if ((nwg & 7) == 0) lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
-  const int64_t head = lid / NSPLIT;
-  const int split = (int)(lid - head * NSPLIT);
-  const int64_t bidx = head / p.Hv;
-  const int hv = (int)(head - bidx * p.Hv);
+  if (!p.cu && (nwg & 7) == 0) lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
+  const int64_t slot_head = lid / NSPLIT;
+  const int split = (int)(lid - slot_head * NSPLIT);
+  int64_t bidx = slot_head / p.Hv;
+  const int hv = (int)(slot_head - bidx * p.Hv);
+  if (p.cu && p.B <= kRankMax) {
+    int* lens = reinterpret_cast<int*>(smem);   // LDS is free until the pipeline starts
+    int* pick = lens + kRankMax;
+    for (int n = tid; n < (int)p.B; n += (int)blockDim.x) {
+      int64_t a0, a1;
+      seq_range(n, a0, a1);
+      lens[n] = (int)(a1 - a0);
+    }
+    __syncthreads();
+    for (int n = tid; n < (int)p.B; n += (int)blockDim.x) {
+      const int ln = lens[n];
+      int rank = 0;
+      for (int m = 0; m < (int)p.B; ++m) {
+        const int lm = lens[m];
+        rank += (lm > ln || (lm == ln && m < n)) ? 1 : 0;
+      }
+      if (rank == (int)bidx) *pick = n;   // exactly one sequence has each rank
+    }
+    __syncthreads();
+    bidx = *pick;
+    __syncthreads();
+  }
+  const int64_t head = bidx * p.Hv + hv;   // state index
   const int hk = hv / (p.Hv / p.Hk);
   const int c0 = split * DVS;
   int64_t tok0 = bidx * p.T, Tn = p.T;
-  if (p.cu) {  // packed sequences: clamped range, so malformed offsets stay inside
-    int64_t a0 = p.cu[bidx], a1 = p.cu[bidx + 1];
-    a0 = a0 < 0 ? 0 : (a0 > p.T ? p.T : a0);
-    a1 = a1 < a0 ? a0 : (a1 > p.T ? p.T : a1);
+  if (p.cu) {
+    int64_t a0, a1;
+    seq_range(bidx, a0, a1);
     tok0 = a0;
     Tn = a1 - a0;
   }
   const int64_t nchunks = (Tn + kC - 1) / kC;
-  const int tid = threadIdx.x;
   if (Tn == 0) {  // an empty sequence only passes its state through
     if (p.state_out) {
       const int64_t base = head * (int64_t)DK * DV + c0;
