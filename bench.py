@@ -132,32 +132,43 @@ def time_cold(fn, torch, flush, steps, warmup):
     return times[len(times) // 2], times[0], warm
 
 
-def exact_path_fraction(g, channel, torch, sub=16, limit=110.0):
-    """Fraction of (sequence, value head, 16-token sub-block) units the chunk
-    kernel runs on its exact token path, from the log-decay tensor g
-    ([B, T, H_v, d_k] or [B, T, H_v]) and the kernel's own criterion: with G
-    the cumulative log2-decay from the sub-block start, the factored form
-    needs |G - m_h| <= limit (m_h = G at token 3 for the first half, at token
-    11 for the second) with channel gates, and no rise G_t - min_{s<=t} G_s,
-    G_t or G_15 - G_t above it with scalar gates."""
+def sub_block_paths(g, channel, torch, sub=16, limit=110.0, c01_limit=124.0, floor=15.0):
+    """Fractions of (sequence, value head, 16-token sub-block) units that the
+    chunk kernel scans a second time with floored decays, and that it runs on
+    its exact token path, from the log-decay tensor g ([B, T, H_v, d_k] or
+    [B, T, H_v]) and the kernel's own criterion.  With G the cumulative
+    log2-decay from the sub-block start, channel gates need |G - m_h| <= limit
+    (m_h = G at token 3 for the first half, at token 11 for the second),
+    m_0 - m_1 <= c01_limit and the rising-state bounds; a sub-block that fails
+    is scanned again with every per-token log2-decay raised to -floor, and
+    takes the token path only if it still fails.  Scalar gates: no rise
+    G_t - min_{s<=t} G_s, G_t or G_15 - G_t above the limit (no floor)."""
     B, T = g.shape[0], g.shape[1]
     Tb = (T // sub) * sub
     x = g[:, :Tb].float() * 1.4426950408889634
     if not channel:
         x = x.unsqueeze(-1)
     x = x.reshape(B, Tb // sub, sub, x.shape[2], x.shape[3])
-    G = torch.cumsum(x, dim=2)
-    g15 = G[:, :, 15:16]
-    if channel:
-        m0, m1 = G[:, :, 3:4], G[:, :, 11:12]
-        mh = torch.cat([m0.expand(-1, -1, 8, -1, -1), m1.expand(-1, -1, 8, -1, -1)], dim=2)
-        worst = torch.maximum((G - mh).abs(), torch.maximum(mh, g15 - mh))
-        worst = torch.maximum(worst, torch.maximum(m1 - m0, g15))
-    else:
-        rise = G - torch.cummin(G, dim=2).values
-        worst = torch.maximum(torch.maximum(G, g15 - G), rise)
-    flagged = (worst.amax(dim=(2, 4)) > limit)
-    return float(flagged.float().mean())
+
+    def fails(lx):
+        G = torch.cumsum(lx, dim=2)
+        g15 = G[:, :, 15:16]
+        if channel:
+            m0, m1 = G[:, :, 3:4], G[:, :, 11:12]
+            mh = torch.cat([m0.expand(-1, -1, 8, -1, -1), m1.expand(-1, -1, 8, -1, -1)], dim=2)
+            worst = torch.maximum((G - mh).abs(), torch.maximum(mh, g15 - mh) + (limit - 10.0))
+            worst = torch.maximum(worst, torch.maximum(m1 - m0, g15) + (limit - 10.0))
+            worst = torch.maximum(worst, (m0 - m1) + (limit - c01_limit))
+        else:
+            rise = G - torch.cummin(G, dim=2).values
+            worst = torch.maximum(torch.maximum(G, g15 - G), rise)
+        return worst.amax(dim=(2, 4)) > limit
+
+    first = fails(x)
+    if not channel:
+        return 0.0, float(first.float().mean())
+    second = first & fails(torch.clamp(x, min=-floor))
+    return float(first.float().mean()), float(second.float().mean())
 
 
 def realistic_gates(gdn, synth, torch, cfg):
@@ -181,7 +192,8 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
     (median and min) and warm, against the same algorithmic bytes and flops
     as the headline workload.  The rows "*_mamba2_gates" run the B8 T4096
     shapes on gates from gdn_gates over the Mamba-2 recipe and report the
-    fraction of sub-blocks on the exact path."""
+    fractions of sub-blocks scanned with floored decays and on the exact
+    path."""
     res = {}
     flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)   # 512 MB
     rows = [("gdn1_fp32_small", None, None), ("gdn1_bf16_train", None, None),
@@ -200,7 +212,7 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
             inp["g"], inp["beta_or_b"] = g.reshape(inp["g"].shape), beta.reshape(inp["g"].shape)
             if cfg.channel:
                 inp["w"] = w.reshape(inp["v"].shape)
-            frac = exact_path_fraction(inp["g"], cfg.channel, torch)
+            floored, frac = sub_block_paths(inp["g"], cfg.channel, torch)
         o = torch.empty((cfg.B, cfg.T, cfg.Hv, cfg.dv), dtype=cfg.io_dtype, device=dev)
         s = torch.empty((cfg.B, cfg.Hv, cfg.dk, cfg.dv), dtype=torch.float32, device=dev)
 
@@ -225,6 +237,7 @@ def secondary_chunk_workloads(gdn, synth, torch, dev, steps=10, warmup=2):
                     "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
                                        (PEAK_FP32_TFLOPS if io_bytes == 4 else PEAK_BF16_TFLOPS), 4)}
         if frac is not None:
+            res[key]["floored_fraction"] = round(floored, 6)
             res[key]["exact_path_fraction"] = round(frac, 6)
         del inp, o, s
         torch.cuda.empty_cache()

@@ -24,10 +24,16 @@
 // token (m0 = G_3, m1 = G_11), so a factor spans at most four tokens of decay:
 //   L = -e exp(G - m_h),  M = q exp(G - m_h),  R = k exp(m_h - G)
 // gives the two diagonal 8x8 quadrants; the lower-left quadrant (t >= 8 > s)
-// uses L'' = L exp(m1 - m0) = -e exp(G - m0) against R (exp(G_t - m0) <= 1
-// there).  A sub-block where some |G - m_h| exceeds kRange (log2 units) runs
-// the exact token recurrence instead; on realistic Mamba-2 gates this is
-// about one sub-block in a thousand.
+// pairs L (reference m1) with R' = R exp(m1 - m0) = k exp(m1 - G) <= 1.
+// The factors must stay finite and exp(m1 - m0) a normal float.  A sub-block
+// whose decays break that (some |G - m_h| > kRange, or m0 - m1 > kC01Min,
+// log2 units) is redone with every per-token decay raised to at least
+// 2^-kFloor: a term that crosses such a token then carries 2^-15 in place of
+// a smaller true factor, a change of at most 2^-15 of its undecayed size,
+// well under the rounding of the bf16 operands (2^-9).  Floored, four tokens
+// span at most 60 and eight at most 120, so the retry always fits when
+// alpha <= 1; only a rising state (alpha > 1) can still leave the range, and
+// such a sub-block runs the exact token recurrence.
 //
 // With scalar gates (Gated DeltaNet, DeltaNet) the decay factors out of the
 // Gram matrices exactly: A[t,s] = beta_t exp(G_t - G_s) (k_t . k_s), applied
@@ -61,6 +67,8 @@ constexpr int kSB = 16;           // tokens per sub-block
 constexpr int kRankMax = 256;     // packed sequences ranked by length in the kernel
 constexpr int kSbThreads = 512;   // 4 consumer + 4 producer waves
 constexpr float kRange = 110.f;   // largest |G - m_h| (log2) of the factored form
+constexpr float kC01Min = 124.f;  // largest m0 - m1 (log2): exp(m1 - m0) stays normal
+constexpr float kFloor = 15.f;    // per-token decay floor (log2) of the second scan
 
 // One [16][DK] bf16 operand block.  Rows are DK contiguous channels in
 // 16-byte chunks of 8; the chunks of a row are XOR-permuted by the row, in
@@ -440,50 +448,76 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
               if constexpr (HAS_G) zero_raw(rg[i]);
             }
         }
-        // cumulative log2-decay over the sub-block: 4 tokens in-thread, then
-        // an exclusive scan over the 4 token quads of the lane quad
-        float G[4][CPL];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (HAS_G) {
-            unpack<GT, CPL>(rg[i], G[i]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) G[i][e] = 0.f;
-          }
-        }
-        float mh[CPL], fln[CPL], fkh[CPL], c01[CPL];
-        float worst = 0.f;
         float* dvec = vecp(slot) + pw * DK + ch0;
+        float G[4][CPL], mh[CPL], fln[CPL], fkh[CPL], c01[CPL];
+        float worst;
+        // cumulative log2-decay over the sub-block (4 tokens in-thread, then
+        // an exclusive scan over the 4 token quads of the lane quad), the
+        // references and factors, and the largest exponent the factored form
+        // would meet.  Pass 0 takes the exact decays; a sub-block they put out
+        // of range is scanned again with each per-token decay raised to at
+        // least 2^-kFloor.  One that still fails (a rising state) keeps its
+        // flag and runs the exact recurrence.
+        auto scan = [&](const bool floored) {
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          G[0][e] *= kLog2e;
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (HAS_G) {
+              unpack<GT, CPL>(rg[i], G[i]);
+            } else {
 #pragma unroll
-          for (int i = 1; i < 4; ++i) G[i][e] = fmaf(G[i][e], kLog2e, G[i - 1][e]);
-          // (every lane evaluates the DPP reads: a read under a branch
-          // would see the lanes that took the other side as inactive)
-          const float tot = G[3][e];
-          const float sh1 = quad_perm(tot, 0x90);
-          float s = tot + (qd >= 1 ? sh1 : 0.f);
-          const float sh2 = quad_perm(s, 0x44);
-          s = s + (qd >= 2 ? sh2 : 0.f);
-          const float excl = s - tot;
+              for (int e = 0; e < CPL; ++e) G[i][e] = 0.f;
+            }
+          }
+          worst = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) G[i][e] += excl;
-          const float m0 = quad_perm(G[3][e], 0x00);   // G at token 3
-          const float m1 = quad_perm(G[3][e], 0xAA);   // G at token 11
-          const float g15 = quad_perm(G[3][e], 0xFF);
-          mh[e] = qd < 2 ? m0 : m1;
-          fln[e] = exp2_fast(mh[e]);
-          fkh[e] = exp2_fast(g15 - mh[e]);
-          c01[e] = exp2_fast(m1 - m0);
-          // channel decay of the whole sub-block (one lane per channel group)
-          if (qd == 0) dvec[e] = exp2_fast(g15);
-          // per-channel factors that exceed 1 only when some g > 0; each
-          // may reach 2^10 so that no product of two factors overflows
-          worst = fmaxf(worst, fmaxf(fmaxf(mh[e], g15 - mh[e]), fmaxf(m1 - m0, g15)) +
-                                   (kRange - 10.f));
-        }
+          for (int e = 0; e < CPL; ++e) {
+            if (!floored) {
+              G[0][e] *= kLog2e;
+#pragma unroll
+              for (int i = 1; i < 4; ++i) G[i][e] = fmaf(G[i][e], kLog2e, G[i - 1][e]);
+            } else {
+              float acc = 0.f;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float lg = G[i][e] * kLog2e;
+                acc += lg < -kFloor ? -kFloor : lg;   // (a NaN stays NaN)
+                G[i][e] = acc;
+              }
+            }
+            // (every lane evaluates the DPP reads: a read under a branch
+            // would see the lanes that took the other side as inactive)
+            const float tot = G[3][e];
+            const float sh1 = quad_perm(tot, 0x90);
+            float s = tot + (qd >= 1 ? sh1 : 0.f);
+            const float sh2 = quad_perm(s, 0x44);
+            s = s + (qd >= 2 ? sh2 : 0.f);
+            const float excl = s - tot;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G[i][e] += excl;
+            const float m0 = quad_perm(G[3][e], 0x00);   // G at token 3
+            const float m1 = quad_perm(G[3][e], 0xAA);   // G at token 11
+            const float g15 = quad_perm(G[3][e], 0xFF);
+            mh[e] = qd < 2 ? m0 : m1;
+            fln[e] = exp2_fast(mh[e]);
+            fkh[e] = exp2_fast(g15 - mh[e]);
+            c01[e] = exp2_fast(m1 - m0);
+            // channel decay of the whole sub-block (one lane per channel group)
+            if (qd == 0) dvec[e] = exp2_fast(g15);
+            // the lane's tokens against their reference: |G - m_h| <= kRange
+            const float hi = fmaxf(fmaxf(G[0][e], G[1][e]), fmaxf(G[2][e], G[3][e]));
+            const float lo = fminf(fminf(G[0][e], G[1][e]), fminf(G[2][e], G[3][e]));
+            worst = fmaxf(worst, fmaxf(hi - mh[e], mh[e] - lo));
+            // per-channel factors that exceed 1 only when some g > 0; each
+            // may reach 2^10 so that no product of two factors overflows.
+            // exp(m1 - m0) stays a normal float (R' = R exp(m1 - m0) must
+            // not vanish while R is large).
+            worst = fmaxf(worst, fmaxf(fmaxf(mh[e], g15 - mh[e]), fmaxf(m1 - m0, g15)) +
+                                     (kRange - 10.f));
+            worst = fmaxf(worst, (m0 - m1) + (kRange - kC01Min));
+          }
+        };
+        scan(false);
+        if (__any(!(worst <= kRange))) scan(true);
         // gated operands, token by token; each operand row of the lane's
         // CPL channels goes out as one store.  M waits in registers until the
         // L rows it shares storage with have been read by the Gram products.
@@ -505,7 +539,6 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
             for (int h = 0; h < 2; ++h) {
               const int e = 2 * e2 + h;
               const float x = G[i][e] - mh[e];
-              worst = fmaxf(worst, fabsf(x));
               const float e1 = exp2_fast(x);
               const float e2v = exp2_fast(-x);
               Lv[h] = -(bv[e] * kv[e]) * e1;

@@ -118,9 +118,10 @@ def test_zero_initial_state_null_pointer():
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
 def test_strong_decay(io, channel):
     """Log-decay of -30 per token.  Channel gates: every 16-token sub-block
-    leaves the range of the factored form and runs the exact recurrence.
-    Scalar gates: the decay is an exact element-wise mask, so the MFMA path
-    holds."""
+    leaves the range of the factored form with its exact decays and is
+    scanned again with each per-token decay raised to 2^-15 (a change far
+    below the bf16 rounding).  Scalar gates: the decay is an exact
+    element-wise mask, so the MFMA path holds."""
     cfg = _cfg(io=io, T=150, channel=channel)
     inp = to_dev(synth.chunk_inputs(cfg))
     inp["g"] = torch.full_like(inp["g"], -30.0)
@@ -136,27 +137,34 @@ def test_mixed_chunks_strong_decay_in_one_chunk_only():
     _check(inp, TOL_FP32, label="middle chunk g=-30")
 
 
-# Sub-block patterns (16 tokens each; F = factored MFMA path, S = exact path),
-# ragged last chunk: both transitions inside a chunk and across chunks.
-_PATTERN = {True: "FSFS" + "FFFF" + "SSSS" + "SFFF" + "FFSF" + "S",
+# Sub-block patterns (16 tokens each; F = factored MFMA path, D = factored
+# with floored decays, S = exact token path), ragged last chunk: the
+# transitions inside a chunk and across chunks.  An S is followed by an F.
+_PATTERN = {True: "FSFD" + "DFFF" + "SFDS" + "FDDF" + "FFSF" + "D",
             False: "FSFF" + "SFFF" + "FSFS" + "FFFF" + "SF"}
 
 
 def _force_pattern(inp, channel):
-    """Make the sub-blocks marked S leave the factored range.  Channel gates:
-    a log-decay of -30 per token.  Scalar gates, where any decay stays an
-    exact mask: a growing state, g = +5 per token over the whole sub-block
-    (the rise exceeds the range only after 16 tokens), followed by a
-    sub-block that decays by as much (g = -5) so the state stays finite."""
+    """Give the sub-blocks marked D and S their decays.  D (channel gates): a
+    log-decay of -30 per token, out of the factored range until floored.  S:
+    a growing state, which no floor brings back into range; channel gates
+    g = +1 per token (the factors may grow by 2^10 at most), scalar gates
+    g = +5 (the rise exceeds the range only after 16 tokens).  The sub-block
+    after an S decays by as much, so the state stays finite."""
     g = inp["g"].clone()
     T = g.shape[1]
     pat = _PATTERN[channel]
+    rise = 1.0 if channel else 5.0
     for sb, c in enumerate(pat):
         lo, hi = 16 * sb, min(16 * sb + 16, T)
-        if c == "S" and lo < T:
-            g[:, lo:hi] = -30.0 if channel else 5.0
-            if not channel and hi < T:
-                g[:, hi:min(hi + 16, T)] = -5.0
+        if lo >= T:
+            continue
+        if c == "D":
+            g[:, lo:hi] = -30.0
+        elif c == "S":
+            g[:, lo:hi] = rise
+            if hi < T:
+                g[:, hi:min(hi + 16, T)] = -rise
     inp["g"] = g
     return inp
 
@@ -175,6 +183,32 @@ def test_sub_block_transitions_bf16(channel):
     for lo in range(0, T, 16):
         e = relerr(o[:, lo:lo + 16], o_ref[:, lo:lo + 16])
         assert e <= TOL_BF16, (lo, _PATTERN[channel][lo // 16], e)
+
+
+def test_reference_ratio_underflow_channel():
+    """Channel gates whose decays keep every |G - m_h| in range while
+    exp(m1 - m0) leaves the normal floats: log2-decay -25 at tokens 4-7 and
+    9-11 of a sub-block, none at token 8.  The pair (8, 7) crosses no decay,
+    so its term is whole, and q_8 = k_7 = k_8 makes it carry o_8.  The
+    kernel must not lose it through the factor exp(m1 - m0) = 2^-175."""
+    cfg = _cfg(io=torch.bfloat16, T=80, channel=True, B=2, Hk=1, Hv=2)
+    inp = to_dev(synth.chunk_inputs(cfg))
+    g = inp["g"].clone()
+    for base in (0, 48):
+        g[:, base:base + 16] = -0.05
+        g[:, base + 4:base + 8] = -25.0 / math.log2(math.e)
+        g[:, base + 8] = 0.0
+        g[:, base + 9:base + 12] = -25.0 / math.log2(math.e)
+        k = inp["k"]
+        k[:, base + 7] = k[:, base + 8]
+        inp["q"][:, base + 8] = k[:, base + 8]
+    inp["g"] = g
+    _check(inp, TOL_BF16, label="exp(m1 - m0) underflow")
+    o, _ = _gpu(inp)
+    o_ref, _ = _ref(inp)
+    for t in (8, 56):
+        e = relerr(o[:, t], o_ref[:, t])
+        assert e <= TOL_BF16, (t, e)
 
 
 @pytest.mark.parametrize("channel", [True, False])
