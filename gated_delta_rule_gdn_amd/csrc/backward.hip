@@ -142,9 +142,10 @@ struct FwdLds {
   T KgT[DK][TP];                                     // k ge  [channel][token]
   float Gl[DK][TP];                                  // cumulative log2-decay
   float gend[DK];
-  float A[kCkpt][kCkpt + 1];                         // exact Gram matrix
+  float A[kCkpt][kCkpt + 1];                         // exact channels' share of A
   float sb[kCkpt], sgl[kCkpt];
-  int unsafe;
+  uint32_t badm[DK / 32];                            // channels taken term by term
+  int unsafe;                                        // some channel is
 };
 
 // A thread's share of one block's row inputs (4 channels of one token).
@@ -224,11 +225,12 @@ struct RevLds {
   T dOt[kCols][TP], DUt[kCols][TP];                     // [column][token]
   float Gl[DK][TP];                                     // cumulative log2-decay
   float ref[DK], lend[DK], gend[DK];
-  float A[kCkpt][kCkpt + 1], P[kCkpt][kCkpt + 1];       // exact Gram matrices
+  float A[kCkpt][kCkpt + 1], P[kCkpt][kCkpt + 1];       // exact channels' share of A, Pm
   float M3[kCkpt][kCkpt + 1], M4[kCkpt][kCkpt + 1];
   float vs[4][kCkpt];                                   // scalar gates: sum_j v du per tile
   float sb[kCkpt], sgl[kCkpt];
-  int unsafe;
+  uint32_t badm[DK / 32];                               // channels taken term by term
+  int unsafe;                                           // some channel is
   // bf16 operands: the exit-state gradient as D^T [column][row], the X1
   // operand of the column waves (fp32 operands keep D tiles in registers).
   static constexpr bool kDl = sizeof(T) == 2;
@@ -437,6 +439,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       const int nt = FULL ? kCkpt : (int)((T - t0) < kCkpt ? (T - t0) : kCkpt);
       const int64_t mn = m + 1 < nblk ? m + 1 : m;   // the next block (or this one again)
       ld.store(F, tid);
+      if (tid < DK / 32) F.badm[tid] = 0u;
       if (tid == 0) F.unsafe = 0;
       float vv[4], wv[4];
 #pragma unroll
@@ -461,8 +464,10 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
         const float lend = acc;
         if (qt == 0) F.gend[i] = exp2_fast(lend);
         st4f(&F.Gl[i][4 * qt], G);
+        // a channel whose range takes the factors past the bound leaves the
+        // factored products (zero operands) and is added term by term
+        const bool bad = CHANNEL && 0.5f * (gmax - gmin) > kSafeLog2;
         float kg[4];
-        bool bad = false;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int s = 4 * qt + ii;
@@ -470,24 +475,31 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
           const float e = (CHANNEL ? F.b[s][i] : F.sb[s]) * kk;
           const float fq = CHANNEL ? exp2_fast(G[ii] - ref) : 1.f;
           const float fk = CHANNEL ? exp2_fast(ref - G[ii]) : 1.f;
-          if (CHANNEL) bad |= fabsf(G[ii] - ref) > kSafeLog2;
           kg[ii] = kk * exp2_fast(lend - G[ii]);
-          F.Kf[s][i] = from_f32<TO>(kk * fk);
-          F.Ef[s][i] = from_f32<TO>(e * fq);
+          F.Kf[s][i] = from_f32<TO>(bad ? 0.f : kk * fk);
+          F.Ef[s][i] = from_f32<TO>(bad ? 0.f : e * fq);
           F.Egm[s][i] = from_f32<TO>(-e * exp2_fast(G[ii]));
         }
         st4<TO>(&F.KgT[i][4 * qt], kg[0], kg[1], kg[2], kg[3]);
-        if (bad) F.unsafe = 1;
+        if (bad && qt == 0) {
+          atomicOr(&F.badm[i >> 5], 1u << (i & 31));
+          F.unsafe = 1;
+        }
       }
       lds_barrier();
       const bool exact = CHANNEL && F.unsafe != 0;   // uniform over the workgroup
       if (exact) {
+        // the term-by-term channels' share of A[s][t] = sum_i e_s k_t 2^(Gl_s - Gl_t)
         if (tid < kCkpt * kCkpt) {
           const int s = tid >> 4, t = tid & 15;
           float sa = 0.f;
           if (s > t) {
-            for (int i = 0; i < DK; ++i)
-              sa += F.b[s][i] * F.k[s][i] * F.k[t][i] * exp2_fast(F.Gl[i][s] - F.Gl[i][t]);
+#pragma unroll 1
+            for (int w = 0; w < DK / 32; ++w)
+              for (uint32_t m = F.badm[w]; m != 0u; m &= m - 1u) {
+                const int i = 32 * w + __builtin_ctz(m);
+                sa += F.b[s][i] * F.k[s][i] * F.k[t][i] * exp2_fast(F.Gl[i][s] - F.Gl[i][t]);
+              }
           }
           F.A[s][t] = sa;
         }
@@ -501,7 +513,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
           for (int ii = 0; ii < 4; ++ii)
             ck[(m * DK + 16 * rb + 4 * g4 + ii) * kCols + 16 * ct + n] = Sc[rb][ii];
         Frag4<float> nr, nc;   // rowL(N), accL(N), N = -A
-        if (!exact) {
+        {
           f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aAt = aA;
 #pragma unroll
           for (int kb = 0; kb < RB; ++kb) {
@@ -518,15 +530,13 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
               grn = r >= n ? token_decay(F, r, n) : 0.f;
               gnr = n >= r ? token_decay(F, n, r) : 0.f;
             }
-            nc.v[ii] = n < r ? -aA[ii] * grn : 0.f;
-            nr.v[ii] = r < n ? -aAt[ii] * gnr : 0.f;
-          }
-        } else {
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int r = 4 * g4 + ii;
-            nc.v[ii] = -F.A[r][n];
-            nr.v[ii] = -F.A[n][r];
+            float xc = aA[ii] * grn, xr = aAt[ii] * gnr;
+            if (exact) {
+              xc += F.A[r][n];
+              xr += F.A[n][r];
+            }
+            nc.v[ii] = n < r ? -xc : 0.f;
+            nr.v[ii] = r < n ? -xr : 0.f;
           }
         }
         // rowL((I + A)^{-1}) = accL(T^T), T = (I + N)(I + N^2)(I + N^4)(I + N^8)
@@ -651,6 +661,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     dps += __shfl_xor(dps, 32);
 
     ld.store(L, tid);
+    if (tid < DK / 32) L.badm[tid] = 0u;
     if (tid == 0) L.unsafe = 0;
     float vv[4], wv[4];
 #pragma unroll
@@ -681,8 +692,10 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
         L.gend[i] = exp2_fast(lend);
       }
       st4f(&L.Gl[i][4 * qt], G);
+      // as in the forward walk: a channel out of range has zero factored
+      // operands and is added term by term
+      const bool bad = CHANNEL && 0.5f * (gmax - gmin) > kSafeLog2;
       float kf[4], qf[4], ef[4], qg[4], eg[4];
-      bool bad = false;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int s = 4 * qt + ii;
@@ -691,10 +704,9 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
         const float gs = exp2_fast(G[ii]), ge = exp2_fast(lend - G[ii]);
         const float fq = CHANNEL ? exp2_fast(G[ii] - ref) : 1.f;
         const float fk = CHANNEL ? exp2_fast(ref - G[ii]) : 1.f;
-        if (CHANNEL) bad |= fabsf(G[ii] - ref) > kSafeLog2;
-        kf[ii] = kk * fk;
-        qf[ii] = qq * fq;
-        ef[ii] = e * fq;
+        kf[ii] = bad ? 0.f : kk * fk;
+        qf[ii] = bad ? 0.f : qq * fq;
+        ef[ii] = bad ? 0.f : e * fq;
         qg[ii] = scale * qq * gs;
         eg[ii] = -e * gs;
         L.Kg[s][i] = from_f32<TO>(kk * ge);
@@ -707,22 +719,29 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       st4<TO>(&L.EfT[i][4 * qt], ef[0], ef[1], ef[2], ef[3]);
       st4<TO>(&L.QgT[i][4 * qt], qg[0], qg[1], qg[2], qg[3]);
       st4<TO>(&L.EgT[i][4 * qt], eg[0], eg[1], eg[2], eg[3]);
-      if (bad) L.unsafe = 1;
+      if (bad && qt == 0) {
+        atomicOr(&L.badm[i >> 5], 1u << (i & 31));
+        L.unsafe = 1;
+      }
     }
     lds_barrier();
     const bool exact = CHANNEL && L.unsafe != 0;   // uniform over the workgroup
 
     if (exact) {
-      // Gram matrices term by term: A[s][t] = sum_i e_s k_t 2^(Gl_s - Gl_t).
+      // the term-by-term channels' share of A[s][t] = sum_i e_s k_t 2^(Gl_s - Gl_t)
+      // and of Pm (q_s in place of e_s)
       if (tid < kCkpt * kCkpt) {
         const int s = tid >> 4, t = tid & 15;
         float sa = 0.f, sp = 0.f;
         if (s >= t) {
-          for (int i = 0; i < DK; ++i) {
-            const float kt = L.k[t][i] * exp2_fast(L.Gl[i][s] - L.Gl[i][t]);
-            sa += L.b[s][i] * L.k[s][i] * kt;
-            sp += L.q[s][i] * kt;
-          }
+#pragma unroll 1
+          for (int w = 0; w < DK / 32; ++w)
+            for (uint32_t m = L.badm[w]; m != 0u; m &= m - 1u) {
+              const int i = 32 * w + __builtin_ctz(m);
+              const float kt = L.k[t][i] * exp2_fast(L.Gl[i][s] - L.Gl[i][t]);
+              sa += L.b[s][i] * L.k[s][i] * kt;
+              sp += L.q[s][i] * kt;
+            }
         }
         L.A[s][t] = s > t ? sa : 0.f;
         L.P[s][t] = s >= t ? sp : 0.f;
@@ -735,7 +754,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     if (colw) {
       Frag4<float> nr, nc;   // rowL(N), accL(N), N = -A
       Frag4<TO> pT;          // rowL(scale Pm^T) = scale accL(Pm)
-      if (!exact) {
+      {
         f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aAt = aA, aP = aA;
 #pragma unroll
         for (int kb = 0; kb < RB; ++kb) {
@@ -754,17 +773,15 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
             grn = r >= n ? token_decay(L, r, n) : 0.f;
             gnr = n >= r ? token_decay(L, n, r) : 0.f;
           }
-          nc.v[ii] = n < r ? -aA[ii] * grn : 0.f;
-          nr.v[ii] = r < n ? -aAt[ii] * gnr : 0.f;
-          pT.v[ii] = from_f32<TO>(r >= n ? scale * aP[ii] * grn : 0.f);
-        }
-      } else {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int r = 4 * g4 + ii;
-          nc.v[ii] = -L.A[r][n];
-          nr.v[ii] = -L.A[n][r];
-          pT.v[ii] = from_f32<TO>(scale * L.P[r][n]);
+          float xc = aA[ii] * grn, xr = aAt[ii] * gnr, xp = aP[ii] * grn;
+          if (exact) {
+            xc += L.A[r][n];
+            xr += L.A[n][r];
+            xp += L.P[r][n];
+          }
+          nc.v[ii] = n < r ? -xc : 0.f;
+          nr.v[ii] = r < n ? -xr : 0.f;
+          pT.v[ii] = from_f32<TO>(r >= n ? scale * xp : 0.f);
         }
       }
       // (I + A)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0), as accL.
@@ -830,7 +847,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     const Frag4<TO> kfb = ld_frag4<TO>(&L.KfT[ch][4 * g4]);   // accL(Kf) tile
     const Frag4<TO> qfb = ld_frag4<TO>(&L.QfT[ch][4 * g4]);
     const Frag4<TO> efb = ld_frag4<TO>(&L.EfT[ch][4 * g4]);
-    if (!exact) {
+    {
       Frag4<TO> a1, a2;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -845,11 +862,12 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       }
       mma16(dQa, a1, kfb);
       mma16(dKa, a2, qfb);
-    } else if (wave == 0) {
+    }
+    if (exact && wave == 0) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) L.M3[4 * g4 + ii][n] = m3[ii];
     }
-    lds_barrier();   // DU tiles (and the exact path's M3) visible
+    lds_barrier();   // DU tiles (and M3 for the term-by-term channels) visible
 
     if (colw) {
       // dv = w du, dw = v du (scalar gates: w = beta)
@@ -885,7 +903,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       mma16(m4, ua[c], dua);       // M4[4g+ii][n]
       mma16(m4t, dua, ua[c]);      // M4[n][4g+ii]
     }
-    if (!exact) {
+    {
       Frag4<TO> a3, a4;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -915,34 +933,57 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       }
       put_dl();   // read by the next block's column waves, after the end barrier
     }
+    // this lane's channel is taken term by term (its factored operands were
+    // zero, so the products above left nothing for it)
+    const bool bad_ch = exact && ((L.badm[ch >> 5] >> (ch & 31)) & 1u);
     if (exact) {
       if (wave == 0) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) L.M4[4 * g4 + ii][n] = m4[ii];
       }
       lds_barrier();
-      // intra-block terms term by term, with 2^(Gl_s - Gl_t) for s > t
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int s = 4 * g4 + ii;
-        const float Gs = L.Gl[ch][s];
+      // Intra-block terms of this wave's term-by-term channels, one channel
+      // at a time by the whole wave: lane 4 s + j takes token s against the
+      // partners t = 4 j .. 4 j + 3, with 2^(Gl_s - Gl_t) for s > t; the
+      // lane quad sums them and the channel's own lanes pick up their tokens.
+      const int sl = lane >> 2, jq = lane & 3;
+      const uint32_t wm = (L.badm[(16 * wave) >> 5] >> ((16 * wave) & 31)) & 0xffffu;
+#pragma unroll 1
+      for (uint32_t m = wm; m != 0u; m &= m - 1u) {   // uniform over the wave
+        const int c = 16 * wave + __builtin_ctz(m);
+        const float Gs = L.Gl[c][sl];
         float aq = 0.f, ae = 0.f, ak = 0.f;
-        for (int t2 = 0; t2 < kCkpt; ++t2) {
-          const float Gt = L.Gl[ch][t2];
-          if (t2 < s) {
-            const float kg = L.k[t2][ch] * exp2_fast(Gs - Gt);
-            aq += L.M3[t2][s] * kg;
-            ae += L.M4[t2][s] * kg;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t2 = 4 * jq + u;
+          const float Gt = L.Gl[c][t2];
+          if (t2 < sl) {
+            const float kg = L.k[t2][c] * exp2_fast(Gs - Gt);
+            aq += L.M3[t2][sl] * kg;
+            ae += L.M4[t2][sl] * kg;
           }
-          if (t2 > s) {
-            const float x = scale * L.M3[s][t2] * L.q[t2][ch] -
-                            L.M4[s][t2] * L.b[t2][ch] * L.k[t2][ch];
+          if (t2 > sl) {
+            const float x = scale * L.M3[sl][t2] * L.q[t2][c] -
+                            L.M4[sl][t2] * L.b[t2][c] * L.k[t2][c];
             ak += x * exp2_fast(Gt - Gs);
           }
         }
-        dQa[ii] = aq;
-        dEa[ii] = ae;
-        dKa[ii] = ak;
+        aq += __shfl_xor(aq, 1);
+        ae += __shfl_xor(ae, 1);
+        ak += __shfl_xor(ak, 1);
+        aq += __shfl_xor(aq, 2);
+        ae += __shfl_xor(ae, 2);
+        ak += __shfl_xor(ak, 2);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int src = 4 * (4 * g4 + ii);
+          const float vq = __shfl(aq, src), ve = __shfl(ae, src), vk = __shfl(ak, src);
+          if (ch == c) {
+            dQa[ii] = vq;
+            dEa[ii] = ve;
+            dKa[ii] = vk;
+          }
+        }
       }
     }
 
@@ -951,7 +992,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       const float4 G4 = *reinterpret_cast<const float4*>(&L.Gl[ch][4 * g4]);
       const float Gv[4] = {G4.x, G4.y, G4.z, G4.w};
       const float ref = L.ref[ch], lend = L.lend[ch];
-      const bool fac = CHANNEL && !exact;
+      const bool fac = CHANNEL && !bad_ch;
       const int send = nt - 1;   // the block's last token
       // dG: every pair of terms that share a decay factor contributes once
       // at each end, so the pairs whose factor is identically 1 -- the
