@@ -149,14 +149,15 @@ constexpr int kFG = 4;    // G_t (log2)
 constexpr int kFD = 5;    // [0] = D = exp(G_15)
 
 __device__ __forceinline__ float quad_perm(float x, int pat) {
+  // every lane reads a lane of its own quad, so no lane keeps an old value
   int v = __builtin_bit_cast(int, x);
   int r;
   switch (pat) {
-    case 0x00: r = __builtin_amdgcn_update_dpp(0, v, 0x00, 0xf, 0xf, false); break;
-    case 0x90: r = __builtin_amdgcn_update_dpp(0, v, 0x90, 0xf, 0xf, false); break;
-    case 0x44: r = __builtin_amdgcn_update_dpp(0, v, 0x44, 0xf, 0xf, false); break;
-    case 0xAA: r = __builtin_amdgcn_update_dpp(0, v, 0xAA, 0xf, 0xf, false); break;
-    default: r = __builtin_amdgcn_update_dpp(0, v, 0xFF, 0xf, 0xf, false); break;
+    case 0x00: r = __builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false); break;
+    case 0x90: r = __builtin_amdgcn_mov_dpp(v, 0x90, 0xf, 0xf, false); break;
+    case 0x44: r = __builtin_amdgcn_mov_dpp(v, 0x44, 0xf, 0xf, false); break;
+    case 0xAA: r = __builtin_amdgcn_mov_dpp(v, 0xAA, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_mov_dpp(v, 0xFF, 0xf, 0xf, false); break;
   }
   return __builtin_bit_cast(float, r);
 }
@@ -557,9 +558,11 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           const int r = 4 * qd + i;
           st_words<CPL / 2>(sLn + B::ax(r, ch0), wLn);
           st_words<CPL / 2>(sQb + B::ax(r, ch0), wQb);
-          if (B::half_swapped(r)) {
-            const uint32_t a0 = wKh[0], a1 = wKh[1];
-            wKh[0] = wKh[2]; wKh[1] = wKh[3]; wKh[2] = a0; wKh[3] = a1;
+          if constexpr (B::kWide) {   // (a lane's row piece is one 16-byte chunk)
+            if (B::half_swapped(r)) {
+              const uint32_t a0 = wKh[0], a1 = wKh[1];
+              wKh[0] = wKh[2]; wKh[1] = wKh[3]; wKh[2] = a0; wKh[3] = a1;
+            }
           }
           st_words<CPL / 2>(sKh + B::at(r, ch0), wKh);
           st_words<CPL / 2>(sLM + B::at(r, ch0), wL);

@@ -73,6 +73,27 @@ def test_packed_sequences_match_oracle_per_sequence(channel, io, gate):
         assert relerr(s_out[n:n + 1], s_ref) <= tol, (n, "state")
 
 
+def test_more_sequences_than_the_kernel_ranks():
+    """300 packed sequences: above the 256 the kernel orders longest first,
+    so they run in their given order; every one must still match the oracle."""
+    announce("varlen N=300")
+    rng = np.random.default_rng(5)
+    lengths = [int(x) for x in rng.integers(0, 40, size=300)]
+    lengths[123] = 150
+    packed, s0, cu = _packed(lengths, channel=True, Hk=1, Hv=2, dk=64, dv=64)
+    d = _dev(packed)
+    s_out = torch.full_like(s0, float("nan")).cuda()
+    o, _ = gdn.gdn_chunk_fwd_varlen(d["q"], d["k"], d["v"], d["beta_or_b"], cu.cuda(), w=d["w"],
+                                    g=d["g"], state_in=s0.cuda(), state_out=s_out)
+    torch.cuda.synchronize()
+    for n in range(len(lengths)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        o_ref, s_ref = _oracle_seq(packed, s0, a, b, n)
+        if b > a:
+            assert relerr(o[a:b].unsqueeze(0), o_ref) <= TOL_BF16, (n, "o")
+        assert relerr(s_out[n:n + 1], s_ref) <= TOL_BF16, (n, "state")
+
+
 def test_packed_equals_separate_calls_bitwise():
     announce("varlen vs separate gdn_chunk_fwd calls")
     packed, s0, cu = _packed(LENGTHS, channel=True)
