@@ -397,6 +397,55 @@ def block_op_workloads(gdn, synth, torch, dev, steps=20, warmup=3):
     return res
 
 
+def fused_gate_workloads(gdn, synth, torch, dev, steps=20, warmup=3):
+    """Gate activations inside the chunk kernel (gdn_chunk_fwd_gated) against
+    gdn_gates followed by gdn_chunk_fwd, at the GDN-2 and GDN-1 B8 T4096
+    shapes on the block recipe's raw projections (warm, back-to-back
+    launches, HIP events on the launch stream)."""
+    res = {}
+    for name in ("gdn2_bf16_train", "gdn1_bf16_train"):
+        cfg = synth.CONFIGS[name]
+        inp = synth.chunk_inputs(cfg, device="cuda")
+        bcfg = synth.BlockConfig("gates", N=cfg.B, T=cfg.T, Hk=cfg.Hk, Hv=cfg.Hv, dk=cfg.dk,
+                                 dv=cfg.dv, channel=cfg.channel, io_dtype=torch.bfloat16,
+                                 gate_dtype=torch.bfloat16, seed=7)
+        blk = synth.block_inputs(bcfg, device="cuda", conv_state=False)
+        B, T, Hv, d = cfg.B, cfg.T, cfg.Hv, cfg.dk
+        shape = (B, T, Hv, d) if cfg.channel else (B, T, Hv)
+        o = torch.empty((B, T, Hv, d), dtype=torch.bfloat16, device=dev)
+        s = torch.empty((B, Hv, d, d), dtype=torch.float32, device=dev)
+        g, beta, w = gdn.gdn_gates(blk["a_raw"], blk["b_raw"], Hv, w_raw=blk["w_raw"],
+                                   A_log=blk["A_log"], dt_bias=blk["dt_bias"], d_k=d, d_v=d)
+
+        def two_step():
+            gdn.gdn_gates(blk["a_raw"], blk["b_raw"], Hv, w_raw=blk["w_raw"], A_log=blk["A_log"],
+                          dt_bias=blk["dt_bias"], d_k=d, d_v=d, g=g, beta_or_b=beta, w=w)
+            gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], beta.view(shape),
+                              w=None if w is None else w.view(B, T, Hv, d), g=g.view(shape),
+                              state_out=s, o=o)
+
+        def fused():
+            gdn.gdn_chunk_fwd_gated(inp["q"], inp["k"], inp["v"], blk["b_raw"], a_raw=blk["a_raw"],
+                                    w_raw=blk["w_raw"], A_log=blk["A_log"], dt_bias=blk["dt_bias"],
+                                    state_out=s, o=o)
+        row = {}
+        for key, fn in (("gates_then_chunk_ms", two_step), ("fused_ms", fused)):
+            for _ in range(warmup):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            ev[0].record()
+            for _ in range(steps):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            row[key] = round(ev[0].elapsed_time(ev[1]) / steps, 4)
+        res[name] = row
+        del inp, blk, o, s, g, beta, w
+        torch.cuda.empty_cache()
+    return res
+
+
 def backward_exact_fraction(g, torch, block=16, limit=96.0):
     """Fraction of (sequence, 16-token block, value head, channel) units the
     backward computes term by term, from channel log-decays g [B, T, H_v,
@@ -742,6 +791,7 @@ def main():
         out["secondary"] = secondary_chunk_workloads(gdn, synth, torch, dev)
     if not args.no_block_ops:
         out["block_ops"] = block_op_workloads(gdn, synth, torch, dev)
+        out["block_ops"]["fused_gates"] = fused_gate_workloads(gdn, synth, torch, dev)
     if not args.no_backward:
         out["backward"] = backward_workload(gdn, synth, torch, dev)
     if args.copy_calibration:  # the last GPU work of the process

@@ -192,6 +192,13 @@ struct Params {
   const float* state_in;
   float* state_out;
   void* o;
+  // Raw gate projections (the kernel applies the activations): b, g and w
+  // are then the projections of beta|b, of the decay and of w, read with
+  // these row strides (elements); A_log and dt_bias are per column of g's
+  // projection, or nullptr (0).
+  int64_t ld_b = 0, ld_g = 0, ld_w = 0;
+  const float* A_log = nullptr;
+  const float* dt_bias = nullptr;
 };
 
 }  // namespace

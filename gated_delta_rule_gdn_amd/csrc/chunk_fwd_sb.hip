@@ -259,7 +259,10 @@ __device__ __forceinline__ Frag4<float> unit_lower_inverse(const Frag4<float>& n
   return r;  // accL(T^T) = rowL(T)
 }
 
-template <typename GT, int DK, int DV, bool CHANNEL, bool HAS_G>
+// RAW: b, g and w are the raw gate projections (row strides p.ld_b, p.ld_g,
+// p.ld_w) and the kernel applies the activations where it reads them:
+// sigmoid for beta|b and w, the Mamba-2 log-decay for g.
+template <typename GT, int DK, int DV, bool CHANNEL, bool HAS_G, bool RAW>
 __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   using T = bf16;
   using L = SbLds<DK, CHANNEL>;
@@ -372,14 +375,18 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   const uint32_t v_tok = (uint32_t)(p.Hv * DV * 2);   // bytes per token of v (and o)
 
   const uint32_t qk_tok = (uint32_t)(p.Hk * DK * (int)sizeof(T));   // bytes per token
-  const uint32_t gc_tok = (uint32_t)(p.Hv * DK * (int)sizeof(GT));
-  const uint32_t gs_tok = (uint32_t)(p.Hv * (int)sizeof(GT));
+  // bytes per token of beta|b and of g (the projections' row strides when raw)
+  const uint32_t gb_tok = RAW ? (uint32_t)(p.ld_b * (int64_t)sizeof(GT))
+                              : (uint32_t)(p.Hv * (CHANNEL ? DK : 1) * (int)sizeof(GT));
+  const uint32_t gg_tok = RAW ? (uint32_t)(p.ld_g * (int64_t)sizeof(GT)) : gb_tok;
   const char* bq = reinterpret_cast<const char*>(gq) + ((uint64_t)tok0 * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
   const char* bk = reinterpret_cast<const char*>(gk) + ((uint64_t)tok0 * qk_tok + (uint32_t)(hk * DK * (int)sizeof(T)));
-  const char* bbc = reinterpret_cast<const char*>(gb) + ((uint64_t)tok0 * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
-  const char* bgc = reinterpret_cast<const char*>(gg) + ((uint64_t)tok0 * gc_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
-  const char* bbs = reinterpret_cast<const char*>(gb) + ((uint64_t)tok0 * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
-  const char* bgs = reinterpret_cast<const char*>(gg) + ((uint64_t)tok0 * gs_tok + (uint32_t)(hv * (int)sizeof(GT)));
+  const char* bbc = reinterpret_cast<const char*>(gb) + ((uint64_t)tok0 * gb_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
+  const char* bgc = reinterpret_cast<const char*>(gg) + ((uint64_t)tok0 * gg_tok + (uint32_t)(hv * DK * (int)sizeof(GT)));
+  const char* bbs = reinterpret_cast<const char*>(gb) + ((uint64_t)tok0 * gb_tok + (uint32_t)(hv * (int)sizeof(GT)));
+  const char* bgs = reinterpret_cast<const char*>(gg) + ((uint64_t)tok0 * gg_tok + (uint32_t)(hv * (int)sizeof(GT)));
+  // raw gates: the gate projections' token offsets (rows of the exact path)
+  auto gate_row = [&](int64_t tok, int64_t ld) -> int64_t { return (tok0 + tok) * ld; };
 
   if (wave >= 4) {
     if constexpr (!CHANNEL) __builtin_amdgcn_s_setprio(3);
@@ -409,15 +416,15 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           const uint64_t tu = (uint64_t)t0;
           const char* cq = bq + tu * qk_tok;
           const char* ck = bk + tu * qk_tok;
-          const char* cb = bbc + tu * gc_tok;
-          const char* cg2 = bgc + tu * gc_tok;
+          const char* cb = bbc + tu * gb_tok;
+          const char* cg2 = bgc + tu * gg_tok;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t tl = (uint32_t)(4 * qd + i);
             ld_raw<QB>(cq + (tl * qk_tok + oq), rq[i]);
             ld_raw<QB>(ck + (tl * qk_tok + oq), rk[i]);
-            ld_raw<GB>(cb + (tl * gc_tok + og), rb[i]);
-            if constexpr (HAS_G) ld_raw<GB>(cg2 + (tl * gc_tok + og), rg[i]);
+            ld_raw<GB>(cb + (tl * gb_tok + og), rb[i]);
+            if constexpr (HAS_G) ld_raw<GB>(cg2 + (tl * gg_tok + og), rg[i]);
           }
         } else {
 #pragma unroll
@@ -427,11 +434,14 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
             const uint64_t tu = (uint64_t)t;
             ld_raw<QB>(bq + (tu * qk_tok + oq), rq[i]);
             ld_raw<QB>(bk + (tu * qk_tok + oq), rk[i]);
-            ld_raw<GB>(bbc + (tu * gc_tok + og), rb[i]);
-            if constexpr (HAS_G) ld_raw<GB>(bgc + (tu * gc_tok + og), rg[i]);
+            ld_raw<GB>(bbc + (tu * gb_tok + og), rb[i]);
+            if constexpr (HAS_G) ld_raw<GB>(bgc + (tu * gg_tok + og), rg[i]);
           }
         }
       };
+      // raw gates: A_log and dt_bias of the lane's channels (read where used)
+      const float* pA = RAW && p.A_log ? p.A_log + hv * DK + ch0 : nullptr;
+      const float* pD = RAW && p.dt_bias ? p.dt_bias + hv * DK + ch0 : nullptr;
       T* priv = reinterpret_cast<T*>(smem + L::kPriv + pw * L::PRIV);
       T* sLM = priv;              // L, then M (rows 0..15)
       T* sR = priv + 16 * DK;     // R (rows 0..15)
@@ -450,6 +460,9 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
             }
         }
         float* dvec = vecp(slot) + pw * DK + ch0;
+        const bool partial = ci * kC + kSB * pw + kSB > Tn;   // wave-uniform
+        const int64_t tq = ci * kC + kSB * pw + 4 * qd;       // first token of the lane
+        (void)tq;
         float G[4][CPL], mh[CPL], fln[CPL], fkh[CPL], c01[CPL];
         float worst;
         // cumulative log2-decay over the sub-block (4 tokens in-thread, then
@@ -464,6 +477,15 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           for (int i = 0; i < 4; ++i) {
             if constexpr (HAS_G) {
               unpack<GT, CPL>(rg[i], G[i]);
+              if constexpr (RAW) {
+                // the decay of an absent token must stay 1 (g = 0)
+                const bool here = !partial || tq + i < Tn;
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) {
+                  const float nA = neg_exp_f(pA ? pA[e] : 0.f), dt = pD ? pD[e] : 0.f;
+                  G[i][e] = here ? log_decay_f(G[i][e], nA, dt) : 0.f;
+                }
+              }
             } else {
 #pragma unroll
               for (int e = 0; e < CPL; ++e) G[i][e] = 0.f;
@@ -532,6 +554,10 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           unpack<T, CPL>(rq[i], qv);
           unpack<T, CPL>(rk[i], kv);
           unpack<GT, CPL>(rb[i], bv);
+          if constexpr (RAW) {
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) bv[e] = sigmoid_f(bv[e]);   // absent tokens: k = 0
+          }
           uint32_t wLn[CPL / 2], wQb[CPL / 2], wKh[CPL / 2], wL[CPL / 2], wR[CPL / 2], wR2[CPL / 2];
 #pragma unroll
           for (int e2 = 0; e2 < CPL / 2; ++e2) {
@@ -640,6 +666,9 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       // 32 kb + 8 g .. + 7 of every 32-channel block (the MFMA fragment).
       Raw<16> rq[KB], rk[KB], rv[2];
       uint32_t ub = 0u, ug = 0u;
+      // raw gates: -exp(A_log) and dt_bias of the head
+      const float nAs = RAW ? neg_exp_f(p.A_log ? p.A_log[hv] : 0.f) : 0.f;
+      const float dts = RAW && p.dt_bias ? p.dt_bias[hv] : 0.f;
       // v rows of the sub-block for the consumers, whole 16-byte pieces:
       // lane l takes token 8 h + l / 8 and columns 8 (l % 8) .. + 7
       const char* bvs = reinterpret_cast<const char*>(gv) + ((uint64_t)tok0 * v_tok + (uint32_t)((hv * DV + c0) * 2));
@@ -658,8 +687,8 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           ld_raw<16>(bq + (tu * qk_tok + (uint32_t)((32 * kb + 8 * g) * 2)), rq[kb]);
           ld_raw<16>(bk + (tu * qk_tok + (uint32_t)((32 * kb + 8 * g) * 2)), rk[kb]);
         }
-        ub = ld_word<GT>(bbs + tu * gs_tok);
-        if constexpr (HAS_G) ug = ld_word<GT>(bgs + tu * gs_tok);
+        ub = ld_word<GT>(bbs + tu * gb_tok);
+        if constexpr (HAS_G) ug = ld_word<GT>(bgs + tu * gg_tok);
       };
       auto produce = [&](int64_t ci) {
         const int slot = (int)(ci & 1);
@@ -671,8 +700,13 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           kf[kb].v = __builtin_bit_cast(bf16x8, make_uint4(rk[kb].w[0], rk[kb].w[1], rk[kb].w[2], rk[kb].w[3]));
           qf[kb].v = __builtin_bit_cast(bf16x8, make_uint4(rq[kb].w[0], rq[kb].w[1], rq[kb].w[2], rq[kb].w[3]));
         }
-        const float beta = present ? word_f32<GT>(ub) : 0.f;
-        float x = (HAS_G && present) ? word_f32<GT>(ug) * kLog2e : 0.f;
+        float beta = present ? word_f32<GT>(ub) : 0.f;
+        float x = (HAS_G && present) ? word_f32<GT>(ug) : 0.f;
+        if constexpr (RAW) {
+          beta = present ? sigmoid_f(beta) : 0.f;
+          x = (HAS_G && present) ? log_decay_f(x, nAs, dts) : 0.f;
+        }
+        x *= kLog2e;
         // inclusive prefix over the 16 tokens of the row
         x += dpp_row_shr(x, 1);
         x += dpp_row_shr(x, 2);
@@ -783,7 +817,8 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         S[t][i] = sin ? sin[row * DV + col] : 0.f;
       }
   }
-  const uint32_t w_tok = (uint32_t)(p.Hv * DV * (int)sizeof(GT));
+  const uint32_t w_tok = RAW ? (uint32_t)(p.ld_w * (int64_t)sizeof(GT))
+                             : (uint32_t)(p.Hv * DV * (int)sizeof(GT));
   // v (and w) of the 16 tokens 16 sb + 4 g + i of a chunk for this column,
   // two tokens per register: zv/zw are prefetched a chunk ahead, cv/cw hold
   // the chunk being consumed (fp32 write gates keep one per word).  The reads
@@ -883,9 +918,38 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       const int64_t qk_off = ((tok0 + tok) * p.Hk + hk) * (int64_t)DK;
       const int64_t gt = (tok0 + tok) * p.Hv + hv;
       float sbeta = 0.f, salpha = 1.f;
+      // raw channel gates: the token's activated b and alpha, computed by the
+      // wave (two channels per lane) into its quarter of the flagged
+      // sub-block's first operand block, which nothing reads in this chunk
+      // (a wave's LDS accesses complete in order, so no barrier is needed)
+      const float* gact = nullptr;
+      if constexpr (CHANNEL && RAW) {
+        float* gsc = reinterpret_cast<float*>(opblk(slot, 0, (int)((tb - cb) / kSB))) + wave * 2 * DK;
+#pragma unroll
+        for (int c = lane; c < DK; c += 64) {
+          gsc[c] = sigmoid_f(to_f32(gb[gate_row(tok, p.ld_b) + hv * DK + c]));
+          float al = 1.f;
+          if constexpr (HAS_G) {
+            const int col = hv * DK + c;
+            al = exp2_fast(log_decay_f(to_f32(gg[gate_row(tok, p.ld_g) + col]),
+                                       neg_exp_f(p.A_log ? p.A_log[col] : 0.f),
+                                       p.dt_bias ? p.dt_bias[col] : 0.f) * kLog2e);
+          }
+          gsc[DK + c] = al;
+        }
+        gact = gsc;
+      }
       if constexpr (!CHANNEL) {
-        sbeta = to_f32(gb[gt]);
-        if constexpr (HAS_G) salpha = exp2_fast(to_f32(gg[gt]) * kLog2e);
+        if constexpr (RAW) {
+          sbeta = sigmoid_f(to_f32(gb[gate_row(tok, p.ld_b) + hv]));
+          if constexpr (HAS_G)
+            salpha = exp2_fast(log_decay_f(to_f32(gg[gate_row(tok, p.ld_g) + hv]),
+                                           neg_exp_f(p.A_log ? p.A_log[hv] : 0.f),
+                                           p.dt_bias ? p.dt_bias[hv] : 0.f) * kLog2e);
+        } else {
+          sbeta = to_f32(gb[gt]);
+          if constexpr (HAS_G) salpha = exp2_fast(to_f32(gg[gt]) * kLog2e);
+        }
       }
       float rp = 0.f;
 #pragma unroll
@@ -894,12 +958,18 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         float kr[4], er[4], ar[4];
         load_f32<4, T>(gk + qk_off + row, kr);
         if constexpr (CHANNEL) {
-          load_f32<4, GT>(gb + gt * DK + row, er);
-          if constexpr (HAS_G) {
+          if constexpr (RAW) {
+            const float4 e4 = *reinterpret_cast<const float4*>(gact + row);
+            const float4 a4 = *reinterpret_cast<const float4*>(gact + DK + row);
+            er[0] = e4.x; er[1] = e4.y; er[2] = e4.z; er[3] = e4.w;
+            ar[0] = a4.x; ar[1] = a4.y; ar[2] = a4.z; ar[3] = a4.w;
+          } else if constexpr (HAS_G) {
+            load_f32<4, GT>(gb + gt * DK + row, er);
             load_f32<4, GT>(gg + gt * DK + row, ar);
 #pragma unroll
             for (int i = 0; i < 4; ++i) ar[i] = exp2_fast(ar[i] * kLog2e);
           } else {
+            load_f32<4, GT>(gb + gt * DK + row, er);
 #pragma unroll
             for (int i = 0; i < 4; ++i) ar[i] = 1.f;
           }
@@ -916,7 +986,10 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       rp += __shfl_xor(rp, 16);
       rp += __shfl_xor(rp, 32);
       float z = to_f32(gv[gt * DV + col]);
-      if constexpr (CHANNEL) z *= to_f32(gw[gt * DV + col]);
+      if constexpr (CHANNEL) {
+        if constexpr (RAW) z *= sigmoid_f(to_f32(gw[gate_row(tok, p.ld_w) + hv * DV + col]));
+        else z *= to_f32(gw[gt * DV + col]);
+      }
       else z *= sbeta;
       const float d = z - rp;
       float op = 0.f;
@@ -1008,12 +1081,17 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       } else if constexpr (decltype(zpre)::value) {
         // prefetched words: tokens past the end already hold zero
         zz[i] = zval(sb, i);
-        ww[i] = wval(sb, i);
+        ww[i] = RAW ? sigmoid_f(wval(sb, i)) : wval(sb, i);
       } else {
         const int64_t t = tb + 4 * g + i;
         const int64_t tc = t < Tn - 1 ? t : Tn - 1;
         zz[i] = t < Tn ? to_f32(gv[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]) : 0.f;
-        ww[i] = CHANNEL ? to_f32(gw[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]) : 0.f;
+        if constexpr (CHANNEL) {
+          if constexpr (RAW) ww[i] = sigmoid_f(to_f32(gw[gate_row(tc, p.ld_w) + hv * DV + col]));
+          else ww[i] = to_f32(gw[((tok0 + tc) * p.Hv + hv) * (int64_t)DV + col]);
+        } else {
+          ww[i] = 0.f;
+        }
       }
     }
     if constexpr (CHANNEL) {
@@ -1144,14 +1222,15 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   }
 }
 
-template <typename GT, int DK, int DV, bool CH, bool HG>
+template <typename GT, int DK, int DV, bool CH, bool HG, bool RAW = false>
 hipError_t launch_sb_typed(const ChunkArgs& a, hipStream_t stream) {
   Params p;
   p.B = a.B; p.T = a.T; p.cu = a.cu_seqlens; p.Hk = a.Hk; p.Hv = a.Hv; p.scale = a.scale;
   p.q = a.q; p.k = a.k; p.v = a.v; p.b = a.b; p.w = a.w; p.g = a.g;
   p.state_in = a.state_in; p.state_out = a.state_out; p.o = a.o;
+  p.ld_b = a.ld_b; p.ld_g = a.ld_g; p.ld_w = a.ld_w; p.A_log = a.A_log; p.dt_bias = a.dt_bias;
   const int64_t nwg = a.B * a.Hv * (DV / 64);
-  chunk_fwd_sb_kernel<GT, DK, DV, CH, HG><<<dim3((unsigned)nwg), dim3(kSbThreads), 0, stream>>>(p);
+  chunk_fwd_sb_kernel<GT, DK, DV, CH, HG, RAW><<<dim3((unsigned)nwg), dim3(kSbThreads), 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -1172,10 +1251,21 @@ hipError_t sb_dims(const ChunkArgs& a, hipStream_t s) {
   return sb_gates<GT, 64, 64>(a, s);
 }
 
+// Raw gate projections: bf16 projections, d_k = d_v = 128.
+hipError_t sb_raw(const ChunkArgs& a, hipStream_t s) {
+  if (a.gate != DType::BF16 || a.dk != 128 || a.dv != 128) return hipErrorNotSupported;
+  const bool hg = a.g != nullptr;
+  if (a.channel) return hg ? launch_sb_typed<bf16, 128, 128, true, true, true>(a, s)
+                           : launch_sb_typed<bf16, 128, 128, true, false, true>(a, s);
+  return hg ? launch_sb_typed<bf16, 128, 128, false, true, true>(a, s)
+            : launch_sb_typed<bf16, 128, 128, false, false, true>(a, s);
+}
+
 }  // namespace
 
 // bf16 operands: sub-block producer/consumer kernel.
 hipError_t launch_chunk_fwd_sb(const ChunkArgs& a, hipStream_t stream) {
+  if (a.raw_gates) return sb_raw(a, stream);
   if (a.gate == DType::F32) return sb_dims<float>(a, stream);
   return sb_dims<bf16>(a, stream);
 }

@@ -317,6 +317,86 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_chunk_fwd_gated(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
+                               const gdn_raw_gates* gt, const float* state_in, float* state_out,
+                               void* o, void* stream) {
+  if (!d || !gt) return GDN_ERR_INVALID_ARG;
+  if (d->B < 0 || d->T < 0) return GDN_ERR_INVALID_ARG;
+  gdn_status st = check_common(d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
+                               d->gate_mode, d->scale);
+  if (st != GDN_OK) return st;
+  if (d->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  if (d->io_dtype != GDN_BF16 || d->gate_dtype != GDN_BF16 || d->d_k != 128 || d->d_v != 128)
+    return GDN_ERR_UNSUPPORTED;
+  const double elems = (double)d->B * (double)d->T * (double)d->H_v * (double)(d->d_k + d->d_v);
+  if (elems > 9.0e15) return GDN_ERR_INVALID_ARG;
+  if ((double)d->T > 2.0e9) return GDN_ERR_UNSUPPORTED;
+  if ((double)d->B * (double)d->H_v * 2.0 > 2.0e9) return GDN_ERR_UNSUPPORTED;  // grid size
+  const bool ch = d->gate_mode == GDN_GATES_CHANNEL;
+  const int64_t ncol = ch ? (int64_t)d->H_v * d->d_k : d->H_v;   // columns of a and b
+  const int64_t nw = (int64_t)d->H_v * d->d_v;                     // columns of w
+  if (!gt->b || (ch ? !gt->w : gt->w != nullptr)) return GDN_ERR_INVALID_ARG;
+  if (gt->ld_b < ncol || (gt->a && gt->ld_a < ncol) || (ch && gt->ld_w < nw))
+    return GDN_ERR_INVALID_ARG;
+  // a 64-token chunk of a projection is addressed with 32-bit byte offsets
+  const int64_t ld_max = int64_t(1) << 24;
+  if (gt->ld_b > ld_max || gt->ld_a > ld_max || gt->ld_w > ld_max) return GDN_ERR_UNSUPPORTED;
+  // channel gates: a and b rows are read in 16-byte pieces
+  if (ch && ((gt->ld_b % 8) != 0 || !aligned16(gt->b) ||
+             (gt->a && ((gt->ld_a % 8) != 0 || !aligned16(gt->a)))))
+    return GDN_ERR_INVALID_ARG;
+  auto al2 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; };
+  auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (!al2(gt->b) || (gt->a && !al2(gt->a)) || (gt->w && !al2(gt->w))) return GDN_ERR_INVALID_ARG;
+  if ((gt->A_log && !al4(gt->A_log)) || (gt->dt_bias && !al4(gt->dt_bias)))
+    return GDN_ERR_INVALID_ARG;
+  if (d->B == 0) return GDN_OK;
+  const int64_t rows = d->B * d->T;
+  const int64_t heads = d->B * d->H_v;
+  const int64_t nstate = heads * d->d_k * d->d_v;
+  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out)))
+    return GDN_ERR_INVALID_ARG;
+  const Span si = span(state_in, nstate, 4), so = span(state_out, nstate, 4);
+  if (si.valid() && overlaps(so, si) && !(si.lo == so.lo && si.hi == so.hi))
+    return GDN_ERR_INVALID_ARG;
+  if (d->T == 0) {
+    if (!state_out || state_out == state_in) return GDN_OK;
+    hipError_t e = gdn::launch_state_copy(state_in, state_out, nstate,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
+  if (!q || !k || !v || !o) return GDN_ERR_INVALID_ARG;
+  const void* a16[] = {q, k, v, o};
+  for (const void* p : a16)
+    if (!aligned16(p)) return GDN_ERR_INVALID_ARG;
+  // row-strided projections: from the first element to the last row's end
+  auto pspan = [&](const void* p, int64_t ld, int64_t cols) {
+    return span(p, p ? (rows - 1) * ld + cols : 0, 2);
+  };
+  const Span sq = span(q, rows * d->H_k * d->d_k, 2), sk = span(k, rows * d->H_k * d->d_k, 2);
+  const Span sv = span(v, rows * d->H_v * d->d_v, 2), sO = span(o, rows * d->H_v * d->d_v, 2);
+  const Span sa = pspan(gt->a, gt->ld_a, ncol), sb = pspan(gt->b, gt->ld_b, ncol);
+  const Span sw = pspan(gt->w, gt->ld_w, nw);
+  const Span sA = span(gt->A_log, ncol, 4), sD = span(gt->dt_bias, ncol, 4);
+  const Span inputs[] = {sq, sk, sv, sa, sb, sw, sA, sD};
+  for (const Span& in : inputs)
+    if (overlaps(sO, in) || overlaps(so, in)) return GDN_ERR_INVALID_ARG;
+  if (overlaps(sO, si) || overlaps(sO, so)) return GDN_ERR_INVALID_ARG;
+
+  gdn::ChunkArgs a;
+  a.B = d->B; a.T = d->T; a.Hk = d->H_k; a.Hv = d->H_v; a.dk = d->d_k; a.dv = d->d_v;
+  a.io = gdn::DType::BF16; a.gate = gdn::DType::BF16;
+  a.channel = ch; a.scale = d->scale;
+  a.q = q; a.k = k; a.v = v; a.b = gt->b; a.w = gt->w; a.g = gt->a;
+  a.state_in = state_in; a.state_out = state_out; a.o = o;
+  a.raw_gates = true;
+  a.ld_b = gt->ld_b; a.ld_g = gt->ld_a; a.ld_w = gt->ld_w;
+  a.A_log = gt->A_log; a.dt_bias = gt->dt_bias;
+  hipError_t e = gdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 gdn_status gdn_chunk_fwd_varlen(const gdn_varlen_desc* d, const int64_t* cu_seqlens,
                                 const void* q, const void* k, const void* v,
                                 const void* beta_or_b, const void* w, const void* g,

@@ -86,6 +86,29 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
+// Gate activations, on the hardware exp / log / reciprocal:
+//   sigmoid(x)  = 1 / (1 + 2^(-x log2 e))   (0 and 1 at the saturated ends)
+//   softplus(x) = max(x, 0) + log(1 + t),  t = e^-|x| in (0, 1]; for
+//                 t < 2^-10 the series t - t^2/2 replaces the log, which
+//                 would lose t's low bits in 1 + t.
+// The Mamba-2 log-decay is g = -exp(A_log) softplus(a + dt_bias); callers
+// that reuse a column's -exp(A_log) pass it as neg_A.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.f + exp2_fast(-x * kLog2e));
+}
+__device__ __forceinline__ float softplus_f(float x) {
+  const float t = exp2_fast(-fabsf(x) * kLog2e);
+  const float l = t < 0x1p-10f ? t - 0.5f * t * t
+                               : __builtin_amdgcn_logf(1.f + t) * 0.6931471805599453f;
+  return fmaxf(x, 0.f) + l;
+}
+__device__ __forceinline__ float neg_exp_f(float A_log) { return -exp2_fast(A_log * kLog2e); }
+__device__ __forceinline__ float log_decay_f(float a, float neg_A, float dt) {
+  return neg_A * softplus_f(a + dt);
+}
+
+// ---------------------------------------------------------------------------
 // MFMA fragments (wave64, 16x16 output tiles).
 //
 // For D[16x16] += A[16xK] * B[Kx16] a lane l = 16*g + j (g = 0..3, j = 0..15)

@@ -33,6 +33,11 @@ struct ChunkArgs {
   const float* state_in;
   float* state_out;
   void* o;
+  // raw gate projections (b, g, w hold the projections; see chunk_common.hpp)
+  bool raw_gates = false;
+  int64_t ld_b = 0, ld_g = 0, ld_w = 0;
+  const float* A_log = nullptr;
+  const float* dt_bias = nullptr;
 };
 
 // Short causal convolution of the q, k, v branch (+ SiLU, L2 norm of q, k).

@@ -288,26 +288,13 @@ __global__ __launch_bounds__(kThreads) void conv_state_kernel(ConvArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Gate activations, on the hardware exp / log / reciprocal:
-//   sigmoid(x)  = 1 / (1 + 2^(-x log2 e))   (0 and 1 at the saturated ends)
-//   softplus(x) = max(x, 0) + log(1 + t),  t = e^-|x| in (0, 1]; for
-//                 t < 2^-10 the series t - t^2/2 replaces the log, which
-//                 would lose t's low bits in 1 + t.
-// The vector kernel handles 8 consecutive columns per thread (every row
-// stride a multiple of 8 and the pointers 16-byte aligned); the scalar kernel
-// one element.  Flat indices are 32-bit (the host checks the counts fit).
+// Gate activations (sigmoid_f, softplus_f: gdn_device.hpp).  The vector
+// kernel handles 8 consecutive columns per thread (every row stride a
+// multiple of 8 and the pointers 16-byte aligned); the scalar kernel one
+// element.  Flat indices are 32-bit (the host checks the counts fit).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float sigmoid_f(float x) {
-  return __builtin_amdgcn_rcpf(1.f + exp2_fast(-x * kLog2e));
-}
-__device__ __forceinline__ float softplus_f(float x) {
-  const float t = exp2_fast(-fabsf(x) * kLog2e);
-  const float l = t < 0x1p-10f ? t - 0.5f * t * t
-                               : __builtin_amdgcn_logf(1.f + t) * 0.6931471805599453f;
-  return fmaxf(x, 0.f) + l;
-}
 __device__ __forceinline__ float decay_f(float a, float A_log, float dt) {
-  return -exp2_fast(A_log * kLog2e) * softplus_f(a + dt);
+  return log_decay_f(a, neg_exp_f(A_log), dt);
 }
 
 template <typename TI, typename TO>

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_SCALAR, GDN_GATES_CHANNEL = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class GdnFwdDesc(ctypes.Structure):
@@ -29,6 +29,12 @@ class GdnFwdDesc(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
                 ("gate_mode", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("scale", ctypes.c_float)]
+
+
+class GdnRawGates(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("ld_a", ctypes.c_int64), ("ld_b", ctypes.c_int64), ("ld_w", ctypes.c_int64)]
 
 
 class GdnVarlenDesc(ctypes.Structure):
@@ -99,6 +105,9 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp = ctypes.c_void_p
     lib.gdn_chunk_fwd.argtypes = [ctypes.POINTER(GdnFwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_gated.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_gated.argtypes = [ctypes.POINTER(GdnFwdDesc), vp, vp, vp,
+                                        ctypes.POINTER(GdnRawGates), vp, vp, vp, vp]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
     lib.gdn_chunk_fwd_varlen.argtypes = [ctypes.POINTER(GdnVarlenDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                          vp, vp, vp]
@@ -212,6 +221,50 @@ def gdn_chunk_fwd(q, k, v, beta_or_b, w=None, g=None, state_in=None, state_out=N
                            _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_fwd")
+    return o, state_out
+
+
+def gdn_chunk_fwd_gated(q, k, v, b_raw, a_raw=None, w_raw=None, A_log=None, dt_bias=None,
+                        state_in=None, state_out=None, o=None, scale: float = 1.0, chunk: int = 64,
+                        stream=None):
+    """Chunkwise forward on raw gate projections, the activations applied in
+    the kernel (see include/gdn.h).  Returns (o, state_out).
+
+    q, k [B,T,Hk,dk]; v [B,T,Hv,dv]; b_raw, a_raw [B*T, >= Hv] (scalar gates)
+    or [B*T, >= Hv dk] (channel gates, then w_raw [B*T, >= Hv dv] is
+    required): column blocks of a projection output are fine.  a_raw None
+    means alpha = 1.  A_log, dt_bias fp32 [columns of a] or None.
+    """
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    io = q.dtype
+    gdt = b_raw.dtype
+    channel = w_raw is not None
+    rows = B * T
+    ncol = Hv * dk if channel else Hv
+    _check(q, "q", (B, T, Hk, dk), io)
+    _check(k, "k", (B, T, Hk, dk), io)
+    _check(v, "v", (B, T, Hv, dv), io)
+    ld_b = _check_rows(b_raw, "b_raw", rows, ncol, gdt)
+    ld_a = _check_rows(a_raw, "a_raw", rows, ncol, gdt) if a_raw is not None else 0
+    ld_w = _check_rows(w_raw, "w_raw", rows, Hv * dv, gdt) if channel else 0
+    _check(A_log, "A_log", (ncol,), torch.float32)
+    _check(dt_bias, "dt_bias", (ncol,), torch.float32)
+    _check(state_in, "state_in", (B, Hv, dk, dv), torch.float32)
+    _check(state_out, "state_out", (B, Hv, dk, dv), torch.float32)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=io, device=q.device)
+    _check(o, "o", (B, T, Hv, dv), io)
+    if io not in _DT or gdt not in _DT:
+        raise ValueError("q and the projections must be float32 or bfloat16")
+    desc = GdnFwdDesc(B, T, Hk, Hv, dk, dv, _DT[io], _DT[gdt],
+                      GDN_GATES_CHANNEL if channel else GDN_GATES_SCALAR, chunk, float(scale))
+    gates = GdnRawGates(_ptr(a_raw), _ptr(b_raw), _ptr(w_raw), _ptr(A_log), _ptr(dt_bias),
+                        ld_a, ld_b, ld_w)
+    st = lib.gdn_chunk_fwd_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(gates),
+                                 _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_fwd_gated")
     return o, state_out
 
 

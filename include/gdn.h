@@ -53,10 +53,10 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
+#define GDN_ABI_VERSION 7  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
                               gdn_gates, gdn_output_gate; 4: adds gdn_backward;
                               5: adds gdn_backward_varlen; 6: adds
-                              gdn_backward_noalloc */
+                              gdn_backward_noalloc; 7: adds gdn_chunk_fwd_gated */
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -111,6 +111,41 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* desc, const void* q, const void* k,
                          const void* v, const void* beta_or_b, const void* w,
                          const void* g, const float* state_in, float* state_out,
                          void* o, void* stream);
+
+/* Raw gate projections for gdn_chunk_fwd_gated. */
+typedef struct gdn_raw_gates {
+  const void* a;         /* decay projection [B*T, ld_a] gate_dtype, or NULL => alpha = 1 */
+  const void* b;         /* beta|b projection [B*T, ld_b] gate_dtype                        */
+  const void* w;         /* CHANNEL: write-gate projection [B*T, ld_w]; SCALAR: NULL        */
+  const float* A_log;    /* [columns of a] fp32, or NULL (0)                                */
+  const float* dt_bias;  /* [columns of a] fp32, or NULL (0)                                */
+  int64_t ld_a, ld_b, ld_w;  /* row strides in elements (>= columns, <= 2^24)               */
+} gdn_raw_gates;
+
+/*
+ * gdn_chunk_fwd_gated -- gdn_chunk_fwd with the gate activations of
+ * gdn_gates applied inside the recurrence kernel, where it reads each gate
+ * (the notes page "Gated DeltaNet", §Architecture et versions hybrides,
+ * Figure 1: the gates come from plain projections; alpha takes the Mamba-2
+ * parameterisation):
+ *
+ *   g = log(alpha) = -exp(A_log[j]) * softplus(a[r][j] + dt_bias[j])
+ *   beta_or_b = sigmoid(b[r][j]),  w = sigmoid(w[r][j])   (CHANNEL)
+ *
+ * The result is that of gdn_gates followed by gdn_chunk_fwd, except that the
+ * activated gates are not rounded to gate_dtype in between.  Columns per row
+ * r = token: SCALAR H_v (a, b); CHANNEL H_v d_k (a, b) and H_v d_v (w), in
+ * the layouts of gdn_chunk_fwd's gates; the projections are read with their
+ * row strides, so they may be column blocks of one projection output.
+ * Supported: io_dtype = gate_dtype = BF16, d_k = d_v = 128, equal-length
+ * sequences (else GDN_ERR_UNSUPPORTED).  CHANNEL gates read a and b rows in
+ * 16-byte pieces: those two need ld % 8 == 0 and 16-byte aligned pointers;
+ * otherwise projections are 2-byte and A_log, dt_bias 4-byte aligned.
+ * Arguments q, k, v, state_in, state_out, o, stream: as gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_gated(const gdn_fwd_desc* desc, const void* q, const void* k,
+                               const void* v, const gdn_raw_gates* gates,
+                               const float* state_in, float* state_out, void* o, void* stream);
 
 /* Chunked forward over packed sequences of different lengths. */
 typedef struct gdn_varlen_desc {

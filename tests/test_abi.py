@@ -25,7 +25,7 @@ def test_header_declares_expected_entry_points():
          "gdn_abi_version", "gdn_short_conv", "gdn_gates", "gdn_output_gate", "gdn_backward",
          "gdn_backward_workspace_size", "gdn_backward_varlen",
          "gdn_backward_varlen_workspace_size", "gdn_backward_noalloc",
-         "gdn_backward_noalloc_max_bytes"])
+         "gdn_backward_noalloc_max_bytes", "gdn_chunk_fwd_gated"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert gdn.abi_version() == 6
+    assert gdn.abi_version() == 7
     for st in range(4):
         s = gdn.status_string(st)
         assert s.startswith("GDN_")
@@ -126,6 +126,58 @@ def test_fwd_rejects_output_overlapping_input():
 
 def test_fwd_empty_batch_is_a_noop():
     assert _fwd(_fwd_desc(B=0)) == gdn.GDN_OK
+
+
+def _gated(desc, gates=None, **ptrs):
+    """gdn_chunk_fwd_gated with fake pointers; gates defaults to channel raw
+    projections with row strides of a fused projection output."""
+    names = ["q", "k", "v", "s_in", "s_out", "o"]
+    p = {n: _addr(i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    ch = desc is not None and desc.gate_mode == gdn.GDN_GATES_CHANNEL
+    g = dict(a=_addr(10), b=_addr(11), w=_addr(12) if ch else None, A_log=_addr(13),
+             dt_bias=_addr(14), ld_a=4096 if ch else 64, ld_b=4096 if ch else 64, ld_w=4096)
+    if gates:
+        g.update(gates)
+    raw = gdn.GdnRawGates(**g)
+    return gdn.lib.gdn_chunk_fwd_gated(ctypes.byref(desc) if desc is not None else None,
+                                       p["q"], p["k"], p["v"], ctypes.byref(raw),
+                                       p["s_in"], p["s_out"], p["o"], None)
+
+
+@pytest.mark.parametrize("desc_kw,gates,expected", [
+    (dict(d_k=64), None, 2),                          # built for d_k = d_v = 128 only
+    (dict(d_v=64), None, 2),
+    (dict(io_dtype=gdn.GDN_F32, gate_dtype=gdn.GDN_F32), None, 2),
+    (dict(gate_dtype=gdn.GDN_F32), None, 2),
+    (dict(chunk=32), None, 2),
+    (dict(B=-1), None, 1),
+    (dict(), dict(b=None), 1),                        # b projection required
+    (dict(), dict(w=None), 1),                        # channel gates need w
+    (dict(gate_mode=gdn.GDN_GATES_SCALAR), dict(w=_addr(12)), 1),   # scalar gates forbid it
+    (dict(), dict(ld_b=100), 1),                      # fewer columns than H_v d_k = 512
+    (dict(), dict(ld_a=500), 1),
+    (dict(), dict(ld_w=511), 1),
+    (dict(), dict(ld_b=1028), 1),                     # channel rows read in 16-byte pieces
+    (dict(), dict(b=_addr(11, 8)), 1),
+    (dict(), dict(ld_b=2 ** 25), 2),                  # a chunk beyond 32-bit offsets
+    (dict(), dict(A_log=_addr(13, 2)), 1),
+])
+def test_gated_fwd_rejects_bad_arguments(desc_kw, gates, expected):
+    assert _gated(_fwd_desc(**desc_kw), gates) == expected
+
+
+def test_gated_fwd_pointer_rules():
+    assert _gated(None) == gdn.GDN_ERR_INVALID_ARG
+    assert _gated(_fwd_desc(), q=None) == gdn.GDN_ERR_INVALID_ARG
+    assert _gated(_fwd_desc(), o=_addr(5, 2)) == gdn.GDN_ERR_INVALID_ARG       # misaligned o
+    assert _gated(_fwd_desc(), o=_addr(11, 64)) == gdn.GDN_ERR_INVALID_ARG     # o inside b
+    assert _gated(_fwd_desc(), s_out=_addr(12, 64)) == gdn.GDN_ERR_INVALID_ARG  # state inside w
+    # scalar gates: 2-byte projections at any even offset and row stride
+    assert _gated(_fwd_desc(gate_mode=gdn.GDN_GATES_SCALAR, B=0),
+                  dict(b=_addr(11, 2), ld_b=13, ld_a=13)) == gdn.GDN_OK
+    assert _gated(_fwd_desc(B=0)) == gdn.GDN_OK
+    assert _gated(_fwd_desc(T=0), s_out=_addr(3)) == gdn.GDN_OK               # in place, nothing to do
 
 
 def test_fwd_zero_tokens_in_place_state_is_a_noop():
