@@ -789,9 +789,9 @@ def main():
     out["device_copy_GBps"] = copy_bandwidth(torch, dev)
     if not args.no_secondary:
         out["secondary"] = secondary_chunk_workloads(gdn, synth, torch, dev)
+        out["secondary"]["fused_gates"] = fused_gate_workloads(gdn, synth, torch, dev)
     if not args.no_block_ops:
         out["block_ops"] = block_op_workloads(gdn, synth, torch, dev)
-        out["block_ops"]["fused_gates"] = fused_gate_workloads(gdn, synth, torch, dev)
     if not args.no_backward:
         out["backward"] = backward_workload(gdn, synth, torch, dev)
     if args.copy_calibration:  # the last GPU work of the process
