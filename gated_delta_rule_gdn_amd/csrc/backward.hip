@@ -539,21 +539,35 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
             nr.v[ii] = r < n ? -xr : 0.f;
           }
         }
-        // rowL((I + A)^{-1}) = accL(T^T), T = (I + N)(I + N^2)(I + N^4)(I + N^8)
-        auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
-          f32x4 a = {0.f, 0.f, 0.f, 0.f};
-          mma16(a, x, y);
-          return f32frag(a);
-        };
-        const Frag4<float> n2c = prod(nr, nc), n2r = prod(nc, nr);
-        const Frag4<float> n4c = prod(n2r, n2c), n4r = prod(n2c, n2r);
-        const Frag4<float> n8r = prod(n4c, n4r);
+        // rowL((I + A)^{-1}) = accL(T^T), T = (I + N)(I + N^2)(I + N^4)(I + N^8):
+        // bf16 operands take the fp16 products while |N| allows them (one
+        // MFMA per product), otherwise (and for fp32 operands) the fp32 chain
         f32x4 trow;
+        bool have_t = false;
+        if constexpr (!std::is_same<TO, float>::value) {
+          float nmax;
+          const Frag4<float> tt = unit_lower_inverse(nr, nc, g4, n, nmax);
+          if (!__any(!(nmax <= kNBig))) {   // uniform over the wave
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) trow[ii] = n8r.v[ii] + (4 * g4 + ii == n ? 1.f : 0.f);
-        mma16(trow, n4c, f32frag(trow));
-        mma16(trow, n2c, f32frag(trow));
-        mma16(trow, nc, f32frag(trow));
+            for (int ii = 0; ii < 4; ++ii) trow[ii] = tt.v[ii];
+            have_t = true;
+          }
+        }
+        if (!have_t) {
+          auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            mma16(a, x, y);
+            return f32frag(a);
+          };
+          const Frag4<float> n2c = prod(nr, nc), n2r = prod(nc, nr);
+          const Frag4<float> n4c = prod(n2r, n2c), n4r = prod(n2c, n2r);
+          const Frag4<float> n8r = prod(n4c, n4r);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) trow[ii] = n8r.v[ii] + (4 * g4 + ii == n ? 1.f : 0.f);
+          mma16(trow, n4c, f32frag(trow));
+          mma16(trow, n2c, f32frag(trow));
+          mma16(trow, nc, f32frag(trow));
+        }
         // W = Z - (gs e) S, U = T W
         f32x4 wt;
 #pragma unroll
@@ -785,20 +799,35 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
         }
       }
       // (I + A)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0), as accL.
-      auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        mma16(a, x, y);
-        return f32frag(a);
-      };
-      const Frag4<float> n2c = prod(nr, nc), n2r = prod(nc, nr);
-      const Frag4<float> n4c = prod(n2r, n2c), n4r = prod(n2c, n2r);
-      const Frag4<float> n8c = prod(n4r, n4c);
+      // accL(T) = rowL(T^T), and T^T is the same product of N^T, so bf16
+      // operands take the fp16 products on (accL(N), rowL(N)) while |N|
+      // allows them; otherwise (and for fp32 operands) the fp32 chain.
       f32x4 tinv;
+      bool have_t = false;
+      if constexpr (!std::is_same<TO, float>::value) {
+        float nmax;
+        const Frag4<float> tt = unit_lower_inverse(nc, nr, g4, n, nmax);
+        if (!__any(!(nmax <= kNBig))) {   // uniform over the wave
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) tinv[ii] = n8c.v[ii] + (4 * g4 + ii == n ? 1.f : 0.f);
-      mma16(tinv, n4r, f32frag(tinv));
-      mma16(tinv, n2r, f32frag(tinv));
-      mma16(tinv, nr, f32frag(tinv));
+          for (int ii = 0; ii < 4; ++ii) tinv[ii] = tt.v[ii];
+          have_t = true;
+        }
+      }
+      if (!have_t) {
+        auto prod = [](const Frag4<float>& x, const Frag4<float>& y) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+          mma16(a, x, y);
+          return f32frag(a);
+        };
+        const Frag4<float> n2c = prod(nr, nc), n2r = prod(nc, nr);
+        const Frag4<float> n4c = prod(n2r, n2c), n4r = prod(n2c, n2r);
+        const Frag4<float> n8c = prod(n4r, n4c);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) tinv[ii] = n8c.v[ii] + (4 * g4 + ii == n ? 1.f : 0.f);
+        mma16(tinv, n4r, f32frag(tinv));
+        mma16(tinv, n2r, f32frag(tinv));
+        mma16(tinv, nr, f32frag(tinv));
+      }
       // RHS = (k ge) D + scale Pm^T dO for this column tile
       f32x4 rhs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -202,63 +202,6 @@ __device__ __forceinline__ Frag4<bf16> ld_tr16(const bf16* p) {
   return f;
 }
 
-typedef _Float16 sb_h4 __attribute__((ext_vector_type(4)));
-typedef _Float16 sb_h2 __attribute__((ext_vector_type(2)));
-typedef float sb_f2 __attribute__((ext_vector_type(2)));
-
-// Largest entry of N the fp16 inverse accepts.  With |N| <= m entrywise, an
-// entry of N^k is at most m^k C(14, k - 1) (paths of k strictly descending
-// steps), so every power and partial product below stays under
-// m (1 + m)^14 = 4.3e4 for m = 1.125, inside fp16's 65504; a sub-block above
-// it takes the exact path.  Unit keys with gates in [0, 1] and decay <= 1
-// give |N| <= 1.
-constexpr float kNBig = 1.125f;
-
-// (I + A)^{-1} of a 16x16 unit lower-triangular matrix from N = -A (strictly
-// lower, N^16 = 0):  (I + A)^{-1} = (I + N)(I + N^2)(I + N^4)(I + N^8), on the
-// fp16 MFMA with fp32 accumulation (one v_mfma_f32_16x16x16_f16 per product;
-// fp16 operands carry 11 significant bits, finer than the bf16 in which T is
-// stored).  Layouts (lane = 16 g + j):
-//   rowL(X): X[j][4g + i]      accL(X): X[4g + i][j]
-// mma(acc, rowL(X), accL(Y)) adds accL(X Y); accL(X) = rowL(X^T).
-// In: nr = rowL(N), nc = accL(N).  Out: rowL(T), T = (I + A)^{-1}, and nmax =
-// the lane's largest |N| entry.
-__device__ __forceinline__ Frag4<float> unit_lower_inverse(const Frag4<float>& nr,
-                                                           const Frag4<float>& nc, int g, int j,
-                                                           float& nmax) {
-  auto h = [](float a, float b, float c, float d) {
-    const sb_h2 lo = __builtin_convertvector((sb_f2){a, b}, sb_h2);
-    const sb_h2 hi = __builtin_convertvector((sb_f2){c, d}, sb_h2);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
-  };
-  nmax = fmaxf(fmaxf(fabsf(nr.v[0]), fabsf(nr.v[1])), fmaxf(fabsf(nr.v[2]), fabsf(nr.v[3])));
-  auto hv = [&h](const f32x4& x) { return h(x[0], x[1], x[2], x[3]); };
-  auto mma = [](const sb_h4& a, const sb_h4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-  };
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  const sb_h4 hr = h(nr.v[0], nr.v[1], nr.v[2], nr.v[3]);
-  const sb_h4 hc = h(nc.v[0], nc.v[1], nc.v[2], nc.v[3]);
-  const sb_h4 n2c = hv(mma(hr, hc, z));    // accL(N^2)
-  const sb_h4 n2r = hv(mma(hc, hr, z));    // rowL(N^2)
-  const sb_h4 n4c = hv(mma(n2r, n2c, z));  // accL(N^4)
-  const sb_h4 n4r = hv(mma(n2c, n2r, z));  // rowL(N^4)
-  const sb_h4 n8c = hv(mma(n4r, n4c, z));  // accL(N^8)
-  // accL(T^T), T^T = (I + N^8)^T (I + N^4)^T (I + N^2)^T (I + N)^T, by left
-  // products C + X C starting from accL((I + N)^T) = rowL(I + N); C enters
-  // the accumulator in fp32 and only the product X C is rounded
-  f32x4 t;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) t[i] = nr.v[i] + ((4 * g + i == j) ? 1.f : 0.f);
-  t = mma(n2c, hv(t), t);
-  t = mma(n4c, hv(t), t);
-  t = mma(n8c, hv(t), t);
-  Frag4<float> r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = t[i];
-  return r;  // accL(T^T) = rowL(T)
-}
-
 // RAW: b, g and w are the raw gate projections (row strides p.ld_b, p.ld_g,
 // p.ld_w) and the kernel applies the activations where it reads them:
 // sigmoid for beta|b and w, the Mamba-2 log-decay for g.
