@@ -42,12 +42,18 @@
 // initial state -- U = (I + A)^{-1} (Z - (gs e) S), S' = Diag(gend) S +
 // (ge k)^T U, the state tiles in the column waves' MFMA accumulators -- and
 // stores the entry state of every block, the final state and every u_t in
-// the workspace.  Phase 2 walks the blocks backwards with the exit-state
+// the workspace, in the operand type (phase 2 reads them as MFMA operands;
+// only the row sum of D (.) S at the block end sees the rounded state).
+// Phase 2 walks the blocks backwards with the exit-state
 // gradient D held by every wave w as D^T tiles of rows 16w..16w+15 (bf16
 // operands: also as a bf16 copy in LDS for the column waves' (k ge) D) and
 // evaluates the block form above.  The per-row gradients (dq, dk, db, dg) are
-// partial over the column block; they go to the workspace and a second
-// kernel sums them over column blocks and over the value heads of a key head.
+// partial over the column block.  With channel gates, one value head per key
+// head and at most two column blocks, each block adds its part straight into
+// the outputs (cleared first): a sum of two addends is the same in either
+// order, so the result stays deterministic.  Otherwise the parts go to the
+// workspace and a second kernel sums them over column blocks and over the
+// value heads of a key head.
 // Only the first block walked in each phase can be short, so the others are
 // compiled without per-token guards.
 #include "chunk_common.hpp"
@@ -95,6 +101,20 @@ __device__ __forceinline__ void st4f(float* p, const float* v) {
 __device__ __forceinline__ void ld4f(const float* p, float* v) {
   const float4 x = *reinterpret_cast<const float4*>(p);
   v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+__device__ __forceinline__ void ld4f(const bf16* p, float* v) {
+  const uint2 x = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xffff0000u);
+  v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+
+// Adds one of exactly two addends into an fp32 output that starts at zero.
+// Subnormal addends are flushed first, so that 0 + x is x exactly; the result
+// is then the rounded sum of the two whichever lands first (and whatever the
+// atomic unit does with subnormals), so it is bitwise deterministic.
+__device__ __forceinline__ void add_pair(float* p, float x) {
+  x = fabsf(x) < 1.17549435e-38f ? 0.f : x;
+  unsafeAtomicAdd(p, x);
 }
 
 // N consecutive elements of T kept as loaded (converted when stored to LDS,
@@ -247,8 +267,7 @@ struct RevLoad {
   static constexpr int TPC = kCols / CPT;
   RawN<IO, 4> k, q;
   RawN<GT, 4> b, g;
-  RawN<IO, CPT> dO;
-  float u[CPT];
+  RawN<IO, CPT> dO, u;
   float sb, sg;
   bool rv, cv;
 
@@ -276,8 +295,7 @@ struct RevLoad {
       const int64_t t = cv ? tcc : Tn - 1;
       const int64_t off = ((tok0 + t) * p.Hv + hv) * p.dv + (int64_t)cb * kCols + j0;
       load_raw<IO, CPT>(static_cast<const IO*>(p.d_o) + off, dO);
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) u[j] = p.u[off + j];
+      load_raw<IO, CPT>(static_cast<const IO*>(p.u) + off, u);
     }
   }
 
@@ -314,14 +332,15 @@ struct RevLoad {
       L.sb[tr] = sb * mr;
       L.sgl[tr] = HAS_G ? sg * kLog2e * mr : 0.f;
     }
-    float y[CPT];
+    float y[CPT], yu[CPT];
     unpack_raw<IO, CPT>(dO, y);
+    unpack_raw<IO, CPT>(u, yu);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const T d = from_f32<T>(y[j] * mc);
       L.dOr[tc][j0 + j] = d;
       L.dOt[j0 + j][tc] = d;
-      L.Ur[tc][j0 + j] = from_f32<T>(u[j] * mc);
+      L.Ur[tc][j0 + j] = from_f32<T>(yu[j] * mc);
     }
   }
 };
@@ -394,7 +413,8 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   }
 
   // nblk checkpoints (state before each 16-token block) + the final state
-  float* ck = p.ckpt + (((int64_t)hv * ncb + cb) * p.slots + slot0) * (int64_t)DK * kCols;
+  // (in the operand type: phase 2 uses them as MFMA operands and in one row sum)
+  TO* ck = static_cast<TO*>(p.ckpt) + (((int64_t)hv * ncb + cb) * p.slots + slot0) * (int64_t)DK * kCols;
 
   const int g4 = lane >> 4, n = lane & 15;
   const bool colw = wave < 4;                // column waves own state tiles of columns 16 wave..
@@ -511,7 +531,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii)
-            ck[(m * DK + 16 * rb + 4 * g4 + ii) * kCols + 16 * ct + n] = Sc[rb][ii];
+            ck[(m * DK + 16 * rb + 4 * g4 + ii) * kCols + 16 * ct + n] = from_f32<TO>(Sc[rb][ii]);
         Frag4<float> nr, nc;   // rowL(N), accL(N), N = -A
         {
           f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aAt = aA;
@@ -583,7 +603,9 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int s = 4 * g4 + ii;
-          if (s < nt) p.u[((tok0 + t0 + s) * p.Hv + hv) * p.dv + colg + 16 * ct + n] = ut[ii];
+          if (s < nt)
+            static_cast<TO*>(p.u)[((tok0 + t0 + s) * p.Hv + hv) * p.dv + colg + 16 * ct + n] =
+                from_f32<TO>(ut[ii]);
         }
         const Frag4<TO> uf = frag4_from_acc<TO>(ut);
 #pragma unroll
@@ -603,7 +625,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          ck[(nblk * DK + 16 * rb + 4 * g4 + ii) * kCols + 16 * ct + n] = Sc[rb][ii];
+          ck[(nblk * DK + 16 * rb + 4 * g4 + ii) * kCols + 16 * ct + n] = from_f32<TO>(Sc[rb][ii]);
     }
   }
   // The u and the states written above are read back below through global
@@ -1058,16 +1080,39 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       const float t1 = __shfl(dG[0], n + 16), t2 = __shfl(dG[0], n + 32);
       const float t3 = __shfl(dG[0], n + 48);
       const float after = (g4 < 1 ? t1 : 0.f) + (g4 < 2 ? t2 : 0.f) + (g4 < 3 ? t3 : 0.f);
+      if (CHANNEL && p.direct) {
+        // (token, key head) rows are (token, value head) rows here; one
+        // column block stores, two add into outputs cleared beforehand
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int s = 4 * g4 + ii;
-        if (s < nt) {
-          const int64_t row = (tok0 + t0 + s) * p.Hv + hv;
-          float* pp = p.part + ((int64_t)cb * 4 * NR + row) * DK + ch;
-          pp[0] = dq[ii];
-          pp[NR * DK] = dk[ii];
-          pp[2 * NR * DK] = db[ii];
-          pp[3 * NR * DK] = dG[ii] + after;
+        for (int ii = 0; ii < 4; ++ii) {
+          const int s = 4 * g4 + ii;
+          if (s < nt) {
+            const int64_t o = ((tok0 + t0 + s) * p.Hv + hv) * DK + ch;
+            if (ncb == 1) {
+              p.dq_out[o] = dq[ii];
+              p.dk_out[o] = dk[ii];
+              p.db[o] = db[ii];
+              if (p.dg) p.dg[o] = dG[ii] + after;
+            } else {
+              add_pair(p.dq_out + o, dq[ii]);
+              add_pair(p.dk_out + o, dk[ii]);
+              add_pair(p.db + o, db[ii]);
+              if (p.dg) add_pair(p.dg + o, dG[ii] + after);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int s = 4 * g4 + ii;
+          if (s < nt) {
+            const int64_t row = (tok0 + t0 + s) * p.Hv + hv;
+            float* pp = p.part + ((int64_t)cb * 4 * NR + row) * DK + ch;
+            pp[0] = dq[ii];
+            pp[NR * DK] = dk[ii];
+            pp[2 * NR * DK] = db[ii];
+            pp[3 * NR * DK] = dG[ii] + after;
+          }
         }
       }
     }
@@ -1137,12 +1182,38 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs p) {
   }
 }
 
+// Clears up to four fp32 arrays of n4 float4 each (a null pointer is
+// skipped); a kernel rather than a memset, so that the call can be captured
+// into a graph.
+__global__ __launch_bounds__(256) void zero4_kernel(float* a, float* b, float* c, float* d,
+                                                    int64_t n4) {
+  float* const ptr[4] = {a, b, c, d};
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (!ptr[j]) continue;
+    float4* q = reinterpret_cast<float4*>(ptr[j]);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) q[i] = z;
+  }
+}
+
 template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.B * a.Hv), (unsigned)(a.dv / kCols));
+  const int ncb = a.dv / kCols;
+  hipError_t e;
+  if (a.direct && ncb == 2) {
+    const int64_t n4 = a.rows * a.Hv * DK / 4;
+    const int64_t want = (n4 + 255) / 256;
+    zero4_kernel<<<dim3((unsigned)(want < 16384 ? want : 16384)), 256, 0, stream>>>(
+        a.dq_out, a.dk_out, a.db, a.dg, n4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(a.B * a.Hv), (unsigned)ncb);
   bwd_kernel<DK, CHANNEL, HAS_G, IO, GT><<<grid, DK * 4, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  e = hipGetLastError();
+  if (e != hipSuccess || a.direct) return e;
   bwd_reduce_kernel<DK, CHANNEL><<<dim3((unsigned)a.rows), 256, 0, stream>>>(a);
   return hipGetLastError();
 }

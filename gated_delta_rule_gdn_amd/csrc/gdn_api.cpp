@@ -112,7 +112,8 @@ gdn_status check_pointers(int64_t rows, int64_t heads_state, int32_t Hk, int32_t
 namespace {
 
 struct BwdLayout {
-  int64_t nblk, slots, ckpt_floats, u_floats, part_floats;
+  int64_t nblk, slots, ckpt_elems, u_elems, part_floats;
+  bool direct;   // row gradients written straight to the outputs, no partials
   size_t ckpt_off, u_off, part_off, total;
 };
 
@@ -134,12 +135,15 @@ BwdLayout bwd_layout(const BwdShape& d) {
   L.nblk = d.cu ? 0 : gdn::bwd_checkpoint_blocks(d.T);
   // packed sequences: sequence n uses slots floor(start/16) + 2n onwards
   L.slots = d.cu ? d.rows / 16 + 2 * d.N + 2 : d.N * (L.nblk + 1);
-  L.ckpt_floats = (int64_t)d.Hv * L.slots * d.dk * d.dv;
-  L.u_floats = hrows * d.dv;
-  L.part_floats = ncb * 4 * hrows * d.dk + ncb * hrows;
+  // checkpoints and u are kept in the io type (the matrix-product operand type)
+  const size_t eb = d.io == GDN_BF16 ? 2 : 4;
+  L.ckpt_elems = (int64_t)d.Hv * L.slots * d.dk * d.dv;
+  L.u_elems = hrows * d.dv;
+  L.direct = d.mode == GDN_GATES_CHANNEL && d.Hv == d.Hk && ncb <= 2;
+  L.part_floats = L.direct ? 0 : ncb * 4 * hrows * d.dk + ncb * hrows;
   L.ckpt_off = 0;
-  L.u_off = align256((size_t)L.ckpt_floats * 4);
-  L.part_off = L.u_off + align256((size_t)L.u_floats * 4);
+  L.u_off = align256((size_t)L.ckpt_elems * eb);
+  L.part_off = L.u_off + align256((size_t)L.u_elems * eb);
   L.total = L.part_off + align256((size_t)L.part_floats * 4);
   return L;
 }
@@ -245,9 +249,10 @@ gdn_status run_backward(const BwdShape& d, const void* q, const void* k, const v
   a.q = q; a.k = k; a.v = v; a.b = beta_or_b; a.w = w; a.g = g; a.d_o = d_o;
   a.state_in = state_in; a.d_state_out = d_state_out;
   char* ws = static_cast<char*>(workspace);
-  a.ckpt = reinterpret_cast<float*>(ws + L.ckpt_off);
-  a.u = reinterpret_cast<float*>(ws + L.u_off);
+  a.ckpt = ws + L.ckpt_off;
+  a.u = ws + L.u_off;
   a.part = reinterpret_cast<float*>(ws + L.part_off);
+  a.direct = L.direct;
   a.nblk = L.nblk;
   a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.db = db; a.dw = dw; a.dg = dg;
   a.d_state_in = d_state_in;

@@ -95,7 +95,13 @@ struct BwdArgs {
   float scale;
   const void *q, *k, *v, *b, *w, *g, *d_o;
   const float *state_in, *d_state_out;
-  float *ckpt, *u, *part;
+  // checkpoint states and u in the MFMA operand type (io), partial row
+  // gradients in fp32; with `direct` the row gradients go straight to the
+  // outputs (channel gates, H_v == H_k, at most two column blocks) and
+  // `part` is unused
+  void *ckpt, *u;
+  float* part;
+  bool direct;
   int64_t nblk;
   float *dq_out, *dk_out, *dv_out, *db, *dw, *dg, *d_state_in;
 };

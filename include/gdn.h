@@ -241,10 +241,12 @@ typedef struct gdn_bwd_desc {
  * gdn_backward_workspace_size -- bytes of device workspace gdn_backward needs
  * for this descriptor (0 for an invalid descriptor or when there is no
  * token): the states every 16 tokens and the final state
- * (B H_v (ceil(T/16) + 1) d_k d_v fp32), the per-token vectors u
- * (B T H_v d_v fp32) and per-64-column partial row gradients
+ * (B H_v (ceil(T/16) + 1) d_k d_v elements of io_dtype), the per-token
+ * vectors u (B T H_v d_v elements of io_dtype) and, unless the gates are
+ * CHANNEL with H_v == H_k and d_v <= 128 (then the row gradients go straight
+ * to the outputs), per-64-column partial row gradients
  * (d_v/64 * B T H_v (4 d_k + 1) fp32), each rounded up to 256 bytes.
- * 4.6 GB at B 8, T 4096, H_v 16, d_k = d_v = 128.
+ * 1.35 GB at B 8, T 4096, H 16, d_k = d_v = 128, bf16, channel gates.
  */
 size_t gdn_backward_workspace_size(const gdn_bwd_desc* desc);
 
@@ -257,7 +259,7 @@ size_t gdn_backward_workspace_size(const gdn_bwd_desc* desc);
  * that update, run in reverse over blocks of 16 tokens (the block form is
  * written out in backward.hip).  The kernels recompute the forward states
  * from checkpoints kept in the workspace: states and accumulation in fp32,
- * matrix-product operands in io_dtype.
+ * matrix-product operands and stored checkpoints in io_dtype.
  *
  *   q, k, v, beta_or_b, w, g, state_in   as for gdn_chunk_fwd (inputs)
  *   d_o          [B, T, H_v, d_v]  io_dtype
@@ -292,8 +294,8 @@ gdn_status gdn_backward(const gdn_bwd_desc* desc, const void* q, const void* k, 
  * gdn_backward_noalloc_max_bytes() bytes (64 MiB) on each GPU it runs on,
  * held until the process ends; the call allocates nothing.  A descriptor
  * whose gdn_backward_workspace_size exceeds that returns GDN_ERR_UNSUPPORTED
- * (for example B 1, T 384, H_v 16, d_k = d_v = 128 fits; the B 8, T 4096
- * training shape does not).  All calls on one GPU share its array: calls that
+ * (for example B 1, T 1792, H 16, d_k = d_v = 128 with bf16 inputs and
+ * channel gates fits; the B 8, T 4096 training shape does not).  All calls on one GPU share its array: calls that
  * overlap on one GPU (other streams or host threads) race, and must be
  * serialised by the caller.
  */

@@ -438,13 +438,23 @@ def _bwd(desc, ws_bytes=None, **ptrs):
 
 
 def test_backward_workspace_size_formula():
+    r = lambda x: (x + 255) // 256 * 256
+    # channel gates, one value head per key head: bf16 checkpoints and u, no partials
     d = _bwd_desc(B=8, T=4096, H_k=16, H_v=16)
     got = gdn.lib.gdn_backward_workspace_size(ctypes.byref(d))
-    ck = 8 * 16 * 257 * 128 * 128 * 4
-    u = 8 * 4096 * 16 * 128 * 4
+    ck = 8 * 16 * 257 * 128 * 128 * 2
+    u = 8 * 4096 * 16 * 128 * 2
+    assert got == r(ck) + r(u)
+    assert got < 1.5e9
+    # grouped heads (or scalar gates, or fp32): partial row gradients too
+    part = (2 * 4 * 8 * 4096 * 32 * 128 + 2 * 8 * 4096 * 32) * 4
+    d = _bwd_desc(B=8, T=4096, H_k=16, H_v=32)
+    ck2, u2 = 2 * ck, 2 * u
+    assert gdn.lib.gdn_backward_workspace_size(ctypes.byref(d)) == r(ck2) + r(u2) + r(part)
+    d = _bwd_desc(B=8, T=4096, H_k=16, H_v=16, io_dtype=gdn.GDN_F32, gate_dtype=gdn.GDN_F32,
+                  gate_mode=gdn.GDN_GATES_SCALAR)
     part = (2 * 4 * 8 * 4096 * 16 * 128 + 2 * 8 * 4096 * 16) * 4
-    r = lambda x: (x + 255) // 256 * 256
-    assert got == r(ck) + r(u) + r(part)
+    assert gdn.lib.gdn_backward_workspace_size(ctypes.byref(d)) == r(2 * ck) + r(2 * u) + r(part)
     assert gdn.lib.gdn_backward_workspace_size(ctypes.byref(_bwd_desc(T=0))) == 0
     assert gdn.lib.gdn_backward_workspace_size(ctypes.byref(_bwd_desc(H_v=3))) == 0
     assert gdn.lib.gdn_backward_workspace_size(None) == 0
@@ -515,8 +525,8 @@ def test_backward_varlen_validation():
                              gate_mode=gdn.GDN_GATES_CHANNEL, scale=1.0)
     n = gdn.lib.gdn_backward_varlen_workspace_size(ctypes.byref(d))
     r = lambda x: (x + 255) // 256 * 256
-    ck = 4 * (100 // 16 + 2 * 3 + 2) * 128 * 128 * 4
-    u = 100 * 4 * 128 * 4
+    ck = 4 * (100 // 16 + 2 * 3 + 2) * 128 * 128 * 2
+    u = 100 * 4 * 128 * 2
     part = (2 * 4 * 100 * 4 * 128 + 2 * 100 * 4) * 4
     assert n == r(ck) + r(u) + r(part)
     names = ["q", "k", "v", "b", "w", "g", "s_in", "d_o", "d_sT", "ws", "dq", "dk", "dv", "db",

@@ -56,7 +56,7 @@ def test_noalloc_matches_backward_on_two_calls(channel, io):
 
 def test_noalloc_rejects_a_workspace_beyond_its_array():
     cap = gdn.gdn_backward_noalloc_max_bytes()
-    B, T, H, d = 1, 512, 16, 128
+    B, T, H, d = 1, 2048, 16, 128
     assert gdn.gdn_backward_workspace_size(torch.empty(B, T, H, d), torch.empty(B, T, H, d),
                                            torch.empty(B, T, H, d), w=torch.empty(B, T, H, d)) > cap
     inp, d_o, d_sT = _inputs(B, T, H, d, True, torch.bfloat16, seed=5)
