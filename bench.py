@@ -65,11 +65,14 @@ def decode_algorithmic(cfg, io_bytes=2, gate_bytes=2):
 # while these files are unchanged.
 KERNEL_SOURCES = {
     "chunk_fwd": ("chunk_fwd_sb.hip", "chunk_fwd.hip", "chunk_common.hpp", "gdn_device.hpp"),
+    "chunk_fwd_save": ("chunk_fwd_sb.hip", "chunk_common.hpp", "gdn_device.hpp"),
     "decode_step": ("decode.hip", "gdn_device.hpp"),
     "short_conv": ("layer_ops.hip", "gdn_device.hpp"),
     "gates": ("layer_ops.hip", "gdn_device.hpp"),
     "output_gate": ("layer_ops.hip", "gdn_device.hpp"),
     "backward": ("backward.hip", "chunk_common.hpp", "gdn_device.hpp"),
+    "backward_saved": ("backward.hip", "chunk_common.hpp", "gdn_device.hpp"),
+    "backward_fill": ("backward.hip",),
     "backward_reduce": ("backward.hip", "chunk_common.hpp", "gdn_device.hpp"),
 }
 
@@ -503,6 +506,36 @@ def backward_workload(gdn, synth, torch, dev, steps=5, warmup=2):
                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                         "flops_per_launch": flops,
                         "traffic": measured_traffic("backward", None)}}
+    # The training pair on the same inputs: gdn_chunk_fwd then gdn_backward
+    # (which rebuilds the forward's states first), against gdn_chunk_fwd_save
+    # (which leaves them in the workspace) then gdn_backward_saved.
+    o = torch.empty_like(inp["v"])
+    s_out = torch.empty((cfg.B, cfg.Hv, cfg.dk, cfg.dv), device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    fwd_ms = timed(lambda: gdn.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta_or_b"],
+                                             w=inp["w"], g=inp["g"], state_out=s_out, o=o))
+    save_ms = timed(lambda: gdn.gdn_chunk_fwd_save(inp["q"], inp["k"], inp["v"], inp["beta_or_b"],
+                                                   w=inp["w"], g=inp["g"], state_out=s_out, o=o,
+                                                   workspace=ws))
+    saved_ms = timed(lambda: gdn.gdn_backward_saved(inp["q"], inp["k"], inp["v"], inp["beta_or_b"],
+                                                    d_o, ws, w=inp["w"], g=inp["g"], grads=grads))
+    res["saved_states"] = {
+        "forward_ms": round(fwd_ms, 3), "forward_save_ms": round(save_ms, 3),
+        "backward_saved_ms": round(saved_ms, 3),
+        "forward_plus_backward_ms": round(fwd_ms + ms, 3),
+        "forward_save_plus_backward_saved_ms": round(save_ms + saved_ms, 3)}
+    del o, s_out
     # the same shape on gates from gdn_gates over the Mamba-2 recipe: the
     # channels whose decay range in a block exceeds the factored form's are
     # taken term by term
@@ -564,17 +597,33 @@ def cpu_baseline(args):
 
 
 KERNEL_KEYS = {"chunk_fwd": ("chunk_fwd_sb_kernel", "chunk_fwd_kernel"),
+               "chunk_fwd_save": (),
                "decode_step": ("decode_kernel",),
                "short_conv": ("short_conv_kernel",),
                "gates": ("gates_kernel", "gates_vec_kernel"),
                "output_gate": ("output_gate_kernel",),
                "backward": ("bwd_kernel",),
+               "backward_saved": (),
+               "backward_fill": ("zero4_kernel",),
                "backward_reduce": ("bwd_reduce_kernel",)}
+
+
+def _last_template_arg_true(name, params):
+    """Whether a kernel's last template argument (a bool) is true, in the
+    mangled (...Lb1EEEv<params>) or the demangled (..., true>(<params>)) name."""
+    return ("Lb1EEEv" + params[0]) in name or name.endswith("true>(" + params[1] + ")")
 
 
 def _kernel_key(name):
     for key, pats in KERNEL_KEYS.items():
         if any(p in name for p in pats):
+            # the variants that store (forward) or read (backward) the saved
+            # states carry a last template argument of true
+            if key == "chunk_fwd" and "chunk_fwd_sb_kernel" in name and _last_template_arg_true(
+                    name, ("NS0_6ParamsE", "gdn::(anonymous namespace)::Params")):
+                return "chunk_fwd_save"
+            if key == "backward" and _last_template_arg_true(name, ("NS_7BwdArgsE", "gdn::BwdArgs")):
+                return "backward_saved"
             return key
     return None
 

@@ -366,7 +366,9 @@ __device__ __forceinline__ float token_decay(const Lds& L, int s, int t) {
   return exp2_fast(L.Gl[0][s] - L.Gl[0][t]);
 }
 
-template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT>
+// REV_ONLY: the checkpoints and u are in the workspace already (written by
+// the chunk forward); only phase 2 runs.  Otherwise p.phases selects.
+template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT, bool REV_ONLY>
 __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   constexpr int RB = DK / 16;               // 16-row blocks of the state
   using TO = IO;                            // MFMA operand type
@@ -412,8 +414,9 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     return;
   }
 
-  // nblk checkpoints (state before each 16-token block) + the final state
-  // (in the operand type: phase 2 uses them as MFMA operands and in one row sum)
+  // nblk checkpoints (state before each 16-token block) + the final state,
+  // each stored [column][channel] (kCols rows of DK), in the operand type
+  // (phase 2 uses them as MFMA operands and in one row sum)
   TO* ck = static_cast<TO*>(p.ckpt) + (((int64_t)hv * ncb + cb) * p.slots + slot0) * (int64_t)DK * kCols;
 
   const int g4 = lane >> 4, n = lane & 15;
@@ -438,7 +441,8 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   // Column wave ct holds the state's columns 16 ct.. over all rows as accL
   // tiles Sc[rb] (S[16rb + 4 g4 + ii][16 ct + n]) and per block solves
   // U = (I + A)^{-1} (Z - (gs e) S) and updates S' = Diag(gend) S + (ge k)^T U.
-  {
+  // (Skipped when the forward kernel has stored the checkpoints and u.)
+  if (!REV_ONLY && (p.phases & 1)) {
     FwdLds<DK, TO>& F = sm.fwd;
     f32x4 Sc[RB];
 #pragma unroll
@@ -529,9 +533,8 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
         // the block's entry state
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii)
-            ck[(m * DK + 16 * rb + 4 * g4 + ii) * kCols + 16 * ct + n] = from_f32<TO>(Sc[rb][ii]);
+          st4<TO>(ck + (m * kCols + 16 * ct + n) * DK + 16 * rb + 4 * g4, Sc[rb][0], Sc[rb][1],
+                  Sc[rb][2], Sc[rb][3]);
         Frag4<float> nr, nc;   // rowL(N), accL(N), N = -A
         {
           f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aAt = aA;
@@ -623,11 +626,11 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     if (colw) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          ck[(nblk * DK + 16 * rb + 4 * g4 + ii) * kCols + 16 * ct + n] = from_f32<TO>(Sc[rb][ii]);
+        st4<TO>(ck + (nblk * kCols + 16 * ct + n) * DK + 16 * rb + 4 * g4, Sc[rb][0], Sc[rb][1],
+                Sc[rb][2], Sc[rb][3]);
     }
   }
+  if (!REV_ONLY && !(p.phases & 2)) return;
   // The u and the states written above are read back below through global
   // memory by other threads of this workgroup: make them visible.
   __threadfence_block();
@@ -643,6 +646,10 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
   constexpr bool DL = RevLds<DK, TO>::kDl;
   f32x4 Dt[4], Dc[DL ? 1 : RB];
   float Sf[4][4];                            // S[ch][16c + 4 g4 + ii]: the block's entry state
+  auto ld_ck = [&](int64_t blk, int c, float* x) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) x[ii] = to_f32(ck[(blk * kCols + 16 * c + 4 * g4 + ii) * DK + ch]);
+  };
   {
     const float* dso = p.d_state_out ? p.d_state_out + head * (int64_t)DK * p.dv + colg : nullptr;
 #pragma unroll
@@ -651,7 +658,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
       if (dso) ld4f(dso + (int64_t)ch * p.dv + 16 * c + 4 * g4, x);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) Dt[c][ii] = x[ii];
-      ld4f(ck + ((nblk - 1) * DK + ch) * kCols + 16 * c + 4 * g4, Sf[c]);
+      ld_ck(nblk - 1, c, Sf[c]);
     }
     if constexpr (!DL) {
 #pragma unroll
@@ -881,7 +888,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     for (int c = 0; c < 4; ++c) sfr[c] = frag4_of<TO>(Sf[c]);   // accL(S^T) tile
 #pragma unroll
     for (int c = 0; c < 4; ++c)   // the next block's entry state
-      ld4f(ck + (mp * DK + ch) * kCols + 16 * c + 4 * g4, Sf[c]);
+      ld_ck(mp, c, Sf[c]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       ua[c] = ld_frag4<TO>(&L.Ur[n][16 * c + 4 * g4]);     // rowL(U)
@@ -1202,7 +1209,7 @@ template <int DK, bool CHANNEL, bool HAS_G, typename IO, typename GT>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int ncb = a.dv / kCols;
   hipError_t e;
-  if (a.direct && ncb == 2) {
+  if (a.direct && ncb == 2 && (a.phases & 2)) {
     const int64_t n4 = a.rows * a.Hv * DK / 4;
     const int64_t want = (n4 + 255) / 256;
     zero4_kernel<<<dim3((unsigned)(want < 16384 ? want : 16384)), 256, 0, stream>>>(
@@ -1211,9 +1218,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)(a.B * a.Hv), (unsigned)ncb);
-  bwd_kernel<DK, CHANNEL, HAS_G, IO, GT><<<grid, DK * 4, 0, stream>>>(a);
+  if (a.phases == 2) bwd_kernel<DK, CHANNEL, HAS_G, IO, GT, true><<<grid, DK * 4, 0, stream>>>(a);
+  else bwd_kernel<DK, CHANNEL, HAS_G, IO, GT, false><<<grid, DK * 4, 0, stream>>>(a);
   e = hipGetLastError();
-  if (e != hipSuccess || a.direct) return e;
+  if (e != hipSuccess || a.direct || !(a.phases & 2)) return e;
   bwd_reduce_kernel<DK, CHANNEL><<<dim3((unsigned)a.rows), 256, 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -262,6 +262,13 @@ struct Params {
   int64_t ld_b = 0, ld_g = 0, ld_w = 0;
   const float* A_log = nullptr;
   const float* dt_bias = nullptr;
+  // Optional (nullptr: not written): the state entering every 16-token block
+  // and every u, bf16, in the layouts the backward's reverse walk reads (see
+  // backward.hip); ck_slots and ck_nblk are its slot count and blocks per
+  // sequence.
+  bf16* ck = nullptr;
+  bf16* u = nullptr;
+  int64_t ck_slots = 0, ck_nblk = 0;
 };
 
 }  // namespace

@@ -205,7 +205,8 @@ __device__ __forceinline__ Frag4<bf16> ld_tr16(const bf16* p) {
 // RAW: b, g and w are the raw gate projections (row strides p.ld_b, p.ld_g,
 // p.ld_w) and the kernel applies the activations where it reads them:
 // sigmoid for beta|b and w, the Mamba-2 log-decay for g.
-template <typename GT, int DK, int DV, bool CHANNEL, bool HAS_G, bool RAW>
+// SAVE: also store each 16-token block's entry state and every u (p.ck, p.u).
+template <typename GT, int DK, int DV, bool CHANNEL, bool HAS_G, bool RAW, bool SAVE>
 __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   using T = bf16;
   using L = SbLds<DK, CHANNEL>;
@@ -760,6 +761,20 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         S[t][i] = sin ? sin[row * DV + col] : 0.f;
       }
   }
+  // Saved for the backward (when asked): block m's entry state as the
+  // [column][channel] row of this lane's column (16-byte pieces of 8
+  // channels), and u of every token.
+  T* ckb = nullptr;
+  if constexpr (SAVE) {
+    const int64_t slot0 = p.cu ? tok0 / kSB + 2 * bidx : bidx * (p.ck_nblk + 1);
+    ckb = p.ck + (((int64_t)hv * NSPLIT + split) * p.ck_slots + slot0) * (int64_t)DK * DVS +
+          (int64_t)(16 * wave + j) * DK + 8 * g;
+  }
+  auto save_state = [&](int64_t tb, const Frag8<T>* sf) {
+    T* dst = ckb + (tb / kSB) * (int64_t)DVS * DK;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<Frag8<T>*>(dst + 32 * kb) = sf[kb];
+  };
   const uint32_t w_tok = RAW ? (uint32_t)(p.ld_w * (int64_t)sizeof(GT))
                              : (uint32_t)(p.Hv * DV * (int)sizeof(GT));
   // v (and w) of the 16 tokens 16 sb + 4 g + i of a chunk for this column,
@@ -855,6 +870,12 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   // Exact token-by-token recurrence for tokens [tb, min(tb + 16, Tn)) of the
   // chunk in the given slot that starts at token cb.
   auto tokens_path = [&](int slot, int64_t cb, int64_t tb) {
+    if constexpr (SAVE) {
+      Frag8<T> sf[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sf[kb] = frag8_from_acc<T>(S[2 * kb], S[2 * kb + 1]);
+      save_state(tb, sf);
+    }
     for (int tl = 0; tl < kSB; ++tl) {
       const int64_t tok = tb + tl;
       if (tok >= Tn) break;
@@ -935,6 +956,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       }
       else z *= sbeta;
       const float d = z - rp;
+      if (SAVE && g == 0) p.u[gt * DV + col] = from_f32<T>(d);
       float op = 0.f;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
@@ -1009,6 +1031,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
     Frag8<T> sf[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sf[kb] = frag8_from_acc<T>(S[2 * kb], S[2 * kb + 1]);
+    if constexpr (SAVE) save_state(tb, sf);
     f32x4 X, O = {0.f, 0.f, 0.f, 0.f};
     float zz[4], ww[4];
     const bool full_sb = tb + kSB <= Tn;  // wave-uniform
@@ -1075,6 +1098,13 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
     f32x4 U = {0.f, 0.f, 0.f, 0.f};
     mma16(U, td, xf);  // U[4g+i][j]
     const Frag4<T> uo = frag4_from_acc<T>(U);
+    if constexpr (SAVE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = tb + 4 * g + i;
+        if (full_sb || t < Tn) p.u[((tok0 + t) * p.Hv + hv) * (int64_t)DV + col] = uo.v[i];
+      }
+    }
     Frag4<T> uk = uo;
     if constexpr (!CHANNEL) {
       f32x4 us = {U[0] * fk[0], U[1] * fk[1], U[2] * fk[2], U[3] * fk[3]};
@@ -1167,13 +1197,26 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
 
 template <typename GT, int DK, int DV, bool CH, bool HG, bool RAW = false>
 hipError_t launch_sb_typed(const ChunkArgs& a, hipStream_t stream) {
+  const bool save = a.ck != nullptr;
   Params p;
   p.B = a.B; p.T = a.T; p.cu = a.cu_seqlens; p.Hk = a.Hk; p.Hv = a.Hv; p.scale = a.scale;
   p.q = a.q; p.k = a.k; p.v = a.v; p.b = a.b; p.w = a.w; p.g = a.g;
   p.state_in = a.state_in; p.state_out = a.state_out; p.o = a.o;
   p.ld_b = a.ld_b; p.ld_g = a.ld_g; p.ld_w = a.ld_w; p.A_log = a.A_log; p.dt_bias = a.dt_bias;
+  p.ck = static_cast<bf16*>(a.ck); p.u = static_cast<bf16*>(a.u);
+  p.ck_slots = a.ck_slots; p.ck_nblk = a.ck_nblk;
   const int64_t nwg = a.B * a.Hv * (DV / 64);
-  chunk_fwd_sb_kernel<GT, DK, DV, CH, HG, RAW><<<dim3((unsigned)nwg), dim3(kSbThreads), 0, stream>>>(p);
+  if constexpr (RAW) {
+    if (save) return hipErrorNotSupported;
+    chunk_fwd_sb_kernel<GT, DK, DV, CH, HG, true, false>
+        <<<dim3((unsigned)nwg), dim3(kSbThreads), 0, stream>>>(p);
+  } else if (save) {
+    chunk_fwd_sb_kernel<GT, DK, DV, CH, HG, false, true>
+        <<<dim3((unsigned)nwg), dim3(kSbThreads), 0, stream>>>(p);
+  } else {
+    chunk_fwd_sb_kernel<GT, DK, DV, CH, HG, false, false>
+        <<<dim3((unsigned)nwg), dim3(kSbThreads), 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -181,7 +181,7 @@ gdn_status run_backward(const BwdShape& d, const void* q, const void* k, const v
                         const float* state_in, const void* d_o, const float* d_state_out,
                         void* workspace, size_t workspace_bytes, float* dq, float* dk,
                         float* dv, float* db, float* dw, float* dg, float* d_state_in,
-                        void* stream) {
+                        void* stream, int phases = 3) {
   gdn_status st = check_bwd_shape(d);
   if (st != GDN_OK) return st;
   if (d.N == 0) return GDN_OK;
@@ -256,8 +256,25 @@ gdn_status run_backward(const BwdShape& d, const void* q, const void* k, const v
   a.nblk = L.nblk;
   a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.db = db; a.dw = dw; a.dg = dg;
   a.d_state_in = d_state_in;
+  a.phases = phases;
   hipError_t e = gdn::launch_backward(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// Checks of gdn_chunk_fwd's descriptor that come before any pointer is read.
+gdn_status check_fwd_desc(const gdn_fwd_desc* d) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  if (d->B < 0 || d->T < 0) return GDN_ERR_INVALID_ARG;
+  gdn_status st = check_common(d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
+                               d->gate_mode, d->scale);
+  if (st != GDN_OK) return st;
+  if (d->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  // Guard index arithmetic: every element count must fit comfortably in int64.
+  const double elems = (double)d->B * (double)d->T * (double)d->H_v * (double)(d->d_k + d->d_v);
+  if (elems > 9.0e15) return GDN_ERR_INVALID_ARG;
+  if ((double)d->T > 2.0e9) return GDN_ERR_UNSUPPORTED;
+  if ((double)d->B * (double)d->H_v * 2.0 > 2.0e9) return GDN_ERR_UNSUPPORTED;  // grid size
+  return GDN_OK;
 }
 
 }  // namespace
@@ -279,17 +296,8 @@ const char* gdn_status_string(gdn_status s) {
 gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
                          const void* beta_or_b, const void* w, const void* g,
                          const float* state_in, float* state_out, void* o, void* stream) {
-  if (!d) return GDN_ERR_INVALID_ARG;
-  if (d->B < 0 || d->T < 0) return GDN_ERR_INVALID_ARG;
-  gdn_status st = check_common(d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
-                               d->gate_mode, d->scale);
+  gdn_status st = check_fwd_desc(d);
   if (st != GDN_OK) return st;
-  if (d->chunk != 64) return GDN_ERR_UNSUPPORTED;
-  // Guard index arithmetic: every element count must fit comfortably in int64.
-  const double elems = (double)d->B * (double)d->T * (double)d->H_v * (double)(d->d_k + d->d_v);
-  if (elems > 9.0e15) return GDN_ERR_INVALID_ARG;
-  if ((double)d->T > 2.0e9) return GDN_ERR_UNSUPPORTED;
-  if ((double)d->B * (double)d->H_v * 2.0 > 2.0e9) return GDN_ERR_UNSUPPORTED;  // grid size
   if (d->B == 0) return GDN_OK;  // nothing to read or write
   const int64_t rows = d->B * d->T;
   const int64_t heads = d->B * d->H_v;
@@ -319,6 +327,72 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
   a.state_in = state_in; a.state_out = state_out; a.o = o;
   hipError_t e = gdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn_status gdn_chunk_fwd_save(const gdn_fwd_desc* d, const void* q, const void* k,
+                              const void* v, const void* beta_or_b, const void* w, const void* g,
+                              const float* state_in, float* state_out, void* o, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  gdn_status st = check_fwd_desc(d);
+  if (st != GDN_OK) return st;
+  if (d->B == 0 || d->T == 0)   // nothing for a backward to read
+    return gdn_chunk_fwd(d, q, k, v, beta_or_b, w, g, state_in, state_out, o, stream);
+  const BwdShape bs{d->B, d->B * d->T, d->T, nullptr, d->H_k, d->H_v, d->d_k, d->d_v,
+                    d->io_dtype, d->gate_dtype, d->gate_mode, d->scale};
+  st = check_bwd_shape(bs);
+  if (st != GDN_OK) return st;
+  const BwdLayout L = bwd_layout(bs);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < L.total) return GDN_ERR_INVALID_ARG;
+  const int64_t rows = d->B * d->T, heads = d->B * d->H_v;
+  st = check_pointers(rows, heads, d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
+                      d->gate_mode, q, k, v, beta_or_b, w, g, state_in, state_out, o, false);
+  if (st != GDN_OK) return st;
+  // the workspace is written: it overlaps no tensor of the call
+  const int64_t ib = dtype_bytes(d->io_dtype), gb = dtype_bytes(d->gate_dtype);
+  const int64_t gcols = d->gate_mode == GDN_GATES_CHANNEL ? d->d_k : 1;
+  const int64_t S = heads * d->d_k * d->d_v;
+  const Span sws = span(workspace, (int64_t)L.total, 1);
+  const Span all[] = {span(q, rows * d->H_k * d->d_k, ib), span(k, rows * d->H_k * d->d_k, ib),
+                      span(v, rows * d->H_v * d->d_v, ib), span(beta_or_b, rows * d->H_v * gcols, gb),
+                      span(w, rows * d->H_v * d->d_v, gb), span(g, rows * d->H_v * gcols, gb),
+                      span(state_in, S, 4), span(state_out, S, 4),
+                      span(o, rows * d->H_v * d->d_v, ib)};
+  for (const Span& x : all)
+    if (overlaps(sws, x)) return GDN_ERR_INVALID_ARG;
+
+  gdn::ChunkArgs a;
+  a.B = d->B; a.T = d->T; a.Hk = d->H_k; a.Hv = d->H_v; a.dk = d->d_k; a.dv = d->d_v;
+  a.io = to_dtype(d->io_dtype); a.gate = to_dtype(d->gate_dtype);
+  a.channel = d->gate_mode == GDN_GATES_CHANNEL; a.scale = d->scale;
+  a.q = q; a.k = k; a.v = v; a.b = beta_or_b; a.w = w; a.g = g;
+  a.state_in = state_in; a.state_out = state_out; a.o = o;
+  char* ws = static_cast<char*>(workspace);
+  const bool in_kernel = d->io_dtype == GDN_BF16;   // the bf16 kernel stores them itself
+  if (in_kernel) {
+    a.ck = ws + L.ckpt_off;
+    a.u = ws + L.u_off;
+    a.ck_slots = L.slots;
+    a.ck_nblk = L.nblk;
+  }
+  hipError_t e = gdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  if (in_kernel) return GDN_OK;
+  // other kernels: the backward's own forward rebuild fills the workspace
+  gdn::BwdArgs b;
+  b.B = d->B; b.T = d->T; b.cu = nullptr; b.rows = rows; b.slots = L.slots;
+  b.Hk = d->H_k; b.Hv = d->H_v; b.dk = d->d_k; b.dv = d->d_v;
+  b.io = a.io; b.gate = a.gate; b.channel = a.channel; b.scale = d->scale;
+  b.q = q; b.k = k; b.v = v; b.b = beta_or_b; b.w = w; b.g = g; b.d_o = nullptr;
+  b.state_in = state_in; b.d_state_out = nullptr;
+  b.ckpt = ws + L.ckpt_off; b.u = ws + L.u_off;
+  b.part = reinterpret_cast<float*>(ws + L.part_off);
+  b.direct = L.direct;
+  b.phases = 1;
+  b.nblk = L.nblk;
+  b.dq_out = b.dk_out = b.dv_out = b.db = b.dw = b.dg = b.d_state_in = nullptr;
+  e = gdn::launch_backward(b, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
@@ -468,6 +542,18 @@ gdn_status gdn_backward(const gdn_bwd_desc* d, const void* q, const void* k, con
   if (!d) return GDN_ERR_INVALID_ARG;
   return run_backward(shape_of(d), q, k, v, beta_or_b, w, g, state_in, d_o, d_state_out,
                       workspace, workspace_bytes, dq, dk, dv, db, dw, dg, d_state_in, stream);
+}
+
+gdn_status gdn_backward_saved(const gdn_bwd_desc* d, const void* q, const void* k, const void* v,
+                              const void* beta_or_b, const void* w, const void* g,
+                              const float* state_in, const void* d_o, const float* d_state_out,
+                              void* workspace, size_t workspace_bytes, float* dq, float* dk,
+                              float* dv, float* db, float* dw, float* dg, float* d_state_in,
+                              void* stream) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  return run_backward(shape_of(d), q, k, v, beta_or_b, w, g, state_in, d_o, d_state_out,
+                      workspace, workspace_bytes, dq, dk, dv, db, dw, dg, d_state_in, stream,
+                      /*phases=*/2);
 }
 
 size_t gdn_backward_varlen_workspace_size(const gdn_bwd_varlen_desc* d) {

@@ -38,6 +38,11 @@ struct ChunkArgs {
   int64_t ld_b = 0, ld_g = 0, ld_w = 0;
   const float* A_log = nullptr;
   const float* dt_bias = nullptr;
+  // optional: what the backward's forward rebuild stores (BwdArgs ckpt and u,
+  // bf16, in the backward's layout; ck_slots and ck_nblk as there)
+  void* ck = nullptr;
+  void* u = nullptr;
+  int64_t ck_slots = 0, ck_nblk = 0;
 };
 
 // Short causal convolution of the q, k, v branch (+ SiLU, L2 norm of q, k).
@@ -102,6 +107,7 @@ struct BwdArgs {
   void *ckpt, *u;
   float* part;
   bool direct;
+  int phases = 3;                     // 1: forward rebuild only, 2: reverse walk only
   int64_t nblk;
   float *dq_out, *dk_out, *dv_out, *db, *dw, *dg, *d_state_in;
 };

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_SCALAR, GDN_GATES_CHANNEL = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class GdnFwdDesc(ctypes.Structure):
@@ -119,6 +119,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn_backward.argtypes = [ctypes.POINTER(GdnBwdDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  vp, ctypes.c_size_t, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_backward.restype = ctypes.c_int
+    lib.gdn_backward_saved.argtypes = lib.gdn_backward.argtypes
+    lib.gdn_backward_saved.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_save.argtypes = [ctypes.POINTER(GdnFwdDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                       vp, vp, ctypes.c_size_t, vp]
+    lib.gdn_chunk_fwd_save.restype = ctypes.c_int
     lib.gdn_backward_noalloc.argtypes = [ctypes.POINTER(GdnBwdDesc), vp, vp, vp, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_backward_noalloc.restype = ctypes.c_int
@@ -184,15 +189,7 @@ def _check(t, name, shape=None, dtype=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def gdn_chunk_fwd(q, k, v, beta_or_b, w=None, g=None, state_in=None, state_out=None, o=None,
-                  scale: float = 1.0, chunk: int = 64, stream=None):
-    """Chunkwise forward (see include/gdn.h).  Returns (o, state_out).
-
-    q, k [B,T,Hk,dk]; v [B,T,Hv,dv]; beta_or_b [B,T,Hv] (scalar gates) or
-    [B,T,Hv,dk] (channel gates, then w [B,T,Hv,dv] is required); g like
-    beta_or_b or None; state_in/state_out [B,Hv,dk,dv] fp32 or None.  o is
-    allocated when not given.
-    """
+def _fwd_desc(q, k, v, beta_or_b, w, g, state_in, state_out, o, scale, chunk):
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     io = q.dtype
@@ -216,12 +213,49 @@ def gdn_chunk_fwd(q, k, v, beta_or_b, w=None, g=None, state_in=None, state_out=N
         raise ValueError("gates must be float32 or bfloat16")
     desc = GdnFwdDesc(B, T, Hk, Hv, dk, dv, _DT[io], _DT[gdt],
                       GDN_GATES_CHANNEL if channel else GDN_GATES_SCALAR, chunk, float(scale))
+    return desc, o
+
+
+def gdn_chunk_fwd(q, k, v, beta_or_b, w=None, g=None, state_in=None, state_out=None, o=None,
+                  scale: float = 1.0, chunk: int = 64, stream=None):
+    """Chunkwise forward (see include/gdn.h).  Returns (o, state_out).
+
+    q, k [B,T,Hk,dk]; v [B,T,Hv,dv]; beta_or_b [B,T,Hv] (scalar gates) or
+    [B,T,Hv,dk] (channel gates, then w [B,T,Hv,dv] is required); g like
+    beta_or_b or None; state_in/state_out [B,Hv,dk,dv] fp32 or None.  o is
+    allocated when not given.
+    """
+    desc, o = _fwd_desc(q, k, v, beta_or_b, w, g, state_in, state_out, o, scale, chunk)
     st = lib.gdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b),
                            _ptr(w), _ptr(g), _ptr(state_in), _ptr(state_out), _ptr(o),
                            _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_fwd")
     return o, state_out
+
+
+def _workspace(workspace, need, device):
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def gdn_chunk_fwd_save(q, k, v, beta_or_b, w=None, g=None, state_in=None, state_out=None,
+                       o=None, scale: float = 1.0, chunk: int = 64, workspace=None, stream=None):
+    """gdn_chunk_fwd that also fills a backward workspace for gdn_backward_saved
+    (see include/gdn.h).  Returns (o, state_out, workspace); the workspace is
+    allocated (gdn_backward_workspace_size bytes) when not given."""
+    desc, o = _fwd_desc(q, k, v, beta_or_b, w, g, state_in, state_out, o, scale, chunk)
+    need = gdn_backward_workspace_size(q, v, beta_or_b, w, scale)
+    workspace, nbytes = _workspace(workspace, need, q.device)
+    st = lib.gdn_chunk_fwd_save(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b),
+                                _ptr(w), _ptr(g), _ptr(state_in), _ptr(state_out), _ptr(o),
+                                _ptr(workspace), ctypes.c_size_t(nbytes), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_fwd_save")
+    return o, state_out, workspace
 
 
 def gdn_chunk_fwd_gated(q, k, v, b_raw, a_raw=None, w_raw=None, A_log=None, dt_bias=None,
@@ -541,23 +575,39 @@ def gdn_backward(q, k, v, beta_or_b, d_o, w=None, g=None, state_in=None, d_state
     gdn_backward_workspace_size(...) bytes (allocated when None); `grads` may
     hold preallocated outputs under the same keys.
     """
+    return _backward_call(lib.gdn_backward, "gdn_backward", q, k, v, beta_or_b, d_o, w, g,
+                          state_in, d_state_out, scale, workspace, need_dg, need_d_state_in,
+                          grads, stream)
+
+
+def _backward_call(fn, name, q, k, v, beta_or_b, d_o, w, g, state_in, d_state_out, scale,
+                   workspace, need_dg, need_d_state_in, grads, stream):
     out = _bwd_outputs(q, k, v, beta_or_b, d_o, w, g, state_in, d_state_out, need_dg,
                        need_d_state_in, grads)
     desc = _bwd_desc(q, v, beta_or_b, w, scale)
     need = int(lib.gdn_backward_workspace_size(ctypes.byref(desc)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
-    nbytes = workspace.numel() * workspace.element_size()
-    st = lib.gdn_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b),
-                          _ptr(w), _ptr(g), _ptr(state_in), _ptr(d_o), _ptr(d_state_out),
-                          _ptr(workspace), ctypes.c_size_t(nbytes), _ptr(out["dq"]),
-                          _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["db"]), _ptr(out["dw"]),
-                          _ptr(out["dg"]), _ptr(out["d_state_in"]), _stream(stream))
+    workspace, nbytes = _workspace(workspace, need, q.device)
+    st = fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b), _ptr(w), _ptr(g),
+            _ptr(state_in), _ptr(d_o), _ptr(d_state_out), _ptr(workspace),
+            ctypes.c_size_t(nbytes), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+            _ptr(out["db"]), _ptr(out["dw"]), _ptr(out["dg"]), _ptr(out["d_state_in"]),
+            _stream(stream))
     if st != GDN_OK:
-        raise GdnError(st, "gdn_backward")
+        raise GdnError(st, name)
     return out
+
+
+def gdn_backward_saved(q, k, v, beta_or_b, d_o, workspace, w=None, g=None, state_in=None,
+                       d_state_out=None, scale: float = 1.0, need_dg: bool = True,
+                       need_d_state_in: bool = True, grads=None, stream=None):
+    """gdn_backward over a workspace that gdn_chunk_fwd_save filled for the same
+    inputs (see include/gdn.h): only the reverse walk runs.  Returns the same
+    dict as gdn_backward."""
+    if workspace is None:
+        raise ValueError("gdn_backward_saved needs the workspace gdn_chunk_fwd_save filled")
+    return _backward_call(lib.gdn_backward_saved, "gdn_backward_saved", q, k, v, beta_or_b, d_o,
+                          w, g, state_in, d_state_out, scale, workspace, need_dg,
+                          need_d_state_in, grads, stream)
 
 
 def gdn_backward_noalloc_max_bytes() -> int:

@@ -53,10 +53,11 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
+#define GDN_ABI_VERSION 8  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
                               gdn_gates, gdn_output_gate; 4: adds gdn_backward;
                               5: adds gdn_backward_varlen; 6: adds
-                              gdn_backward_noalloc; 7: adds gdn_chunk_fwd_gated */
+                              gdn_backward_noalloc; 7: adds gdn_chunk_fwd_gated;
+                              8: adds gdn_chunk_fwd_save, gdn_backward_saved */
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -308,6 +309,46 @@ gdn_status gdn_backward_noalloc(const gdn_bwd_desc* desc, const void* q, const v
 
 /* Bytes of the static workspace gdn_backward_noalloc uses on each GPU. */
 size_t gdn_backward_noalloc_max_bytes(void);
+
+/*
+ * gdn_chunk_fwd_save -- gdn_chunk_fwd that also leaves in `workspace` what
+ * gdn_backward otherwise recomputes first: the state entering every 16-token
+ * block and every token's u = z - Sbar^T e (the recurrence of backward.hip),
+ * so that a training step runs the recurrence forward once ("Gated
+ * DeltaNet-2", Methodologie §3: the backward pass needs the forward's
+ * states).  With bf16 io the chunk kernel stores them as it goes (the state
+ * as bf16, the operand precision of the backward's products); with fp32 io
+ * the backward's own rebuild runs after the forward.
+ *
+ *   desc, q, k, v, beta_or_b, w, g, state_in, state_out, o, stream
+ *                 as gdn_chunk_fwd
+ *   workspace     DEVICE, >= gdn_backward_workspace_size() bytes of the
+ *                 gdn_bwd_desc with the same B, T, heads, dims, dtypes, gate
+ *                 mode and scale; 16-byte aligned; must not overlap any
+ *                 tensor of the call.  Its contents are for
+ *                 gdn_backward_saved only.
+ * Returns as gdn_chunk_fwd, and GDN_ERR_INVALID_ARG for a missing, short or
+ * overlapping workspace.
+ */
+gdn_status gdn_chunk_fwd_save(const gdn_fwd_desc* desc, const void* q, const void* k,
+                              const void* v, const void* beta_or_b, const void* w,
+                              const void* g, const float* state_in, float* state_out, void* o,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_backward_saved -- gdn_backward for a workspace that gdn_chunk_fwd_save
+ * filled for the same descriptor and the same q, k, v, gates and state_in:
+ * only the reverse walk runs.  Arguments and results as gdn_backward; the
+ * workspace's saved contents are read (and the rest overwritten).  A
+ * workspace that does not hold them gives meaningless gradients, never an
+ * access outside the arguments.
+ */
+gdn_status gdn_backward_saved(const gdn_bwd_desc* desc, const void* q, const void* k,
+                              const void* v, const void* beta_or_b, const void* w,
+                              const void* g, const float* state_in, const void* d_o,
+                              const float* d_state_out, void* workspace, size_t workspace_bytes,
+                              float* dq, float* dk, float* dv, float* db, float* dw, float* dg,
+                              float* d_state_in, void* stream);
 
 /* Gradients over packed sequences of different lengths. */
 typedef struct gdn_bwd_varlen_desc {

@@ -25,7 +25,8 @@ def test_header_declares_expected_entry_points():
          "gdn_abi_version", "gdn_short_conv", "gdn_gates", "gdn_output_gate", "gdn_backward",
          "gdn_backward_workspace_size", "gdn_backward_varlen",
          "gdn_backward_varlen_workspace_size", "gdn_backward_noalloc",
-         "gdn_backward_noalloc_max_bytes", "gdn_chunk_fwd_gated"])
+         "gdn_backward_noalloc_max_bytes", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_save",
+         "gdn_backward_saved"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert gdn.abi_version() == 7
+    assert gdn.abi_version() == 8
     for st in range(4):
         s = gdn.status_string(st)
         assert s.startswith("GDN_")
@@ -488,6 +489,57 @@ def test_backward_pointer_rules():
     assert _bwd(sc, dw=_addr(14)) == gdn.GDN_ERR_INVALID_ARG                  # dw in scalar mode
     assert _bwd(_bwd_desc(B=0)) == gdn.GDN_OK
     assert _bwd(_bwd_desc(T=0), d_s0=None) == gdn.GDN_OK
+
+
+def _fwd_save(desc, ws_bytes=None, **ptrs):
+    names = ["q", "k", "v", "b", "w", "g", "s_in", "s_out", "o", "ws"]
+    p = {n: _addr(i) for i, n in enumerate(names)}
+    if desc.gate_mode == gdn.GDN_GATES_SCALAR:
+        p["w"] = None
+    p.update(ptrs)
+    if ws_bytes is None:
+        bd = _bwd_desc(B=desc.B, T=desc.T, H_k=desc.H_k, H_v=desc.H_v, d_k=desc.d_k,
+                       d_v=desc.d_v, io_dtype=desc.io_dtype, gate_dtype=desc.gate_dtype,
+                       gate_mode=desc.gate_mode, scale=desc.scale)
+        ws_bytes = gdn.lib.gdn_backward_workspace_size(ctypes.byref(bd))
+    args = [p[n] for n in names]
+    return gdn.lib.gdn_chunk_fwd_save(ctypes.byref(desc), *args, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_forward_save_validation():
+    """The forward's checks, then the workspace's: present, aligned, large
+    enough, overlapping nothing (no launch happens on a rejected call)."""
+    assert _fwd_save(_fwd_desc(chunk=32)) == gdn.GDN_ERR_UNSUPPORTED
+    assert _fwd_save(_fwd_desc(H_v=3)) == gdn.GDN_ERR_INVALID_ARG
+    assert _fwd_save(_fwd_desc(), ws=None) == gdn.GDN_ERR_INVALID_ARG
+    assert _fwd_save(_fwd_desc(), ws=_addr(9, 8)) == gdn.GDN_ERR_INVALID_ARG
+    assert _fwd_save(_fwd_desc(), ws_bytes=1000) == gdn.GDN_ERR_INVALID_ARG
+    assert _fwd_save(_fwd_desc(), ws=_addr(8, 64)) == gdn.GDN_ERR_INVALID_ARG   # over o
+    assert _fwd_save(_fwd_desc(), q=None) == gdn.GDN_ERR_INVALID_ARG
+    assert _fwd_save(_fwd_desc(B=0)) == gdn.GDN_OK
+
+
+def test_backward_saved_validation():
+    """gdn_backward_saved takes gdn_backward's arguments and checks."""
+    names = ["q", "k", "v", "b", "w", "g", "s_in", "d_o", "d_sT", "ws", "dq", "dk", "dv", "db",
+             "dw", "dg", "d_s0"]
+
+    def call(desc, ws_bytes=None, **ptrs):
+        p = {n: _addr(i) for i, n in enumerate(names)}
+        p.update(ptrs)
+        if ws_bytes is None:
+            ws_bytes = gdn.lib.gdn_backward_workspace_size(ctypes.byref(desc))
+        args = [p[n] for n in names]
+        return gdn.lib.gdn_backward_saved(ctypes.byref(desc), *args[:10],
+                                          ctypes.c_size_t(ws_bytes), *args[10:], None)
+
+    assert call(_bwd_desc(), ws_bytes=1000) == gdn.GDN_ERR_INVALID_ARG
+    assert call(_bwd_desc(), dq=None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(_bwd_desc(), dk=_addr(10, 16)) == gdn.GDN_ERR_INVALID_ARG
+    assert call(_bwd_desc(H_v=3), ws_bytes=1 << 40) == gdn.GDN_ERR_INVALID_ARG
+    assert call(_bwd_desc(B=0)) == gdn.GDN_OK
+    assert gdn.lib.gdn_backward_saved(None, *([None] * 10), ctypes.c_size_t(0),
+                                      *([None] * 7), None) == gdn.GDN_ERR_INVALID_ARG
 
 
 # ---------------------------------------------------------------------------
