@@ -711,6 +711,9 @@ def main():
                     help="time only gdn_chunk_fwd on this workload (a key of synth.CONFIGS, "
                          "optionally with the suffix _mamba2_gates) and print its timing; "
                          "for profiling one kernel in isolation")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward row (gdn_backward and the saved-state pair) "
+                         "and print it; for profiling the backward kernels in isolation")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KERNEL_STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
@@ -739,6 +742,10 @@ def main():
     if args.workload:
         print(json.dumps(single_workload(gdn, synth, torch, dev, args.workload, args.steps,
                                          args.warmup)), flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps(backward_workload(gdn, synth, torch, dev, steps=args.steps,
+                                           warmup=args.warmup)), flush=True)
         return
     cfg_c = synth.CONFIGS["gdn2_bf16_train"]
     cfg_d = synth.CONFIGS["gdn2_decode"]
