@@ -8,7 +8,7 @@ from .gdn import (  # noqa: F401
     GDN_GATES_CHANNEL, GDN_GATES_SCALAR, GDN_OK, GdnBwdDesc, GdnBwdVarlenDesc, GdnConvDesc, GdnDecodeDesc, GdnError,
     GdnFwdDesc, GdnGateDesc, GdnNormDesc, GdnRawGates, GdnVarlenDesc, abi_version, gdn_backward,
     gdn_backward_noalloc, gdn_backward_noalloc_max_bytes, gdn_backward_saved,
-    gdn_backward_varlen, gdn_backward_workspace_size, gdn_chunk_fwd,
-    gdn_chunk_fwd_gated, gdn_chunk_fwd_save, gdn_chunk_fwd_varlen, gdn_decode_step, gdn_gates, gdn_output_gate, gdn_short_conv, lib,
+    gdn_backward_varlen, gdn_backward_varlen_saved, gdn_backward_workspace_size, gdn_chunk_fwd,
+    gdn_chunk_fwd_gated, gdn_chunk_fwd_save, gdn_chunk_fwd_varlen, gdn_chunk_fwd_varlen_save, gdn_decode_step, gdn_gates, gdn_output_gate, gdn_short_conv, lib,
     status_string,
 )

@@ -277,6 +277,67 @@ gdn_status check_fwd_desc(const gdn_fwd_desc* d) {
   return GDN_OK;
 }
 
+// The chunk forward over the shape bs (equal-length or packed by bs.cu) with
+// the backward's checkpoints and u left in `workspace`; the forward's own
+// argument checks have passed.  The bf16 chunk kernel stores them as it goes;
+// other configurations run the backward's forward rebuild after the forward.
+gdn_status run_fwd_save(const BwdShape& bs, const void* q, const void* k, const void* v,
+                        const void* beta_or_b, const void* w, const void* g,
+                        const float* state_in, float* state_out, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  gdn_status st = check_bwd_shape(bs);
+  if (st != GDN_OK) return st;
+  const BwdLayout L = bwd_layout(bs);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < L.total) return GDN_ERR_INVALID_ARG;
+  // the workspace is written: it overlaps no tensor of the call
+  const int64_t rows = bs.rows, heads = bs.N * bs.Hv;
+  const int64_t ib = dtype_bytes(bs.io), gb = dtype_bytes(bs.gate);
+  const int64_t gcols = bs.mode == GDN_GATES_CHANNEL ? bs.dk : 1;
+  const int64_t S = heads * bs.dk * bs.dv;
+  const Span sws = span(workspace, (int64_t)L.total, 1);
+  const Span all[] = {span(q, rows * bs.Hk * bs.dk, ib), span(k, rows * bs.Hk * bs.dk, ib),
+                      span(v, rows * bs.Hv * bs.dv, ib), span(beta_or_b, rows * bs.Hv * gcols, gb),
+                      span(w, rows * bs.Hv * bs.dv, gb), span(g, rows * bs.Hv * gcols, gb),
+                      span(state_in, S, 4), span(state_out, S, 4),
+                      span(o, rows * bs.Hv * bs.dv, ib), span(bs.cu, bs.N + 1, 8)};
+  for (const Span& x : all)
+    if (overlaps(sws, x)) return GDN_ERR_INVALID_ARG;
+
+  gdn::ChunkArgs a;
+  a.B = bs.N; a.T = bs.cu ? rows : bs.T; a.cu_seqlens = bs.cu;
+  a.Hk = bs.Hk; a.Hv = bs.Hv; a.dk = bs.dk; a.dv = bs.dv;
+  a.io = to_dtype(bs.io); a.gate = to_dtype(bs.gate);
+  a.channel = bs.mode == GDN_GATES_CHANNEL; a.scale = bs.scale;
+  a.q = q; a.k = k; a.v = v; a.b = beta_or_b; a.w = w; a.g = g;
+  a.state_in = state_in; a.state_out = state_out; a.o = o;
+  char* ws = static_cast<char*>(workspace);
+  const bool in_kernel = bs.io == GDN_BF16;
+  if (in_kernel) {
+    a.ck = ws + L.ckpt_off;
+    a.u = ws + L.u_off;
+    a.ck_slots = L.slots;
+    a.ck_nblk = L.nblk;
+  }
+  hipError_t e = gdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  if (in_kernel) return GDN_OK;
+  gdn::BwdArgs b;
+  b.B = bs.N; b.T = bs.T; b.cu = bs.cu; b.rows = rows; b.slots = L.slots;
+  b.Hk = bs.Hk; b.Hv = bs.Hv; b.dk = bs.dk; b.dv = bs.dv;
+  b.io = a.io; b.gate = a.gate; b.channel = a.channel; b.scale = bs.scale;
+  b.q = q; b.k = k; b.v = v; b.b = beta_or_b; b.w = w; b.g = g; b.d_o = nullptr;
+  b.state_in = state_in; b.d_state_out = nullptr;
+  b.ckpt = ws + L.ckpt_off; b.u = ws + L.u_off;
+  b.part = reinterpret_cast<float*>(ws + L.part_off);
+  b.direct = L.direct;
+  b.phases = 1;
+  b.nblk = L.nblk;
+  b.dq_out = b.dk_out = b.dv_out = b.db = b.dw = b.dg = b.d_state_in = nullptr;
+  e = gdn::launch_backward(b, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,62 +399,14 @@ gdn_status gdn_chunk_fwd_save(const gdn_fwd_desc* d, const void* q, const void* 
   if (st != GDN_OK) return st;
   if (d->B == 0 || d->T == 0)   // nothing for a backward to read
     return gdn_chunk_fwd(d, q, k, v, beta_or_b, w, g, state_in, state_out, o, stream);
-  const BwdShape bs{d->B, d->B * d->T, d->T, nullptr, d->H_k, d->H_v, d->d_k, d->d_v,
-                    d->io_dtype, d->gate_dtype, d->gate_mode, d->scale};
-  st = check_bwd_shape(bs);
-  if (st != GDN_OK) return st;
-  const BwdLayout L = bwd_layout(bs);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < L.total) return GDN_ERR_INVALID_ARG;
   const int64_t rows = d->B * d->T, heads = d->B * d->H_v;
   st = check_pointers(rows, heads, d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
                       d->gate_mode, q, k, v, beta_or_b, w, g, state_in, state_out, o, false);
   if (st != GDN_OK) return st;
-  // the workspace is written: it overlaps no tensor of the call
-  const int64_t ib = dtype_bytes(d->io_dtype), gb = dtype_bytes(d->gate_dtype);
-  const int64_t gcols = d->gate_mode == GDN_GATES_CHANNEL ? d->d_k : 1;
-  const int64_t S = heads * d->d_k * d->d_v;
-  const Span sws = span(workspace, (int64_t)L.total, 1);
-  const Span all[] = {span(q, rows * d->H_k * d->d_k, ib), span(k, rows * d->H_k * d->d_k, ib),
-                      span(v, rows * d->H_v * d->d_v, ib), span(beta_or_b, rows * d->H_v * gcols, gb),
-                      span(w, rows * d->H_v * d->d_v, gb), span(g, rows * d->H_v * gcols, gb),
-                      span(state_in, S, 4), span(state_out, S, 4),
-                      span(o, rows * d->H_v * d->d_v, ib)};
-  for (const Span& x : all)
-    if (overlaps(sws, x)) return GDN_ERR_INVALID_ARG;
-
-  gdn::ChunkArgs a;
-  a.B = d->B; a.T = d->T; a.Hk = d->H_k; a.Hv = d->H_v; a.dk = d->d_k; a.dv = d->d_v;
-  a.io = to_dtype(d->io_dtype); a.gate = to_dtype(d->gate_dtype);
-  a.channel = d->gate_mode == GDN_GATES_CHANNEL; a.scale = d->scale;
-  a.q = q; a.k = k; a.v = v; a.b = beta_or_b; a.w = w; a.g = g;
-  a.state_in = state_in; a.state_out = state_out; a.o = o;
-  char* ws = static_cast<char*>(workspace);
-  const bool in_kernel = d->io_dtype == GDN_BF16;   // the bf16 kernel stores them itself
-  if (in_kernel) {
-    a.ck = ws + L.ckpt_off;
-    a.u = ws + L.u_off;
-    a.ck_slots = L.slots;
-    a.ck_nblk = L.nblk;
-  }
-  hipError_t e = gdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
-  if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
-  if (e != hipSuccess) return GDN_ERR_HIP;
-  if (in_kernel) return GDN_OK;
-  // other kernels: the backward's own forward rebuild fills the workspace
-  gdn::BwdArgs b;
-  b.B = d->B; b.T = d->T; b.cu = nullptr; b.rows = rows; b.slots = L.slots;
-  b.Hk = d->H_k; b.Hv = d->H_v; b.dk = d->d_k; b.dv = d->d_v;
-  b.io = a.io; b.gate = a.gate; b.channel = a.channel; b.scale = d->scale;
-  b.q = q; b.k = k; b.v = v; b.b = beta_or_b; b.w = w; b.g = g; b.d_o = nullptr;
-  b.state_in = state_in; b.d_state_out = nullptr;
-  b.ckpt = ws + L.ckpt_off; b.u = ws + L.u_off;
-  b.part = reinterpret_cast<float*>(ws + L.part_off);
-  b.direct = L.direct;
-  b.phases = 1;
-  b.nblk = L.nblk;
-  b.dq_out = b.dk_out = b.dv_out = b.db = b.dw = b.dg = b.d_state_in = nullptr;
-  e = gdn::launch_backward(b, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  const BwdShape bs{d->B, rows, d->T, nullptr, d->H_k, d->H_v, d->d_k, d->d_v,
+                    d->io_dtype, d->gate_dtype, d->gate_mode, d->scale};
+  return run_fwd_save(bs, q, k, v, beta_or_b, w, g, state_in, state_out, o, workspace,
+                      workspace_bytes, stream);
 }
 
 gdn_status gdn_chunk_fwd_gated(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
@@ -526,6 +539,39 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_varlen_desc* d, const int64_t* cu_seql
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_chunk_fwd_varlen_save(const gdn_varlen_desc* d, const int64_t* cu_seqlens,
+                                     const void* q, const void* k, const void* v,
+                                     const void* beta_or_b, const void* w, const void* g,
+                                     const float* state_in, float* state_out, void* o,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  if (d->N <= 0 || d->total_T <= 0)   // nothing for a backward to read
+    return gdn_chunk_fwd_varlen(d, cu_seqlens, q, k, v, beta_or_b, w, g, state_in, state_out, o,
+                                stream);
+  gdn_status st = check_common(d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
+                               d->gate_mode, d->scale);
+  if (st != GDN_OK) return st;
+  if (d->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  const double elems = (double)d->total_T * (double)d->H_v * (double)(d->d_k + d->d_v);
+  if (elems > 9.0e15) return GDN_ERR_INVALID_ARG;
+  if ((double)d->total_T > 2.0e9 || (double)d->N * (double)d->H_v * 2.0 > 2.0e9)
+    return GDN_ERR_UNSUPPORTED;
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0) return GDN_ERR_INVALID_ARG;
+  const int64_t heads = d->N * d->H_v;
+  const Span scu = span(cu_seqlens, d->N + 1, 8);
+  const Span so = span(state_out, heads * d->d_k * d->d_v, 4);
+  const Span sO = span(o, d->total_T * d->H_v * d->d_v, dtype_bytes(d->io_dtype));
+  if (overlaps(scu, so) || overlaps(scu, sO)) return GDN_ERR_INVALID_ARG;
+  st = check_pointers(d->total_T, heads, d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype,
+                      d->gate_dtype, d->gate_mode, q, k, v, beta_or_b, w, g, state_in, state_out,
+                      o, false);
+  if (st != GDN_OK) return st;
+  const BwdShape bs{d->N, d->total_T, 0, cu_seqlens, d->H_k, d->H_v, d->d_k, d->d_v,
+                    d->io_dtype, d->gate_dtype, d->gate_mode, d->scale};
+  return run_fwd_save(bs, q, k, v, beta_or_b, w, g, state_in, state_out, o, workspace,
+                      workspace_bytes, stream);
+}
+
 size_t gdn_backward_workspace_size(const gdn_bwd_desc* d) {
   if (!d) return 0;
   const BwdShape sh = shape_of(d);
@@ -576,6 +622,21 @@ gdn_status gdn_backward_varlen(const gdn_bwd_varlen_desc* d, const int64_t* cu_s
   return run_backward(shape_of(d, cu_seqlens), q, k, v, beta_or_b, w, g, state_in, d_o,
                       d_state_out, workspace, workspace_bytes, dq, dk, dv, db, dw, dg,
                       d_state_in, stream);
+}
+
+gdn_status gdn_backward_varlen_saved(const gdn_bwd_varlen_desc* d, const int64_t* cu_seqlens,
+                                     const void* q, const void* k, const void* v,
+                                     const void* beta_or_b, const void* w, const void* g,
+                                     const float* state_in, const void* d_o,
+                                     const float* d_state_out, void* workspace,
+                                     size_t workspace_bytes, float* dq, float* dk, float* dv,
+                                     float* db, float* dw, float* dg, float* d_state_in,
+                                     void* stream) {
+  if (!d) return GDN_ERR_INVALID_ARG;
+  if (d->N > 0 && !cu_seqlens) return GDN_ERR_INVALID_ARG;
+  return run_backward(shape_of(d, cu_seqlens), q, k, v, beta_or_b, w, g, state_in, d_o,
+                      d_state_out, workspace, workspace_bytes, dq, dk, dv, db, dw, dg,
+                      d_state_in, stream, /*phases=*/2);
 }
 
 gdn_status gdn_short_conv(const gdn_conv_desc* d, const int64_t* cu_seqlens, const void* x,

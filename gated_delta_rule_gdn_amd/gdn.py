@@ -135,6 +135,11 @@ def _load() -> ctypes.CDLL:
                                         vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp, vp, vp,
                                         vp, vp, vp]
     lib.gdn_backward_varlen.restype = ctypes.c_int
+    lib.gdn_backward_varlen_saved.argtypes = lib.gdn_backward_varlen.argtypes
+    lib.gdn_backward_varlen_saved.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_varlen_save.argtypes = [ctypes.POINTER(GdnVarlenDesc), vp, vp, vp, vp, vp,
+                                              vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gdn_chunk_fwd_varlen_save.restype = ctypes.c_int
     lib.gdn_short_conv.argtypes = [ctypes.POINTER(GdnConvDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_short_conv.restype = ctypes.c_int
     lib.gdn_gates.argtypes = [ctypes.POINTER(GdnGateDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -302,17 +307,7 @@ def gdn_chunk_fwd_gated(q, k, v, b_raw, a_raw=None, w_raw=None, A_log=None, dt_b
     return o, state_out
 
 
-def gdn_chunk_fwd_varlen(q, k, v, beta_or_b, cu_seqlens, w=None, g=None, state_in=None,
-                         state_out=None, o=None, scale: float = 1.0, chunk: int = 64,
-                         stream=None):
-    """Chunkwise forward over packed sequences (see include/gdn.h).
-    Returns (o, state_out).
-
-    q, k [total_T,Hk,dk]; v [total_T,Hv,dv]; beta_or_b [total_T,Hv] or
-    [total_T,Hv,dk] (then w [total_T,Hv,dv]); g like beta_or_b or None;
-    cu_seqlens int64 device tensor [N+1] of token offsets; state_in/state_out
-    [N,Hv,dk,dv] fp32 or None.  o is allocated when not given.
-    """
+def _varlen_fwd_desc(q, k, v, beta_or_b, cu_seqlens, w, g, state_in, state_out, o, scale, chunk):
     T, Hk, dk = q.shape
     Hv, dv = v.shape[1], v.shape[2]
     io = q.dtype
@@ -340,12 +335,49 @@ def gdn_chunk_fwd_varlen(q, k, v, beta_or_b, cu_seqlens, w=None, g=None, state_i
         raise ValueError("gates must be float32 or bfloat16")
     desc = GdnVarlenDesc(N, T, Hk, Hv, dk, dv, _DT[io], _DT[gdt],
                          GDN_GATES_CHANNEL if channel else GDN_GATES_SCALAR, chunk, float(scale))
+    return desc, o
+
+
+def gdn_chunk_fwd_varlen(q, k, v, beta_or_b, cu_seqlens, w=None, g=None, state_in=None,
+                         state_out=None, o=None, scale: float = 1.0, chunk: int = 64,
+                         stream=None):
+    """Chunkwise forward over packed sequences (see include/gdn.h).
+    Returns (o, state_out).
+
+    q, k [total_T,Hk,dk]; v [total_T,Hv,dv]; beta_or_b [total_T,Hv] or
+    [total_T,Hv,dk] (then w [total_T,Hv,dv]); g like beta_or_b or None;
+    cu_seqlens int64 device tensor [N+1] of token offsets; state_in/state_out
+    [N,Hv,dk,dv] fp32 or None.  o is allocated when not given.
+    """
+    desc, o = _varlen_fwd_desc(q, k, v, beta_or_b, cu_seqlens, w, g, state_in, state_out, o,
+                               scale, chunk)
     st = lib.gdn_chunk_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
                                   _ptr(beta_or_b), _ptr(w), _ptr(g), _ptr(state_in),
                                   _ptr(state_out), _ptr(o), _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_fwd_varlen")
     return o, state_out
+
+
+def gdn_chunk_fwd_varlen_save(q, k, v, beta_or_b, cu_seqlens, w=None, g=None, state_in=None,
+                              state_out=None, o=None, scale: float = 1.0, chunk: int = 64,
+                              workspace=None, stream=None):
+    """gdn_chunk_fwd_varlen that also fills a backward workspace for
+    gdn_backward_varlen_saved (see include/gdn.h).  Returns (o, state_out,
+    workspace); the workspace is allocated when not given."""
+    desc, o = _varlen_fwd_desc(q, k, v, beta_or_b, cu_seqlens, w, g, state_in, state_out, o,
+                               scale, chunk)
+    bdesc = GdnBwdVarlenDesc(desc.N, desc.total_T, desc.H_k, desc.H_v, desc.d_k, desc.d_v,
+                             desc.io_dtype, desc.gate_dtype, desc.gate_mode, desc.scale)
+    need = int(lib.gdn_backward_varlen_workspace_size(ctypes.byref(bdesc)))
+    workspace, nbytes = _workspace(workspace, need, q.device)
+    st = lib.gdn_chunk_fwd_varlen_save(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(beta_or_b), _ptr(w), _ptr(g),
+                                       _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(workspace),
+                                       ctypes.c_size_t(nbytes), _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_fwd_varlen_save")
+    return o, state_out, workspace
 
 
 def gdn_decode_step(q, k, v, beta_or_b, state, w=None, g=None, o=None, scale: float = 1.0,
@@ -642,6 +674,29 @@ def gdn_backward_varlen(q, k, v, beta_or_b, d_o, cu_seqlens, w=None, g=None, sta
     """Gradients over packed sequences (see include/gdn.h).  Shapes as for
     gdn_chunk_fwd_varlen ([total_T, ...] packed, states [N, ...]); returns the
     same dict of fp32 tensors as gdn_backward."""
+    return _backward_varlen_call(lib.gdn_backward_varlen, "gdn_backward_varlen", q, k, v,
+                                 beta_or_b, d_o, cu_seqlens, w, g, state_in, d_state_out, scale,
+                                 workspace, need_dg, need_d_state_in, grads, stream)
+
+
+def gdn_backward_varlen_saved(q, k, v, beta_or_b, d_o, cu_seqlens, workspace, w=None, g=None,
+                              state_in=None, d_state_out=None, scale: float = 1.0,
+                              need_dg: bool = True, need_d_state_in: bool = True, grads=None,
+                              stream=None):
+    """gdn_backward_varlen over a workspace that gdn_chunk_fwd_varlen_save
+    filled for the same inputs (see include/gdn.h): only the reverse walk
+    runs."""
+    if workspace is None:
+        raise ValueError("gdn_backward_varlen_saved needs the workspace "
+                         "gdn_chunk_fwd_varlen_save filled")
+    return _backward_varlen_call(lib.gdn_backward_varlen_saved, "gdn_backward_varlen_saved", q,
+                                 k, v, beta_or_b, d_o, cu_seqlens, w, g, state_in, d_state_out,
+                                 scale, workspace, need_dg, need_d_state_in, grads, stream)
+
+
+def _backward_varlen_call(fn, fname, q, k, v, beta_or_b, d_o, cu_seqlens, w, g, state_in,
+                          d_state_out, scale, workspace, need_dg, need_d_state_in, grads,
+                          stream):
     T, Hk, dk = q.shape
     Hv, dv = v.shape[1], v.shape[2]
     io = q.dtype
@@ -666,10 +721,7 @@ def gdn_backward_varlen(q, k, v, beta_or_b, d_o, cu_seqlens, w=None, g=None, sta
     desc = GdnBwdVarlenDesc(N, T, Hk, Hv, dk, dv, _DT[io], _DT[gdt],
                             GDN_GATES_CHANNEL if channel else GDN_GATES_SCALAR, float(scale))
     need = int(lib.gdn_backward_varlen_workspace_size(ctypes.byref(desc)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous device tensor")
+    workspace, nbytes = _workspace(workspace, need, q.device)
     f32 = dict(dtype=torch.float32, device=q.device)
     shapes = {"dq": (T, Hk, dk), "dk": (T, Hk, dk), "dv": (T, Hv, dv), "db": gshape,
               "dw": (T, Hv, dv) if channel else None,
@@ -683,13 +735,11 @@ def gdn_backward_varlen(q, k, v, beta_or_b, d_o, cu_seqlens, w=None, g=None, sta
         if out.get(name) is None:
             out[name] = torch.empty(shp, **f32)
         _check(out[name], name, shp, torch.float32)
-    nbytes = workspace.numel() * workspace.element_size()
-    st = lib.gdn_backward_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(beta_or_b), _ptr(w), _ptr(g), _ptr(state_in), _ptr(d_o),
-                                 _ptr(d_state_out), _ptr(workspace), ctypes.c_size_t(nbytes),
-                                 _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["db"]),
-                                 _ptr(out["dw"]), _ptr(out["dg"]), _ptr(out["d_state_in"]),
-                                 _stream(stream))
+    st = fn(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(beta_or_b),
+            _ptr(w), _ptr(g), _ptr(state_in), _ptr(d_o), _ptr(d_state_out), _ptr(workspace),
+            ctypes.c_size_t(nbytes), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+            _ptr(out["db"]), _ptr(out["dw"]), _ptr(out["dg"]), _ptr(out["d_state_in"]),
+            _stream(stream))
     if st != GDN_OK:
-        raise GdnError(st, "gdn_backward_varlen")
+        raise GdnError(st, fname)
     return out

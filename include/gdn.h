@@ -57,7 +57,9 @@ extern "C" {
                               gdn_gates, gdn_output_gate; 4: adds gdn_backward;
                               5: adds gdn_backward_varlen; 6: adds
                               gdn_backward_noalloc; 7: adds gdn_chunk_fwd_gated;
-                              8: adds gdn_chunk_fwd_save, gdn_backward_saved */
+                              8: adds gdn_chunk_fwd_save, gdn_backward_saved and
+                              their packed forms gdn_chunk_fwd_varlen_save,
+                              gdn_backward_varlen_saved */
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -392,6 +394,42 @@ gdn_status gdn_backward_varlen(const gdn_bwd_varlen_desc* desc, const int64_t* c
                                void* workspace, size_t workspace_bytes, float* dq, float* dk,
                                float* dv, float* db, float* dw, float* dg, float* d_state_in,
                                void* stream);
+
+/*
+ * gdn_chunk_fwd_varlen_save -- gdn_chunk_fwd_varlen that also leaves in
+ * `workspace` the states and u gdn_backward_varlen_saved reads, as
+ * gdn_chunk_fwd_save does for equal-length sequences.
+ *
+ *   desc, cu_seqlens, q, k, v, beta_or_b, w, g, state_in, state_out, o, stream
+ *                 as gdn_chunk_fwd_varlen
+ *   workspace     DEVICE, >= gdn_backward_varlen_workspace_size() bytes of the
+ *                 gdn_bwd_varlen_desc with the same N, total_T, heads, dims,
+ *                 dtypes, gate mode and scale; 16-byte aligned; must not
+ *                 overlap any tensor of the call
+ * Returns as gdn_chunk_fwd_varlen, and GDN_ERR_INVALID_ARG for a missing,
+ * short or overlapping workspace.
+ */
+gdn_status gdn_chunk_fwd_varlen_save(const gdn_varlen_desc* desc, const int64_t* cu_seqlens,
+                                     const void* q, const void* k, const void* v,
+                                     const void* beta_or_b, const void* w, const void* g,
+                                     const float* state_in, float* state_out, void* o,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_backward_varlen_saved -- gdn_backward_varlen for a workspace that
+ * gdn_chunk_fwd_varlen_save filled for the same descriptor, offsets and
+ * inputs: only the reverse walk runs.  Arguments and results as
+ * gdn_backward_varlen; a workspace that does not hold them gives meaningless
+ * gradients, never an access outside the arguments.
+ */
+gdn_status gdn_backward_varlen_saved(const gdn_bwd_varlen_desc* desc, const int64_t* cu_seqlens,
+                                     const void* q, const void* k, const void* v,
+                                     const void* beta_or_b, const void* w, const void* g,
+                                     const float* state_in, const void* d_o,
+                                     const float* d_state_out, void* workspace,
+                                     size_t workspace_bytes, float* dq, float* dk, float* dv,
+                                     float* db, float* dw, float* dg, float* d_state_in,
+                                     void* stream);
 
 /* ------------------------------------------------------------------------
  * The operations around the recurrence in a Gated DeltaNet block (notes page

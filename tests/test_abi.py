@@ -26,7 +26,7 @@ def test_header_declares_expected_entry_points():
          "gdn_backward_workspace_size", "gdn_backward_varlen",
          "gdn_backward_varlen_workspace_size", "gdn_backward_noalloc",
          "gdn_backward_noalloc_max_bytes", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_save",
-         "gdn_backward_saved"])
+         "gdn_backward_saved", "gdn_chunk_fwd_varlen_save", "gdn_backward_varlen_saved"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -517,6 +517,33 @@ def test_forward_save_validation():
     assert _fwd_save(_fwd_desc(), ws=_addr(8, 64)) == gdn.GDN_ERR_INVALID_ARG   # over o
     assert _fwd_save(_fwd_desc(), q=None) == gdn.GDN_ERR_INVALID_ARG
     assert _fwd_save(_fwd_desc(B=0)) == gdn.GDN_OK
+
+
+def test_forward_varlen_save_validation():
+    d = gdn.GdnVarlenDesc(N=3, total_T=100, H_k=2, H_v=4, d_k=128, d_v=128,
+                          io_dtype=gdn.GDN_BF16, gate_dtype=gdn.GDN_BF16,
+                          gate_mode=gdn.GDN_GATES_CHANNEL, chunk=64, scale=1.0)
+    bd = gdn.GdnBwdVarlenDesc(N=3, total_T=100, H_k=2, H_v=4, d_k=128, d_v=128,
+                              io_dtype=gdn.GDN_BF16, gate_dtype=gdn.GDN_BF16,
+                              gate_mode=gdn.GDN_GATES_CHANNEL, scale=1.0)
+    need = gdn.lib.gdn_backward_varlen_workspace_size(ctypes.byref(bd))
+    names = ["q", "k", "v", "b", "w", "g", "s_in", "s_out", "o", "ws"]
+
+    def call(cu=_addr(11), ws_bytes=need, **ptrs):
+        p = {n: _addr(i) for i, n in enumerate(names)}
+        p.update(ptrs)
+        args = [p[n] for n in names]
+        return gdn.lib.gdn_chunk_fwd_varlen_save(ctypes.byref(d), cu, *args,
+                                                 ctypes.c_size_t(ws_bytes), None)
+
+    assert call(ws=None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == gdn.GDN_ERR_INVALID_ARG
+    assert call(ws=_addr(11)) == gdn.GDN_ERR_INVALID_ARG      # over cu_seqlens
+    assert call(ws=_addr(2, 32)) == gdn.GDN_ERR_INVALID_ARG   # over v
+    assert call(cu=None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(cu=_addr(11, 4)) == gdn.GDN_ERR_INVALID_ARG   # misaligned offsets
+    assert gdn.lib.gdn_chunk_fwd_varlen_save(None, None, *([None] * 10), ctypes.c_size_t(0),
+                                             None) == gdn.GDN_ERR_INVALID_ARG
 
 
 def test_backward_saved_validation():

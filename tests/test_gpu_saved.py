@@ -168,3 +168,66 @@ def test_saved_rejects_a_short_workspace():
         gdn.gdn_chunk_fwd_save(d["q"], d["k"], d["v"], d["beta_or_b"], w=d["w"], g=d["g"],
                                workspace=short)
     assert ei.value.status == gdn.GDN_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences: gdn_chunk_fwd_varlen_save + gdn_backward_varlen_saved.
+# ---------------------------------------------------------------------------
+VL = [0, 1, 17, 64, 100, 5, 130]   # empty, single-token, ragged, whole and multi-chunk
+
+
+def _packed_case(lengths, channel, io, Hk, Hv, seed=71):
+    total = sum(lengths)
+    inp, d_o, _ = _case(1, total, Hk, Hv, 128, 128, channel, io, seed=seed)
+    packed = {k: (None if v is None else v[0].contiguous()) for k, v in inp.items()
+              if k != "state_in"}
+    gen = torch.Generator().manual_seed(seed + 3)
+    N = len(lengths)
+    s0 = 0.3 * torch.randn((N, Hv, 128, 128), generator=gen)
+    dsT = torch.randn((N, Hv, 128, 128), generator=gen)
+    cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()), dtype=torch.int64)
+    return packed, d_o[0].contiguous(), s0, dsT, cu
+
+
+@pytest.mark.parametrize("channel", [True, False])
+@pytest.mark.parametrize("io,Hk,Hv", [(torch.bfloat16, 2, 2), (torch.bfloat16, 1, 2),
+                                      (torch.float32, 2, 2)])
+def test_saved_packed_sequences(channel, io, Hk, Hv):
+    """Per sequence against the oracle; the forward's o and final states
+    bitwise those of gdn_chunk_fwd_varlen (fp32: the gradients bitwise those
+    of gdn_backward_varlen)."""
+    announce(f"saved packed ch={channel} io={io} H={Hk}/{Hv}")
+    packed, d_o, s0, dsT, cu = _packed_case(VL, channel, io, Hk, Hv)
+    d = _dev(packed)
+    cud, s0d, dsd, dod = cu.cuda(), s0.cuda(), dsT.cuda(), d_o.cuda()
+    o_s, s_s, ws = gdn.gdn_chunk_fwd_varlen_save(d["q"], d["k"], d["v"], d["beta_or_b"], cud,
+                                                 w=d["w"], g=d["g"], state_in=s0d,
+                                                 state_out=torch.empty_like(s0d))
+    got = gdn.gdn_backward_varlen_saved(d["q"], d["k"], d["v"], d["beta_or_b"], dod, cud, ws,
+                                        w=d["w"], g=d["g"], state_in=s0d, d_state_out=dsd)
+    o_p, s_p = gdn.gdn_chunk_fwd_varlen(d["q"], d["k"], d["v"], d["beta_or_b"], cud, w=d["w"],
+                                        g=d["g"], state_in=s0d, state_out=torch.empty_like(s0d))
+    plain = gdn.gdn_backward_varlen(d["q"], d["k"], d["v"], d["beta_or_b"], dod, cud, w=d["w"],
+                                    g=d["g"], state_in=s0d, d_state_out=dsd)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_p) and torch.equal(s_s, s_p)
+    tol = tol_for(io)
+    for n in range(len(VL)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b == a:   # an empty sequence passes its state gradient through
+            assert torch.equal(got["d_state_in"][n].cpu(), dsT[n]), n
+            continue
+        sl = lambda x: None if x is None else x[a:b].unsqueeze(0)
+        ref = oracle.backward(sl(packed["q"]), sl(packed["k"]), sl(packed["v"]),
+                              sl(packed["beta_or_b"]), sl(d_o), w=sl(packed["w"]),
+                              g=sl(packed["g"]), state_in=s0[n:n + 1], d_state_out=dsT[n:n + 1])
+        for name in ["dq", "dk", "dv", "db", "dw", "dg"]:
+            if ref[name] is None:
+                continue
+            e = relerr(got[name][a:b].unsqueeze(0), ref[name])
+            assert e <= tol, (n, name, e)
+        assert relerr(got["d_state_in"][n:n + 1], ref["d_state_in"]) <= tol, n
+    if io == torch.float32:
+        for name in NAMES:
+            if got[name] is not None:
+                assert torch.equal(got[name], plain[name]), name
