@@ -173,6 +173,30 @@ def test_backward_is_deterministic_and_in_place_state_gradient():
         assert torch.equal(a[n], c[n]), n
 
 
+def test_backward_direct_row_gradients_are_deterministic():
+    """Channel gates with one value head per key head: the two 64-column
+    workgroups of a head add their row gradients straight into the outputs
+    (exactly two addends onto zero, in whichever order they land).  Repeated
+    calls, plain and from saved states, are bitwise equal; plain and saved
+    agree to the bf16 tolerance."""
+    announce("backward direct row gradients: determinism")
+    inp, d_o, d_sT = _case(4, 500, 4, 4, 128, 128, True, torch.bfloat16, seed=12)
+    runs = [_run(inp, d_o, d_sT) for _ in range(4)]
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    _, _, ws = gdn.gdn_chunk_fwd_save(d["q"], d["k"], d["v"], d["beta_or_b"], w=d["w"], g=d["g"],
+                                      state_in=d["state_in"])
+    saved = [gdn.gdn_backward_saved(d["q"], d["k"], d["v"], d["beta_or_b"], d_o.cuda(), ws,
+                                    w=d["w"], g=d["g"], state_in=d["state_in"],
+                                    d_state_out=d_sT.cuda()) for _ in range(4)]
+    torch.cuda.synchronize()
+    for n in NAMES:
+        for r in runs[1:]:
+            assert torch.equal(runs[0][n], r[n]), n
+        for r in saved[1:]:
+            assert torch.equal(saved[0][n], r[n]), n
+        assert relerr(saved[0][n], runs[0][n]) <= 2e-2, n
+
+
 def test_backward_full_size_sampled_heads():
     """The GDN-2 B8 T4096 H16 d128 shape as bench.py launches it: two (sequence,
     head) pairs recomputed by the oracle on their own."""
