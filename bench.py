@@ -298,10 +298,16 @@ def single_workload(gdn, synth, torch, dev, name, steps, warmup):
         ms = ev[0].elapsed_time(ev[1]) / steps
         return {"workload": name, "ms": round(ms, 4),
                 "tokens_per_s": round(vcfg.total_T / (ms * 1e-3), 1)}
-    base = name[:-len("_mamba2_gates")] if name.endswith("_mamba2_gates") else name
+    mamba2 = name.endswith("_mamba2_gates")
+    fp32g = name.endswith("_fp32_gates")
+    base = name[:-len("_mamba2_gates")] if mamba2 else (name[:-len("_fp32_gates")] if fp32g else name)
     cfg = synth.CONFIGS[base]
+    if fp32g:
+        cfg = synth.ChunkConfig(base, B=cfg.B, T=cfg.T, Hk=cfg.Hk, Hv=cfg.Hv, dk=cfg.dk, dv=cfg.dv,
+                                channel=cfg.channel, io_dtype=cfg.io_dtype,
+                                gate_dtype=torch.float32, seed=cfg.seed)
     inp = synth.chunk_inputs(cfg, device="cuda")
-    if base != name:
+    if mamba2:
         g, beta, w = realistic_gates(gdn, synth, torch, cfg)
         inp["g"], inp["beta_or_b"] = g.reshape(inp["g"].shape), beta.reshape(inp["g"].shape)
         if cfg.channel:
@@ -709,7 +715,8 @@ def main():
                     help="cap on oracle threads (the box's CPU share)")
     ap.add_argument("--workload", default=None,
                     help="time only gdn_chunk_fwd on this workload (a key of synth.CONFIGS, "
-                         "optionally with the suffix _mamba2_gates) and print its timing; "
+                         "optionally with the suffix _mamba2_gates or _fp32_gates) and print "
+                         "its timing; "
                          "for profiling one kernel in isolation")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward row (gdn_backward and the saved-state pair) "

@@ -353,36 +353,42 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       // addressing: a wave-uniform 64-bit base per sub-block plus a per-lane
       // 32-bit offset.  A sub-block that is not whole (the last chunk; it may
       // even start past the end) clamps absolute token indices to the last
-      // token instead.
-      auto load = [&](int64_t ci) {
+      // token instead.  load_tok issues token i's q, k and b (qkb) and/or g
+      // (gg).  With bf16 gates each register is reloaded for the next chunk as
+      // soon as its values have been consumed, so the loads have the element
+      // work to land (measured: 7 % on the GDN-2 B8 shape); fp32 gates, whose
+      // raw registers are twice as wide, load after the element work (early,
+      // they spilled 60 VGPRs and took 45 % longer).
+      auto load_tok = [&](int64_t ci, int i, bool qkb, bool gg) {
         const int64_t t0 = ci * kC + kSB * pw;          // first token of the sub-block
         if (t0 + kSB <= Tn) {                           // wave-uniform
           const uint64_t tu = (uint64_t)t0;
-          const char* cq = bq + tu * qk_tok;
-          const char* ck = bk + tu * qk_tok;
-          const char* cb = bbc + tu * gb_tok;
-          const char* cg2 = bgc + tu * gg_tok;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t tl = (uint32_t)(4 * qd + i);
-            ld_raw<QB>(cq + (tl * qk_tok + oq), rq[i]);
-            ld_raw<QB>(ck + (tl * qk_tok + oq), rk[i]);
-            ld_raw<GB>(cb + (tl * gb_tok + og), rb[i]);
-            if constexpr (HAS_G) ld_raw<GB>(cg2 + (tl * gg_tok + og), rg[i]);
+          const uint32_t tl = (uint32_t)(4 * qd + i);
+          if (qkb) {
+            ld_raw<QB>(bq + tu * qk_tok + (tl * qk_tok + oq), rq[i]);
+            ld_raw<QB>(bk + tu * qk_tok + (tl * qk_tok + oq), rk[i]);
+            ld_raw<GB>(bbc + tu * gb_tok + (tl * gb_tok + og), rb[i]);
           }
+          if constexpr (HAS_G)
+            if (gg) ld_raw<GB>(bgc + tu * gg_tok + (tl * gg_tok + og), rg[i]);
         } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            int64_t t = t0 + 4 * qd + i;
-            t = t < Tn - 1 ? t : Tn - 1;
-            const uint64_t tu = (uint64_t)t;
+          int64_t t = t0 + 4 * qd + i;
+          t = t < Tn - 1 ? t : Tn - 1;
+          const uint64_t tu = (uint64_t)t;
+          if (qkb) {
             ld_raw<QB>(bq + (tu * qk_tok + oq), rq[i]);
             ld_raw<QB>(bk + (tu * qk_tok + oq), rk[i]);
             ld_raw<GB>(bbc + (tu * gb_tok + og), rb[i]);
-            if constexpr (HAS_G) ld_raw<GB>(bgc + (tu * gg_tok + og), rg[i]);
           }
+          if constexpr (HAS_G)
+            if (gg) ld_raw<GB>(bgc + (tu * gg_tok + og), rg[i]);
         }
       };
+      auto load = [&](int64_t ci) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_tok(ci, i, true, true);
+      };
+      constexpr bool kEarly = sizeof(GT) == 2;
       // raw gates: A_log and dt_bias of the lane's channels (read where used)
       const float* pA = RAW && p.A_log ? p.A_log + hv * DK + ch0 : nullptr;
       const float* pD = RAW && p.dt_bias ? p.dt_bias + hv * DK + ch0 : nullptr;
@@ -485,6 +491,12 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         };
         scan(false);
         if (__any(!(worst <= kRange))) scan(true);
+        // the next chunk's g (the last chunk re-reads itself)
+        const int64_t cn = ci + 1 < nchunks ? ci + 1 : ci;
+        if constexpr (HAS_G && kEarly) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) load_tok(cn, i, false, true);
+        }
         // gated operands, token by token; each operand row of the lane's
         // CPL channels goes out as one store.  M waits in registers until the
         // L rows it shares storage with have been read by the Gram products.
@@ -498,6 +510,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           unpack<T, CPL>(rq[i], qv);
           unpack<T, CPL>(rk[i], kv);
           unpack<GT, CPL>(rb[i], bv);
+          if constexpr (kEarly) load_tok(cn, i, true, false);   // the next chunk's q, k, b
           if constexpr (RAW) {
 #pragma unroll
             for (int e = 0; e < CPL; ++e) bv[e] = sigmoid_f(bv[e]);   // absent tokens: k = 0
@@ -539,8 +552,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           st_words<CPL / 2>(sR + B::at(r, ch0), wR);
           if (qd < 2) st_words<CPL / 2>(sR2 + B::at(r, ch0), wR2);
         }
-        // next chunk's raw inputs (the last chunk re-reads itself)
-        load(ci + 1 < nchunks ? ci + 1 : ci);
+        if constexpr (!kEarly) load(cn);   // the next chunk's raw inputs
 
         // Gram blocks; L carries the sign, so L . R = -A = N.  Layouts
         // (lane = 16 g + j):
