@@ -87,35 +87,64 @@ struct Blk {
   static constexpr int NCH = DK / 8;
   static constexpr int BYTES = 16 * DK * 2;
   static constexpr bool kWide = NCH >= 16;
-  __device__ static int sw(int r) {
+  __host__ __device__ static constexpr int sw(int r) {
     if constexpr (kWide) return 4 * ((r >> 2) ^ (r & 3)) + (r >> 2);
     else return (r >> 1) % NCH;
   }
-  __device__ static int at(int r, int c) { return r * DK + ((((c >> 3) ^ sw(r))) << 3) + (c & 7); }
-  __device__ static int ax(int r, int c) {
+  __host__ __device__ static constexpr int at(int r, int c) {
+    return r * DK + ((((c >> 3) ^ sw(r))) << 3) + (c & 7);
+  }
+  __host__ __device__ static constexpr int ax(int r, int c) {
     if constexpr (kWide) return r * DK + ((((c >> 3) ^ r)) << 3) + (c & 7);
     else return at(r, c);
   }
-  __device__ static int ath(int r, int c) {
+  __host__ __device__ static constexpr int ath(int r, int c) {
     if constexpr (kWide) return at(r, c) ^ (((r >> 2) & 1) << 2);
     else return at(r, c);
   }
   // does row r hold its chunks' halves exchanged (ath)?
-  __device__ static bool half_swapped(int r) { return kWide && ((r >> 2) & 1); }
+  __host__ __device__ static constexpr bool half_swapped(int r) { return kWide && ((r >> 2) & 1); }
 };
 
 // Element (r, c) of a [64][64] bf16 tile of v or o rows (token r, column c
 // of the workgroup's slice): the 32-byte column segments of a row are
 // XOR-permuted by r / 2, so that accesses of 4 rows x 16 columns (the
 // transposing reads of v, the output fragments) spread over the banks.
-__device__ __forceinline__ int vo_at(int r, int c) {
+__host__ __device__ constexpr int vo_at(int r, int c) {
   return r * 64 + (((c >> 4) ^ ((r >> 1) & 3)) << 4) + (c & 15);
 }
 
 // Element (r, c) of a 16x16 bf16 block (T, P), read and written as four
 // consecutive columns per lane: the 4-column group is XOR-permuted by r / 4
 // (conflict-free 8-byte accesses for lane 16 g + j at row j, group g).
-__device__ __forceinline__ int tp_at(int r, int c) { return r * 16 + (((c >> 2) ^ ((r >> 2) & 3)) << 2) + (c & 3); }
+__host__ __device__ constexpr int tp_at(int r, int c) {
+  return r * 16 + (((c >> 2) ^ ((r >> 2) & 3)) << 2) + (c & 3);
+}
+
+// Compile-time check of a placement: every (row, column) of a ROWS x COLS
+// block lands inside the block, on an element of its own (a permutation), so
+// no access through it can leave its LDS block or alias another element.
+template <int ROWS, int COLS, typename F>
+constexpr bool is_permutation(F f) {
+  bool seen[ROWS * COLS] = {};
+  for (int r = 0; r < ROWS; ++r)
+    for (int c = 0; c < COLS; ++c) {
+      const int o = f(r, c);
+      if (o < 0 || o >= ROWS * COLS || seen[o]) return false;
+      seen[o] = true;
+    }
+  return true;
+}
+template <int DK>
+constexpr bool blk_placements_ok() {
+  using B = Blk<DK>;
+  return is_permutation<16, DK>([](int r, int c) { return B::at(r, c); }) &&
+         is_permutation<16, DK>([](int r, int c) { return B::ax(r, c); }) &&
+         is_permutation<16, DK>([](int r, int c) { return B::ath(r, c); });
+}
+static_assert(blk_placements_ok<64>() && blk_placements_ok<128>(), "operand block placements");
+static_assert(is_permutation<64, 64>([](int r, int c) { return vo_at(r, c); }), "v/o tile placement");
+static_assert(is_permutation<16, 16>([](int r, int c) { return tp_at(r, c); }), "T/P block placement");
 
 template <int DK, bool CHANNEL>
 struct SbLds {
@@ -138,6 +167,16 @@ struct SbLds {
   static constexpr int PRIV = CHANNEL ? 5 * BLK / 2 : 0;
   static constexpr int kTotal = kPriv + 4 * PRIV;
   static_assert(kTotal <= 160 * 1024, "LDS budget");
+  // every region starts 16-byte aligned (whole-chunk accesses) and ends
+  // before the next begins
+  static_assert(kOps % 16 == 0 && kT % 16 == 0 && kP % 16 == 0 && kVec % 16 == 0 &&
+                    kFlag % 16 == 0 && kVt % 16 == 0 && kOt % 16 == 0 && SLOT % 16 == 0 &&
+                    kPriv % 16 == 0 && PRIV % 16 == 0,
+                "LDS regions 16-byte aligned");
+  static_assert(kOps + NOPS * 4 * BLK <= kT && kT + 4 * TPB <= kP && kP + 4 * TPB <= kVec &&
+                    kVec + VEC <= kFlag && kFlag + 16 <= kVt && kVt + VO <= kOt &&
+                    kOt + VO <= SLOT && 2 * SLOT <= kPriv,
+                "LDS regions disjoint");
 };
 
 // Scalar-gate factor arrays of one sub-block, [6][16] floats.
