@@ -395,9 +395,10 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       // token instead.  load_tok issues token i's q, k and b (qkb) and/or g
       // (gg).  With bf16 gates each register is reloaded for the next chunk as
       // soon as its values have been consumed, so the loads have the element
-      // work to land (measured: 7 % on the GDN-2 B8 shape); fp32 gates, whose
-      // raw registers are twice as wide, load after the element work (early,
-      // they spilled 60 VGPRs and took 45 % longer).
+      // work to land (measured: 7 % on the GDN-2 B8 shape).  With fp32 gates,
+      // whose raw registers are twice as wide, only q and k reload early and b
+      // and g after the element work (all four early spilled 60 VGPRs and took
+      // 45 % longer; q and k early gained 3.6 %).
       auto load_tok = [&](int64_t ci, int i, bool qkb, bool gg) {
         const int64_t t0 = ci * kC + kSB * pw;          // first token of the sub-block
         if (t0 + kSB <= Tn) {                           // wave-uniform
@@ -428,6 +429,26 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         for (int i = 0; i < 4; ++i) load_tok(ci, i, true, true);
       };
       constexpr bool kEarly = sizeof(GT) == 2;
+      // fp32 gates: q and k of token i early, b and g after the element work
+      auto load_qk_tok = [&](int64_t ci, int i) {
+        const int64_t t0 = ci * kC + kSB * pw;
+        int64_t t = t0 + 4 * qd + i;
+        t = t < Tn - 1 ? t : Tn - 1;
+        const uint64_t tu = (uint64_t)t;
+        ld_raw<QB>(bq + (tu * qk_tok + oq), rq[i]);
+        ld_raw<QB>(bk + (tu * qk_tok + oq), rk[i]);
+      };
+      auto load_bg = [&](int64_t ci) {
+        const int64_t t0 = ci * kC + kSB * pw;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int64_t t = t0 + 4 * qd + i;
+          t = t < Tn - 1 ? t : Tn - 1;
+          const uint64_t tu = (uint64_t)t;
+          ld_raw<GB>(bbc + (tu * gb_tok + og), rb[i]);
+          if constexpr (HAS_G) ld_raw<GB>(bgc + (tu * gg_tok + og), rg[i]);
+        }
+      };
       // raw gates: A_log and dt_bias of the lane's channels (read where used)
       const float* pA = RAW && p.A_log ? p.A_log + hv * DK + ch0 : nullptr;
       const float* pD = RAW && p.dt_bias ? p.dt_bias + hv * DK + ch0 : nullptr;
@@ -550,6 +571,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           unpack<T, CPL>(rk[i], kv);
           unpack<GT, CPL>(rb[i], bv);
           if constexpr (kEarly) load_tok(cn, i, true, false);   // the next chunk's q, k, b
+          else load_qk_tok(cn, i);                              // the next chunk's q, k
           if constexpr (RAW) {
 #pragma unroll
             for (int e = 0; e < CPL; ++e) bv[e] = sigmoid_f(bv[e]);   // absent tokens: k = 0
@@ -591,7 +613,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           st_words<CPL / 2>(sR + B::at(r, ch0), wR);
           if (qd < 2) st_words<CPL / 2>(sR2 + B::at(r, ch0), wR2);
         }
-        if constexpr (!kEarly) load(cn);   // the next chunk's raw inputs
+        if constexpr (!kEarly) load_bg(cn);   // the next chunk's b and g
 
         // Gram blocks; L carries the sign, so L . R = -A = N.  Layouts
         // (lane = 16 g + j):
