@@ -135,17 +135,17 @@ def time_cold(fn, torch, flush, steps, warmup):
     return times[len(times) // 2], times[0], warm
 
 
-def sub_block_paths(g, channel, torch, sub=16, limit=110.0, c01_limit=124.0, floor=15.0):
+def sub_block_paths(g, channel, torch, sub=16, limit=110.0, floor=13.0):
     """Fractions of (sequence, value head, 16-token sub-block) units that the
     chunk kernel scans a second time with floored decays, and that it runs on
     its exact token path, from the log-decay tensor g ([B, T, H_v, d_k] or
     [B, T, H_v]) and the kernel's own criterion.  With G the cumulative
-    log2-decay from the sub-block start, channel gates need |G - m_h| <= limit
-    (m_h = G at token 3 for the first half, at token 11 for the second),
-    m_0 - m_1 <= c01_limit and the rising-state bounds; a sub-block that fails
-    is scanned again with every per-token log2-decay raised to -floor, and
-    takes the token path only if it still fails.  Scalar gates: no rise
-    G_t - min_{s<=t} G_s, G_t or G_15 - G_t above the limit (no floor)."""
+    log2-decay from the sub-block start, channel gates need |G - m| <= limit
+    (m = G at token 7) and the rising-state bounds (m, G_15 - m and G_15 at
+    most 10); a sub-block that fails is scanned again with every per-token
+    log2-decay raised to -floor, and takes the token path only if it still
+    fails.  Scalar gates: no rise G_t - min_{s<=t} G_s, G_t or G_15 - G_t
+    above the limit (no floor)."""
     B, T = g.shape[0], g.shape[1]
     Tb = (T // sub) * sub
     x = g[:, :Tb].float() * 1.4426950408889634
@@ -157,11 +157,9 @@ def sub_block_paths(g, channel, torch, sub=16, limit=110.0, c01_limit=124.0, flo
         G = torch.cumsum(lx, dim=2)
         g15 = G[:, :, 15:16]
         if channel:
-            m0, m1 = G[:, :, 3:4], G[:, :, 11:12]
-            mh = torch.cat([m0.expand(-1, -1, 8, -1, -1), m1.expand(-1, -1, 8, -1, -1)], dim=2)
-            worst = torch.maximum((G - mh).abs(), torch.maximum(mh, g15 - mh) + (limit - 10.0))
-            worst = torch.maximum(worst, torch.maximum(m1 - m0, g15) + (limit - 10.0))
-            worst = torch.maximum(worst, (m0 - m1) + (limit - c01_limit))
+            m = G[:, :, 7:8]
+            worst = torch.maximum((G - m).abs(),
+                                  torch.maximum(torch.maximum(m, g15 - m), g15) + (limit - 10.0))
         else:
             rise = G - torch.cummin(G, dim=2).values
             worst = torch.maximum(torch.maximum(G, g15 - G), rise)

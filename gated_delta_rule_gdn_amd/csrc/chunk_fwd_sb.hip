@@ -19,21 +19,21 @@
 // state-side operands never overflow however strong the decay.
 //
 // Inside a diagonal block, A[t,s] = sum_c e_t,c k_s,c exp(G_t,c - G_s,c)
-// (s < t) and P[t,s] (s <= t) are MFMA products of factored operands.  Each
-// 8-token half uses its own reference, the cumulative log-decay at its 4th
-// token (m0 = G_3, m1 = G_11), so a factor spans at most four tokens of decay:
-//   L = -e exp(G - m_h),  M = q exp(G - m_h),  R = k exp(m_h - G)
-// gives the two diagonal 8x8 quadrants; the lower-left quadrant (t >= 8 > s)
-// pairs L (reference m1) with R' = R exp(m1 - m0) = k exp(m1 - G) <= 1.
-// The factors must stay finite and exp(m1 - m0) a normal float.  A sub-block
-// whose decays break that (some |G - m_h| > kRange, or m0 - m1 > kC01Min,
-// log2 units) is redone with every per-token decay raised to at least
-// 2^-kFloor: a term that crosses such a token then carries 2^-15 in place of
-// a smaller true factor, a change of at most 2^-15 of its undecayed size,
-// well under the rounding of the bf16 operands (2^-9).  Floored, four tokens
-// span at most 60 and eight at most 120, so the retry always fits when
-// alpha <= 1; only a rising state (alpha > 1) can still leave the range, and
-// such a sub-block runs the exact token recurrence.
+// (s < t) and P[t,s] (s <= t) are MFMA products of factored operands around
+// one reference per channel, the cumulative log-decay at the block's middle
+// token (m = G_7), so a factor spans at most eight tokens of decay:
+//   L = -e exp(G - m),  M = q exp(G - m),  R = k exp(m - G)
+// and A = L R^T, P = M R^T below the diagonal (each product there is
+// exp(G_t - G_s) <= 1 times the operands; the products above it are never
+// used).  The factors must stay finite: a sub-block whose decays put some
+// |G - m| above kRange (log2 units) is redone with every per-token decay
+// raised to at least 2^-kFloor.  A term that crosses such a token then
+// carries 2^-kFloor = 2^-13 in place of a smaller true factor, a change of at
+// most 2^-13 of its undecayed size, well under the rounding of the bf16
+// operands (2^-9).  Floored, eight tokens span at most 104 < kRange, so the
+// retry always fits when alpha <= 1; only a rising state (alpha > 1) can
+// still leave the range, and such a sub-block runs the exact token
+// recurrence.
 //
 // With scalar gates (Gated DeltaNet, DeltaNet) the decay factors out of the
 // Gram matrices exactly: A[t,s] = beta_t exp(G_t - G_s) (k_t . k_s), applied
@@ -66,9 +66,9 @@ struct IntTag {
 constexpr int kSB = 16;           // tokens per sub-block
 constexpr int kRankMax = 256;     // packed sequences ranked by length in the kernel
 constexpr int kSbThreads = 512;   // 4 consumer + 4 producer waves
-constexpr float kRange = 110.f;   // largest |G - m_h| (log2) of the factored form
-constexpr float kC01Min = 124.f;  // largest m0 - m1 (log2): exp(m1 - m0) stays normal
-constexpr float kFloor = 15.f;    // per-token decay floor (log2) of the second scan
+constexpr float kRange = 110.f;   // largest |G - m| (log2) of the factored form
+constexpr float kFloor = 13.f;    // per-token decay floor (log2) of the second scan
+static_assert(8.f * kFloor <= kRange, "a floored sub-block fits the factored form");
 
 // One [16][DK] bf16 operand block.  Rows are DK contiguous channels in
 // 16-byte chunks of 8; the chunks of a row are XOR-permuted by the row, in
@@ -163,8 +163,8 @@ struct SbLds {
   static constexpr int kVt = kFlag + 16;
   static constexpr int kOt = kVt + VO;
   static constexpr int SLOT = kOt + VO;
-  static constexpr int kPriv = 2 * SLOT;         // channel: per producer wave L|M, R, R'
-  static constexpr int PRIV = CHANNEL ? 5 * BLK / 2 : 0;
+  static constexpr int kPriv = 2 * SLOT;         // channel: per producer wave L, M, R
+  static constexpr int PRIV = CHANNEL ? 3 * BLK : 0;
   static constexpr int kTotal = kPriv + 4 * PRIV;
   static_assert(kTotal <= 160 * 1024, "LDS budget");
   // every region starts 16-byte aligned (whole-chunk accesses) and ends
@@ -193,6 +193,7 @@ __device__ __forceinline__ float quad_perm(float x, int pat) {
   int r;
   switch (pat) {
     case 0x00: r = __builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false); break;
+    case 0x55: r = __builtin_amdgcn_mov_dpp(v, 0x55, 0xf, 0xf, false); break;
     case 0x90: r = __builtin_amdgcn_mov_dpp(v, 0x90, 0xf, 0xf, false); break;
     case 0x44: r = __builtin_amdgcn_mov_dpp(v, 0x44, 0xf, 0xf, false); break;
     case 0xAA: r = __builtin_amdgcn_mov_dpp(v, 0xAA, 0xf, 0xf, false); break;
@@ -453,9 +454,9 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       const float* pA = RAW && p.A_log ? p.A_log + hv * DK + ch0 : nullptr;
       const float* pD = RAW && p.dt_bias ? p.dt_bias + hv * DK + ch0 : nullptr;
       T* priv = reinterpret_cast<T*>(smem + L::kPriv + pw * L::PRIV);
-      T* sLM = priv;              // L, then M (rows 0..15)
-      T* sR = priv + 16 * DK;     // R (rows 0..15)
-      T* sR2 = priv + 32 * DK;    // R' = R exp(m1 - m0), rows 0..7
+      T* sL = priv;               // L (rows 0..15)
+      T* sM = priv + 16 * DK;     // M
+      T* sR = priv + 32 * DK;     // R
 
       auto produce = [&](int64_t ci) {
         const int slot = (int)(ci & 1);
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         const bool partial = ci * kC + kSB * pw + kSB > Tn;   // wave-uniform
         const int64_t tq = ci * kC + kSB * pw + 4 * qd;       // first token of the lane
         (void)tq;
-        float G[4][CPL], mh[CPL], fln[CPL], fkh[CPL], c01[CPL];
+        float G[4][CPL], mh[CPL], fln[CPL], fkh[CPL];
         float worst;
         // cumulative log2-decay over the sub-block (4 tokens in-thread, then
         // an exclusive scan over the 4 token quads of the lane quad), the
@@ -527,26 +528,19 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
             const float excl = s - tot;
 #pragma unroll
             for (int i = 0; i < 4; ++i) G[i][e] += excl;
-            const float m0 = quad_perm(G[3][e], 0x00);   // G at token 3
-            const float m1 = quad_perm(G[3][e], 0xAA);   // G at token 11
+            mh[e] = quad_perm(G[3][e], 0x55);            // G at token 7
             const float g15 = quad_perm(G[3][e], 0xFF);
-            mh[e] = qd < 2 ? m0 : m1;
             fln[e] = exp2_fast(mh[e]);
             fkh[e] = exp2_fast(g15 - mh[e]);
-            c01[e] = exp2_fast(m1 - m0);
             // channel decay of the whole sub-block (one lane per channel group)
             if (qd == 0) dvec[e] = exp2_fast(g15);
-            // the lane's tokens against their reference: |G - m_h| <= kRange
+            // the lane's tokens against the reference: |G - m| <= kRange
             const float hi = fmaxf(fmaxf(G[0][e], G[1][e]), fmaxf(G[2][e], G[3][e]));
             const float lo = fminf(fminf(G[0][e], G[1][e]), fminf(G[2][e], G[3][e]));
             worst = fmaxf(worst, fmaxf(hi - mh[e], mh[e] - lo));
             // per-channel factors that exceed 1 only when some g > 0; each
-            // may reach 2^10 so that no product of two factors overflows.
-            // exp(m1 - m0) stays a normal float (R' = R exp(m1 - m0) must
-            // not vanish while R is large).
-            worst = fmaxf(worst, fmaxf(fmaxf(mh[e], g15 - mh[e]), fmaxf(m1 - m0, g15)) +
-                                     (kRange - 10.f));
-            worst = fmaxf(worst, (m0 - m1) + (kRange - kC01Min));
+            // may reach 2^10 so that no product of two factors overflows
+            worst = fmaxf(worst, fmaxf(fmaxf(mh[e], g15 - mh[e]), g15) + (kRange - 10.f));
           }
         };
         scan(false);
@@ -558,12 +552,10 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
           for (int i = 0; i < 4; ++i) load_tok(cn, i, false, true);
         }
         // gated operands, token by token; each operand row of the lane's
-        // CPL channels goes out as one store.  M waits in registers until the
-        // L rows it shares storage with have been read by the Gram products.
+        // CPL channels goes out as one store
         T* sLn = opblk(slot, 0, pw);
         T* sQb = opblk(slot, 1, pw);
         T* sKh = opblk(slot, 2, pw);
-        uint32_t mpk[4][CPL / 2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float qv[CPL], kv[CPL], bv[CPL];
@@ -576,7 +568,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
 #pragma unroll
             for (int e = 0; e < CPL; ++e) bv[e] = sigmoid_f(bv[e]);   // absent tokens: k = 0
           }
-          uint32_t wLn[CPL / 2], wQb[CPL / 2], wKh[CPL / 2], wL[CPL / 2], wR[CPL / 2], wR2[CPL / 2];
+          uint32_t wLn[CPL / 2], wQb[CPL / 2], wKh[CPL / 2], wL[CPL / 2], wM[CPL / 2], wR[CPL / 2];
 #pragma unroll
           for (int e2 = 0; e2 < CPL / 2; ++e2) {
             float Lv[2], Mv[2], Rv[2];
@@ -594,10 +586,9 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
             wLn[e2] = pack_bf16x2(Lv[0] * fln[e], Lv[1] * fln[e + 1]);
             wQb[e2] = pack_bf16x2(Mv[0] * fln[e], Mv[1] * fln[e + 1]);
             wKh[e2] = pack_bf16x2(Rv[0] * fkh[e], Rv[1] * fkh[e + 1]);
-            wR2[e2] = pack_bf16x2(Rv[0] * c01[e], Rv[1] * c01[e + 1]);
             wL[e2] = pack_bf16x2(Lv[0], Lv[1]);
+            wM[e2] = pack_bf16x2(Mv[0], Mv[1]);
             wR[e2] = pack_bf16x2(Rv[0], Rv[1]);
-            mpk[i][e2] = pack_bf16x2(Mv[0], Mv[1]);
           }
           const int r = 4 * qd + i;
           st_words<CPL / 2>(sLn + B::ax(r, ch0), wLn);
@@ -609,59 +600,40 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
             }
           }
           st_words<CPL / 2>(sKh + B::at(r, ch0), wKh);
-          st_words<CPL / 2>(sLM + B::at(r, ch0), wL);
+          st_words<CPL / 2>(sL + B::at(r, ch0), wL);
+          st_words<CPL / 2>(sM + B::at(r, ch0), wM);
           st_words<CPL / 2>(sR + B::at(r, ch0), wR);
-          if (qd < 2) st_words<CPL / 2>(sR2 + B::at(r, ch0), wR2);
         }
         if constexpr (!kEarly) load_bg(cn);   // the next chunk's b and g
 
         // Gram blocks; L carries the sign, so L . R = -A = N.  Layouts
         // (lane = 16 g + j):
-        //   ac = L_{4g+i} . R_j     = N[t][s], t = 4g+i, s = j
-        //   ar = R_{4g+i} . L_j     = N[t][s], t = j, s = 4g+i
-        //   a2c, a2r: the same with R' (lower-left quadrant t >= 8 > s:
-        //     L there has the reference m1, and R' = k exp(m1 - G) <= 1)
-        //   p1 = R_{4g+i} . M_j, p2 = R'_{4g+i} . M_j = P[t][s], t = j, s = 4g+i
-        Frag8<T> rf[KB], r2f[KB];
+        //   ac = L_{4g+i} . R_j = N[t][s], t = 4g+i, s = j
+        //   ar = R_{4g+i} . L_j = N[t][s], t = j, s = 4g+i
+        //   pr = R_{4g+i} . M_j = P[t][s], t = j, s = 4g+i
+        // (this wave's LDS operations run in order, so its own stores above
+        // complete before these reads)
+        f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ar = ac, pr = ac;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          rf[kb] = ld_frag8<T>(sR + B::at(j, 32 * kb + 8 * g));
-          r2f[kb] = ld_frag8<T>(sR2 + B::at(j & 7, 32 * kb + 8 * g));
-        }
-        f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ar = ac, a2c = ac, a2r = ac, p1 = ac, p2 = ac;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const Frag8<T> lf = ld_frag8<T>(sLM + B::at(j, 32 * kb + 8 * g));
-          mma32(ac, lf, rf[kb]);
-          mma32(ar, rf[kb], lf);
-          mma32(a2c, lf, r2f[kb]);
-          mma32(a2r, r2f[kb], lf);
-        }
-        // M replaces L in the shared rows (this wave's LDS operations run in
-        // order, so the L fragment reads above complete first)
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st_words<CPL / 2>(sLM + B::at(4 * qd + i, ch0), mpk[i]);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const Frag8<T> mf = ld_frag8<T>(sLM + B::at(j, 32 * kb + 8 * g));
-          mma32(p1, rf[kb], mf);
-          mma32(p2, r2f[kb], mf);
+          const Frag8<T> rf = ld_frag8<T>(sR + B::at(j, 32 * kb + 8 * g));
+          const Frag8<T> lf = ld_frag8<T>(sL + B::at(j, 32 * kb + 8 * g));
+          const Frag8<T> mf = ld_frag8<T>(sM + B::at(j, 32 * kb + 8 * g));
+          mma32(ac, lf, rf);
+          mma32(ar, rf, lf);
+          mma32(pr, rf, mf);
         }
         // N strictly lower in both layouts; P lower incl. diagonal.  Selects
-        // (not products) drop the unused quadrants, which may hold inf or NaN
-        // from the factors' products.
+        // (not products) drop the entries above the diagonal, whose factors'
+        // products may be inf or NaN.
         Frag4<float> nr, nc;
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tc = 4 * g + i;  // t of ac, s of ar
-          const float av = (tc >= 8 && j < 8) ? a2c[i] : ac[i];
-          nc.v[i] = (j < tc) ? av : 0.f;
-          const float bvv = (j >= 8 && tc < 8) ? a2r[i] : ar[i];
-          nr.v[i] = (tc < j) ? bvv : 0.f;
-          const float pp = (j >= 8 && tc < 8) ? p2[i] : p1[i];
-          pv[i] = (tc <= j) ? pp : 0.f;
+          nc.v[i] = (j < tc) ? ac[i] : 0.f;
+          nr.v[i] = (tc < j) ? ar[i] : 0.f;
+          pv[i] = (tc <= j) ? pr[i] : 0.f;
         }
         float nmax;
         const Frag4<float> tt = unit_lower_inverse(nr, nc, g, j, nmax);

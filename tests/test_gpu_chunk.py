@@ -186,11 +186,12 @@ def test_sub_block_transitions_bf16(channel):
 
 
 def test_reference_ratio_underflow_channel():
-    """Channel gates whose decays keep every |G - m_h| in range while
-    exp(m1 - m0) leaves the normal floats: log2-decay -25 at tokens 4-7 and
-    9-11 of a sub-block, none at token 8.  The pair (8, 7) crosses no decay,
-    so its term is whole, and q_8 = k_7 = k_8 makes it carry o_8.  The
-    kernel must not lose it through the factor exp(m1 - m0) = 2^-175."""
+    """Channel gates with strong decays on both sides of an undecayed pair:
+    log2-decay -25 at tokens 4-7 and 9-11 of a sub-block, none at token 8,
+    so that |G - m| reaches 100 around the reference m = G_7 (still inside
+    the factored range) and the operands' factors span 2^-100 .. 2^75.  The
+    pair (8, 7) crosses no decay, so its term is whole, and q_8 = k_7 = k_8
+    makes it carry o_8: the factored products must keep it."""
     cfg = _cfg(io=torch.bfloat16, T=80, channel=True, B=2, Hk=1, Hv=2)
     inp = to_dev(synth.chunk_inputs(cfg))
     g = inp["g"].clone()
@@ -203,7 +204,7 @@ def test_reference_ratio_underflow_channel():
         k[:, base + 7] = k[:, base + 8]
         inp["q"][:, base + 8] = k[:, base + 8]
     inp["g"] = g
-    _check(inp, TOL_BF16, label="exp(m1 - m0) underflow")
+    _check(inp, TOL_BF16, label="strong decays around an undecayed pair")
     o, _ = _gpu(inp)
     o_ref, _ = _ref(inp)
     for t in (8, 56):
