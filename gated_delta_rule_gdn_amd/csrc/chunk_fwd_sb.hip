@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
         const bool partial = ci * kC + kSB * pw + kSB > Tn;   // wave-uniform
         const int64_t tq = ci * kC + kSB * pw + 4 * qd;       // first token of the lane
         (void)tq;
-        float G[4][CPL], mh[CPL], fln[CPL], fkh[CPL];
+        float G[4][CPL], fln[CPL], fkh[CPL];
         float worst;
         // cumulative log2-decay over the sub-block (4 tokens in-thread, then
         // an exclusive scan over the 4 token quads of the lane quad), the
@@ -526,21 +526,23 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
             const float sh2 = quad_perm(s, 0x44);
             s = s + (qd >= 2 ? sh2 : 0.f);
             const float excl = s - tot;
+            const float g3 = G[3][e] + excl;             // G at the lane's last token
+            const float m = quad_perm(g3, 0x55);         // the reference, G at token 7
+            const float g15 = quad_perm(g3, 0xFF);
+            // from here on G holds the exponents G - m of the factors
+            const float c = excl - m;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) G[i][e] += excl;
-            mh[e] = quad_perm(G[3][e], 0x55);            // G at token 7
-            const float g15 = quad_perm(G[3][e], 0xFF);
-            fln[e] = exp2_fast(mh[e]);
-            fkh[e] = exp2_fast(g15 - mh[e]);
+            for (int i = 0; i < 4; ++i) G[i][e] += c;
+            fln[e] = exp2_fast(m);
+            fkh[e] = exp2_fast(g15 - m);
             // channel decay of the whole sub-block (one lane per channel group)
-            if (qd == 0) dvec[e] = exp2_fast(g15);
+            if (qd == 0) dvec[e] = fln[e] * fkh[e];
             // the lane's tokens against the reference: |G - m| <= kRange
-            const float hi = fmaxf(fmaxf(G[0][e], G[1][e]), fmaxf(G[2][e], G[3][e]));
-            const float lo = fminf(fminf(G[0][e], G[1][e]), fminf(G[2][e], G[3][e]));
-            worst = fmaxf(worst, fmaxf(hi - mh[e], mh[e] - lo));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) worst = fmaxf(worst, fabsf(G[i][e]));
             // per-channel factors that exceed 1 only when some g > 0; each
             // may reach 2^10 so that no product of two factors overflows
-            worst = fmaxf(worst, fmaxf(fmaxf(mh[e], g15 - mh[e]), g15) + (kRange - 10.f));
+            worst = fmaxf(worst, fmaxf(fmaxf(m, g15 - m), g15) + (kRange - 10.f));
           }
         };
         scan(false);
@@ -575,7 +577,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int e = 2 * e2 + h;
-              const float x = G[i][e] - mh[e];
+              const float x = G[i][e];
               const float e1 = exp2_fast(x);
               const float e2v = exp2_fast(-x);
               Lv[h] = -(bv[e] * kv[e]) * e1;
