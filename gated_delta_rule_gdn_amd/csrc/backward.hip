@@ -377,6 +377,7 @@ __global__ __launch_bounds__(DK * 4) void bwd_kernel(BwdArgs p) {
     RevLds<DK, TO> rev;
   };
   __shared__ Smem sm;
+  lds_nan_fill(&sm, (int)sizeof(Smem));
 
   const int64_t head = blockIdx.x;          // b * Hv + hv
   const int cb = blockIdx.y;
@@ -1250,5 +1251,9 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
   if (a.gate == DType::F32) return launch_bwd_types<bf16, float>(a, stream);
   return launch_bwd_types<bf16, bf16>(a, stream);
 }
+
+#ifdef GDN_CHECK
+unsigned check_violations_backward() { return take_check_violations(); }
+#endif
 
 }  // namespace gdn

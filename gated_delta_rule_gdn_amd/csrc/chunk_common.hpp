@@ -115,6 +115,7 @@ __device__ __forceinline__ float word_f32(uint32_t w) {
 // Store 4 consecutive fp32 values as T.
 template <typename T>
 __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {
+  lds_check(p, 4 * (int)sizeof(T));
   if constexpr (sizeof(T) == 2) {
     bf16x4 h = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
     *reinterpret_cast<bf16x4*>(p) = h;
@@ -125,6 +126,7 @@ __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {
 
 template <typename T>
 __device__ __forceinline__ Frag8<T> ld_frag8(const T* p) {
+  lds_check(p, 8 * (int)sizeof(T));
   Frag8<T> f;
   if constexpr (sizeof(T) == 2) {
     f.v = *reinterpret_cast<const bf16x8*>(p);
@@ -139,6 +141,7 @@ __device__ __forceinline__ Frag8<T> ld_frag8(const T* p) {
 
 template <typename T>
 __device__ __forceinline__ Frag4<T> ld_frag4(const T* p) {
+  lds_check(p, 4 * (int)sizeof(T));
   Frag4<T> f;
   if constexpr (sizeof(T) == 2) {
     f.v = *reinterpret_cast<const bf16x4*>(p);

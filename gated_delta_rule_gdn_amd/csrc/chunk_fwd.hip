@@ -90,6 +90,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(Params p) {
   static_assert(CPT % 4 == 0 && NWC >= 1 && NWC <= 4, "shape");
 
   __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+  lds_nan_fill(smem, L::kTotal);
   T* sLn = reinterpret_cast<T*>(smem + L::kLn);
   T* sM = reinterpret_cast<T*>(smem + L::kM);
   T* sR = reinterpret_cast<T*>(smem + L::kRK);
@@ -662,5 +663,9 @@ hipError_t launch_state_copy(const float* state_in, float* state_out, int64_t n,
   state_copy_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(state_in, state_out, n);
   return hipGetLastError();
 }
+
+#ifdef GDN_CHECK
+unsigned check_violations_chunk() { return take_check_violations(); }
+#endif
 
 }  // namespace gdn

@@ -225,6 +225,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // N packed words to LDS in one store (16 or 8 bytes).
 template <int N>
 __device__ __forceinline__ void st_words(bf16* p, const uint32_t* w) {
+  lds_check(p, 4 * N);
   if constexpr (N == 4) *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   else *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
 }
@@ -235,6 +236,7 @@ typedef short sb_v4s __attribute__((ext_vector_type(4)));
 // the lanes' 8-byte reads of 4 rows x 16 columns come back as lane l holding
 // column l of the 4 rows.
 __device__ __forceinline__ Frag4<bf16> ld_tr16(const bf16* p) {
+  lds_check(p, 8);
   const sb_v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) sb_v4s*)(p));
   Frag4<bf16> f;
@@ -259,6 +261,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   constexpr int NSB = kC / kSB;  // 4
 
   __shared__ __attribute__((aligned(16))) char smem[L::kTotal];
+  lds_nan_fill(smem, L::kTotal);
 
   const T* __restrict__ gq = static_cast<const T*>(p.q);
   const T* __restrict__ gk = static_cast<const T*>(p.k);
@@ -339,23 +342,35 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   const int j = lane & 15;
   const int g = lane >> 4;
 
+  // (the debug build checks every block index against the layout)
   auto opblk = [&](int slot, int op, int sb) -> T* {
+    check_true(slot >= 0 && slot < 2 && op >= 0 && op < L::NOPS && sb >= 0 && sb < NSB);
     return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kOps + (op * NSB + sb) * L::BLK);
   };
   auto tblk = [&](int slot, int sb) -> T* {
+    check_true(slot >= 0 && slot < 2 && sb >= 0 && sb < NSB);
     return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kT + sb * L::TPB);
   };
   auto pblk = [&](int slot, int sb) -> T* {
+    check_true(slot >= 0 && slot < 2 && sb >= 0 && sb < NSB);
     return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kP + sb * L::TPB);
   };
   auto vecp = [&](int slot) -> float* {
+    check_true(slot >= 0 && slot < 2);
     return reinterpret_cast<float*>(smem + slot * L::SLOT + L::kVec);
   };
   auto flagp = [&](int slot) -> int* {
+    check_true(slot >= 0 && slot < 2);
     return reinterpret_cast<int*>(smem + slot * L::SLOT + L::kFlag);
   };
-  auto vtile = [&](int slot) -> T* { return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kVt); };
-  auto otile = [&](int slot) -> T* { return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kOt); };
+  auto vtile = [&](int slot) -> T* {
+    check_true(!CHANNEL && slot >= 0 && slot < 2);
+    return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kVt);
+  };
+  auto otile = [&](int slot) -> T* {
+    check_true(!CHANNEL && slot >= 0 && slot < 2);
+    return reinterpret_cast<T*>(smem + slot * L::SLOT + L::kOt);
+  };
   const uint32_t v_tok = (uint32_t)(p.Hv * DV * 2);   // bytes per token of v (and o)
 
   const uint32_t qk_tok = (uint32_t)(p.Hk * DK * (int)sizeof(T));   // bytes per token
@@ -453,6 +468,7 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
       // raw gates: A_log and dt_bias of the lane's channels (read where used)
       const float* pA = RAW && p.A_log ? p.A_log + hv * DK + ch0 : nullptr;
       const float* pD = RAW && p.dt_bias ? p.dt_bias + hv * DK + ch0 : nullptr;
+      check_true(pw >= 0 && pw < 4);
       T* priv = reinterpret_cast<T*>(smem + L::kPriv + pw * L::PRIV);
       T* sL = priv;               // L (rows 0..15)
       T* sM = priv + 16 * DK;     // M
@@ -1302,5 +1318,24 @@ hipError_t launch_chunk_fwd_sb(const ChunkArgs& a, hipStream_t stream) {
   if (a.gate == DType::F32) return sb_dims<float>(a, stream);
   return sb_dims<bf16>(a, stream);
 }
+
+#ifdef GDN_CHECK
+unsigned check_violations_chunk_sb() { return take_check_violations(); }
+
+namespace {
+__global__ __launch_bounds__(64) void check_selftest_kernel(float* out) {
+  __shared__ float buf[64];
+  lds_nan_fill(buf, (int)sizeof buf);
+  const int l = (int)threadIdx.x;
+  out[l] = buf[l];                        // in bounds, never written
+  lds_check(buf + 64 + l, 4);             // one past the end: counted, not made
+}
+}  // namespace
+
+hipError_t launch_check_selftest(float* out, hipStream_t stream) {
+  check_selftest_kernel<<<1, 64, 0, stream>>>(out);
+  return hipGetLastError();
+}
+#endif
 
 }  // namespace gdn

@@ -67,6 +67,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   __shared__ float s_alpha[DK], s_ae[DK], s_aq[DK], s_k[DK];
   __shared__ float s_qk[WAVES];
   __shared__ float s_red[WAVES][CG][8];
+  lds_nan_fill(s_alpha, sizeof s_alpha);
+  lds_nan_fill(s_ae, sizeof s_ae);
+  lds_nan_fill(s_aq, sizeof s_aq);
+  lds_nan_fill(s_k, sizeof s_k);
+  lds_nan_fill(s_qk, sizeof s_qk);
+  lds_nan_fill(s_red, sizeof s_red);
 
   const IO* qh = q + (n * Hk + hk) * (int64_t)DK;
   const IO* kh = k + (n * Hk + hk) * (int64_t)DK;
@@ -212,5 +218,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.dk == 64 && a.dv == 128) return pick_gates<64, 128>(a, stream);
   return pick_gates<64, 64>(a, stream);
 }
+
+#ifdef GDN_CHECK
+unsigned check_violations_decode() { return take_check_violations(); }
+#endif
 
 }  // namespace gdn

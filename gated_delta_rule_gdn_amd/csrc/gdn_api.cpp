@@ -10,10 +10,28 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 
 #include "gdn_kernels.hpp"
 
 namespace {
+
+// Status of a call whose launches returned e.  The debug build (-DGDN_CHECK)
+// also waits for the work to finish and reads the kernels' LDS-check
+// counters (all modules, so that they are reset for the next call).
+gdn_status launched(hipError_t e) {
+  if (e != hipSuccess) return GDN_ERR_HIP;
+#ifdef GDN_CHECK
+  const unsigned long long v = (unsigned long long)gdn::check_violations_decode() +
+                               gdn::check_violations_chunk() + gdn::check_violations_chunk_sb() +
+                               gdn::check_violations_backward();
+  if (v != 0) {
+    fprintf(stderr, "libgdn_check: %llu LDS accesses outside the layout\n", v);
+    return GDN_ERR_CHECK;
+  }
+#endif
+  return GDN_OK;
+}
 
 struct Span {
   uintptr_t lo, hi;  // [lo, hi)
@@ -200,7 +218,7 @@ gdn_status run_backward(const BwdShape& d, const void* q, const void* k, const v
     if (!d_state_in || d_state_in == d_state_out) return GDN_OK;
     hipError_t e = gdn::launch_state_copy(d_state_out, d_state_in, S,
                                           static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return launched(e);
   }
   const int64_t rows = d.rows;
   st = check_pointers(rows, heads, d.Hk, d.Hv, d.dk, d.dv, d.io, d.gate, d.mode, q, k, v,
@@ -258,7 +276,7 @@ gdn_status run_backward(const BwdShape& d, const void* q, const void* k, const v
   a.d_state_in = d_state_in;
   a.phases = phases;
   hipError_t e = gdn::launch_backward(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  return launched(e);
 }
 
 // Checks of gdn_chunk_fwd's descriptor that come before any pointer is read.
@@ -335,7 +353,7 @@ gdn_status run_fwd_save(const BwdShape& bs, const void* q, const void* k, const 
   b.nblk = L.nblk;
   b.dq_out = b.dk_out = b.dv_out = b.db = b.dw = b.dg = b.d_state_in = nullptr;
   e = gdn::launch_backward(b, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  return launched(e);
 }
 
 }  // namespace
@@ -350,6 +368,7 @@ const char* gdn_status_string(gdn_status s) {
     case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG: invalid argument";
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: configuration not supported";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP runtime error at launch";
+    case GDN_ERR_CHECK: return "GDN_ERR_CHECK: LDS access outside the kernel's layout (debug build)";
   }
   return "GDN_ERR_UNKNOWN: unknown status code";
 }
@@ -374,7 +393,7 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
     if (!state_out || state_out == state_in) return GDN_OK;
     hipError_t e = gdn::launch_state_copy(state_in, state_out, heads * d->d_k * d->d_v,
                                           static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return launched(e);
   }
   st = check_pointers(rows, heads, d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype, d->gate_dtype,
                       d->gate_mode, q, k, v, beta_or_b, w, g, state_in, state_out, o, false);
@@ -388,7 +407,7 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
   a.state_in = state_in; a.state_out = state_out; a.o = o;
   hipError_t e = gdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  return launched(e);
 }
 
 gdn_status gdn_chunk_fwd_save(const gdn_fwd_desc* d, const void* q, const void* k,
@@ -455,7 +474,7 @@ gdn_status gdn_chunk_fwd_gated(const gdn_fwd_desc* d, const void* q, const void*
     if (!state_out || state_out == state_in) return GDN_OK;
     hipError_t e = gdn::launch_state_copy(state_in, state_out, nstate,
                                           static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return launched(e);
   }
   if (!q || !k || !v || !o) return GDN_ERR_INVALID_ARG;
   const void* a16[] = {q, k, v, o};
@@ -486,7 +505,7 @@ gdn_status gdn_chunk_fwd_gated(const gdn_fwd_desc* d, const void* q, const void*
   a.A_log = gt->A_log; a.dt_bias = gt->dt_bias;
   hipError_t e = gdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  return launched(e);
 }
 
 gdn_status gdn_chunk_fwd_varlen(const gdn_varlen_desc* d, const int64_t* cu_seqlens,
@@ -520,7 +539,7 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_varlen_desc* d, const int64_t* cu_seql
     if (!state_out || state_out == state_in) return GDN_OK;
     hipError_t e = gdn::launch_state_copy(state_in, state_out, heads * d->d_k * d->d_v,
                                           static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return launched(e);
   }
   st = check_pointers(d->total_T, heads, d->H_k, d->H_v, d->d_k, d->d_v, d->io_dtype,
                       d->gate_dtype, d->gate_mode, q, k, v, beta_or_b, w, g, state_in, state_out,
@@ -536,7 +555,7 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_varlen_desc* d, const int64_t* cu_seql
   a.state_in = state_in; a.state_out = state_out; a.o = o;
   hipError_t e = gdn::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return GDN_ERR_UNSUPPORTED;
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  return launched(e);
 }
 
 gdn_status gdn_chunk_fwd_varlen_save(const gdn_varlen_desc* d, const int64_t* cu_seqlens,
@@ -693,7 +712,7 @@ gdn_status gdn_short_conv(const gdn_conv_desc* d, const int64_t* cu_seqlens, con
   a.x = x; a.w = conv_w; a.s_in = conv_state_in; a.s_out = conv_state_out;
   a.q = q; a.k = k; a.v = v;
   hipError_t e = gdn::launch_short_conv(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  return launched(e);
 }
 
 gdn_status gdn_gates(const gdn_gate_desc* d, const void* a_raw, const void* b_raw,
@@ -747,7 +766,7 @@ gdn_status gdn_gates(const gdn_gate_desc* d, const void* a_raw, const void* b_ra
   a.a = a_raw; a.b = b_raw; a.w_raw = w_raw; a.A_log = A_log; a.dt_bias = dt_bias;
   a.g = g; a.beta = beta_or_b; a.w = w;
   hipError_t e = gdn::launch_gates(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  return launched(e);
 }
 
 gdn_status gdn_output_gate(const gdn_norm_desc* d, const void* o, const void* z,
@@ -779,7 +798,25 @@ gdn_status gdn_output_gate(const gdn_norm_desc* d, const void* o, const void* z,
   a.io = to_dtype(d->io_dtype); a.eps = d->eps;
   a.o = o; a.z = z; a.weight = weight; a.y = y;
   hipError_t e = gdn::launch_output_gate(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  return launched(e);
+}
+
+gdn_status gdn_check_selftest(float* out64, void* stream) {
+#ifdef GDN_CHECK
+  if (!out64) return GDN_ERR_INVALID_ARG;
+  unsigned long long before = (unsigned long long)gdn::check_violations_decode() +
+                              gdn::check_violations_chunk() + gdn::check_violations_chunk_sb() +
+                              gdn::check_violations_backward();
+  (void)before;   // whatever an earlier call left is cleared first
+  if (gdn::launch_check_selftest(out64, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GDN_ERR_HIP;
+  const unsigned v = gdn::check_violations_chunk_sb();
+  return v == 64u ? GDN_OK : GDN_ERR_CHECK;
+#else
+  (void)out64;
+  (void)stream;
+  return GDN_ERR_UNSUPPORTED;
+#endif
 }
 
 gdn_status gdn_decode_step(const gdn_decode_desc* d, const void* q, const void* k,
@@ -803,7 +840,7 @@ gdn_status gdn_decode_step(const gdn_decode_desc* d, const void* q, const void* 
   a.q = q; a.k = k; a.v = v; a.b = beta_or_b; a.w = w; a.g = g;
   a.state = state; a.o = o;
   hipError_t e = gdn::launch_decode(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  return launched(e);
 }
 
 }  // extern "C"

@@ -16,6 +16,53 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
+// Debug build (-DGDN_CHECK, libgdn_check.so).  A kernel first fills its LDS
+// with 0xFF bytes, a NaN in fp32, bf16 and fp16, so that a read of LDS that
+// nothing wrote reaches the outputs as NaN; and every LDS access through the
+// checked helpers (lds_check) is compared with the kernel's static LDS size.
+// An access past the end is counted in the module's device counter, which
+// the C ABI of that build reads after each launch (take_check_violations).
+// In the normal build both helpers compile to nothing.
+// ---------------------------------------------------------------------------
+#ifdef GDN_CHECK
+static __device__ unsigned int g_check_violations;
+__device__ __forceinline__ void lds_check(const void* p, int bytes) {
+#if __HIP_DEVICE_COMPILE__   // (the builtins exist only in the device pass)
+  if (__builtin_amdgcn_is_shared((const __attribute__((address_space(0))) void*)p)) {
+    const auto lp = (const __attribute__((address_space(3))) char*)p;
+    const uint32_t off = (uint32_t)(uintptr_t)lp;
+    if (off + (uint32_t)bytes > __builtin_amdgcn_groupstaticsize())
+      atomicAdd(&g_check_violations, 1u);
+  }
+#else
+  (void)p; (void)bytes;
+#endif
+}
+// A condition the caller's indices must meet (counted when they do not).
+__device__ __forceinline__ void check_true(bool ok) {
+  if (!ok) atomicAdd(&g_check_violations, 1u);
+}
+__device__ __forceinline__ void lds_nan_fill(void* base, int bytes) {
+  uint32_t* w = static_cast<uint32_t*>(base);
+  for (int i = (int)threadIdx.x; i < bytes / 4; i += (int)blockDim.x) w[i] = 0xFFFFFFFFu;
+  __syncthreads();
+}
+// Host side: the module's count since the last call (all its work finished),
+// reset to zero; ~0u if the counter cannot be read.
+static inline unsigned take_check_violations() {
+  unsigned v = 0, z = 0;
+  if (hipDeviceSynchronize() != hipSuccess) return ~0u;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_violations), sizeof v) != hipSuccess) return ~0u;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_check_violations), &z, sizeof z) != hipSuccess) return ~0u;
+  return v;
+}
+#else
+__device__ __forceinline__ void lds_check(const void*, int) {}
+__device__ __forceinline__ void check_true(bool) {}
+__device__ __forceinline__ void lds_nan_fill(void*, int) {}
+#endif
+
+// ---------------------------------------------------------------------------
 // Scalar conversions.  bf16 -> fp32 is exact; fp32 -> bf16 rounds to nearest
 // even (v_cvt_pk_bf16_f32 on gfx950).
 // ---------------------------------------------------------------------------

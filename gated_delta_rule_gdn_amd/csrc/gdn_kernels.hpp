@@ -122,6 +122,18 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_chunk_fwd(const ChunkArgs& a, hipStream_t stream);
 // bf16-operand sub-block variant (called by launch_chunk_fwd).
 hipError_t launch_chunk_fwd_sb(const ChunkArgs& a, hipStream_t stream);
+
+#ifdef GDN_CHECK
+// Debug build: LDS accesses out of range counted by each module's kernels
+// since the previous call (after all work on the device has finished).
+unsigned check_violations_decode();
+unsigned check_violations_chunk();
+unsigned check_violations_chunk_sb();
+unsigned check_violations_backward();
+// One block: out[l] = never-written LDS word l, and one counted (unmade)
+// access past the kernel's LDS per lane (64 in all).
+hipError_t launch_check_selftest(float* out, hipStream_t stream);
+#endif
 // state_out = state_in (or 0 when state_in is NULL) for n floats; used when
 // there are no tokens to process.
 hipError_t launch_state_copy(const float* state_in, float* state_out, int64_t n,

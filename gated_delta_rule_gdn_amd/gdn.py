@@ -17,9 +17,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP = 0, 1, 2, 3
+GDN_ERR_CHECK = 4   # the debug library libgdn_check.so only
 GDN_F32, GDN_BF16 = 0, 1
 GDN_GATES_SCALAR, GDN_GATES_CHANNEL = 0, 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class GdnFwdDesc(ctypes.Structure):
@@ -148,6 +149,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_output_gate.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_check_selftest.argtypes = [vp, vp]
+    lib.gdn_check_selftest.restype = ctypes.c_int
     lib.gdn_abi_version.argtypes = []
     lib.gdn_abi_version.restype = ctypes.c_int
     if lib.gdn_abi_version() != ABI_VERSION:
@@ -164,6 +167,14 @@ def status_string(status: int) -> str:
 
 def abi_version() -> int:
     return lib.gdn_abi_version()
+
+
+def check_selftest(out64, stream=None) -> int:
+    """gdn_check_selftest: the raw status (GDN_OK from the debug library when
+    its LDS checks fire, GDN_ERR_UNSUPPORTED from libgdn.so); out64 is a
+    64-element fp32 device tensor."""
+    _check(out64, "out64", shape=(64,), dtype=torch.float32)
+    return lib.gdn_check_selftest(_ptr(out64), _stream(stream))
 
 
 _DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}

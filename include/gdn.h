@@ -53,19 +53,25 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
+#define GDN_ABI_VERSION 9  /* 2: adds gdn_chunk_fwd_varlen; 3: adds gdn_short_conv,
                               gdn_gates, gdn_output_gate; 4: adds gdn_backward;
                               5: adds gdn_backward_varlen; 6: adds
                               gdn_backward_noalloc; 7: adds gdn_chunk_fwd_gated;
                               8: adds gdn_chunk_fwd_save, gdn_backward_saved and
                               their packed forms gdn_chunk_fwd_varlen_save,
-                              gdn_backward_varlen_saved */
+                              gdn_backward_varlen_saved; 9: adds
+                              GDN_ERR_CHECK and gdn_check_selftest */
 
 typedef enum gdn_status {
   GDN_OK = 0,
   GDN_ERR_INVALID_ARG = 1, /* NULL/misaligned/overlapping pointer, bad shape  */
   GDN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement      */
-  GDN_ERR_HIP = 3          /* the HIP runtime reported an error at launch      */
+  GDN_ERR_HIP = 3,         /* the HIP runtime reported an error at launch      */
+  GDN_ERR_CHECK = 4        /* debug build libgdn_check.so only (-DGDN_CHECK):
+                              a kernel of the call accessed LDS outside its
+                              layout; that build waits for every launch to
+                              finish and reads its device counters, which the
+                              normal libgdn.so never does */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -556,6 +562,17 @@ typedef struct gdn_norm_desc {
  */
 gdn_status gdn_output_gate(const gdn_norm_desc* desc, const void* o, const void* z,
                            const float* weight, void* y, void* stream);
+
+/* Self-test of the debug build libgdn_check.so (not an operation of the
+ * method: it proves that build's LDS checks fire).  One small kernel on
+ * `stream` writes to out64 (64 fp32, device memory, caller-owned) what it
+ * reads from LDS that it never wrote, and computes (without making) one
+ * address past the end of its LDS per lane, which the check must count.
+ * Returns GDN_OK when the count is exactly 64 (the caller then expects
+ * out64 to hold NaN, the fill pattern), GDN_ERR_CHECK otherwise; waits for
+ * the kernel.  NULL out64: GDN_ERR_INVALID_ARG.  The normal libgdn.so
+ * returns GDN_ERR_UNSUPPORTED and touches nothing. */
+gdn_status gdn_check_selftest(float* out64, void* stream);
 
 /* Static, never-NULL description of a status code. */
 const char* gdn_status_string(gdn_status s);

@@ -26,7 +26,8 @@ def test_header_declares_expected_entry_points():
          "gdn_backward_workspace_size", "gdn_backward_varlen",
          "gdn_backward_varlen_workspace_size", "gdn_backward_noalloc",
          "gdn_backward_noalloc_max_bytes", "gdn_chunk_fwd_gated", "gdn_chunk_fwd_save",
-         "gdn_backward_saved", "gdn_chunk_fwd_varlen_save", "gdn_backward_varlen_saved"])
+         "gdn_backward_saved", "gdn_chunk_fwd_varlen_save", "gdn_backward_varlen_saved",
+         "gdn_check_selftest"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,9 +39,25 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(gdn.lib, name)
 
 
+def test_check_library_exports_every_declared_symbol():
+    """The debug twin (-DGDN_CHECK) has the same ABI; loaded here without any
+    GPU call."""
+    path = os.path.join(os.path.dirname(gdn.gdn.LIB_PATH), "libgdn_check.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(gdn_\w+)$", out, flags=re.M))
+    assert set(_declared_functions()) <= exported
+    lib = ctypes.CDLL(path)
+    lib.gdn_abi_version.restype = ctypes.c_int
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    assert lib.gdn_abi_version() == gdn.abi_version()
+    assert lib.gdn_status_string(4).startswith(b"GDN_ERR_CHECK")
+
+
 def test_version_and_status_strings():
-    assert gdn.abi_version() == 8
-    for st in range(4):
+    assert gdn.abi_version() == 9
+    for st in range(5):
         s = gdn.status_string(st)
         assert s.startswith("GDN_")
     assert "UNKNOWN" in gdn.status_string(99)
