@@ -286,10 +286,17 @@ __global__ __launch_bounds__(kSbThreads, 1) void chunk_fwd_sb_kernel(Params p) {
   // L2).  Packed sequences: workgroups start in dispatch order with the
   // longest sequence first (ties by index), so that the short ones fill in
   // behind; the rank is computed here when there are at most kRankMax
-  // sequences.
+  // sequences.  Within each run of 16 workgroups the two slices of a head
+  // are 8 apart, so they too share an XCD while the order stays longest
+  // first.
   const int64_t nwg = (int64_t)gridDim.x;
   int64_t lid = blockIdx.x;
-  if (!p.cu && (nwg & 7) == 0) lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
+  if (!p.cu && (nwg & 7) == 0) {
+    lid = (lid & 7) * (nwg >> 3) + (lid >> 3);
+  } else if (p.cu && NSPLIT == 2 && (nwg & 15) == 0) {
+    const int64_t r = lid & 15;
+    lid = (lid - r) + 2 * (r & 7) + (r >> 3);
+  }
   const int64_t slot_head = lid / NSPLIT;
   const int split = (int)(lid - slot_head * NSPLIT);
   int64_t bidx = slot_head / p.Hv;
